@@ -1,0 +1,125 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that its pins
+catch every one of them.  This shows the pins are sharp enough to trust."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import formats as F
+from oracle import ops as O
+from tests import test_oracle_a8 as A8
+from tests import test_oracle_formats as TF
+from tests import test_oracle_gemv as TG
+from tests import test_oracle_moe as TM
+
+pytestmark = pytest.mark.cpu
+
+
+def _e2m1_wrong_bias(codes):
+    c = np.asarray(codes).astype(np.int64)
+    s, e, m = (c >> 3) & 1, (c >> 1) & 3, c & 1
+    mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e))  # bias dropped
+    return np.where(s == 1, -mag, mag)
+
+
+def _e4m3_fnuz_bias(b):
+    b = np.asarray(b).astype(np.int64)
+    s, e, m = (b >> 7) & 1, (b >> 3) & 15, b & 7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -7, (1.0 + m / 8.0) * np.exp2(e - 8.0))
+    return np.where(s == 1, -mag, mag)
+
+
+def _nvfp4_divides_tensor_scale(w, rows=None):
+    r = O._rows(w, rows)
+    c = F.decode_e2m1(w["codes"][r])
+    s = F.decode_e4m3(w["scales"][r])
+    n, k = c.shape
+    return (c.reshape(n, k // 16, 16) * s[:, :, None]).reshape(n, k) / np.float64(np.float32(w["tensor_scale"]))
+
+
+def _nvfp4_scale_per_32(w, rows=None):
+    r = O._rows(w, rows)
+    c = F.decode_e2m1(w["codes"][r])
+    s = F.decode_e4m3(w["scales"][r])
+    n, k = c.shape
+    idx = np.minimum(np.arange(k) // 32, s.shape[1] - 1)  # wrong block length
+    return c * s[:, idx] * np.float64(np.float32(w["tensor_scale"]))
+
+
+def _q4_no_offset(w, rows=None):
+    r = O._rows(w, rows)
+    q = w["codes"][r].astype(np.float64)
+    d = F.decode_f16(w["scales"][r])
+    n, k = q.shape
+    return (q.reshape(n, k // 32, 32) * d[:, :, None]).reshape(n, k)
+
+
+def _quant_half_away(x):
+    x = np.asarray(x, dtype=np.float32)
+    m, k = x.shape
+    xb = x.reshape(m, k // 32, 32)
+    amax = np.max(np.abs(xb), axis=2)
+    d32 = (amax / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = xb / d32[:, :, None]
+    q = np.where(d32[:, :, None] == 0, 0, np.clip(np.sign(r) * np.floor(np.abs(r) + 0.5), -127, 127)).astype(np.int8)
+    return q.reshape(m, k), d32.astype(np.float16).view(np.uint16), q.astype(np.int32).sum(axis=2)
+
+
+def _router_tie_high(logits, top_k):
+    L = np.asarray(logits, dtype=np.float32)
+    t, e = L.shape
+    ids = np.empty((t, top_k), np.int32)
+    w = np.empty((t, top_k))
+    for i in range(t):
+        order = sorted(range(e), key=lambda j: (-float(L[i, j]), -j))[:top_k]
+        ids[i] = order
+        ex = np.exp(L[i, order].astype(np.float64) - L[i, order].max())
+        w[i] = ex / ex.sum()
+    return ids, w
+
+
+def _swiglu_swapped(h):
+    h = np.asarray(h, dtype=np.float64)
+    i = h.shape[-1] // 2
+    return O.silu(h[..., i:]) * h[..., :i]
+
+
+def _gemv_transposed_x(w, x, rows=None):
+    W = O.dequant(w, rows)
+    X = O.act_values(x)
+    return X[:, ::-1] @ W.T
+
+
+MUTATIONS = [
+    ("e2m1 exponent bias dropped", [(F, "decode_e2m1", _e2m1_wrong_bias), (O, "decode_e2m1", _e2m1_wrong_bias),
+                                    (oracle, "decode_e2m1", _e2m1_wrong_bias)],
+     [TF.test_e2m1_matches_ocp_table, TG.test_ex1_nvfp4_one_block]),
+    ("e4m3 read as the FNUZ bias", [(F, "decode_e4m3", _e4m3_fnuz_bias), (O, "decode_e4m3", _e4m3_fnuz_bias),
+                                    (oracle, "decode_e4m3", _e4m3_fnuz_bias)],
+     [TF.test_e4m3_all_256_against_torch, TG.test_ex6_nvfp4_two_rows_two_blocks_pins_scale_indexing]),
+    ("tensor scale divides", [(O, "dequant_nvfp4", _nvfp4_divides_tensor_scale)],
+     [TG.test_ex1_nvfp4_one_block]),
+    ("NVFP4 block of 32", [(O, "dequant_nvfp4", _nvfp4_scale_per_32)],
+     [TG.test_ex6_nvfp4_two_rows_two_blocks_pins_scale_indexing]),
+    ("Q4_0 offset of 8 dropped", [(O, "dequant_q4_0", _q4_no_offset)],
+     [TG.test_ex3_q4_0_one_block, TG.test_ex8_q4_0_two_rows_two_blocks]),
+    ("activations reversed along k", [(O, "gemv", _gemv_transposed_x), (oracle, "gemv", _gemv_transposed_x)],
+     [TG.test_nonsquare_orientation, TG.test_ex6_nvfp4_two_rows_two_blocks_pins_scale_indexing]),
+    ("quantizer rounds half away from zero", [(O, "quantize_q8_0_act", _quant_half_away),
+                                              (oracle, "quantize_q8_0_act", _quant_half_away)],
+     [A8.test_quantizer_ties_round_half_even]),
+    ("router breaks ties to the higher index", [(O, "route_topk", _router_tie_high),
+                                                (oracle, "route_topk", _router_tie_high)],
+     [TM.test_ex5_router_tie_to_lower_index]),
+    ("gate and up swapped", [(O, "swiglu", _swiglu_swapped), (oracle, "swiglu", _swiglu_swapped)],
+     [TM.test_swiglu_gate_is_first_half]),
+]
+
+
+@pytest.mark.parametrize("name,patches,pins", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_mutation(name, patches, pins, monkeypatch):
+    for mod, attr, fn in patches:
+        monkeypatch.setattr(mod, attr, fn)
+    for pin in pins:
+        with pytest.raises(AssertionError):
+            pin()
