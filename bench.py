@@ -1,0 +1,471 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantized decode GEMV path on one MI355X.
+
+Default workload: one batch-1 decode step of a 9B-class dense MLP with NVFP4
+weights -- fused gate+up GEMV [24576 x 4096] with the SwiGLU epilogue, then
+the down GEMV [4096 x 12288] -- on seeded synthetic weights.  A step is both
+kernels.  The metric is achieved HBM bandwidth over the algorithmic bytes
+(packed codes + scales once, activations in, outputs out).
+
+Measurement:
+  * the weights exist in R copies (>= 1 GiB in total) and step i uses copy
+    i mod R, so no step finds its weights in the 256 MB Infinity Cache or L2;
+  * warmup and timed steps each run as one HIP-graph replay (the pages' decode
+    is one graph replay per token); the timed replay is bracketed by
+    synchronisations and HIP events;
+  * the dominant kernel is timed alone with HIP events around every launch on
+    its own stream, behind a long blocking copy so the GPU never waits on the
+    CPU between launches;
+  * the CPU baseline is the oracle (fp64 numpy) on a bounded sample of rows.
+
+Prints one JSON line.  ``--config`` selects the other workloads (Q8_0, W4A8,
+MoE, prefill) for design measurements.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized GEMV achieved HBM GB/s (% of ~8 TB/s) + µs/call, batch 1"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+ROTATE_BYTES = 1 << 30
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for d in ("moe_expert_gemv_amd/csrc", "include"):
+        for name in sorted(os.listdir(os.path.join(ROOT, d))):
+            with open(os.path.join(ROOT, d, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel: str, launch_bytes_alg: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the summary is missing or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel)
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- workloads
+
+class Workload:
+    name = ""
+    dominant = ""
+    bound = "hbm"
+
+    def step(self, i: int):  # enqueue step i on the current stream
+        raise NotImplementedError
+
+    def dominant_launch(self, i: int):
+        raise NotImplementedError
+
+
+def _copies(unit_bytes: int) -> int:
+    return max(2, int(np.ceil(ROTATE_BYTES / unit_bytes)))
+
+
+class DenseLayer(Workload):
+    """gate+up [2I x H] + SwiGLU, then down [H x I], batch m."""
+
+    def __init__(self, m=1):
+        import torch
+        import moe_expert_gemv_amd as qg
+        import synth
+
+        self.qg = qg
+        self.m = m
+        self.H, self.I = 4096, 12288
+        case = synth.nvfp4_layer_case(m=m)
+        self.case = case
+        gu = qg.qg_pack_nvfp4(case.gate_up["codes"], case.gate_up["scales"])
+        dn = qg.qg_pack_nvfp4(case.down["codes"], case.down["scales"])
+        self.R = _copies(gu.nbytes + dn.nbytes)
+        self.gu = torch.from_numpy(gu).cuda().repeat(self.R, 1)  # R x bytes, each row 256-B aligned
+        self.dn = torch.from_numpy(dn).cuda().repeat(self.R, 1)
+        assert gu.nbytes % 256 == 0 and dn.nbytes % 256 == 0
+        self.x = torch.from_numpy(case.x.view(np.int16).copy()).cuda()
+        self.a = torch.empty((m, self.I), dtype=torch.int16, device="cuda")
+        self.y = torch.empty((m, self.H), dtype=torch.float32, device="cuda")
+        H, I = self.H, self.I
+        # algorithmic bytes: packed codes + scales, activations in, outputs out
+        self.alg_gu = (2 * I) * (H // 2) + (2 * I) * (H // 16) + 2 * m * H + 2 * m * I
+        self.alg_dn = H * (I // 2) + H * (I // 16) + 2 * m * I + 4 * m * H
+        self.alg_step = self.alg_gu + self.alg_dn
+        self.flops_step = 2 * m * (2 * I * H + H * I)
+        self.name = (f"nvfp4 dense decode layer (9B-class): gate+up {2 * I}x{H} + SwiGLU, down {H}x{I}, "
+                     f"bf16 activations, batch {m}")
+        self.dominant = "gate+up GEMV with SwiGLU epilogue"
+        self.dominant_bytes = self.alg_gu
+
+    def _gate_up(self, i):
+        self.qg.qgemv_nvfp4_swiglu(self.gu[i % self.R], 0.01, self.I, self.H, self.x, self.m, self.a, None)
+
+    def step(self, i):
+        self._gate_up(i)
+        self.qg.qgemv_nvfp4(self.dn[i % self.R], 0.01, self.H, self.I, self.a, self.m, self.y)
+
+    def dominant_launch(self, i):
+        self._gate_up(i)
+
+    def cpu_baseline(self, budget_s=12.0):
+        """The oracle on the first rows of both matrices, scaled to GB/s."""
+        import oracle
+        from threadpoolctl import threadpool_limits
+
+        case = self.case
+        H, I, m = self.H, self.I, self.m
+        rows_gu = 0
+        t0 = time.perf_counter()
+        total = 0.0
+        done_bytes = 0
+        chunk = 256
+        with threadpool_limits(limits=1):
+            while time.perf_counter() - t0 < budget_s and rows_gu < I:
+                r = np.arange(rows_gu, min(rows_gu + chunk, I))
+                both = np.concatenate([r, r + I])
+                t1 = time.perf_counter()
+                h = oracle.gemv(case.gate_up, case.x, both)
+                oracle.swiglu_bf16(h)
+                dn_rows = np.arange(min(H, len(r) * H // I + 1))
+                oracle.gemv(case.down, np.zeros((m, I), np.float32), dn_rows)
+                total += time.perf_counter() - t1
+                done_bytes += len(both) * (H // 2 + H // 16) + len(dn_rows) * (I // 2 + I // 16)
+                rows_gu += chunk
+        return {"value": done_bytes / total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"gate+up rows 0..{2 * min(rows_gu, I)} (of {2 * I}) and a proportional share of "
+                          f"down rows, fp64 numpy dequant + dot, {total:.1f} s, 1 thread"}
+
+
+class Q8Gemv(Workload):
+    def __init__(self, m=1):
+        import torch
+        import moe_expert_gemv_amd as qg
+        import synth
+
+        self.qg, self.m = qg, m
+        case = synth.q8_gemv_case(m=m)
+        self.case = case
+        buf = qg.qg_pack_q8_0(case.w["codes"], case.w["scales"])
+        self.R = _copies(buf.nbytes)
+        self.w = torch.from_numpy(buf).cuda().repeat(self.R, 1)
+        self.x = torch.from_numpy(case.x).cuda()
+        self.y = torch.empty((m, 1024), dtype=torch.float32, device="cuda")
+        self.alg_step = 1024 * 1024 + 1024 * 32 * 2 + 4 * m * 1024 * 2
+        self.dominant_bytes = self.alg_step
+        self.flops_step = 2 * m * 1024 * 1024
+        self.name = f"q8_0 GEMV 1024x1024, fp32 activations, batch {m}"
+        self.dominant = "Q8_0 GEMV"
+
+    def step(self, i):
+        self.qg.qgemv_q8_0(self.w[i % self.R], 1024, 1024, self.x, self.m, self.y)
+
+    dominant_launch = step
+
+
+class W4A8Gemv(Workload):
+    def __init__(self, m=1):
+        import torch
+        import moe_expert_gemv_amd as qg
+        import synth
+
+        self.qg, self.m = qg, m
+        self.N, self.K = 17408, 5120
+        case = synth.w4a8_case(m=m)
+        buf = qg.qg_pack_q4_0(case.w["codes"], case.w["scales"])
+        self.R = _copies(buf.nbytes)
+        self.w = torch.from_numpy(buf).cuda().repeat(self.R, 1)
+        self.x = torch.from_numpy(case.x).cuda()
+        K = self.K
+        self.xq = torch.empty((m, K), dtype=torch.int8, device="cuda")
+        self.xd = torch.empty((m, K // 32), dtype=torch.int16, device="cuda")
+        self.xs = torch.empty((m, K // 32), dtype=torch.int32, device="cuda")
+        self.y = torch.empty((m, self.N), dtype=torch.float32, device="cuda")
+        N = self.N
+        self.dominant_bytes = N * K // 2 + N * (K // 32) * 2 + m * (K + K // 32 * 6) + 4 * m * N
+        self.alg_step = self.dominant_bytes + m * K * 4 + m * (K + K // 32 * 6)
+        self.flops_step = 2 * m * N * K
+        self.name = f"q4_0 x q8_0 (W4A8) GEMV {N}x{K} (27B-class), batch {m}"
+        self.dominant = "W4A8 GEMV"
+
+    def step(self, i):
+        self.qg.qg_quantize_q8_0_act(self.x, self.m, self.K, self.xq, self.xd, self.xs)
+        self.dominant_launch(i)
+
+    def dominant_launch(self, i):
+        self.qg.qgemv_q4_0_a8(self.w[i % self.R], self.N, self.K, self.xq, self.xd, self.xs, self.m, self.y)
+
+
+class MoE(Workload):
+    def __init__(self, t=1):
+        import torch
+        import moe_expert_gemv_amd as qg
+        import oracle
+        import synth
+
+        self.qg, self.t = qg, t
+        L = synth.moe_case(t=t)
+        E = L.n_experts + 1
+        H, I = L.hidden, L.inter
+        gs = qg.qg_packed_bytes(qg.QG_NVFP4, 2 * I, H)
+        ds = qg.qg_packed_bytes(qg.QG_NVFP4, H, I)
+        gu = np.concatenate([qg.qg_pack_nvfp4(L.gate_up[e]["codes"], L.gate_up[e]["scales"]) for e in range(E)])
+        dn = np.concatenate([qg.qg_pack_nvfp4(L.down[e]["codes"], L.down[e]["scales"]) for e in range(E)])
+        self.R = _copies(gu.nbytes + dn.nbytes)
+        self.gu = torch.from_numpy(gu).cuda().repeat(self.R, 1)
+        self.dn = torch.from_numpy(dn).cuda().repeat(self.R, 1)
+        self.gs, self.ds = gs, ds
+        self.scales = torch.full((E,), 0.01, dtype=torch.float32, device="cuda")
+        self.L = L
+        # a fresh routing per step (logits drawn per step) so steps touch different experts
+        self.S = 64
+        g = synth.rng(synth.seed_for(4, 900))
+        logits = synth.logits_f32(g, self.S * t, L.n_experts)
+        self.logits = torch.from_numpy(logits).cuda().view(self.S, t, L.n_experts)
+        self.x = torch.from_numpy(L.x.view(np.int16).copy()).cuda()
+        self.ids = torch.empty((t, 8), dtype=torch.int32, device="cuda")
+        self.w = torch.empty((t, 8), dtype=torch.float32, device="cuda")
+        self.y = torch.empty((t, H), dtype=torch.float32, device="cuda")
+        self.descs = []
+        for r in range(self.R):
+            d = qg.QgMoeDesc(n_experts=256, top_k=8, has_shared=1, flags=0, hidden=H, inter=I,
+                             gate_up=self.gu[r].data_ptr(), gate_up_stride=gs, down=self.dn[r].data_ptr(),
+                             down_stride=ds, gate_up_scale=self.scales.data_ptr(),
+                             down_scale=self.scales.data_ptr())
+            self.descs.append(d)
+        self.ws_bytes = qg.moe_workspace_bytes(self.descs[0], t)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        # algorithmic bytes: the active experts' packed weights + activations
+        u = []
+        for s in range(self.S):
+            ids, _ = oracle.route_topk(logits.reshape(self.S, t, -1)[s], 8)
+            u.append(len(set(ids.ravel().tolist())) + 1)
+        self.mean_active = float(np.mean(u))
+        self.alg_step = int(self.mean_active * (2 * I * H * 9 // 16 + H * I * 9 // 16)) + t * (2 * H + 4 * H)
+        self.dominant_bytes = int(self.mean_active * (2 * I * H * 9 // 16)) + t * 2 * H
+        self.flops_step = int(2 * t * 9 * (2 * I * H + H * I))
+        self.name = (f"moe decode (35B-A3B-like): 256 routed + 1 shared experts, hidden {H}, inter {I}, "
+                     f"top-8, {t} token(s), routing drawn per step")
+        self.dominant = "route + grouped expert GEMVs (3 kernels)"
+
+    def step(self, i):
+        qg = self.qg
+        qg.moe_route_topk(self.logits[i % self.S], self.t, 256, 8, self.ids, self.w)
+        qg.moe_gemv_grouped(self.descs[i % self.R], self.x, self.ids, self.w, self.t, self.y, self.ws,
+                            self.ws_bytes)
+
+    dominant_launch = step
+
+
+class Prefill(Workload):
+    def __init__(self, m=512):
+        import torch
+        import moe_expert_gemv_amd as qg
+        import synth
+
+        self.qg, self.m = qg, m
+        self.N, self.K = 12288, 4096
+        case = synth.prefill_case(m=m)
+        buf = qg.qg_pack_nvfp4(case.w["codes"], case.w["scales"])
+        self.R = _copies(buf.nbytes)
+        self.w = torch.from_numpy(buf).cuda().repeat(self.R, 1)
+        self.x = torch.from_numpy(case.x.view(np.int16).copy()).cuda()
+        self.y = torch.empty((m, self.N), dtype=torch.int16, device="cuda")
+        N, K = self.N, self.K
+        self.alg_step = N * K * 9 // 16 + 2 * m * K + 2 * m * N
+        self.dominant_bytes = self.alg_step
+        self.flops_step = 2 * m * N * K
+        self.bound = "mfma" if m >= 96 else "hbm"
+        self.name = f"prefill GEMM: X bf16 [{m}x{K}] x NVFP4 W [{N}x{K}], bf16 out"
+        self.dominant = "prefill MFMA GEMM"
+
+    def step(self, i):
+        self.qg.qgemm_prefill(self.w[i % self.R], 0.01, self.N, self.K, self.x, self.m, self.y)
+
+    dominant_launch = step
+
+
+CONFIGS = {
+    "dense": lambda: DenseLayer(1),
+    "dense-m4": lambda: DenseLayer(4),
+    "q8": lambda: Q8Gemv(1),
+    "w4a8": lambda: W4A8Gemv(1),
+    "w4a8-m4": lambda: W4A8Gemv(4),
+    "moe": lambda: MoE(1),
+    "moe-t4": lambda: MoE(4),
+    "prefill64": lambda: Prefill(64),
+    "prefill128": lambda: Prefill(128),
+    "prefill512": lambda: Prefill(512),
+}
+
+
+# ---------------------------------------------------------------- timing
+
+def _blocker(stream):
+    """Keep the GPU busy ~2 ms so the CPU can queue work ahead of it."""
+    import torch
+
+    with torch.cuda.stream(stream):
+        a = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(6):
+            b.copy_(a)
+    return a, b
+
+
+def time_steps(wl: Workload, steps: int, warmup: int, use_graph: bool):
+    import torch
+
+    stream = torch.cuda.Stream()
+    if use_graph:
+        with torch.cuda.stream(stream):
+            wl.step(0)  # first eager call outside capture
+        torch.cuda.synchronize()
+        gw = torch.cuda.CUDAGraph()
+        gt = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw, stream=stream):
+            for i in range(warmup):
+                wl.step(i)
+        with torch.cuda.graph(gt, stream=stream):
+            for i in range(steps):
+                wl.step(warmup + i)
+        run_w, run_t = gw.replay, gt.replay
+    else:
+        def run_w():
+            for i in range(warmup):
+                wl.step(i)
+
+        def run_t():
+            for i in range(steps):
+                wl.step(warmup + i)
+
+    with torch.cuda.stream(stream):
+        run_w()
+    torch.cuda.synchronize()
+    keep = _blocker(stream)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        run_t()
+        t1.record(stream)
+    torch.cuda.synchronize()
+    del keep
+    return t0.elapsed_time(t1) / steps  # ms per step
+
+
+def time_dominant(wl: Workload, launches: int):
+    """Average duration of the dominant kernel: HIP events around each launch
+    on its own stream, queued behind a blocker so launches run back to back."""
+    import torch
+
+    stream = torch.cuda.Stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    with torch.cuda.stream(stream):
+        wl.dominant_launch(0)
+    torch.cuda.synchronize()
+    keep = _blocker(stream)
+    with torch.cuda.stream(stream):
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            wl.dominant_launch(i + 1)
+            b.record(stream)
+    torch.cuda.synchronize()
+    del keep
+    d = np.array([a.elapsed_time(b) for a, b in ev])  # ms
+    return float(np.mean(d)), float(np.median(d))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="dense", choices=sorted(CONFIGS))
+    ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of a graph replay")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode GEMV path runs on a single device (the "
+              "multi-GPU sharding is a design note, not built); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import moe_expert_gemv_amd as qg
+
+    qg.lib()
+    print(f"[bench] building workload {args.config}", file=sys.stderr, flush=True)
+    wl = CONFIGS[args.config]()
+    print(f"[bench] {wl.name}; {getattr(wl, 'R', 1)} weight copies; timing", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    ms = time_steps(wl, args.steps, args.warmup, not args.no_graph)
+    dom_mean, dom_median = time_dominant(wl, max(20, min(args.steps, 200)))
+    value = wl.alg_step / (ms * 1e-3) / 1e9
+
+    if wl.bound == "mfma":
+        achieved = wl.flops_step / (dom_mean * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    else:
+        achieved = wl.dominant_bytes / (dom_mean * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    roof["traffic"] = traffic_from_profile(args.config, wl.dominant_bytes)
+    roof["kernel"] = wl.dominant
+    roof["us_per_launch"] = dom_mean * 1e3
+    roof["us_per_launch_median"] = dom_median * 1e3
+    roof["alg_bytes_per_launch"] = wl.dominant_bytes
+
+    cpu = None
+    if not args.no_cpu_baseline and hasattr(wl, "cpu_baseline"):
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = wl.cpu_baseline(args.cpu_budget)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "us_per_step": ms * 1e3,
+        "pct_of_peak_hbm": 100.0 * value / PEAK_HBM_GBS,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generators; random codes/scales of the stated distributions)",
+        "config": {"workload": wl.name, "alg_bytes_per_step": wl.alg_step,
+                   "weight_copies_rotated": getattr(wl, "R", 1),
+                   "graph_replay": not args.no_graph, "source_digest": source_digest()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

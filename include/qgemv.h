@@ -1,0 +1,257 @@
+/*
+ * qgemv.h -- C ABI of the block-quantized GEMV library for AMD Instinct MI355X
+ * (gfx950 / CDNA4).
+ *
+ * The operation: the decode-step matrix-vector product y = W x over weights
+ * stored in a block-scaled quantized format, with the dequantization fused
+ * into the weight load.  The source pages build their decode on exactly this
+ * (LumenLLM README, feature list: GEMVs for decode and native NVFP4/FP8
+ * kernels; bw24 README, feature list: the NVFP4 (W4) decode path with a
+ * split-plane repack, a dp4a matvec and per-shape dispatch; memra README,
+ * feature list: NVFP4 / Q4_0 / Q8_0 split-plane matvecs).  Formats:
+ *
+ *   NVFP4  16-element blocks; E2M1 codes (OCP MX v1.0), one E4M3 scale per
+ *          block (OCP OFP8 v1.0, the variant without infinities), one fp32
+ *          scale per tensor.  w = e2m1(c) * e4m3(s_b) * s_t.
+ *   Q8_0   32-element blocks; int8 codes, one fp16 scale.  w = d * q.
+ *   Q4_0   32-element blocks; 4-bit codes, one fp16 scale.  w = d * (q - 8).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Logical weight layout is row-major W[n][k]; row r produces output r.
+ *    Activations are token-major x[m][k]; outputs y[m][n].
+ *  - Ownership: the caller allocates and frees every buffer.  The library
+ *    allocates nothing and keeps no state between calls (besides an immutable
+ *    device-property cache), so calls are thread-safe and stream-ordered.
+ *  - Pointers named "device" must point to device memory of the current HIP
+ *    device; "host" pointers to host memory.  Device pointers must be 16-byte
+ *    aligned, packed weight buffers 256-byte aligned.  Inputs never alias
+ *    outputs.
+ *  - stream: a hipStream_t passed as void* (NULL = the default stream).  Every
+ *    device entry point only enqueues work: no host synchronisation and no
+ *    allocation, so calls may be captured into a HIP graph.
+ *  - Errors: every argument check runs on the host before any HIP call; a
+ *    failed check returns a negative QG_E* status and enqueues nothing.  A
+ *    launch failure returns QG_EHIP (qg_last_hip_error() holds the hipError_t
+ *    of the most recent failure).  Faults inside a kernel surface at the
+ *    caller's next synchronisation, as for any HIP kernel.
+ *  - k must be a positive multiple of 32 for every format (NVFP4's 16-element
+ *    blocks come in pairs per 16-byte load); n >= 1.
+ *  - Reductions run in a fixed order that depends on k only, never on m, the
+ *    grid or timing: results are bitwise reproducible, and token t of a
+ *    batch-m call equals, bitwise, a batch-1 call on token t.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+#define QG_OK            0
+#define QG_EINVAL       (-1) /* null pointer, bad shape, misalignment, bad code */
+#define QG_EUNSUPPORTED (-2) /* shape outside what the kernels implement */
+#define QG_ENOSPC       (-4) /* destination or workspace buffer too small */
+#define QG_EHIP         (-5) /* HIP runtime or launch error */
+
+/* ---------------------------------------------------------------- formats */
+#define QG_NVFP4 1
+#define QG_Q8_0  2
+#define QG_Q4_0  3
+
+#define QG_ABI_VERSION    1
+#define QG_LAYOUT_VERSION 1  /* packed device layout described below */
+#define QG_MAX_M          16 /* largest token count of the GEMV entry points */
+
+/* ABI and packed-layout versions this library implements. */
+int qg_abi_version(void);
+int qg_layout_version(void);
+/* Static English text for a status code (never NULL). */
+const char* qg_status_string(int status);
+/* hipError_t of the most recent QG_EHIP return on any thread (0 if none). */
+int qg_last_hip_error(void);
+
+/* ------------------------------------------------------ packed layout V1
+ * The "split-plane repack" of the pages (bw24 README and memra README, feature
+ * lists): codes and scales live in separate planes so that each lane streams
+ * 16 contiguous code bytes per load and the scales follow in a plane of their
+ * own.  A packed matrix is one buffer:
+ *
+ *   [codes plane][pad to 256 B][scale plane][pad to 256 B]
+ *
+ *   NVFP4  codes: n rows of k/2 bytes; byte j of a row holds element 2j in its
+ *          low nibble and element 2j+1 in its high nibble.
+ *          scales: n rows of k/16 E4M3 bytes, block b covering elements
+ *          [16b, 16b+16).
+ *   Q4_0   codes: n rows of k/2 bytes; block b occupies bytes [16b, 16b+16)
+ *          and byte i of a block holds element 32b+i (low nibble) and element
+ *          32b+16+i (high nibble).
+ *          scales: n rows of k/32 fp16 bit patterns.
+ *   Q8_0   codes: n rows of k int8.  scales: n rows of k/32 fp16 bit patterns.
+ *
+ * Every row of every plane starts 16-byte aligned when k % 32 == 0.
+ */
+
+/* Bytes of a packed matrix (0 if fmt/n/k are invalid). */
+size_t qg_packed_bytes(int fmt, int64_t n, int64_t k);
+/* Byte offset of the scale plane inside a packed matrix (0 if invalid). */
+size_t qg_scale_plane_offset(int fmt, int64_t n, int64_t k);
+
+/* Packers: logical host arrays -> packed host buffer (copy it to the device
+ * afterwards).  codes: one code per byte, row-major [n][k] (NVFP4 and Q4_0
+ * codes must be 0..15, else QG_EINVAL).  scales: raw bit patterns, row-major
+ * [n][k/B].  dst: host, dst_bytes >= qg_packed_bytes(), else QG_ENOSPC.
+ * Padding bytes are written as zero.  Exact: unpack(pack(c, s)) == (c, s). */
+int qg_pack_nvfp4(const uint8_t* codes, const uint8_t* scales_e4m3, int64_t n, int64_t k,
+                  void* dst, size_t dst_bytes);
+int qg_pack_q4_0(const uint8_t* codes, const uint16_t* scales_f16, int64_t n, int64_t k,
+                 void* dst, size_t dst_bytes);
+int qg_pack_q8_0(const int8_t* codes, const uint16_t* scales_f16, int64_t n, int64_t k,
+                 void* dst, size_t dst_bytes);
+
+/* Unpackers: the exact inverse of the packers (host -> host). */
+int qg_unpack_nvfp4(const void* src, size_t src_bytes, int64_t n, int64_t k,
+                    uint8_t* codes, uint8_t* scales_e4m3);
+int qg_unpack_q4_0(const void* src, size_t src_bytes, int64_t n, int64_t k,
+                   uint8_t* codes, uint16_t* scales_f16);
+int qg_unpack_q8_0(const void* src, size_t src_bytes, int64_t n, int64_t k,
+                   int8_t* codes, uint16_t* scales_f16);
+
+/* ------------------------------------------------------ dequantization
+ * out[r][c] = the weight value, fp32 (device, [n][k]).  NVFP4: e2m1*e4m3 is
+ * exact and the product with tensor_scale is rounded once (to nearest even);
+ * Q4_0 and Q8_0 values are exact in fp32.  Runs the same device decode code
+ * as the GEMV kernels; meant for verification, not for the decode path.
+ * tensor_scale is ignored for Q4_0 / Q8_0. */
+int qg_dequant(int fmt, const void* w, float tensor_scale, int64_t n, int64_t k,
+               float* out, void* stream);
+
+/* ------------------------------------------------------ fused-dequant GEMVs
+ * y[t][r] = sum_c w[r][c] * x[t][c] for t < m, r < n, fp32 accumulation and
+ * fp32 output.  1 <= m <= QG_MAX_M (speculative verify of up to K+1 tokens
+ * in one batched call, bw24 README, MTP speculative decoding entry; larger m
+ * belongs to qgemm_prefill: QG_EUNSUPPORTED).
+ *
+ * Q8_0 x fp32 activations.  w: device packed Q8_0 [n][k]; x: device fp32
+ * [m][k]; y: device fp32 [m][n]. */
+int qgemv_q8_0(const void* w, int64_t n, int64_t k, const float* x, int64_t m,
+               float* y, void* stream);
+
+/* NVFP4 x bf16 activations.  w: device packed NVFP4 [n][k]; x: device bf16
+ * bit patterns [m][k]; y: device fp32 [m][n].  The tensor scale multiplies
+ * each row sum. */
+int qgemv_nvfp4(const void* w, float tensor_scale, int64_t n, int64_t k,
+                const uint16_t* x, int64_t m, float* y, void* stream);
+
+/* NVFP4 fused gate+up GEMV with the SwiGLU epilogue of an MLP.  w_gu: device
+ * packed NVFP4 [2*inter][k] whose rows [0, inter) are the gate projection and
+ * rows [inter, 2*inter) the up projection.  a: device bf16 [m][inter] with
+ * a = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g)).  h (nullable):
+ * device fp32 [m][2*inter] receives g and u (the plain GEMV outputs). */
+int qgemv_nvfp4_swiglu(const void* w_gu, float tensor_scale, int64_t inter, int64_t k,
+                       const uint16_t* x, int64_t m, uint16_t* a, float* h, void* stream);
+
+/* Q8_0 activation quantizer for the W4A8 path (bw24 README: W4A8 integer
+ * path).  Per 32-element block of x (device fp32 [m][k]): amax = max|x|,
+ * d32 = amax / 127 (correctly rounded fp32), xd = fp16_rne(d32),
+ * xq = clamp(round_half_even(x / d32), -127, 127) (x / d32 correctly
+ * rounded), a zero block gives d = 0 and q = 0; xs = sum of xq over the block.
+ * xq: device int8 [m][k]; xd: device fp16 bits [m][k/32]; xs (nullable):
+ * device int32 [m][k/32].  Any m >= 1. */
+int qg_quantize_q8_0_act(const float* x, int64_t m, int64_t k, int8_t* xq, uint16_t* xd,
+                         int32_t* xs, void* stream);
+
+/* Q4_0 weights x Q8_0 activations, integer block dots (W4A8).  Per block b:
+ * isum_b = sum_j (q_w - 8) * q_x exactly in int32, then
+ * y += fp32(d_w) * fp32(d_x) * isum_b in fp32.  w: device packed Q4_0 [n][k];
+ * xq/xd/xs as produced by qg_quantize_q8_0_act (xs nullable: then the block
+ * sums are recomputed in the kernel); y: device fp32 [m][n]. */
+int qgemv_q4_0_a8(const void* w, int64_t n, int64_t k, const int8_t* xq, const uint16_t* xd,
+                  const int32_t* xs, int64_t m, float* y, void* stream);
+
+/* ------------------------------------------------------ MoE decode
+ * Router: for each of t tokens pick the top_k largest of n_experts fp32
+ * logits (ties to the lower expert index), ordered by logit descending then
+ * index ascending; weights = exp(l - l_max) / sum over the selection (the
+ * softmax renormalised over the chosen experts).  Selection compares the fp32
+ * logits exactly (top-k routing is discontinuous: bw24 README, sigmoid-router
+ * MoE entry).  logits: device fp32 [t][n_experts]; ids: device int32
+ * [t][top_k]; weights: device fp32 [t][top_k].  1 <= t, 1 <= top_k <= 16,
+ * top_k <= n_experts <= 1024.  NaN logits give an unspecified selection. */
+int moe_route_topk(const float* logits, int64_t t, int64_t n_experts, int64_t top_k,
+                   int32_t* ids, float* weights, void* stream);
+
+#define QG_MOE_KEEP_H 1 /* also store the gate/up outputs h in the workspace */
+
+/* One MoE layer's experts.  Routed experts 0..n_experts-1; when has_shared is
+ * 1, expert n_experts is a shared expert that every token uses with weight 1.
+ * Every expert has NVFP4 gate_up [2*inter][hidden] (gate rows first) and down
+ * [hidden][inter]; expert e's packed matrices start at gate_up + e *
+ * gate_up_stride and down + e * down_stride (device, strides in bytes,
+ * multiples of 256, at least qg_packed_bytes of the matrix).  Tensor scales:
+ * device fp32 arrays of n_experts + has_shared entries. */
+typedef struct qg_moe_desc {
+    int32_t n_experts;
+    int32_t top_k;
+    int32_t has_shared;
+    int32_t flags;          /* QG_MOE_KEEP_H, or 0 */
+    int64_t hidden;
+    int64_t inter;
+    const void* gate_up;
+    int64_t gate_up_stride;
+    const void* down;
+    int64_t down_stride;
+    const float* gate_up_scale;
+    const float* down_scale;
+} qg_moe_desc;
+
+/* Workspace bytes moe_gemv_grouped needs for t tokens (0 if d is invalid). */
+size_t moe_workspace_bytes(const qg_moe_desc* d, int64_t t);
+
+/* Workspace layout for t tokens, P = t * (top_k + has_shared) pairs (offsets
+ * in bytes from ws, each region 256-byte aligned, in this order):
+ *   int32 n_groups                 number of active experts incl. shared
+ *   int32 experts[P]               active expert ids ascending, shared last
+ *   int32 offsets[P + 1]           group g owns pairs [offsets[g], offsets[g+1])
+ *   int32 pair_token[P]            token of each pair (ascending within a group)
+ *   int32 pair_slot[P]             slot s < top_k, or top_k for the shared expert
+ *   uint16 a[P][inter]             bf16 SwiGLU outputs per pair
+ *   float h[P][2*inter]            (only with QG_MOE_KEEP_H) gate/up outputs per pair
+ *   float o[P][hidden]             down outputs per pair (unweighted)
+ *   uint32 tickets[...]            internal combine counters
+ * This is the expert-major CSR batching of bw24 README (MoE feature entry):
+ * each active expert's weights are streamed once for all its tokens.
+ *
+ * moe_gemv_grouped: y[t] = sum_s weights[t][s] * down_e(a) + down_shared(a_sh)
+ * with a = bf16_rne(silu(g) * u) and [g; u] = gate_up_e(x[t]), expert e =
+ * ids[t][s]; the sum runs over slots in ascending order, then the shared
+ * expert.  x: device bf16 [t][hidden]; ids/weights: device, as written by
+ * moe_route_topk (ids must be distinct per token and < n_experts); y: device
+ * fp32 [t][hidden]; ws: device, ws_bytes >= moe_workspace_bytes (else
+ * QG_ENOSPC).  1 <= t <= QG_MAX_M, top_k <= 8, hidden and inter multiples of
+ * 32.  Routing never returns to the host (the pages' decode keeps its
+ * per-token host traffic to a few bytes: bw24 README, CUDA-graph decode). */
+int moe_gemv_grouped(const qg_moe_desc* d, const uint16_t* x, const int32_t* ids,
+                     const float* weights, int64_t t, float* y, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* ------------------------------------------------------ small-M prefill GEMM
+ * Y[t][r] = bf16_rne(s_t * sum_c D[r][c] * X[t][c]) with D = e2m1 * e4m3
+ * (exact in bf16), bf16 matrix-core products and fp32 accumulation; the
+ * prefill counterpart of the decode GEMV over the same packed NVFP4 weights
+ * (LumenLLM README, feature list: NVFP4 prefill GEMMs; memra README, known
+ * gaps: prefill keeps bf16 activations rather than W4A4 numerics).
+ * w: device packed NVFP4 [n][k]; x: device bf16 [m][k]; y: device bf16
+ * [m][n].  Any m >= 1. */
+int qgemm_prefill(const void* w, float tensor_scale, int64_t n, int64_t k, const uint16_t* x,
+                  int64_t m, uint16_t* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

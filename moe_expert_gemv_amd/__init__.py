@@ -1,0 +1,271 @@
+"""Python binding of ``libqgemv.so``, the block-quantized GEMV library for
+MI355X (gfx950).
+
+Argument marshalling only: every function here forwards to the C entry point
+of the same name declared in ``include/qgemv.h``; all arithmetic of the path
+runs in the library's HIP kernels (the packers run in its C++ host code).
+Device buffers are torch tensors on the current HIP device (torch provides
+device memory and streams, nothing else); host buffers are numpy arrays.
+
+If the library has not been built, every call raises ``QGLibraryMissing``
+(build it with ``python -m moe_expert_gemv_amd.build``): there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "QGError", "QGLibraryMissing", "LIB_PATH", "lib", "loaded",
+    "QG_NVFP4", "QG_Q8_0", "QG_Q4_0", "QG_MAX_M", "QG_MOE_KEEP_H",
+    "qg_abi_version", "qg_layout_version", "qg_status_string", "qg_packed_bytes",
+    "qg_scale_plane_offset", "qg_pack_nvfp4", "qg_pack_q4_0", "qg_pack_q8_0",
+    "qg_unpack_nvfp4", "qg_unpack_q4_0", "qg_unpack_q8_0", "qg_dequant",
+    "qgemv_q8_0", "qgemv_nvfp4", "qgemv_nvfp4_swiglu", "qg_quantize_q8_0_act",
+    "qgemv_q4_0_a8", "moe_route_topk", "QgMoeDesc", "moe_workspace_bytes",
+    "moe_gemv_grouped", "qgemm_prefill", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
+
+QG_OK, QG_EINVAL, QG_EUNSUPPORTED, QG_ENOSPC, QG_EHIP = 0, -1, -2, -4, -5
+QG_NVFP4, QG_Q8_0, QG_Q4_0 = 1, 2, 3
+QG_MAX_M = 16
+QG_MOE_KEEP_H = 1
+
+
+class QGLibraryMissing(RuntimeError):
+    pass
+
+
+class QGError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        self.status = status
+        text = lib().qg_status_string(status).decode()
+        extra = ""
+        if status == QG_EHIP:
+            extra = f" (hipError {lib().qg_last_hip_error()})"
+        super().__init__(f"{func}: status {status}: {text}{extra}")
+
+
+class QgMoeDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("has_shared", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("hidden", ctypes.c_int64),
+        ("inter", ctypes.c_int64),
+        ("gate_up", ctypes.c_void_p),
+        ("gate_up_stride", ctypes.c_int64),
+        ("down", ctypes.c_void_p),
+        ("down_stride", ctypes.c_int64),
+        ("gate_up_scale", ctypes.c_void_p),
+        ("down_scale", ctypes.c_void_p),
+    ]
+
+
+_P, _I64, _I32, _F32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+# name -> (restype, argtypes); the full exported C ABI
+_SIGNATURES = {
+    "qg_abi_version": (_I32, []),
+    "qg_layout_version": (_I32, []),
+    "qg_status_string": (ctypes.c_char_p, [_I32]),
+    "qg_last_hip_error": (_I32, []),
+    "qg_packed_bytes": (_SZ, [_I32, _I64, _I64]),
+    "qg_scale_plane_offset": (_SZ, [_I32, _I64, _I64]),
+    "qg_pack_nvfp4": (_I32, [_P, _P, _I64, _I64, _P, _SZ]),
+    "qg_pack_q4_0": (_I32, [_P, _P, _I64, _I64, _P, _SZ]),
+    "qg_pack_q8_0": (_I32, [_P, _P, _I64, _I64, _P, _SZ]),
+    "qg_unpack_nvfp4": (_I32, [_P, _SZ, _I64, _I64, _P, _P]),
+    "qg_unpack_q4_0": (_I32, [_P, _SZ, _I64, _I64, _P, _P]),
+    "qg_unpack_q8_0": (_I32, [_P, _SZ, _I64, _I64, _P, _P]),
+    "qg_dequant": (_I32, [_I32, _P, _F32, _I64, _I64, _P, _P]),
+    "qgemv_q8_0": (_I32, [_P, _I64, _I64, _P, _I64, _P, _P]),
+    "qgemv_nvfp4": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P]),
+    "qgemv_nvfp4_swiglu": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P, _P]),
+    "qg_quantize_q8_0_act": (_I32, [_P, _I64, _I64, _P, _P, _P, _P]),
+    "qgemv_q4_0_a8": (_I32, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
+    "moe_route_topk": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "moe_workspace_bytes": (_SZ, [ctypes.POINTER(QgMoeDesc), _I64]),
+    "moe_gemv_grouped": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "qgemm_prefill": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise QGLibraryMissing(
+                f"{LIB_PATH} is not built; run `python -m moe_expert_gemv_amd.build` first")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def loaded() -> bool:
+    return _lib is not None
+
+
+def _check(func: str, status: int) -> None:
+    if status != QG_OK:
+        raise QGError(func, status)
+
+
+# ---------------------------------------------------------------- marshalling
+
+def _dptr(t):
+    """Device pointer of a torch tensor (or None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _hptr(a: np.ndarray):
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError("expected a C-contiguous array")
+    return a.ctypes.data
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ---------------------------------------------------------------- versions / sizes
+
+def qg_abi_version() -> int:
+    return lib().qg_abi_version()
+
+
+def qg_layout_version() -> int:
+    return lib().qg_layout_version()
+
+
+def qg_status_string(status: int) -> str:
+    return lib().qg_status_string(status).decode()
+
+
+def qg_packed_bytes(fmt: int, n: int, k: int) -> int:
+    return lib().qg_packed_bytes(fmt, n, k)
+
+
+def qg_scale_plane_offset(fmt: int, n: int, k: int) -> int:
+    return lib().qg_scale_plane_offset(fmt, n, k)
+
+
+# ---------------------------------------------------------------- packers (host)
+
+def _pack(func, fmt, codes, scales, code_dtype, scale_dtype):
+    codes = np.ascontiguousarray(codes, dtype=code_dtype)
+    scales = np.ascontiguousarray(scales, dtype=scale_dtype)
+    n, k = codes.shape
+    size = qg_packed_bytes(fmt, n, k)
+    if size == 0:
+        raise QGError(func, QG_EINVAL)
+    out = np.empty(size, dtype=np.uint8)
+    _check(func, getattr(lib(), func)(_hptr(codes), _hptr(scales), n, k, _hptr(out), size))
+    return out
+
+
+def qg_pack_nvfp4(codes, scales_e4m3) -> np.ndarray:
+    return _pack("qg_pack_nvfp4", QG_NVFP4, codes, scales_e4m3, np.uint8, np.uint8)
+
+
+def qg_pack_q4_0(codes, scales_f16) -> np.ndarray:
+    return _pack("qg_pack_q4_0", QG_Q4_0, codes, scales_f16, np.uint8, np.uint16)
+
+
+def qg_pack_q8_0(codes, scales_f16) -> np.ndarray:
+    return _pack("qg_pack_q8_0", QG_Q8_0, codes, scales_f16, np.int8, np.uint16)
+
+
+def _unpack(func, buf, n, k, code_dtype, scale_dtype, blk):
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    codes = np.empty((n, k), dtype=code_dtype)
+    scales = np.empty((n, k // blk), dtype=scale_dtype)
+    _check(func, getattr(lib(), func)(_hptr(buf), buf.nbytes, n, k, _hptr(codes), _hptr(scales)))
+    return codes, scales
+
+
+def qg_unpack_nvfp4(buf, n, k):
+    return _unpack("qg_unpack_nvfp4", buf, n, k, np.uint8, np.uint8, 16)
+
+
+def qg_unpack_q4_0(buf, n, k):
+    return _unpack("qg_unpack_q4_0", buf, n, k, np.uint8, np.uint16, 32)
+
+
+def qg_unpack_q8_0(buf, n, k):
+    return _unpack("qg_unpack_q8_0", buf, n, k, np.int8, np.uint16, 32)
+
+
+# ---------------------------------------------------------------- device entry points
+
+def qg_dequant(fmt, w, tensor_scale, n, k, out, stream=None) -> None:
+    _check("qg_dequant", lib().qg_dequant(fmt, _dptr(w), tensor_scale, n, k, _dptr(out), _stream(stream)))
+
+
+def qgemv_q8_0(w, n, k, x, m, y, stream=None) -> None:
+    _check("qgemv_q8_0", lib().qgemv_q8_0(_dptr(w), n, k, _dptr(x), m, _dptr(y), _stream(stream)))
+
+
+def qgemv_nvfp4(w, tensor_scale, n, k, x, m, y, stream=None) -> None:
+    _check("qgemv_nvfp4",
+           lib().qgemv_nvfp4(_dptr(w), tensor_scale, n, k, _dptr(x), m, _dptr(y), _stream(stream)))
+
+
+def qgemv_nvfp4_swiglu(w_gu, tensor_scale, inter, k, x, m, a, h=None, stream=None) -> None:
+    _check("qgemv_nvfp4_swiglu",
+           lib().qgemv_nvfp4_swiglu(_dptr(w_gu), tensor_scale, inter, k, _dptr(x), m, _dptr(a),
+                                    _dptr(h), _stream(stream)))
+
+
+def qg_quantize_q8_0_act(x, m, k, xq, xd, xs=None, stream=None) -> None:
+    _check("qg_quantize_q8_0_act",
+           lib().qg_quantize_q8_0_act(_dptr(x), m, k, _dptr(xq), _dptr(xd), _dptr(xs), _stream(stream)))
+
+
+def qgemv_q4_0_a8(w, n, k, xq, xd, xs, m, y, stream=None) -> None:
+    _check("qgemv_q4_0_a8",
+           lib().qgemv_q4_0_a8(_dptr(w), n, k, _dptr(xq), _dptr(xd), _dptr(xs), m, _dptr(y),
+                               _stream(stream)))
+
+
+def moe_route_topk(logits, t, n_experts, top_k, ids, weights, stream=None) -> None:
+    _check("moe_route_topk",
+           lib().moe_route_topk(_dptr(logits), t, n_experts, top_k, _dptr(ids), _dptr(weights),
+                                _stream(stream)))
+
+
+def moe_workspace_bytes(desc: QgMoeDesc, t: int) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(desc), t)
+
+
+def moe_gemv_grouped(desc: QgMoeDesc, x, ids, weights, t, y, ws, ws_bytes=None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_gemv_grouped",
+           lib().moe_gemv_grouped(ctypes.byref(desc), _dptr(x), _dptr(ids), _dptr(weights), t,
+                                  _dptr(y), _dptr(ws), nbytes, _stream(stream)))
+
+
+def qgemm_prefill(w, tensor_scale, n, k, x, m, y, stream=None) -> None:
+    _check("qgemm_prefill",
+           lib().qgemm_prefill(_dptr(w), tensor_scale, n, k, _dptr(x), m, _dptr(y), _stream(stream)))

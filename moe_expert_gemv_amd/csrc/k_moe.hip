@@ -1,0 +1,466 @@
+// MoE decode on gfx950: softmax top-k router, expert-major grouping, grouped
+// gate/up GEMV with SwiGLU, grouped down GEMV and the weighted combine.
+//
+// The pages batch routed (token, expert) pairs expert-major so that every
+// active expert's weights are streamed once for all its tokens (bw24 README,
+// MoE feature entry: expert-major CSR batching), and keep routing on the device
+// (bw24 README, CUDA-graph decode: a few bytes of host traffic per token).
+// Here a layer is three launches on one stream:
+//   1. k_route_topk       logits -> ids, weights (one wave per token)
+//   2. k_moe_gate_up      every workgroup rebuilds the CSR from ids in LDS (a
+//                         few hundred integer ops), then one (expert group x
+//                         row tile) of the grouped gate/up GEMV + SwiGLU;
+//                         workgroup (0,0) also publishes the CSR and clears the
+//                         combine counters in the workspace
+//   3. k_moe_down         one (row tile x expert group) of the grouped down
+//                         GEMV; the last workgroup to finish a row tile (an
+//                         integer ticket counter, no float atomics) sums the
+//                         routed outputs in slot order plus the shared expert
+// Grids are sized for the worst case (t * top_k + 1 groups); workgroups whose
+// group does not exist return at once.
+#include <hip/hip_runtime.h>
+
+#include "qg_device.hpp"
+#include "qg_gemv_core.hpp"
+#include "qg_internal.hpp"
+#include "qg_layout.hpp"
+
+namespace qg {
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kMaxTokens = QG_MAX_M;
+constexpr int kMaxTopK = 8;
+constexpr int kMaxPairs = kMaxTokens * (kMaxTopK + 1);
+
+// ------------------------------------------------------------------ router
+
+// One wave per token; each lane holds PER lane logits (expert = i*64 + lane).
+template <int PER>
+__global__ __launch_bounds__(kBlock) void k_route_topk(const float* __restrict__ logits, int t, int e,
+                                                       int top_k, int32_t* __restrict__ ids,
+                                                       float* __restrict__ wts) {
+    const int lane = lane_id();
+    const int tok = int(blockIdx.x) * (kBlock / kWave) + int(threadIdx.x) / kWave;
+    if (tok >= t) return;  // uniform per wave
+    float v[PER];
+    bool taken[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int ex = i * kWave + lane;
+        v[i] = ex < e ? logits[int64_t(tok) * e + ex] : 0.f;
+        taken[i] = ex >= e;
+    }
+    float sel_v[16];
+    int sel_i[16];
+    for (int s = 0; s < top_k; ++s) {
+        // lane-local best among the untaken: larger value, then lower index
+        float bv = 0.f;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int ex = i * kWave + lane;
+            if (!taken[i] && (bi == 0x7fffffff || v[i] > bv)) {
+                bv = v[i];
+                bi = ex;
+            }
+        }
+        // wave-wide best, same ordering (ties to the lower index)
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oi = __shfl_xor(bi, off);
+            const bool better = oi != 0x7fffffff &&
+                                (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
+            if (better) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        sel_v[s] = bv;
+        sel_i[s] = bi;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (i * kWave + lane == bi) taken[i] = true;
+    }
+    if (lane == 0) {
+        float ex[16];
+        float sum = 0.f;
+        for (int s = 0; s < top_k; ++s) {
+            ex[s] = expf(sel_v[s] - sel_v[0]);
+            sum += ex[s];
+        }
+        for (int s = 0; s < top_k; ++s) {
+            ids[int64_t(tok) * top_k + s] = sel_i[s];
+            wts[int64_t(tok) * top_k + s] = ex[s] / sum;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ grouping
+
+struct Csr {
+    int n_groups;
+    int experts[kMaxPairs];
+    int offsets[kMaxPairs + 1];
+    int tok[kMaxPairs];
+    int slot[kMaxPairs];
+};
+
+// Expert-major CSR of the t*k routed pairs (pair p = token p/k, slot p%k):
+// active experts ascending, pairs inside an expert in ascending (token, slot)
+// order, then the shared expert with every token.  Ids are clamped into
+// [0, E) so that bad ids can never index outside the expert arrays.
+__device__ void build_csr(const int32_t* __restrict__ ids, int t, int k, int E, int has_shared,
+                          Csr& c, int* s_e, int* s_first) {
+    const int P = t * k;
+    const int tid = int(threadIdx.x);
+    for (int p = tid; p < P; p += kBlock) s_e[p] = min(max(ids[p], 0), E - 1);
+    __syncthreads();
+    for (int p = tid; p < P; p += kBlock) {
+        const int e = s_e[p];
+        int less = 0, before = 0;
+        for (int q = 0; q < P; ++q) {
+            const int eq = s_e[q];
+            less += eq < e;
+            before += (q < p) & (eq == e);
+        }
+        const int rank = less + before;
+        c.tok[rank] = p / k;
+        c.slot[rank] = p % k;
+        s_first[p] = (before == 0) ? less + 1 : 0;  // 1 + offset of the group, or 0
+    }
+    __syncthreads();
+    for (int p = tid; p < P; p += kBlock) {
+        if (s_first[p]) {
+            const int e = s_e[p];
+            int g = 0;
+            for (int q = 0; q < P; ++q) g += (s_first[q] != 0) & (s_e[q] < e);
+            c.experts[g] = e;
+            c.offsets[g] = s_first[p] - 1;
+        }
+    }
+    if (tid == 0) {
+        int U = 0;
+        for (int q = 0; q < P; ++q) U += s_first[q] != 0;
+        c.offsets[U] = P;
+        if (has_shared) {
+            c.experts[U] = E;
+            c.offsets[U + 1] = P + t;
+        }
+        c.n_groups = U + (has_shared ? 1 : 0);
+    }
+    if (has_shared)
+        for (int i = tid; i < t; i += kBlock) {
+            c.tok[P + i] = i;
+            c.slot[P + i] = k;
+        }
+    __syncthreads();
+}
+
+struct MoeArgs {
+    int E, k, has_shared, flags;
+    int H, I;
+    const uint8_t* gate_up;
+    int64_t gu_stride;
+    const uint8_t* down;
+    int64_t dn_stride;
+    const float* gu_scale;
+    const float* dn_scale;
+    int n_tiles_down;  // row tiles of the down projection (= combine counters)
+};
+
+// ------------------------------------------------------------------ gate/up + SwiGLU
+
+// blockIdx.y = expert group, blockIdx.x = tile of a-rows.  Each group of G
+// lanes owns RA a-rows (RA gate rows and the RA matching up rows).
+template <int MT, int G, int RA>
+__global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_t* __restrict__ x,
+                                                        const int32_t* __restrict__ ids, int t,
+                                                        MoeWorkspace ws) {
+    __shared__ Csr c;
+    __shared__ int s_e[kMaxPairs], s_first[kMaxPairs];
+    build_csr(ids, t, A.k, A.E, A.has_shared, c, s_e, s_first);
+    const int tid = int(threadIdx.x);
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
+        const int P = t * (A.k + A.has_shared);
+        if (tid == 0) *ws.n_groups = c.n_groups;
+        for (int i = tid; i < P; i += kBlock) {
+            ws.pair_tok[i] = c.tok[i];
+            ws.pair_slot[i] = c.slot[i];
+        }
+        for (int i = tid; i < c.n_groups; i += kBlock) ws.experts[i] = c.experts[i];
+        for (int i = tid; i <= c.n_groups; i += kBlock) ws.offsets[i] = c.offsets[i];
+        for (int i = tid; i < A.n_tiles_down; i += kBlock) ws.counters[i] = 0;
+    }
+    const int g = int(blockIdx.y);
+    if (g >= c.n_groups) return;
+    const int e = c.experts[g];
+    const int p0 = c.offsets[g];
+    const int mg = c.offsets[g + 1] - p0;
+
+    constexpr int R = 2 * RA;
+    constexpr int kGroups = kWave / G;
+    const int lane = lane_id();
+    const int grp = lane / G, l = lane % G;
+    const int wave = int(blockIdx.x) * (kBlock / kWave) + tid / kWave;
+    const int unit = wave * kGroups + grp;
+    const int I = A.I, H = A.H;
+
+    const uint8_t* w = A.gate_up + int64_t(e) * A.gu_stride;
+    const int64_t soff = scale_plane_offset(QG_NVFP4, 2 * int64_t(I), H);
+    const float s_t = A.gu_scale[e];
+    int rows[R];
+#pragma unroll
+    for (int r = 0; r < RA; ++r) {
+        rows[r] = min(unit * RA + r, I - 1);
+        rows[RA + r] = I + rows[r];
+    }
+    const uint8_t* codes[R];
+    const uint8_t* scales[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        codes[r] = w + int64_t(rows[r]) * (H / 2);
+        scales[r] = w + soff + int64_t(rows[r]) * (H / 16);
+    }
+    const uint16_t* xp[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) xp[i] = x + int64_t(c.tok[p0 + (i < mg ? i : 0)]) * H;
+
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[r][i] = 0.f;
+    nvfp4_partial<R, MT, G>(codes, scales, xp, mg, H / 32, l, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[r][i] = group_sum<G>(acc[r][i]) * s_t;
+    if (l != 0) return;
+#pragma unroll
+    for (int r = 0; r < RA; ++r) {
+        const int row = unit * RA + r;
+        if (row >= I) break;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            if (i < mg) {
+                const int p = p0 + i;
+                const float gv = acc[r][i], uv = acc[RA + r][i];
+                const float act = gv / (1.0f + expf(-gv)) * uv;
+                ws.a[int64_t(p) * I + row] = uint16_t(f32_to_bf16_rne(act));
+                if (ws.h) {
+                    ws.h[int64_t(p) * 2 * I + row] = gv;
+                    ws.h[int64_t(p) * 2 * I + I + row] = uv;
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ down + combine
+
+// blockIdx.x = row tile of the output, blockIdx.y = expert group.
+template <int MT, int G, int R>
+__global__ __launch_bounds__(kBlock) void k_moe_down(MoeArgs A, const float* __restrict__ wts, int t,
+                                                     float* __restrict__ y, MoeWorkspace ws) {
+    __shared__ int s_off[kMaxPairs + 1];
+    __shared__ int s_tok[kMaxPairs];
+    __shared__ int s_pair[kMaxTokens][kMaxTopK + 1];
+    __shared__ int s_last;
+    const int tid = int(threadIdx.x);
+    const int ng = *ws.n_groups;
+    const int g = int(blockIdx.y);
+    if (g >= ng) return;  // uniform per workgroup
+    const int P = t * (A.k + A.has_shared);
+    for (int i = tid; i <= ng; i += kBlock) s_off[i] = ws.offsets[i];
+    for (int i = tid; i < P; i += kBlock) {
+        s_tok[i] = ws.pair_tok[i];
+        s_pair[ws.pair_tok[i]][ws.pair_slot[i]] = i;
+    }
+    __syncthreads();
+    const int e = ws.experts[g];
+    const int p0 = s_off[g];
+    const int mg = s_off[g + 1] - p0;
+
+    constexpr int kGroups = kWave / G;
+    constexpr int kRowsPerTile = (kBlock / kWave) * kGroups * R;
+    const int lane = lane_id();
+    const int grp = lane / G, l = lane % G;
+    const int wave_in_tile = tid / kWave;
+    const int I = A.I, H = A.H;
+    const int row0 = int(blockIdx.x) * kRowsPerTile + (wave_in_tile * kGroups + grp) * R;
+
+    const uint8_t* w = A.down + int64_t(e) * A.dn_stride;
+    const int64_t soff = scale_plane_offset(QG_NVFP4, H, I);
+    const float s_t = A.dn_scale[e];
+    const uint8_t* codes[R];
+    const uint8_t* scales[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = min(row0 + r, H - 1);
+        codes[r] = w + int64_t(row) * (I / 2);
+        scales[r] = w + soff + int64_t(row) * (I / 16);
+    }
+    const uint16_t* xp[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) xp[i] = ws.a + int64_t(p0 + (i < mg ? i : 0)) * I;
+
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[r][i] = 0.f;
+    nvfp4_partial<R, MT, G>(codes, scales, xp, mg, I / 32, l, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[r][i] = group_sum<G>(acc[r][i]) * s_t;
+    if (l == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = row0 + r;
+            if (row < H) {
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+                    if (i < mg) ws.o[int64_t(p0 + i) * H + row] = acc[r][i];
+            }
+        }
+    }
+    // Publish this group's outputs for the tile; the last arrival combines.
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned ticket = atomicAdd(&ws.counters[blockIdx.x], 1u);
+        s_last = (ticket == unsigned(ng - 1));
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const int tile0 = int(blockIdx.x) * kRowsPerTile;
+    for (int idx = tid; idx < t * kRowsPerTile; idx += kBlock) {
+        const int tt = idx / kRowsPerTile;
+        const int row = tile0 + idx % kRowsPerTile;
+        if (row >= H) continue;
+        float sum = 0.f;
+        for (int s = 0; s < A.k; ++s)
+            sum = fmaf(wts[int64_t(tt) * A.k + s], ws.o[int64_t(s_pair[tt][s]) * H + row], sum);
+        if (A.has_shared) sum += ws.o[int64_t(s_pair[tt][A.k]) * H + row];
+        y[int64_t(tt) * H + row] = sum;
+    }
+    if (tid == 0) ws.counters[blockIdx.x] = 0;
+}
+
+inline int pow2_tokens(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16; }
+
+// Row-tile geometry of the down kernel (used by the workspace layout too).
+inline int down_lanes(int64_t I) { return I / 32 >= 64 ? 64 : 16; }
+inline int down_rows_per_tile(int64_t I) {
+    const int G = down_lanes(I);
+    return (kBlock / kWave) * (kWave / G) * 1;
+}
+
+template <int MT, int GU, int GD>
+hipError_t moe_go(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const float* w, int t,
+                  float* y, const MoeWorkspace& ws, hipStream_t s) {
+    constexpr int RA = 2;
+    const int max_groups = t * A.k + (A.has_shared ? 1 : 0);
+    const int a_rows_per_block = (kBlock / kWave) * (kWave / GU) * RA;
+    const dim3 g1((A.I + a_rows_per_block - 1) / a_rows_per_block, max_groups);
+    hipLaunchKernelGGL((k_moe_gate_up<MT, GU, RA>), g1, dim3(kBlock), 0, s, A, x, ids, t, ws);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const dim3 g2(A.n_tiles_down, max_groups);
+    hipLaunchKernelGGL((k_moe_down<MT, GD, 1>), g2, dim3(kBlock), 0, s, A, w, t, y, ws);
+    return hipGetLastError();
+}
+
+template <int MT>
+hipError_t moe_mt(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const float* w, int t,
+                  float* y, const MoeWorkspace& ws, hipStream_t s) {
+    const bool gu_wide = A.H / 32 >= 64, dn_wide = A.I / 32 >= 64;
+    if (gu_wide && dn_wide) return moe_go<MT, 64, 64>(A, x, ids, w, t, y, ws, s);
+    if (gu_wide) return moe_go<MT, 64, 16>(A, x, ids, w, t, y, ws, s);
+    if (dn_wide) return moe_go<MT, 16, 64>(A, x, ids, w, t, y, ws, s);
+    return moe_go<MT, 16, 16>(A, x, ids, w, t, y, ws, s);
+}
+
+}  // namespace
+
+hipError_t launch_route_topk(const float* logits, int64_t t, int e, int top_k, int32_t* ids, float* w,
+                             hipStream_t s) {
+    const dim3 grid(unsigned((t + 3) / 4));
+    const int per = (e + kWave - 1) / kWave;
+    if (per <= 1)
+        hipLaunchKernelGGL(k_route_topk<1>, grid, dim3(kBlock), 0, s, logits, int(t), e, top_k, ids, w);
+    else if (per <= 4)
+        hipLaunchKernelGGL(k_route_topk<4>, grid, dim3(kBlock), 0, s, logits, int(t), e, top_k, ids, w);
+    else
+        hipLaunchKernelGGL(k_route_topk<16>, grid, dim3(kBlock), 0, s, logits, int(t), e, top_k, ids, w);
+    return hipGetLastError();
+}
+
+// Workspace regions, each 256-byte aligned, in the documented order.  With
+// base == nullptr only the size is computed.
+size_t moe_workspace_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, void* base) {
+    const int64_t P = t * (d->top_k + (d->has_shared ? 1 : 0));
+    const int64_t H = d->hidden, I = d->inter;
+    const int64_t tiles = (H + down_rows_per_tile(I) - 1) / down_rows_per_tile(I);
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) {
+        const int64_t at = off;
+        off = align_up(off + bytes, kPlaneAlign);
+        return at;
+    };
+    const int64_t o_ng = take(4);
+    const int64_t o_ex = take(4 * P);
+    const int64_t o_off = take(4 * (P + 1));
+    const int64_t o_tok = take(4 * P);
+    const int64_t o_slot = take(4 * P);
+    const int64_t o_a = take(2 * P * I);
+    const int64_t o_h = (d->flags & QG_MOE_KEEP_H) ? take(4 * P * 2 * I) : -1;
+    const int64_t o_o = take(4 * P * H);
+    const int64_t o_cnt = take(4 * tiles);
+    if (ws && base) {
+        char* b = static_cast<char*>(base);
+        ws->n_groups = reinterpret_cast<int32_t*>(b + o_ng);
+        ws->experts = reinterpret_cast<int32_t*>(b + o_ex);
+        ws->offsets = reinterpret_cast<int32_t*>(b + o_off);
+        ws->pair_tok = reinterpret_cast<int32_t*>(b + o_tok);
+        ws->pair_slot = reinterpret_cast<int32_t*>(b + o_slot);
+        ws->a = reinterpret_cast<uint16_t*>(b + o_a);
+        ws->h = o_h >= 0 ? reinterpret_cast<float*>(b + o_h) : nullptr;
+        ws->o = reinterpret_cast<float*>(b + o_o);
+        ws->counters = reinterpret_cast<uint32_t*>(b + o_cnt);
+        ws->o_scratch = ws->o;
+    }
+    return size_t(off);
+}
+
+hipError_t launch_moe(const qg_moe_desc* d, const uint16_t* x, const int32_t* ids, const float* w,
+                      int t, float* y, const MoeWorkspace& ws, hipStream_t s) {
+    MoeArgs A;
+    A.E = d->n_experts;
+    A.k = d->top_k;
+    A.has_shared = d->has_shared ? 1 : 0;
+    A.flags = d->flags;
+    A.H = int(d->hidden);
+    A.I = int(d->inter);
+    A.gate_up = static_cast<const uint8_t*>(d->gate_up);
+    A.gu_stride = d->gate_up_stride;
+    A.down = static_cast<const uint8_t*>(d->down);
+    A.dn_stride = d->down_stride;
+    A.gu_scale = d->gate_up_scale;
+    A.dn_scale = d->down_scale;
+    A.n_tiles_down = int((d->hidden + down_rows_per_tile(d->inter) - 1) / down_rows_per_tile(d->inter));
+    switch (pow2_tokens(t)) {
+        case 1: return moe_mt<1>(A, x, ids, w, t, y, ws, s);
+        case 2: return moe_mt<2>(A, x, ids, w, t, y, ws, s);
+        case 4: return moe_mt<4>(A, x, ids, w, t, y, ws, s);
+        case 8: return moe_mt<8>(A, x, ids, w, t, y, ws, s);
+        default: return moe_mt<16>(A, x, ids, w, t, y, ws, s);
+    }
+}
+
+}  // namespace qg

@@ -1,0 +1,148 @@
+// The C entry points: argument validation on the host, then one launch (or a
+// short fixed sequence of launches) on the caller's stream.  Nothing here
+// allocates, synchronises or keeps per-call state.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "qg_internal.hpp"
+#include "qg_layout.hpp"
+#include "qgemv.h"
+
+namespace qg {
+
+extern std::atomic<int> g_last_hip_error;
+
+void record_hip_error(hipError_t e) { g_last_hip_error.store(int(e)); }
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+inline int finish(hipError_t e) {
+    if (e == hipSuccess) return QG_OK;
+    record_hip_error(e);
+    return QG_EHIP;
+}
+
+// Checks shared by the GEMV entry points.
+inline int check_gemv(const void* w, int64_t n, int64_t k, const void* x, int64_t m, const void* y) {
+    if (!w || !x || !y) return QG_EINVAL;
+    if (!aligned(w, 256) || !aligned(x, 16) || !aligned(y, 16)) return QG_EINVAL;
+    if (!valid_shape(n, k) || m < 1) return QG_EINVAL;
+    if (m > QG_MAX_M) return QG_EUNSUPPORTED;
+    return QG_OK;
+}
+
+}  // namespace
+}  // namespace qg
+
+using namespace qg;
+
+extern "C" {
+
+int qg_dequant(int fmt, const void* w, float tensor_scale, int64_t n, int64_t k, float* out,
+               void* stream) {
+    if (!valid_fmt(fmt) || !w || !out || !aligned(w, 256) || !aligned(out, 16)) return QG_EINVAL;
+    if (!valid_shape(n, k)) return QG_EINVAL;
+    return finish(launch_dequant(fmt, static_cast<const uint8_t*>(w), tensor_scale, n, k, out,
+                                 as_stream(stream)));
+}
+
+int qgemv_q8_0(const void* w, int64_t n, int64_t k, const float* x, int64_t m, float* y,
+               void* stream) {
+    if (int st = check_gemv(w, n, k, x, m, y)) return st;
+    return finish(launch_gemv_q8_0(static_cast<const uint8_t*>(w), n, k, x, int(m), y,
+                                   as_stream(stream)));
+}
+
+int qgemv_nvfp4(const void* w, float tensor_scale, int64_t n, int64_t k, const uint16_t* x,
+                int64_t m, float* y, void* stream) {
+    if (int st = check_gemv(w, n, k, x, m, y)) return st;
+    return finish(launch_gemv_nvfp4(static_cast<const uint8_t*>(w), tensor_scale, n, k, x, int(m), y,
+                                    as_stream(stream)));
+}
+
+int qgemv_nvfp4_swiglu(const void* w_gu, float tensor_scale, int64_t inter, int64_t k,
+                       const uint16_t* x, int64_t m, uint16_t* a, float* h, void* stream) {
+    if (inter < 1 || inter > (int64_t(1) << 30)) return QG_EINVAL;
+    if (int st = check_gemv(w_gu, 2 * inter, k, x, m, a)) return st;
+    if (h && !aligned(h, 16)) return QG_EINVAL;
+    return finish(launch_gemv_nvfp4_swiglu(static_cast<const uint8_t*>(w_gu), tensor_scale, inter, k,
+                                           x, int(m), a, h, as_stream(stream)));
+}
+
+int qg_quantize_q8_0_act(const float* x, int64_t m, int64_t k, int8_t* xq, uint16_t* xd,
+                         int32_t* xs, void* stream) {
+    if (!x || !xq || !xd) return QG_EINVAL;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xd, 2) || (xs && !aligned(xs, 4)))
+        return QG_EINVAL;
+    if (m < 1 || !valid_shape(1, k) || m > (int64_t(1) << 31) / (k / 32)) return QG_EINVAL;
+    return finish(launch_quantize_q8_0(x, m, k, xq, xd, xs, as_stream(stream)));
+}
+
+int qgemv_q4_0_a8(const void* w, int64_t n, int64_t k, const int8_t* xq, const uint16_t* xd,
+                  const int32_t* xs, int64_t m, float* y, void* stream) {
+    if (int st = check_gemv(w, n, k, xq, m, y)) return st;
+    if (!xd || !aligned(xd, 2) || (xs && !aligned(xs, 4))) return QG_EINVAL;
+    return finish(launch_gemv_q4_0_a8(static_cast<const uint8_t*>(w), n, k, xq, xd, xs, int(m), y,
+                                      as_stream(stream)));
+}
+
+int moe_route_topk(const float* logits, int64_t t, int64_t n_experts, int64_t top_k, int32_t* ids,
+                   float* weights, void* stream) {
+    if (!logits || !ids || !weights) return QG_EINVAL;
+    if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(weights, 4)) return QG_EINVAL;
+    if (t < 1 || t > (int64_t(1) << 24) || top_k < 1 || n_experts < top_k) return QG_EINVAL;
+    if (top_k > 16 || n_experts > 1024) return QG_EUNSUPPORTED;
+    return finish(launch_route_topk(logits, t, int(n_experts), int(top_k), ids, weights,
+                                    as_stream(stream)));
+}
+
+static int check_moe_desc(const qg_moe_desc* d) {
+    if (!d || !d->gate_up || !d->down || !d->gate_up_scale || !d->down_scale) return QG_EINVAL;
+    if (d->n_experts < 1 || d->top_k < 1 || d->top_k > d->n_experts) return QG_EINVAL;
+    if (d->has_shared != 0 && d->has_shared != 1) return QG_EINVAL;
+    if (d->flags & ~QG_MOE_KEEP_H) return QG_EINVAL;
+    if (!valid_shape(2 * d->inter, d->hidden) || !valid_shape(d->hidden, d->inter)) return QG_EINVAL;
+    if (d->top_k > 8) return QG_EUNSUPPORTED;
+    if (!aligned(d->gate_up, 256) || !aligned(d->down, 256)) return QG_EINVAL;
+    if (d->gate_up_stride % 256 || d->down_stride % 256) return QG_EINVAL;
+    if (d->gate_up_stride < int64_t(packed_bytes(QG_NVFP4, 2 * d->inter, d->hidden))) return QG_EINVAL;
+    if (d->down_stride < int64_t(packed_bytes(QG_NVFP4, d->hidden, d->inter))) return QG_EINVAL;
+    if (d->hidden > (int64_t(1) << 20) || d->inter > (int64_t(1) << 20)) return QG_EUNSUPPORTED;
+    return QG_OK;
+}
+
+size_t moe_workspace_bytes(const qg_moe_desc* d, int64_t t) {
+    if (check_moe_desc(d) != QG_OK || t < 1 || t > QG_MAX_M) return 0;
+    return moe_workspace_layout(d, t, nullptr, nullptr);
+}
+
+int moe_gemv_grouped(const qg_moe_desc* d, const uint16_t* x, const int32_t* ids,
+                     const float* weights, int64_t t, float* y, void* ws, size_t ws_bytes,
+                     void* stream) {
+    if (int st = check_moe_desc(d)) return st;
+    if (!x || !ids || !weights || !y || !ws) return QG_EINVAL;
+    if (!aligned(x, 16) || !aligned(ids, 4) || !aligned(weights, 4) || !aligned(y, 16) ||
+        !aligned(ws, 256))
+        return QG_EINVAL;
+    if (t < 1) return QG_EINVAL;
+    if (t > QG_MAX_M) return QG_EUNSUPPORTED;
+    MoeWorkspace lay;
+    const size_t need = moe_workspace_layout(d, t, &lay, ws);
+    if (ws_bytes < need) return QG_ENOSPC;
+    return finish(launch_moe(d, x, ids, weights, int(t), y, lay, as_stream(stream)));
+}
+
+int qgemm_prefill(const void* w, float tensor_scale, int64_t n, int64_t k, const uint16_t* x,
+                  int64_t m, uint16_t* y, void* stream) {
+    if (!w || !x || !y || !aligned(w, 256) || !aligned(x, 16) || !aligned(y, 16)) return QG_EINVAL;
+    if (!valid_shape(n, k) || m < 1 || m > (int64_t(65535) * 64)) return QG_EINVAL;
+    return finish(launch_prefill(static_cast<const uint8_t*>(w), tensor_scale, n, k, x, m, y,
+                                 as_stream(stream)));
+}
+
+}  // extern "C"

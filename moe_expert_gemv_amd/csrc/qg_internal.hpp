@@ -1,0 +1,51 @@
+// Internal launch interface between the C entry points (qg_api.cpp) and the
+// kernel translation units.  Arguments are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "qgemv.h"
+
+namespace qg {
+
+void record_hip_error(hipError_t e);
+
+// Returns hipSuccess or the launch error.
+hipError_t launch_dequant(int fmt, const uint8_t* w, float s_t, int64_t n, int64_t k, float* out,
+                          hipStream_t s);
+hipError_t launch_gemv_q8_0(const uint8_t* w, int64_t n, int64_t k, const float* x, int m, float* y,
+                            hipStream_t s);
+hipError_t launch_gemv_nvfp4(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x,
+                             int m, float* y, hipStream_t s);
+hipError_t launch_gemv_nvfp4_swiglu(const uint8_t* w, float s_t, int64_t inter, int64_t k,
+                                    const uint16_t* x, int m, uint16_t* a, float* h, hipStream_t s);
+hipError_t launch_quantize_q8_0(const float* x, int64_t m, int64_t k, int8_t* xq, uint16_t* xd,
+                                int32_t* xs, hipStream_t s);
+hipError_t launch_gemv_q4_0_a8(const uint8_t* w, int64_t n, int64_t k, const int8_t* xq,
+                               const uint16_t* xd, const int32_t* xs, int m, float* y,
+                               hipStream_t s);
+hipError_t launch_route_topk(const float* logits, int64_t t, int e, int top_k, int32_t* ids,
+                             float* w, hipStream_t s);
+
+struct MoeWorkspace {
+    int32_t* n_groups;
+    int32_t* experts;
+    int32_t* offsets;
+    int32_t* pair_tok;
+    int32_t* pair_slot;
+    uint16_t* a;
+    float* h;       // nullable
+    float* o;       // nullable
+    uint32_t* counters;
+    float* o_scratch;
+};
+size_t moe_workspace_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, void* base);
+hipError_t launch_moe(const qg_moe_desc* d, const uint16_t* x, const int32_t* ids, const float* w,
+                      int t, float* y, const MoeWorkspace& ws, hipStream_t s);
+
+hipError_t launch_prefill(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x,
+                          int64_t m, uint16_t* y, hipStream_t s);
+
+}  // namespace qg

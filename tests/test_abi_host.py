@@ -1,0 +1,208 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+symbol the header declares, packs and unpacks exactly, and rejects bad
+arguments before touching the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
+
+import moe_expert_gemv_amd as qg
+import synth
+
+pytestmark = pytest.mark.cpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qg.LIB_PATH):
+        pytest.fail("libqgemv.so is not built (python -m moe_expert_gemv_amd.build)")
+    return qg.lib()
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "sizeof")))
+
+
+def test_header_and_binding_agree():
+    assert _header_functions() == sorted(qg.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", qg.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [s for s in _header_functions() if s not in exported]
+    assert not missing, missing
+    for s in _header_functions():
+        assert hasattr(L, s)
+
+
+def test_versions_and_status_strings(L):
+    assert qg.qg_abi_version() == 1
+    assert qg.qg_layout_version() == 1
+    for s in (0, -1, -2, -4, -5):
+        assert qg.qg_status_string(s) and qg.qg_status_string(s) != "unknown status"
+    assert qg.qg_status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("fmt,n,k,codes,scales", [
+    (qg.QG_NVFP4, 3, 64, 96, 12), (qg.QG_Q4_0, 3, 64, 96, 12), (qg.QG_Q8_0, 3, 64, 192, 12),
+    (qg.QG_NVFP4, 24576, 4096, 50331648, 6291456),
+])
+def test_packed_sizes(L, fmt, n, k, codes, scales):
+    off = qg.qg_scale_plane_offset(fmt, n, k)
+    assert off % 256 == 0 and off >= codes and off - codes < 256
+    total = qg.qg_packed_bytes(fmt, n, k)
+    assert total % 256 == 0 and total - off >= scales and total - off - scales < 256
+
+
+@pytest.mark.parametrize("fmt,n,k", [(qg.QG_NVFP4, 1, 16), (qg.QG_NVFP4, 0, 32), (qg.QG_Q8_0, 4, 48),
+                                     (7, 4, 32), (qg.QG_Q4_0, -1, 32)])
+def test_packed_bytes_rejects_bad_shapes(L, fmt, n, k):
+    assert qg.qg_packed_bytes(fmt, n, k) == 0
+
+
+def _roundtrip(fmt, w):
+    if fmt == qg.QG_NVFP4:
+        buf = qg.qg_pack_nvfp4(w["codes"], w["scales"])
+        c, s = qg.qg_unpack_nvfp4(buf, *w["codes"].shape)
+    elif fmt == qg.QG_Q4_0:
+        buf = qg.qg_pack_q4_0(w["codes"], w["scales"])
+        c, s = qg.qg_unpack_q4_0(buf, *w["codes"].shape)
+    else:
+        buf = qg.qg_pack_q8_0(w["codes"], w["scales"])
+        c, s = qg.qg_unpack_q8_0(buf, *w["codes"].shape)
+    assert np.array_equal(c, w["codes"]) and np.array_equal(s, w["scales"])
+    return buf
+
+
+@pytest.mark.parametrize("n,k", [(1, 32), (3, 64), (17, 96), (64, 2048)])
+def test_pack_roundtrip(L, n, k):
+    g = synth.rng(n * 1000 + k)
+    _roundtrip(qg.QG_NVFP4, synth.nvfp4_weights(g, n, k))
+    _roundtrip(qg.QG_Q4_0, synth.q4_0_weights(g, n, k))
+    _roundtrip(qg.QG_Q8_0, synth.q8_0_weights(g, n, k))
+
+
+def test_pack_layout_is_as_documented(L):
+    # NVFP4: byte j = element 2j (low nibble) | element 2j+1 (high nibble)
+    codes = np.arange(64, dtype=np.uint8).reshape(2, 32) % 16
+    scales = np.arange(4, dtype=np.uint8).reshape(2, 2) + 0x30
+    buf = qg.qg_pack_nvfp4(codes, scales)
+    assert buf[0] == (codes[0, 0] | codes[0, 1] << 4) and buf[16] == (codes[1, 0] | codes[1, 1] << 4)
+    off = qg.qg_scale_plane_offset(qg.QG_NVFP4, 2, 32)
+    assert buf[off:off + 4].tolist() == [0x30, 0x31, 0x32, 0x33]
+    # Q4_0: byte i of a block = element i (low) | element 16+i (high)
+    q = (np.arange(32, dtype=np.uint8) % 16)[None]
+    buf = qg.qg_pack_q4_0(q, np.array([[0x3C00]], np.uint16))
+    assert all(buf[i] == (q[0, i] | q[0, 16 + i] << 4) for i in range(16))
+    off = qg.qg_scale_plane_offset(qg.QG_Q4_0, 1, 32)
+    assert buf[off] == 0x00 and buf[off + 1] == 0x3C
+
+
+@settings(max_examples=40, deadline=None)
+@given(n=st.integers(1, 9), kb=st.integers(1, 6), seed=st.integers(0, 2 ** 31 - 1))
+def test_pack_roundtrip_property(n, kb, seed):
+    qg.lib()
+    g = np.random.default_rng(seed)
+    k = 32 * kb
+    nv = {"codes": g.integers(0, 16, (n, k), dtype=np.uint8), "scales": g.integers(0, 256, (n, k // 16), dtype=np.uint8)}
+    q4 = {"codes": g.integers(0, 16, (n, k), dtype=np.uint8), "scales": g.integers(0, 65536, (n, k // 32)).astype(np.uint16)}
+    q8 = {"codes": g.integers(-128, 128, (n, k), dtype=np.int8), "scales": g.integers(0, 65536, (n, k // 32)).astype(np.uint16)}
+    _roundtrip(qg.QG_NVFP4, nv)
+    _roundtrip(qg.QG_Q4_0, q4)
+    _roundtrip(qg.QG_Q8_0, q8)
+
+
+def test_pack_rejects_out_of_range_codes(L):
+    codes = np.zeros((1, 32), np.uint8)
+    codes[0, 5] = 16
+    with pytest.raises(qg.QGError) as e:
+        qg.qg_pack_nvfp4(codes, np.zeros((1, 2), np.uint8))
+    assert e.value.status == qg.QG_EINVAL
+    with pytest.raises(qg.QGError):
+        qg.qg_pack_q4_0(codes, np.zeros((1, 1), np.uint16))
+
+
+def test_pack_rejects_small_destination(L):
+    codes = np.zeros((2, 32), np.uint8)
+    scales = np.zeros((2, 2), np.uint8)
+    buf = np.zeros(100, np.uint8)
+    st_ = L.qg_pack_nvfp4(codes.ctypes.data, scales.ctypes.data, 2, 32, buf.ctypes.data, buf.nbytes)
+    assert st_ == qg.QG_ENOSPC
+    assert L.qg_pack_nvfp4(None, scales.ctypes.data, 2, 32, buf.ctypes.data, 1 << 20) == qg.QG_EINVAL
+
+
+# Host-side validation of the device entry points: each bad call must return
+# its status before any HIP call, so these run without a GPU.  Pointers are
+# fake but aligned; they are never dereferenced.
+FAKE = 0x7F0000000000
+
+
+def test_gemv_argument_checks(L):
+    f = L.qgemv_nvfp4
+    assert f(None, 1.0, 8, 64, FAKE, 1, FAKE, None) == qg.QG_EINVAL          # null weights
+    assert f(FAKE + 16, 1.0, 8, 64, FAKE, 1, FAKE, None) == qg.QG_EINVAL     # misaligned weights
+    assert f(FAKE, 1.0, 8, 64, FAKE + 2, 1, FAKE, None) == qg.QG_EINVAL      # misaligned x
+    assert f(FAKE, 1.0, 8, 48, FAKE, 1, FAKE, None) == qg.QG_EINVAL          # k % 32 != 0
+    assert f(FAKE, 1.0, 0, 64, FAKE, 1, FAKE, None) == qg.QG_EINVAL          # n = 0
+    assert f(FAKE, 1.0, 8, 64, FAKE, 0, FAKE, None) == qg.QG_EINVAL          # m = 0
+    assert f(FAKE, 1.0, 8, 64, FAKE, 17, FAKE, None) == qg.QG_EUNSUPPORTED   # m > 16
+    assert L.qgemv_q8_0(FAKE, 8, 64, FAKE, 17, FAKE, None) == qg.QG_EUNSUPPORTED
+    assert L.qgemv_q4_0_a8(FAKE, 8, 64, FAKE, None, None, 1, FAKE, None) == qg.QG_EINVAL  # null xd
+    assert L.qgemv_nvfp4_swiglu(FAKE, 1.0, 0, 64, FAKE, 1, FAKE, None, None) == qg.QG_EINVAL
+    assert L.qg_quantize_q8_0_act(FAKE, 1, 40, FAKE, FAKE, None, None) == qg.QG_EINVAL
+    assert L.qg_dequant(9, FAKE, 1.0, 8, 64, FAKE, None) == qg.QG_EINVAL
+    assert L.qgemm_prefill(FAKE, 1.0, 8, 64, FAKE, 0, FAKE, None) == qg.QG_EINVAL
+
+
+def test_router_argument_checks(L):
+    f = L.moe_route_topk
+    assert f(None, 1, 256, 8, FAKE, FAKE, None) == qg.QG_EINVAL
+    assert f(FAKE, 1, 4, 8, FAKE, FAKE, None) == qg.QG_EINVAL        # top_k > n_experts
+    assert f(FAKE, 1, 2048, 8, FAKE, FAKE, None) == qg.QG_EUNSUPPORTED
+    assert f(FAKE, 1, 256, 17, FAKE, FAKE, None) == qg.QG_EUNSUPPORTED
+
+
+def _desc(**kw):
+    gu = qg.qg_packed_bytes(qg.QG_NVFP4, 1024, 2048)
+    dn = qg.qg_packed_bytes(qg.QG_NVFP4, 2048, 512)
+    d = qg.QgMoeDesc(n_experts=256, top_k=8, has_shared=1, flags=0, hidden=2048, inter=512,
+                     gate_up=FAKE, gate_up_stride=gu, down=FAKE, down_stride=dn,
+                     gate_up_scale=FAKE, down_scale=FAKE)
+    for key, v in kw.items():
+        setattr(d, key, v)
+    return d
+
+
+def test_moe_workspace_and_checks(L):
+    d = _desc()
+    ws1 = qg.moe_workspace_bytes(d, 1)
+    ws4 = qg.moe_workspace_bytes(d, 4)
+    assert ws1 > 0 and ws4 > ws1 and ws1 % 256 == 0
+    assert qg.moe_workspace_bytes(d, 17) == 0
+    assert qg.moe_workspace_bytes(_desc(top_k=9), 1) == 0
+    assert qg.moe_workspace_bytes(_desc(gate_up_stride=1024), 1) == 0
+    f = L.moe_gemv_grouped
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 1, FAKE, FAKE, ws1 - 256, None) == qg.QG_ENOSPC
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 17, FAKE, FAKE, 1 << 30, None) == qg.QG_EUNSUPPORTED
+    assert f(ctypes.byref(_desc(down=None)), FAKE, FAKE, FAKE, 1, FAKE, FAKE, ws1, None) == qg.QG_EINVAL
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 1, FAKE, FAKE + 16, ws1, None) == qg.QG_EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(qg, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(qg, "_lib", None)
+    with pytest.raises(qg.QGLibraryMissing):
+        qg.qg_abi_version()

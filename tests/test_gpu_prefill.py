@@ -1,0 +1,97 @@
+"""GPU parity of the small-M prefill GEMM (NVFP4 weights, bf16 activations,
+matrix cores, bf16 output)."""
+import numpy as np
+import pytest
+
+import moe_expert_gemv_amd as qg
+import oracle
+import synth
+from tests.conftest import load_golden
+from tests.gpu_util import dev, empty, host, pack_dev, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(w, x_bits):
+    import torch
+
+    n, k = w["codes"].shape
+    m = x_bits.shape[0]
+    y = empty((m, n), torch.int16)
+    qg.qgemm_prefill(pack_dev(w), float(w["tensor_scale"]), n, k, dev(x_bits), m, y)
+    return host(y).view(np.uint16)
+
+
+def check(w, x, rows=None, cols=None, what=""):
+    got_bits = run_prefill(w, x)
+    if rows is not None:
+        got_bits = got_bits[np.ix_(rows, cols)]
+    got = oracle.decode_bf16(got_bits)
+    ref, absum = oracle.prefill(w, x, rows, cols)
+    tol = 1e-5 * absum + 1e-6 + oracle.bf16_ulp(ref)
+    err = np.abs(got - ref)
+    bad = ~(err <= tol)
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside; worst {np.max(err / tol):.3f}"
+    # most outputs are the correctly rounded value of the exact result
+    assert np.mean(got == oracle.round_to_bf16(ref)) > 0.97, what
+
+
+def test_worked_example():
+    require_gpu()
+    ex6 = next(e for e in load_golden("worked_examples.json")["examples"] if e["id"] == "EX-6")
+    ex9 = next(e for e in load_golden("worked_examples.json")["examples"] if e["id"] == "EX-9")
+    w = {"fmt": "nvfp4", "codes": np.array(ex6["codes"], np.uint8), "scales": np.array(ex6["scales"], np.uint8),
+         "tensor_scale": np.float32(ex6["tensor_scale"])}
+    X = np.zeros((2, 32), np.float32)
+    X[0] = 1.0
+    X[1, 20] = 1.0
+    got = oracle.decode_bf16(run_prefill(w, synth.to_bf16_bits(X)))
+    assert got.tolist() == ex9["Y"]
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 32), (3, 17, 64), (64, 64, 64), (65, 130, 96), (100, 300, 512),
+                                   (128, 64, 4096), (7, 1000, 2080), (513, 129, 160)])
+def test_random(m, n, k):
+    require_gpu()
+    print(f"[prefill m={m} n={n} k={k}]", flush=True)
+    g = synth.rng(m * 7 + n * 3 + k)
+    w = synth.nvfp4_weights(g, n, k)
+    x = synth.x_bf16(g, m, k)
+    check(w, x, what=f"prefill {m}x{n}x{k}")
+
+
+def test_one_hot_rows_are_exact():
+    require_gpu()
+    g = synth.rng(8)
+    n, k = 96, 256
+    w = synth.nvfp4_weights(g, n, k, tensor_scale=1.0)
+    cols = [0, 15, 16, 31, 100, 255]
+    X = np.zeros((len(cols), k), np.float32)
+    for i, c in enumerate(cols):
+        X[i, c] = 1.0
+    got = oracle.decode_bf16(run_prefill(w, synth.to_bf16_bits(X)))
+    D = oracle.dequant_nvfp4(w)
+    for i, c in enumerate(cols):
+        assert np.array_equal(got[i], D[:, c])  # e2m1 * e4m3 is exact in bf16
+
+
+def test_rows_are_independent():
+    require_gpu()
+    g = synth.rng(9)
+    w = synth.nvfp4_weights(g, 256, 1024)
+    x = synth.x_bf16(g, 130, 1024)
+    full = run_prefill(w, x)
+    assert np.array_equal(run_prefill(w, x[64:65]), full[64:65])
+    assert np.array_equal(run_prefill(w, x[:5]), full[:5])
+
+
+@pytest.mark.parametrize("m", [64, 128, 512])
+def test_full_size_sampled(m):
+    """X [m x 4096] times the 9B-class [12288 x 4096] NVFP4 matrix."""
+    require_gpu()
+    print(f"[prefill full m={m}]", flush=True)
+    case = synth.prefill_case(m=m)
+    n = case.w["codes"].shape[0]
+    rows = np.unique(np.concatenate([[0, m - 1], synth.rng(4).integers(0, m, 14)]))
+    cols = np.unique(np.concatenate([np.arange(4), np.arange(n - 4, n), synth.rng(5).integers(0, n, 120)]))
+    check(case.w, case.x, rows, cols, f"prefill full m={m}")
