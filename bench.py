@@ -95,7 +95,7 @@ class DenseLayer(Workload):
         self.H, self.I = 4096, 12288
         case = synth.nvfp4_layer_case(m=m)
         self.case = case
-        gu = qg.qg_pack_nvfp4(case.gate_up["codes"], case.gate_up["scales"])
+        gu = qg.qg_pack_nvfp4_gate_up(case.gate_up["codes"], case.gate_up["scales"])
         dn = qg.qg_pack_nvfp4(case.down["codes"], case.down["scales"])
         self.R = _copies(gu.nbytes + dn.nbytes)
         self.gu = torch.from_numpy(gu).cuda().repeat(self.R, 1)  # R x bytes, each row 256-B aligned
@@ -126,32 +126,32 @@ class DenseLayer(Workload):
         self._gate_up(i)
 
     def cpu_baseline(self, budget_s=12.0):
-        """The oracle on the first rows of both matrices, scaled to GB/s."""
+        """The oracle running whole decode steps of this layer (fp64 numpy
+        dequantize + dot, one thread), repeated until the time budget is used;
+        throughput over the same algorithmic bytes as the GPU step."""
         import oracle
         from threadpoolctl import threadpool_limits
 
         case = self.case
-        H, I, m = self.H, self.I, self.m
-        rows_gu = 0
-        t0 = time.perf_counter()
-        total = 0.0
-        done_bytes = 0
-        chunk = 256
+        H, I = self.H, self.I
+        chunk = 2048
+        total, done_bytes, steps = 0.0, 0, 0
         with threadpool_limits(limits=1):
-            while time.perf_counter() - t0 < budget_s and rows_gu < I:
-                r = np.arange(rows_gu, min(rows_gu + chunk, I))
-                both = np.concatenate([r, r + I])
+            while total < budget_s:
                 t1 = time.perf_counter()
-                h = oracle.gemv(case.gate_up, case.x, both)
-                oracle.swiglu_bf16(h)
-                dn_rows = np.arange(min(H, len(r) * H // I + 1))
-                oracle.gemv(case.down, np.zeros((m, I), np.float32), dn_rows)
+                a = np.empty((self.m, I))
+                for r0 in range(0, I, chunk):
+                    r = np.arange(r0, min(r0 + chunk, I))
+                    h = oracle.gemv(case.gate_up, case.x, np.concatenate([r, r + I]))
+                    a[:, r] = oracle.swiglu_bf16(h)
+                for r0 in range(0, H, chunk):
+                    oracle.gemv(case.down, a, np.arange(r0, min(r0 + chunk, H)))
                 total += time.perf_counter() - t1
-                done_bytes += len(both) * (H // 2 + H // 16) + len(dn_rows) * (I // 2 + I // 16)
-                rows_gu += chunk
+                done_bytes += self.alg_step
+                steps += 1
         return {"value": done_bytes / total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-                "sample": f"gate+up rows 0..{2 * min(rows_gu, I)} (of {2 * I}) and a proportional share of "
-                          f"down rows, fp64 numpy dequant + dot, {total:.1f} s, 1 thread"}
+                "sample": f"{steps} whole decode steps of the same layer (gate+up, SwiGLU, down) "
+                          f"in {total:.1f} s, fp64 numpy, 1 thread"}
 
 
 class Q8Gemv(Workload):
@@ -226,7 +226,8 @@ class MoE(Workload):
         H, I = L.hidden, L.inter
         gs = qg.qg_packed_bytes(qg.QG_NVFP4, 2 * I, H)
         ds = qg.qg_packed_bytes(qg.QG_NVFP4, H, I)
-        gu = np.concatenate([qg.qg_pack_nvfp4(L.gate_up[e]["codes"], L.gate_up[e]["scales"]) for e in range(E)])
+        gu = np.concatenate([qg.qg_pack_nvfp4_gate_up(L.gate_up[e]["codes"], L.gate_up[e]["scales"])
+                             for e in range(E)])
         dn = np.concatenate([qg.qg_pack_nvfp4(L.down[e]["codes"], L.down[e]["scales"]) for e in range(E)])
         self.R = _copies(gu.nbytes + dn.nbytes)
         self.gu = torch.from_numpy(gu).cuda().repeat(self.R, 1)

@@ -113,9 +113,20 @@ int qg_pack_q4_0(const uint8_t* codes, const uint16_t* scales_f16, int64_t n, in
 int qg_pack_q8_0(const int8_t* codes, const uint16_t* scales_f16, int64_t n, int64_t k,
                  void* dst, size_t dst_bytes);
 
+/* Fused gate/up matrix of an MLP for qgemv_nvfp4_swiglu and the MoE experts:
+ * logical codes/scales [2*inter][k] with rows [0, inter) the gate projection
+ * and rows [inter, 2*inter) the up projection.  The packed matrix has the
+ * NVFP4 layout above with the rows interleaved: packed row 2i is gate row i
+ * and packed row 2i+1 is up row i, so the two rows that feed output i are one
+ * contiguous run of memory.  Same size as qg_packed_bytes(QG_NVFP4, 2*inter, k). */
+int qg_pack_nvfp4_gate_up(const uint8_t* codes, const uint8_t* scales_e4m3, int64_t inter, int64_t k,
+                          void* dst, size_t dst_bytes);
+
 /* Unpackers: the exact inverse of the packers (host -> host). */
 int qg_unpack_nvfp4(const void* src, size_t src_bytes, int64_t n, int64_t k,
                     uint8_t* codes, uint8_t* scales_e4m3);
+int qg_unpack_nvfp4_gate_up(const void* src, size_t src_bytes, int64_t inter, int64_t k,
+                            uint8_t* codes, uint8_t* scales_e4m3);
 int qg_unpack_q4_0(const void* src, size_t src_bytes, int64_t n, int64_t k,
                    uint8_t* codes, uint16_t* scales_f16);
 int qg_unpack_q8_0(const void* src, size_t src_bytes, int64_t n, int64_t k,
@@ -148,8 +159,8 @@ int qgemv_nvfp4(const void* w, float tensor_scale, int64_t n, int64_t k,
                 const uint16_t* x, int64_t m, float* y, void* stream);
 
 /* NVFP4 fused gate+up GEMV with the SwiGLU epilogue of an MLP.  w_gu: device
- * packed NVFP4 [2*inter][k] whose rows [0, inter) are the gate projection and
- * rows [inter, 2*inter) the up projection.  a: device bf16 [m][inter] with
+ * fused gate/up matrix packed by qg_pack_nvfp4_gate_up (logical rows
+ * [0, inter) gate, [inter, 2*inter) up).  a: device bf16 [m][inter] with
  * a = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g)).  h (nullable):
  * device fp32 [m][2*inter] receives g and u (the plain GEMV outputs). */
 int qgemv_nvfp4_swiglu(const void* w_gu, float tensor_scale, int64_t inter, int64_t k,
@@ -190,7 +201,8 @@ int moe_route_topk(const float* logits, int64_t t, int64_t n_experts, int64_t to
 /* One MoE layer's experts.  Routed experts 0..n_experts-1; when has_shared is
  * 1, expert n_experts is a shared expert that every token uses with weight 1.
  * Every expert has NVFP4 gate_up [2*inter][hidden] (gate rows first) and down
- * [hidden][inter]; expert e's packed matrices start at gate_up + e *
+ * [hidden][inter], gate_up packed by qg_pack_nvfp4_gate_up and down by
+ * qg_pack_nvfp4; expert e's packed matrices start at gate_up + e *
  * gate_up_stride and down + e * down_stride (device, strides in bytes,
  * multiples of 256, at least qg_packed_bytes of the matrix).  Tensor scales:
  * device fp32 arrays of n_experts + has_shared entries. */
@@ -222,7 +234,6 @@ size_t moe_workspace_bytes(const qg_moe_desc* d, int64_t t);
  *   uint16 a[P][inter]             bf16 SwiGLU outputs per pair
  *   float h[P][2*inter]            (only with QG_MOE_KEEP_H) gate/up outputs per pair
  *   float o[P][hidden]             down outputs per pair (unweighted)
- *   uint32 tickets[...]            internal combine counters
  * This is the expert-major CSR batching of bw24 README (MoE feature entry):
  * each active expert's weights are streamed once for all its tokens.
  *

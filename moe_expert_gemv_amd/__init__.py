@@ -21,8 +21,8 @@ __all__ = [
     "QGError", "QGLibraryMissing", "LIB_PATH", "lib", "loaded",
     "QG_NVFP4", "QG_Q8_0", "QG_Q4_0", "QG_MAX_M", "QG_MOE_KEEP_H",
     "qg_abi_version", "qg_layout_version", "qg_status_string", "qg_packed_bytes",
-    "qg_scale_plane_offset", "qg_pack_nvfp4", "qg_pack_q4_0", "qg_pack_q8_0",
-    "qg_unpack_nvfp4", "qg_unpack_q4_0", "qg_unpack_q8_0", "qg_dequant",
+    "qg_scale_plane_offset", "qg_pack_nvfp4", "qg_pack_nvfp4_gate_up", "qg_pack_q4_0", "qg_pack_q8_0",
+    "qg_unpack_nvfp4", "qg_unpack_nvfp4_gate_up", "qg_unpack_q4_0", "qg_unpack_q8_0", "qg_dequant",
     "qgemv_q8_0", "qgemv_nvfp4", "qgemv_nvfp4_swiglu", "qg_quantize_q8_0_act",
     "qgemv_q4_0_a8", "moe_route_topk", "QgMoeDesc", "moe_workspace_bytes",
     "moe_gemv_grouped", "qgemm_prefill", "EXPORTED_SYMBOLS",
@@ -78,9 +78,11 @@ _SIGNATURES = {
     "qg_packed_bytes": (_SZ, [_I32, _I64, _I64]),
     "qg_scale_plane_offset": (_SZ, [_I32, _I64, _I64]),
     "qg_pack_nvfp4": (_I32, [_P, _P, _I64, _I64, _P, _SZ]),
+    "qg_pack_nvfp4_gate_up": (_I32, [_P, _P, _I64, _I64, _P, _SZ]),
     "qg_pack_q4_0": (_I32, [_P, _P, _I64, _I64, _P, _SZ]),
     "qg_pack_q8_0": (_I32, [_P, _P, _I64, _I64, _P, _SZ]),
     "qg_unpack_nvfp4": (_I32, [_P, _SZ, _I64, _I64, _P, _P]),
+    "qg_unpack_nvfp4_gate_up": (_I32, [_P, _SZ, _I64, _I64, _P, _P]),
     "qg_unpack_q4_0": (_I32, [_P, _SZ, _I64, _I64, _P, _P]),
     "qg_unpack_q8_0": (_I32, [_P, _SZ, _I64, _I64, _P, _P]),
     "qg_dequant": (_I32, [_I32, _P, _F32, _I64, _I64, _P, _P]),
@@ -189,6 +191,22 @@ def qg_pack_nvfp4(codes, scales_e4m3) -> np.ndarray:
     return _pack("qg_pack_nvfp4", QG_NVFP4, codes, scales_e4m3, np.uint8, np.uint8)
 
 
+def qg_pack_nvfp4_gate_up(codes, scales_e4m3) -> np.ndarray:
+    """Fused gate/up matrix [2*inter][k] (gate rows first) -> packed, rows interleaved."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales_e4m3, dtype=np.uint8)
+    n, k = codes.shape
+    if n % 2:
+        raise QGError("qg_pack_nvfp4_gate_up", QG_EINVAL)
+    size = qg_packed_bytes(QG_NVFP4, n, k)
+    if size == 0:
+        raise QGError("qg_pack_nvfp4_gate_up", QG_EINVAL)
+    out = np.empty(size, dtype=np.uint8)
+    _check("qg_pack_nvfp4_gate_up",
+           lib().qg_pack_nvfp4_gate_up(_hptr(codes), _hptr(scales), n // 2, k, _hptr(out), size))
+    return out
+
+
 def qg_pack_q4_0(codes, scales_f16) -> np.ndarray:
     return _pack("qg_pack_q4_0", QG_Q4_0, codes, scales_f16, np.uint8, np.uint16)
 
@@ -207,6 +225,15 @@ def _unpack(func, buf, n, k, code_dtype, scale_dtype, blk):
 
 def qg_unpack_nvfp4(buf, n, k):
     return _unpack("qg_unpack_nvfp4", buf, n, k, np.uint8, np.uint8, 16)
+
+
+def qg_unpack_nvfp4_gate_up(buf, inter, k):
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    codes = np.empty((2 * inter, k), dtype=np.uint8)
+    scales = np.empty((2 * inter, k // 16), dtype=np.uint8)
+    _check("qg_unpack_nvfp4_gate_up",
+           lib().qg_unpack_nvfp4_gate_up(_hptr(buf), buf.nbytes, inter, k, _hptr(codes), _hptr(scales)))
+    return codes, scales
 
 
 def qg_unpack_q4_0(buf, n, k):

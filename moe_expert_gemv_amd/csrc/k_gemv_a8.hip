@@ -1,0 +1,275 @@
+// W4A8 path for gfx950: the Q8_0 activation quantizer and the Q4_0 x Q8_0
+// GEMV with exact int32 block dots (v_dot4_i32_i8), after the pages' dp4a /
+// W4A8 integer decode path (bw24 README, NVFP4 (W4) decode path entry).
+//
+// Per 32-element block: isum = sum (q_w - 8) * q_x, computed as
+// sum q_w * q_x - 8 * sum q_x so the 4-bit codes need no per-nibble offset
+// (the activation block sums come from the quantizer), then one fp32 step
+// y += (d_w * d_x) * isum.  Streaming shape as in the NVFP4 kernel.
+#include <hip/hip_runtime.h>
+
+#include "qg_device.hpp"
+#include "qg_gemv_core.hpp"
+#include "qg_internal.hpp"
+#include "qg_layout.hpp"
+
+namespace qg {
+
+namespace {
+
+constexpr int kBlock = 256;
+
+// sum over the block of q_w * q_x (exact int32), codes c, activations x0|x1.
+__device__ __forceinline__ int q4_block_dot(const u32x4& c, const u32x4& x0, const u32x4& x1) {
+    int isum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t lo, hi;
+        q4_unpack(c[q], lo, hi);
+        isum = dot4_i8(lo, x0[q], isum);
+        isum = dot4_i8(hi, x1[q], isum);
+    }
+    return isum;
+}
+
+struct XBlock {
+    u32x4 x0, x1;
+    float dx;
+    int bsum8;  // 8 * sum of the block's q_x
+};
+
+// Block j of token t's activations (j must be a valid block); zeros when !ok.
+__device__ __forceinline__ XBlock load_xblock(const int8_t* xq, const uint16_t* xd, const int32_t* xs, int64_t t,
+                                              int k, int nb, int j, bool ok) {
+    XBlock b;
+    const int8_t* p = xq + t * k + 32 * j;
+    b.x0 = zero_unless(ok, ld16(p));
+    b.x1 = zero_unless(ok, ld16(p + 16));
+    const float dx = f16_to_f32(xd[t * nb + j]);
+    b.dx = ok ? dx : 0.f;
+    int s;
+    if (xs) {
+        s = xs[t * nb + j];
+    } else {
+        s = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            s = dot4_i8(0x01010101u, b.x0[q], s);
+            s = dot4_i8(0x01010101u, b.x1[q], s);
+        }
+    }
+    b.bsum8 = ok ? 8 * s : 0;
+    return b;
+}
+
+// Chunk j of a row = Q4_0 block j: 16 code bytes and one fp16 scale.
+template <int R, int MT, int G, int C>
+__global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restrict__ w, int64_t soff,
+                                                         int n, int k,
+                                                         const int8_t* __restrict__ xq,
+                                                         const uint16_t* __restrict__ xd,
+                                                         const int32_t* __restrict__ xs, int m,
+                                                         float* __restrict__ y) {
+    constexpr int kGroups = kWave / G;
+    const int lane = lane_id();
+    const int grp = lane / G, l = lane % G;
+    const int wave = int(blockIdx.x) * (kBlock / kWave) + int(threadIdx.x) / kWave;
+    const int unit = wave * kGroups + grp;
+    const int64_t crow = k / 2, srow = (k / 32) * 2;
+    const int nb = k / 32;
+
+    const uint8_t* codes[R];
+    const uint8_t* scales[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = min(unit * R + r, n - 1);
+        codes[r] = w + row * crow;
+        scales[r] = w + soff + row * srow;
+    }
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = 0.f;
+
+    if constexpr (C > 0) {
+        u32x4 cw[C][R];
+        float dw[C][R];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int j = c * G + l;
+            const bool ok = j < nb;
+            const int js = ok ? j : 0;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                cw[c][r] = zero_unless(ok, ld_stream16(codes[r] + 16 * js));
+                const float dv = f16_to_f32(ld<uint16_t>(scales[r] + 2 * js));
+                dw[c][r] = ok ? dv : 0.f;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int j = c * G + l;
+            const bool ok = j < nb;
+            const int js = ok ? j : 0;
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                if (t < m) {
+                    const XBlock b = load_xblock(xq, xd, xs, t, k, nb, js, ok);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const int isum = q4_block_dot(cw[c][r], b.x0, b.x1) - b.bsum8;
+                        acc[r][t] = fmaf(dw[c][r] * b.dx, float(isum), acc[r][t]);
+                    }
+                }
+            }
+        }
+    } else {
+        for (int j = l; j < nb; j += G) {
+            u32x4 cw[R];
+            float dw[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                cw[r] = ld_stream16(codes[r] + 16 * j);
+                dw[r] = f16_to_f32(ld<uint16_t>(scales[r] + 2 * j));
+            }
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                if (t < m) {
+                    const XBlock b = load_xblock(xq, xd, xs, t, k, nb, j, true);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const int isum = q4_block_dot(cw[r], b.x0, b.x1) - b.bsum8;
+                        acc[r][t] = fmaf(dw[r] * b.dx, float(isum), acc[r][t]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = group_sum<G>(acc[r][t]);
+    if (l != 0) return;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = unit * R + r;
+        if (row >= n) break;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            if (t < m) y[int64_t(t) * n + row] = acc[r][t];
+    }
+}
+
+// ------------------------------------------------------------------ quantizer
+
+// One thread per 32-element block.
+__global__ __launch_bounds__(kBlock) void k_quantize_q8_0(const float* __restrict__ x, int64_t nblocks,
+                                                          int8_t* __restrict__ xq,
+                                                          uint16_t* __restrict__ xd,
+                                                          int32_t* __restrict__ xs) {
+    const int64_t b = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+    if (b >= nblocks) return;
+    const float* p = x + 32 * b;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 f = ld<float4>(p + 4 * i);
+        v[4 * i] = f.x;
+        v[4 * i + 1] = f.y;
+        v[4 * i + 2] = f.z;
+        v[4 * i + 3] = f.w;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float d32 = amax / 127.0f;  // correctly rounded (no fast-math in this library)
+    const _Float16 d16 = _Float16(d32);
+    uint32_t packed[8];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed[i] = 0;
+    if (d32 != 0.f) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const float r = fminf(fmaxf(rintf(v[i] / d32), -127.f), 127.f);
+            const int q = int(r);
+            sum += q;
+            packed[i / 4] |= uint32_t(q & 0xff) << (8 * (i % 4));
+        }
+    }
+    u32x4* o = reinterpret_cast<u32x4*>(xq + 32 * b);
+    o[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    o[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
+    xd[b] = __builtin_bit_cast(uint16_t, d16);
+    if (xs) xs[b] = sum;
+}
+
+struct Args {
+    const uint8_t* w;
+    int64_t soff;
+    int n, k;
+    const int8_t* xq;
+    const uint16_t* xd;
+    const int32_t* xs;
+    int m;
+    float* y;
+};
+
+template <int G, int C, int MT>
+hipError_t go(const Args& A, hipStream_t s) {
+    constexpr int R = rows_per_group(C, MT);
+    const int64_t units = (int64_t(A.n) + R - 1) / R;
+    const int64_t per_block = (kBlock / kWave) * (kWave / G);
+    const dim3 grid(unsigned((units + per_block - 1) / per_block));
+    hipLaunchKernelGGL((k_gemv_q4_0_a8<R, MT, G, C>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.n, A.k, A.xq,
+                       A.xd, A.xs, A.m, A.y);
+    return hipGetLastError();
+}
+
+template <int G, int MT>
+hipError_t by_chunks(const Args& A, hipStream_t s) {
+    const int C = chunks_per_lane(A.k / 32, G);
+    if constexpr (G == 16) {
+        switch (C) {
+            case 1: return go<16, 1, MT>(A, s);
+            case 2: return go<16, 2, MT>(A, s);
+            case 3: return go<16, 3, MT>(A, s);
+            default: return go<16, 4, MT>(A, s);
+        }
+    } else {
+        switch (C) {
+            case 1: return go<64, 1, MT>(A, s);
+            case 2: return go<64, 2, MT>(A, s);
+            case 3: return go<64, 3, MT>(A, s);
+            case 4: return go<64, 4, MT>(A, s);
+            case 6: return go<64, 6, MT>(A, s);
+            case 8: return go<64, 8, MT>(A, s);
+            default: return go<64, 0, MT>(A, s);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_q4_0_a8(const uint8_t* w, int64_t n, int64_t k, const int8_t* xq,
+                               const uint16_t* xd, const int32_t* xs, int m, float* y,
+                               hipStream_t s) {
+    const Args A{w, scale_plane_offset(QG_Q4_0, n, k), int(n), int(k), xq, xd, xs, m, y};
+    const bool wide = lanes_per_row(k / 32) == 64;
+    switch (token_class(m)) {
+        case 1: return wide ? by_chunks<64, 1>(A, s) : by_chunks<16, 1>(A, s);
+        case 4: return wide ? by_chunks<64, 4>(A, s) : by_chunks<16, 4>(A, s);
+        default: return wide ? by_chunks<64, 16>(A, s) : by_chunks<16, 16>(A, s);
+    }
+}
+
+hipError_t launch_quantize_q8_0(const float* x, int64_t m, int64_t k, int8_t* xq, uint16_t* xd,
+                                int32_t* xs, hipStream_t s) {
+    const int64_t nblocks = m * (k / 32);
+    hipLaunchKernelGGL(k_quantize_q8_0, dim3(unsigned((nblocks + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, x,
+                       nblocks, xq, xd, xs);
+    return hipGetLastError();
+}
+
+}  // namespace qg

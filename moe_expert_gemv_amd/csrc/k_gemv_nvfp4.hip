@@ -1,0 +1,345 @@
+// Dense NVFP4 x bf16 GEMV for gfx950 (wave64), plain or with the SwiGLU
+// epilogue of a fused gate+up projection.
+//
+// The decode step streams every weight byte once and sits at the DRAM
+// bandwidth limit (memra README, known gaps: plain-decode margins at the DRAM
+// wall), so the kernel is shaped around HBM streaming:
+//  * a group of G lanes (G = 64, or 16 for rows shorter than 2048 elements)
+//    owns R rows; each lane loads 16-byte code chunks c*G + l, c < C, so one
+//    wave-wide load reads 1 KB of a row contiguously (non-temporal);
+//  * all R*C code and scale loads are issued before any arithmetic (about
+//    8 KB of weights in flight per wave);
+//  * E2M1 pairs are widened to bf16 by v_cvt_scalef32_pk_bf16_fp4 and
+//    multiplied into fp32 by v_dot2_f32_bf16; each 16-element block's sum is
+//    scaled once by its E4M3 scale, the row sum once by the tensor scale;
+//  * per-lane sums are combined by a fixed DPP/swizzle butterfly.
+// The chunk-to-lane mapping and the reduction order depend only on k, so
+// results are bitwise identical for any token count, grid or schedule.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+
+#include "qg_device.hpp"
+#include "qg_gemv_core.hpp"
+#include "qg_internal.hpp"
+#include "qg_layout.hpp"
+
+namespace qg {
+
+namespace {
+
+constexpr int kBlock = 256;  // threads per workgroup (4 waves)
+
+// Streaming kernel shape, measured on MI355X over rows per unit R in
+// {1, 2, 4, 8} and units per wave U in {1, 2, 4, 8}: four rows per unit for
+// short rows (8 KB of codes per wave at k = 4096), two for long rows (12 KB
+// at k = 12288), one unit per wave.
+template <int C>
+constexpr int kStreamRows = C <= 2 ? 4 : 2;
+constexpr int kStreamUnitsDefault = 1;
+
+// SWIGLU: the matrix is packed with gate/up rows interleaved (packed row 2i =
+// gate i, 2i+1 = up i), so the R consecutive rows of a group are RA = R/2
+// (gate, up) pairs; the epilogue writes a = bf16(silu(g) * u) (and optionally
+// g, u into h).  nout is n (plain) or inter (SwiGLU).
+template <int R, int MT, int G, int C, bool SWIGLU>
+__global__ __launch_bounds__(kBlock) void k_gemv_nvfp4(const uint8_t* __restrict__ w, int64_t soff,
+                                                       float s_t, int nout, int k,
+                                                       const uint16_t* __restrict__ x, int m,
+                                                       float* __restrict__ y,
+                                                       uint16_t* __restrict__ a,
+                                                       float* __restrict__ h) {
+    constexpr int kGroups = kWave / G;
+    const int lane = lane_id();
+    const int grp = lane / G, l = lane % G;
+    const int wave = int(blockIdx.x) * (kBlock / kWave) + int(threadIdx.x) / kWave;
+    const int unit = wave * kGroups + grp;
+    const int64_t crow = k / 2, srow = k / 16;
+
+    // SwiGLU matrices are packed with gate/up rows interleaved, so in both
+    // modes a group's R rows are consecutive packed rows.
+    const int nrows = SWIGLU ? 2 * nout : nout;
+    int rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = min(unit * R + r, nrows - 1);
+    const uint8_t* codes[R];
+    const uint8_t* scales[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        codes[r] = w + rows[r] * crow;
+        scales[r] = w + soff + rows[r] * srow;
+    }
+    const uint16_t* xp[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) xp[t] = x + int64_t(t < m ? t : 0) * k;
+
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = 0.f;
+
+    nvfp4_partial<R, MT, G, C>(codes, scales, xp, m, k / 32, l, acc);
+
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = group_sum<G>(acc[r][t]) * s_t;
+
+    if (l != 0) return;
+    if constexpr (!SWIGLU) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = unit * R + r;
+            if (row >= nout) break;
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                if (t < m) y[int64_t(t) * nout + row] = acc[r][t];
+        }
+    } else {
+        constexpr int RA = R / 2;
+#pragma unroll
+        for (int r = 0; r < RA; ++r) {
+            const int i = unit * RA + r;
+            if (i >= nout) break;
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                if (t < m) {
+                    const float g = acc[2 * r][t], u = acc[2 * r + 1][t];
+                    const float act = g / (1.0f + expf(-g)) * u;
+                    a[int64_t(t) * nout + i] = uint16_t(f32_to_bf16_rne(act));
+                    if (h) {
+                        h[int64_t(t) * 2 * nout + i] = g;
+                        h[int64_t(t) * 2 * nout + nout + i] = u;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// One-token streaming variant.  A wave handles U units (U compile-time):
+// units w, w + W, w + 2W, ... of the W waves in the grid, so at any moment the
+// GPU's waves read neighbouring rows.  The U units run as a straight-line
+// two-deep register pipeline -- the loads of unit i+1 are issued before unit
+// i is decoded and reduced -- and the lane's activation chunks are loaded once
+// (a lane always covers the same k range).  Being straight-line code (no loop
+// back-edge), the compiler counts outstanding loads exactly and keeps the
+// prefetch in flight; sched_barrier stops it from sinking a prefetch below
+// the arithmetic.  Same per-row arithmetic and reduction order as
+// k_gemv_nvfp4.
+template <int R, int G, int C>
+struct StreamBuf {
+    u32x4 cw[C][R];
+    uint32_t sw[C][R];
+};
+
+template <int R, int G, int C, int U, bool SWIGLU>
+__global__ __launch_bounds__(kBlock) void k_gemv_nvfp4_stream(const uint8_t* __restrict__ w, int64_t soff,
+                                                              float s_t, int nout, int k,
+                                                              const uint16_t* __restrict__ x,
+                                                              float* __restrict__ y,
+                                                              uint16_t* __restrict__ a,
+                                                              float* __restrict__ h, int n_wunits) {
+    constexpr int kGroups = kWave / G;
+    constexpr int kPer = SWIGLU ? R / 2 : R;  // output rows per group per unit
+    const int lane = lane_id();
+    const int grp = G == kWave ? 0 : lane / G;  // one group per wave: rows are wave-uniform
+    const int l = G == kWave ? lane : lane % G;
+    const int nwaves = int(gridDim.x) * (kBlock / kWave);
+    // wave-uniform, kept in a scalar register
+    const int wave = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * (kBlock / kWave) + int(threadIdx.x) / kWave);
+    const int64_t crow = k / 2, srow = k / 16;
+    const int nchunks = k / 32;
+
+    // Lanes whose chunk c lies past the end of a row load chunk 0 instead (a
+    // valid address) and drop the result.
+    bool okc[C];
+    uint32_t jc[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int j = c * G + l;
+        okc[c] = j < nchunks;
+        jc[c] = okc[c] ? uint32_t(j) : 0u;
+    }
+    u32x4 xv[C][4];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[c][i] = ld16(x + 32u * jc[c] + 8u * i);
+
+    const int nrows = SWIGLU ? 2 * nout : nout;  // packed rows (gate/up interleaved)
+    auto row_of = [&](int unit, int r) -> int { return min(unit * R + r, nrows - 1); };
+    // unit index of step i, clamped to a valid unit (a clamped step stores nothing)
+    auto wunit_of = [&](int i) -> int { return min(wave + i * nwaves, n_wunits - 1); };
+    auto load = [&](StreamBuf<R, G, C>& b, int wunit) {
+        const int unit = wunit * kGroups + grp;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t row = row_of(unit, r);
+            const uint8_t* cp = w + row * crow;
+            const uint8_t* sp = w + soff + row * srow;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                b.cw[c][r] = ld_stream16(cp + 16u * jc[c]);
+                b.sw[c][r] = ld<uint16_t>(sp + 2u * jc[c]);
+            }
+        }
+    };
+    auto process = [&](const StreamBuf<R, G, C>& b, int wunit, bool store) {
+        const int unit = wunit * kGroups + grp;
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float v = nvfp4_chunk_dot(b.cw[c][r], b.sw[c][r], xv[c], acc[r]);
+                acc[r] = okc[c] ? v : acc[r];
+            }
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = group_sum<G>(acc[r]) * s_t;
+        if (store && l == 0) {
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) {
+                const int i = unit * kPer + r;
+                if (i < nout) {
+                    if constexpr (!SWIGLU) {
+                        y[i] = acc[r];
+                    } else {
+                        const float g = acc[2 * r], u = acc[2 * r + 1];
+                        a[i] = uint16_t(f32_to_bf16_rne(g / (1.0f + expf(-g)) * u));
+                        if (h) {
+                            h[i] = g;
+                            h[nout + i] = u;
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    StreamBuf<R, G, C> buf[2];
+    load(buf[0], wunit_of(0));
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        if (i + 1 < U) load(buf[(i + 1) & 1], wunit_of(i + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        process(buf[i & 1], wunit_of(i), wave + i * nwaves < n_wunits);
+    }
+}
+
+struct Args {
+    const uint8_t* w;
+    int64_t soff;
+    float s_t;
+    int nout, k;
+    const uint16_t* x;
+    int m;
+    float* y;
+    uint16_t* a;
+    float* h;
+};
+
+// Units per wave of the streaming kernel (tunable for a machine through
+// QG_STREAM_UNITS; results do not depend on it): the grid gets units / U
+// waves.
+int stream_units_per_wave() {
+    static const int v = [] {
+        const char* e = std::getenv("QG_STREAM_UNITS");
+        const int x = e ? std::atoi(e) : 0;
+        return x == 1 || x == 2 || x == 4 || x == 8 ? x : kStreamUnitsDefault;
+    }();
+    return v;
+}
+
+template <int G, int C, int U, bool SW>
+hipError_t go_stream_u(const Args& A, int64_t wunits, hipStream_t s) {
+    constexpr int R0 = kStreamRows<C>;
+    constexpr int R = SW ? (R0 < 2 ? 2 : R0) : R0;
+    const int64_t waves = (wunits + U - 1) / U;
+    const dim3 grid(unsigned((waves + kBlock / kWave - 1) / (kBlock / kWave)));
+    hipLaunchKernelGGL((k_gemv_nvfp4_stream<R, G, C, U, SW>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.s_t,
+                       A.nout, A.k, A.x, A.y, A.a, A.h, int(wunits));
+    return hipGetLastError();
+}
+
+template <int G, int C, bool SW>
+hipError_t go_stream(const Args& A, hipStream_t s) {
+    constexpr int R0 = kStreamRows<C>;
+    constexpr int R = SW ? (R0 < 2 ? 2 : R0) : R0;
+    constexpr int per_unit = SW ? R / 2 : R;
+    const int64_t units = (int64_t(A.nout) + per_unit - 1) / per_unit;
+    const int64_t wunits = (units + (kWave / G) - 1) / (kWave / G);
+    switch (stream_units_per_wave()) {
+        case 1: return go_stream_u<G, C, 1, SW>(A, wunits, s);
+        case 2: return go_stream_u<G, C, 2, SW>(A, wunits, s);
+        case 4: return go_stream_u<G, C, 4, SW>(A, wunits, s);
+        default: return go_stream_u<G, C, 8, SW>(A, wunits, s);
+    }
+}
+
+template <int G, int C, int MT, bool SW>
+hipError_t go(const Args& A, hipStream_t s) {
+    if constexpr (MT == 1 && C > 0 && C <= 6) return go_stream<G, C, SW>(A, s);
+    constexpr int R0 = rows_per_group(C, MT);
+    constexpr int R = SW ? (R0 < 2 ? 2 : R0) : R0;
+    constexpr int per_unit = SW ? R / 2 : R;
+    const int64_t units = (int64_t(A.nout) + per_unit - 1) / per_unit;
+    const int64_t per_block = (kBlock / kWave) * (kWave / G);
+    const dim3 grid(unsigned((units + per_block - 1) / per_block));
+    hipLaunchKernelGGL((k_gemv_nvfp4<R, MT, G, C, SW>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.s_t,
+                       A.nout, A.k, A.x, A.m, A.y, A.a, A.h);
+    return hipGetLastError();
+}
+
+template <int G, int MT, bool SW>
+hipError_t by_chunks(const Args& A, hipStream_t s) {
+    const int C = chunks_per_lane(A.k / 32, G);
+    if constexpr (G == 16) {
+        switch (C) {  // rows of fewer than 64 chunks: C <= 4
+            case 1: return go<16, 1, MT, SW>(A, s);
+            case 2: return go<16, 2, MT, SW>(A, s);
+            case 3: return go<16, 3, MT, SW>(A, s);
+            default: return go<16, 4, MT, SW>(A, s);
+        }
+    } else {
+        switch (C) {
+            case 1: return go<64, 1, MT, SW>(A, s);
+            case 2: return go<64, 2, MT, SW>(A, s);
+            case 3: return go<64, 3, MT, SW>(A, s);
+            case 4: return go<64, 4, MT, SW>(A, s);
+            case 6: return go<64, 6, MT, SW>(A, s);
+            case 8: return go<64, 8, MT, SW>(A, s);
+            default: return go<64, 0, MT, SW>(A, s);
+        }
+    }
+}
+
+template <bool SW>
+hipError_t dispatch(const Args& A, hipStream_t s) {
+    const bool wide = lanes_per_row(A.k / 32) == 64;
+    switch (token_class(A.m)) {
+        case 1: return wide ? by_chunks<64, 1, SW>(A, s) : by_chunks<16, 1, SW>(A, s);
+        case 4: return wide ? by_chunks<64, 4, SW>(A, s) : by_chunks<16, 4, SW>(A, s);
+        default: return wide ? by_chunks<64, 16, SW>(A, s) : by_chunks<16, 16, SW>(A, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_nvfp4(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x,
+                             int m, float* y, hipStream_t s) {
+    const Args A{w, scale_plane_offset(QG_NVFP4, n, k), s_t, int(n), int(k), x, m, y, nullptr, nullptr};
+    return dispatch<false>(A, s);
+}
+
+hipError_t launch_gemv_nvfp4_swiglu(const uint8_t* w, float s_t, int64_t inter, int64_t k,
+                                    const uint16_t* x, int m, uint16_t* a, float* h, hipStream_t s) {
+    const Args A{w, scale_plane_offset(QG_NVFP4, 2 * inter, k), s_t, int(inter), int(k), x, m, nullptr, a, h};
+    return dispatch<true>(A, s);
+}
+
+}  // namespace qg

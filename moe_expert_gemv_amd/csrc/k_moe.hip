@@ -10,12 +10,12 @@
 //   2. k_moe_gate_up      every workgroup rebuilds the CSR from ids in LDS (a
 //                         few hundred integer ops), then one (expert group x
 //                         row tile) of the grouped gate/up GEMV + SwiGLU;
-//                         workgroup (0,0) also publishes the CSR and clears the
-//                         combine counters in the workspace
-//   3. k_moe_down         one (row tile x expert group) of the grouped down
-//                         GEMV; the last workgroup to finish a row tile (an
-//                         integer ticket counter, no float atomics) sums the
-//                         routed outputs in slot order plus the shared expert
+//                         workgroup (0,0) also publishes the CSR in the
+//                         workspace
+//   3. k_moe_down         one row tile of the grouped down GEMV, one wave per
+//                         expert group, then the weighted sum of the routed
+//                         outputs in slot order plus the shared expert, done
+//                         inside the workgroup through LDS
 // Grids are sized for the worst case (t * top_k + 1 groups); workgroups whose
 // group does not exist return at once.
 #include <hip/hip_runtime.h>
@@ -168,14 +168,13 @@ struct MoeArgs {
     int64_t dn_stride;
     const float* gu_scale;
     const float* dn_scale;
-    int n_tiles_down;  // row tiles of the down projection (= combine counters)
 };
 
 // ------------------------------------------------------------------ gate/up + SwiGLU
 
 // blockIdx.y = expert group, blockIdx.x = tile of a-rows.  Each group of G
 // lanes owns RA a-rows (RA gate rows and the RA matching up rows).
-template <int MT, int G, int RA>
+template <int MT, int G, int C, int RA>
 __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_t* __restrict__ x,
                                                         const int32_t* __restrict__ ids, int t,
                                                         MoeWorkspace ws) {
@@ -192,7 +191,6 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
         }
         for (int i = tid; i < c.n_groups; i += kBlock) ws.experts[i] = c.experts[i];
         for (int i = tid; i <= c.n_groups; i += kBlock) ws.offsets[i] = c.offsets[i];
-        for (int i = tid; i < A.n_tiles_down; i += kBlock) ws.counters[i] = 0;
     }
     const int g = int(blockIdx.y);
     if (g >= c.n_groups) return;
@@ -211,12 +209,10 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
     const uint8_t* w = A.gate_up + int64_t(e) * A.gu_stride;
     const int64_t soff = scale_plane_offset(QG_NVFP4, 2 * int64_t(I), H);
     const float s_t = A.gu_scale[e];
+    // gate/up rows are interleaved in the packed matrix: R consecutive rows
     int rows[R];
 #pragma unroll
-    for (int r = 0; r < RA; ++r) {
-        rows[r] = min(unit * RA + r, I - 1);
-        rows[RA + r] = I + rows[r];
-    }
+    for (int r = 0; r < R; ++r) rows[r] = min(unit * R + r, 2 * I - 1);
     const uint8_t* codes[R];
     const uint8_t* scales[R];
 #pragma unroll
@@ -233,7 +229,7 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < MT; ++i) acc[r][i] = 0.f;
-    nvfp4_partial<R, MT, G>(codes, scales, xp, mg, H / 32, l, acc);
+    nvfp4_partial<R, MT, G, C>(codes, scales, xp, mg, H / 32, l, acc);
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -247,7 +243,7 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
         for (int i = 0; i < MT; ++i) {
             if (i < mg) {
                 const int p = p0 + i;
-                const float gv = acc[r][i], uv = acc[RA + r][i];
+                const float gv = acc[2 * r][i], uv = acc[2 * r + 1][i];
                 const float act = gv / (1.0f + expf(-gv)) * uv;
                 ws.a[int64_t(p) * I + row] = uint16_t(f32_to_bf16_rne(act));
                 if (ws.h) {
@@ -261,129 +257,126 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
 
 // ------------------------------------------------------------------ down + combine
 
-// blockIdx.x = row tile of the output, blockIdx.y = expert group.
-template <int MT, int G, int R>
-__global__ __launch_bounds__(kBlock) void k_moe_down(MoeArgs A, const float* __restrict__ wts, int t,
-                                                     float* __restrict__ y, MoeWorkspace ws) {
-    __shared__ int s_off[kMaxPairs + 1];
-    __shared__ int s_tok[kMaxPairs];
-    __shared__ int s_pair[kMaxTokens][kMaxTopK + 1];
-    __shared__ int s_last;
-    const int tid = int(threadIdx.x);
-    const int ng = *ws.n_groups;
-    const int g = int(blockIdx.y);
-    if (g >= ng) return;  // uniform per workgroup
-    const int P = t * (A.k + A.has_shared);
-    for (int i = tid; i <= ng; i += kBlock) s_off[i] = ws.offsets[i];
-    for (int i = tid; i < P; i += kBlock) {
-        s_tok[i] = ws.pair_tok[i];
-        s_pair[ws.pair_tok[i]][ws.pair_slot[i]] = i;
-    }
-    __syncthreads();
-    const int e = ws.experts[g];
-    const int p0 = s_off[g];
-    const int mg = s_off[g + 1] - p0;
-
+// blockIdx.x = tile of output rows; the workgroup has one wave per expert
+// group (up to 16; wave w takes groups w, w+16, ...).  Every wave computes
+// its groups' down outputs for the tile into LDS, then the workgroup sums them
+// per token in slot order plus the shared expert: a fixed order, and no
+// synchronisation between workgroups.
+template <int MT, int G, int C, int R>
+__global__ __launch_bounds__(1024) void k_moe_down(MoeArgs A, const float* __restrict__ wts, int t,
+                                                   float* __restrict__ y, MoeWorkspace ws) {
     constexpr int kGroups = kWave / G;
-    constexpr int kRowsPerTile = (kBlock / kWave) * kGroups * R;
+    constexpr int kRows = kGroups * R;  // rows per tile
+    __shared__ int s_off[kMaxPairs + 1];
+    __shared__ int s_exp[kMaxPairs];
+    __shared__ int s_pair[kMaxTokens][kMaxTopK + 1];
+    __shared__ float s_o[kMaxPairs][kRows];
+    const int tid = int(threadIdx.x);
+    const int nthreads = int(blockDim.x);
+    const int nw = nthreads / kWave;
+    const int ng = *ws.n_groups;
+    const int P = t * (A.k + A.has_shared);
+    for (int i = tid; i <= ng; i += nthreads) s_off[i] = ws.offsets[i];
+    for (int i = tid; i < ng; i += nthreads) s_exp[i] = ws.experts[i];
+    for (int i = tid; i < P; i += nthreads) s_pair[ws.pair_tok[i]][ws.pair_slot[i]] = i;
+    __syncthreads();
+
     const int lane = lane_id();
     const int grp = lane / G, l = lane % G;
-    const int wave_in_tile = tid / kWave;
     const int I = A.I, H = A.H;
-    const int row0 = int(blockIdx.x) * kRowsPerTile + (wave_in_tile * kGroups + grp) * R;
-
-    const uint8_t* w = A.down + int64_t(e) * A.dn_stride;
+    const int tile0 = int(blockIdx.x) * kRows;
     const int64_t soff = scale_plane_offset(QG_NVFP4, H, I);
-    const float s_t = A.dn_scale[e];
-    const uint8_t* codes[R];
-    const uint8_t* scales[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int row = min(row0 + r, H - 1);
-        codes[r] = w + int64_t(row) * (I / 2);
-        scales[r] = w + soff + int64_t(row) * (I / 16);
-    }
-    const uint16_t* xp[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) xp[i] = ws.a + int64_t(p0 + (i < mg ? i : 0)) * I;
-
-    float acc[R][MT];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int i = 0; i < MT; ++i) acc[r][i] = 0.f;
-    nvfp4_partial<R, MT, G>(codes, scales, xp, mg, I / 32, l, acc);
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int i = 0; i < MT; ++i) acc[r][i] = group_sum<G>(acc[r][i]) * s_t;
-    if (l == 0) {
+    for (int g = tid / kWave; g < ng; g += nw) {  // uniform per wave
+        const int e = s_exp[g];
+        const int p0 = s_off[g];
+        const int mg = s_off[g + 1] - p0;
+        const uint8_t* w = A.down + int64_t(e) * A.dn_stride;
+        const float s_t = A.dn_scale[e];
+        const uint8_t* codes[R];
+        const uint8_t* scales[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int row = row0 + r;
-            if (row < H) {
+            const int row = min(tile0 + grp * R + r, H - 1);
+            codes[r] = w + int64_t(row) * (I / 2);
+            scales[r] = w + soff + int64_t(row) * (I / 16);
+        }
+        const uint16_t* xp[MT];
 #pragma unroll
-                for (int i = 0; i < MT; ++i)
-                    if (i < mg) ws.o[int64_t(p0 + i) * H + row] = acc[r][i];
+        for (int i = 0; i < MT; ++i) xp[i] = ws.a + int64_t(p0 + (i < mg ? i : 0)) * I;
+        float acc[R][MT];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < MT; ++i) acc[r][i] = 0.f;
+        nvfp4_partial<R, MT, G, C>(codes, scales, xp, mg, I / 32, l, acc);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < MT; ++i) acc[r][i] = group_sum<G>(acc[r][i]) * s_t;
+        if (l == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int row = tile0 + grp * R + r;
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    if (i < mg) {
+                        s_o[p0 + i][grp * R + r] = acc[r][i];
+                        if (row < H) ws.o[int64_t(p0 + i) * H + row] = acc[r][i];
+                    }
+                }
             }
         }
     }
-    // Publish this group's outputs for the tile; the last arrival combines.
-    __threadfence();
     __syncthreads();
-    if (tid == 0) {
-        const unsigned ticket = atomicAdd(&ws.counters[blockIdx.x], 1u);
-        s_last = (ticket == unsigned(ng - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const int tile0 = int(blockIdx.x) * kRowsPerTile;
-    for (int idx = tid; idx < t * kRowsPerTile; idx += kBlock) {
-        const int tt = idx / kRowsPerTile;
-        const int row = tile0 + idx % kRowsPerTile;
+    for (int idx = tid; idx < t * kRows; idx += nthreads) {
+        const int tt = idx / kRows, rr = idx % kRows;
+        const int row = tile0 + rr;
         if (row >= H) continue;
         float sum = 0.f;
-        for (int s = 0; s < A.k; ++s)
-            sum = fmaf(wts[int64_t(tt) * A.k + s], ws.o[int64_t(s_pair[tt][s]) * H + row], sum);
-        if (A.has_shared) sum += ws.o[int64_t(s_pair[tt][A.k]) * H + row];
+        for (int s = 0; s < A.k; ++s) sum = fmaf(wts[int64_t(tt) * A.k + s], s_o[s_pair[tt][s]][rr], sum);
+        if (A.has_shared) sum += s_o[s_pair[tt][A.k]][rr];
         y[int64_t(tt) * H + row] = sum;
     }
-    if (tid == 0) ws.counters[blockIdx.x] = 0;
 }
 
-inline int pow2_tokens(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16; }
-
-// Row-tile geometry of the down kernel (used by the workspace layout too).
-inline int down_lanes(int64_t I) { return I / 32 >= 64 ? 64 : 16; }
-inline int down_rows_per_tile(int64_t I) {
-    const int G = down_lanes(I);
-    return (kBlock / kWave) * (kWave / G) * 1;
-}
-
-template <int MT, int GU, int GD>
+// C = 1 when a row fits in one chunk per lane, else the runtime chunk loop.
+template <int MT, int GU, int CU, int GD, int CD>
 hipError_t moe_go(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const float* w, int t,
                   float* y, const MoeWorkspace& ws, hipStream_t s) {
     constexpr int RA = 2;
     const int max_groups = t * A.k + (A.has_shared ? 1 : 0);
     const int a_rows_per_block = (kBlock / kWave) * (kWave / GU) * RA;
     const dim3 g1((A.I + a_rows_per_block - 1) / a_rows_per_block, max_groups);
-    hipLaunchKernelGGL((k_moe_gate_up<MT, GU, RA>), g1, dim3(kBlock), 0, s, A, x, ids, t, ws);
+    hipLaunchKernelGGL((k_moe_gate_up<MT, GU, CU, RA>), g1, dim3(kBlock), 0, s, A, x, ids, t, ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 g2(A.n_tiles_down, max_groups);
-    hipLaunchKernelGGL((k_moe_down<MT, GD, 1>), g2, dim3(kBlock), 0, s, A, w, t, y, ws);
+    constexpr int kRowsDown = kWave / GD;  // one row per lane group
+    const int waves = max_groups < 16 ? max_groups : 16;
+    const dim3 g2((A.H + kRowsDown - 1) / kRowsDown);
+    hipLaunchKernelGGL((k_moe_down<MT, GD, CD, 1>), g2, dim3(kWave * waves), 0, s, A, w, t, y, ws);
     return hipGetLastError();
+}
+
+template <int MT, int GU, int CU>
+hipError_t moe_down_shape(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const float* w, int t,
+                          float* y, const MoeWorkspace& ws, hipStream_t s) {
+    const int jd = A.I / 32;
+    if (lanes_per_row(jd) == 64)
+        return jd <= 64 ? moe_go<MT, GU, CU, 64, 1>(A, x, ids, w, t, y, ws, s)
+                        : moe_go<MT, GU, CU, 64, 0>(A, x, ids, w, t, y, ws, s);
+    return jd <= 16 ? moe_go<MT, GU, CU, 16, 1>(A, x, ids, w, t, y, ws, s)
+                    : moe_go<MT, GU, CU, 16, 0>(A, x, ids, w, t, y, ws, s);
 }
 
 template <int MT>
 hipError_t moe_mt(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const float* w, int t,
                   float* y, const MoeWorkspace& ws, hipStream_t s) {
-    const bool gu_wide = A.H / 32 >= 64, dn_wide = A.I / 32 >= 64;
-    if (gu_wide && dn_wide) return moe_go<MT, 64, 64>(A, x, ids, w, t, y, ws, s);
-    if (gu_wide) return moe_go<MT, 64, 16>(A, x, ids, w, t, y, ws, s);
-    if (dn_wide) return moe_go<MT, 16, 64>(A, x, ids, w, t, y, ws, s);
-    return moe_go<MT, 16, 16>(A, x, ids, w, t, y, ws, s);
+    const int ju = A.H / 32;
+    if (lanes_per_row(ju) == 64)
+        return ju <= 64 ? moe_down_shape<MT, 64, 1>(A, x, ids, w, t, y, ws, s)
+                        : moe_down_shape<MT, 64, 0>(A, x, ids, w, t, y, ws, s);
+    return ju <= 16 ? moe_down_shape<MT, 16, 1>(A, x, ids, w, t, y, ws, s)
+                    : moe_down_shape<MT, 16, 0>(A, x, ids, w, t, y, ws, s);
 }
 
 }  // namespace
@@ -406,7 +399,6 @@ hipError_t launch_route_topk(const float* logits, int64_t t, int e, int top_k, i
 size_t moe_workspace_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, void* base) {
     const int64_t P = t * (d->top_k + (d->has_shared ? 1 : 0));
     const int64_t H = d->hidden, I = d->inter;
-    const int64_t tiles = (H + down_rows_per_tile(I) - 1) / down_rows_per_tile(I);
     int64_t off = 0;
     auto take = [&](int64_t bytes) {
         const int64_t at = off;
@@ -421,7 +413,6 @@ size_t moe_workspace_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, v
     const int64_t o_a = take(2 * P * I);
     const int64_t o_h = (d->flags & QG_MOE_KEEP_H) ? take(4 * P * 2 * I) : -1;
     const int64_t o_o = take(4 * P * H);
-    const int64_t o_cnt = take(4 * tiles);
     if (ws && base) {
         char* b = static_cast<char*>(base);
         ws->n_groups = reinterpret_cast<int32_t*>(b + o_ng);
@@ -432,8 +423,6 @@ size_t moe_workspace_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, v
         ws->a = reinterpret_cast<uint16_t*>(b + o_a);
         ws->h = o_h >= 0 ? reinterpret_cast<float*>(b + o_h) : nullptr;
         ws->o = reinterpret_cast<float*>(b + o_o);
-        ws->counters = reinterpret_cast<uint32_t*>(b + o_cnt);
-        ws->o_scratch = ws->o;
     }
     return size_t(off);
 }
@@ -453,12 +442,9 @@ hipError_t launch_moe(const qg_moe_desc* d, const uint16_t* x, const int32_t* id
     A.dn_stride = d->down_stride;
     A.gu_scale = d->gate_up_scale;
     A.dn_scale = d->down_scale;
-    A.n_tiles_down = int((d->hidden + down_rows_per_tile(d->inter) - 1) / down_rows_per_tile(d->inter));
-    switch (pow2_tokens(t)) {
+    switch (token_class(t)) {
         case 1: return moe_mt<1>(A, x, ids, w, t, y, ws, s);
-        case 2: return moe_mt<2>(A, x, ids, w, t, y, ws, s);
         case 4: return moe_mt<4>(A, x, ids, w, t, y, ws, s);
-        case 8: return moe_mt<8>(A, x, ids, w, t, y, ws, s);
         default: return moe_mt<16>(A, x, ids, w, t, y, ws, s);
     }
 }

@@ -16,6 +16,26 @@ extern std::atomic<int> g_last_hip_error;
 
 void record_hip_error(hipError_t e) { g_last_hip_error.store(int(e)); }
 
+hipError_t device_cu_count(int* cus) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];  // 0 = not yet queried
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) {
+        if (const int v = cache[dev].load(std::memory_order_relaxed)) {
+            *cus = v;
+            return hipSuccess;
+        }
+    }
+    int v = 0;
+    if (hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev); e != hipSuccess)
+        return e;
+    if (v < 1) v = 1;
+    if (dev >= 0 && dev < kMaxDevices) cache[dev].store(v, std::memory_order_relaxed);
+    *cus = v;
+    return hipSuccess;
+}
+
 namespace {
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }

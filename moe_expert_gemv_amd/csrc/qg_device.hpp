@@ -40,6 +40,20 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_f
 __device__ __forceinline__ float bf16x2_lo(bf16x2 v) { return float(v.x); }
 __device__ __forceinline__ float bf16x2_hi(bf16x2 v) { return float(v.y); }
 
+// One dword of a Q4_0 block (layout V1): lo = elements 4q..4q+3 (low
+// nibbles), hi = elements 16+4q..16+4q+3 (high nibbles), one unsigned code
+// per byte.
+__device__ __forceinline__ void q4_unpack(uint32_t c, uint32_t& lo, uint32_t& hi) {
+    lo = c & 0x0F0F0F0Fu;
+    hi = (c >> 4) & 0x0F0F0F0Fu;
+}
+
+// Signed byte B of c as fp32 (Q8_0 codes).
+template <int B>
+__device__ __forceinline__ float i8_to_f32(uint32_t c) {
+    return float(int32_t(c << (24 - 8 * B)) >> 24);
+}
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -106,5 +120,14 @@ __device__ __forceinline__ u32x4 ld_stream16(const void* p) {
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Branch-free predicated loads: the load is always issued (callers pass an
+// address that is valid either way) and the value is replaced by zero when
+// ok is false.  Keeping loads out of branches lets the compiler count
+// outstanding loads exactly, so later loads stay in flight while earlier
+// data is used.
+__device__ __forceinline__ u32x4 zero_unless(bool ok, const u32x4& v) {
+    return u32x4{ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u};
+}
 
 }  // namespace qg

@@ -100,6 +100,29 @@ int qg_pack_q8_0(const int8_t* codes, const uint16_t* scales, int64_t n, int64_t
     return QG_OK;
 }
 
+// Fused gate/up matrix: logical rows [0, inter) gate, [inter, 2*inter) up;
+// packed row 2i = gate row i, packed row 2i+1 = up row i.
+int qg_pack_nvfp4_gate_up(const uint8_t* codes, const uint8_t* scales, int64_t inter, int64_t k, void* dst,
+                          size_t dst_bytes) {
+    const int64_t n = 2 * inter;
+    int st = check_pack_args(QG_NVFP4, codes, scales, n, k, dst, dst_bytes);
+    if (st) return st;
+    for (int64_t i = 0; i < n * k; ++i)
+        if (codes[i] > 15) return QG_EINVAL;
+    uint8_t* out = static_cast<uint8_t*>(dst);
+    std::memset(out, 0, size_t(qg::packed_bytes(QG_NVFP4, n, k)));
+    const int64_t crow = k / 2, srow = k / 16;
+    uint8_t* splane = out + qg::scale_plane_offset(QG_NVFP4, n, k);
+    for (int64_t r = 0; r < n; ++r) {
+        const int64_t pr = r < inter ? 2 * r : 2 * (r - inter) + 1;  // packed row
+        const uint8_t* c = codes + r * k;
+        uint8_t* o = out + pr * crow;
+        for (int64_t j = 0; j < crow; ++j) o[j] = uint8_t(c[2 * j] | (c[2 * j + 1] << 4));
+        std::memcpy(splane + pr * srow, scales + r * srow, size_t(srow));
+    }
+    return QG_OK;
+}
+
 // ---------------------------------------------------------------- unpackers
 
 int qg_unpack_nvfp4(const void* src, size_t src_bytes, int64_t n, int64_t k, uint8_t* codes,
@@ -115,6 +138,26 @@ int qg_unpack_nvfp4(const void* src, size_t src_bytes, int64_t n, int64_t k, uin
             codes[r * k + 2 * j + 1] = v >> 4;
         }
     std::memcpy(scales, in + qg::scale_plane_offset(QG_NVFP4, n, k), size_t(n * (k / 16)));
+    return QG_OK;
+}
+
+int qg_unpack_nvfp4_gate_up(const void* src, size_t src_bytes, int64_t inter, int64_t k, uint8_t* codes,
+                            uint8_t* scales) {
+    const int64_t n = 2 * inter;
+    int st = check_pack_args(QG_NVFP4, codes, scales, n, k, src, src_bytes);
+    if (st) return st;
+    const uint8_t* in = static_cast<const uint8_t*>(src);
+    const int64_t crow = k / 2, srow = k / 16;
+    const uint8_t* splane = in + qg::scale_plane_offset(QG_NVFP4, n, k);
+    for (int64_t r = 0; r < n; ++r) {
+        const int64_t pr = r < inter ? 2 * r : 2 * (r - inter) + 1;
+        for (int64_t j = 0; j < crow; ++j) {
+            const uint8_t v = in[pr * crow + j];
+            codes[r * k + 2 * j] = v & 15;
+            codes[r * k + 2 * j + 1] = v >> 4;
+        }
+        std::memcpy(scales + r * srow, splane + pr * srow, size_t(srow));
+    }
     return QG_OK;
 }
 

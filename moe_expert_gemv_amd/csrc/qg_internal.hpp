@@ -12,6 +12,9 @@ namespace qg {
 
 void record_hip_error(hipError_t e);
 
+// Compute units of the current device (cached per device after the first call).
+hipError_t device_cu_count(int* cus);
+
 // Returns hipSuccess or the launch error.
 hipError_t launch_dequant(int fmt, const uint8_t* w, float s_t, int64_t n, int64_t k, float* out,
                           hipStream_t s);
@@ -37,9 +40,7 @@ struct MoeWorkspace {
     int32_t* pair_slot;
     uint16_t* a;
     float* h;       // nullable
-    float* o;       // nullable
-    uint32_t* counters;
-    float* o_scratch;
+    float* o;
 };
 size_t moe_workspace_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, void* base);
 hipError_t launch_moe(const qg_moe_desc* d, const uint16_t* x, const int32_t* ids, const float* w,

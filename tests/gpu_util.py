@@ -63,6 +63,11 @@ def pack_dev(w: dict):
     return dev_u8(buf)
 
 
+def pack_dev_gate_up(w: dict):
+    """Pack a fused gate/up NVFP4 matrix (gate rows first) with rows interleaved."""
+    return dev_u8(qg.qg_pack_nvfp4_gate_up(w["codes"], w["scales"]))
+
+
 def assert_within(y_gpu, y_ref, abs_sum, what=""):
     """|y_gpu - y_ref| <= 1e-5 * sum|w*x| + 1e-6 element by element."""
     y_gpu = np.asarray(y_gpu, dtype=np.float64)

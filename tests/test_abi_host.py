@@ -111,6 +111,18 @@ def test_pack_layout_is_as_documented(L):
     assert buf[off] == 0x00 and buf[off + 1] == 0x3C
 
 
+def test_gate_up_pack_interleaves_rows(L):
+    g = synth.rng(12)
+    w = synth.nvfp4_weights(g, 2 * 5, 64)
+    buf = qg.qg_pack_nvfp4_gate_up(w["codes"], w["scales"])
+    c, s = qg.qg_unpack_nvfp4_gate_up(buf, 5, 64)
+    assert np.array_equal(c, w["codes"]) and np.array_equal(s, w["scales"])
+    # the same bytes as the plain packer applied to the interleaved row order
+    order = np.ravel(np.column_stack([np.arange(5), 5 + np.arange(5)]))
+    plain = qg.qg_pack_nvfp4(w["codes"][order], w["scales"][order])
+    assert np.array_equal(buf, plain)
+
+
 @settings(max_examples=40, deadline=None)
 @given(n=st.integers(1, 9), kb=st.integers(1, 6), seed=st.integers(0, 2 ** 31 - 1))
 def test_pack_roundtrip_property(n, kb, seed):

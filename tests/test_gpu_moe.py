@@ -70,7 +70,7 @@ class Layer:
         for e in range(E):
             if L.gate_up[e] is None:
                 continue
-            gu[e] = qg.qg_pack_nvfp4(L.gate_up[e]["codes"], L.gate_up[e]["scales"])
+            gu[e] = qg.qg_pack_nvfp4_gate_up(L.gate_up[e]["codes"], L.gate_up[e]["scales"])
             dn[e] = qg.qg_pack_nvfp4(L.down[e]["codes"], L.down[e]["scales"])
         self.gu = dev_u8(gu)
         self.dn = dev_u8(dn)
@@ -171,9 +171,9 @@ def test_moe_single_expert_matches_dense_kernels():
     layer = Layer(L)
     ids_d, w_d = route_gpu(L.logits, 1)
     y, _, _ = run_moe(layer, L.x, ids_d, w_d)
-    from tests.gpu_util import pack_dev
+    from tests.gpu_util import pack_dev, pack_dev_gate_up
     a = empty((3, 512), torch.int16)
-    qg.qgemv_nvfp4_swiglu(pack_dev(L.gate_up[0]), 0.01, 512, 2048, dev(L.x), 3, a, None)
+    qg.qgemv_nvfp4_swiglu(pack_dev_gate_up(L.gate_up[0]), 0.01, 512, 2048, dev(L.x), 3, a, None)
     yd = empty((3, 2048), torch.float32)
     qg.qgemv_nvfp4(pack_dev(L.down[0]), 0.01, 2048, 512, a, 3, yd)
     # weight 1.0: fmaf(1, o, 0) == o
