@@ -264,12 +264,11 @@ class MoE(Workload):
         self.flops_step = int(2 * t * 9 * (2 * I * H + H * I))
         self.name = (f"moe decode (35B-A3B-like): 256 routed + 1 shared experts, hidden {H}, inter {I}, "
                      f"top-8, {t} token(s), routing drawn per step")
-        self.dominant = "route + grouped expert GEMVs (3 kernels)"
+        self.dominant = "moe_forward: routing + grouped gate/up + SwiGLU, grouped down + combine (2 kernels)"
 
     def step(self, i):
-        qg = self.qg
-        qg.moe_route_topk(self.logits[i % self.S], self.t, 256, 8, self.ids, self.w)
-        qg.moe_gemv_grouped(self.descs[i % self.R], self.x, self.ids, self.w, self.t, self.y, self.ws,
+        # routing + grouped expert GEMVs + combine: two launches
+        self.qg.moe_forward(self.descs[i % self.R], self.x, self.logits[i % self.S], self.t, self.y, self.ws,
                             self.ws_bytes)
 
     dominant_launch = step

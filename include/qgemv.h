@@ -234,6 +234,8 @@ size_t moe_workspace_bytes(const qg_moe_desc* d, int64_t t);
  *   uint16 a[P][inter]             bf16 SwiGLU outputs per pair
  *   float h[P][2*inter]            (only with QG_MOE_KEEP_H) gate/up outputs per pair
  *   float o[P][hidden]             down outputs per pair (unweighted)
+ *   int32 ids[t][top_k]            (moe_forward) the routing it computed
+ *   float weights[t][top_k]        (moe_forward) the routing weights
  * This is the expert-major CSR batching of bw24 README (MoE feature entry):
  * each active expert's weights are streamed once for all its tokens.
  *
@@ -249,6 +251,16 @@ size_t moe_workspace_bytes(const qg_moe_desc* d, int64_t t);
 int moe_gemv_grouped(const qg_moe_desc* d, const uint16_t* x, const int32_t* ids,
                      const float* weights, int64_t t, float* y, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* The whole MoE layer from router logits in two launches: the gate/up kernel
+ * first routes every token itself (exactly as moe_route_topk, so ids and
+ * weights are bitwise the same) and writes ids/weights into the workspace,
+ * then the grouped GEMVs and the combine run as in moe_gemv_grouped.  The
+ * result equals moe_route_topk followed by moe_gemv_grouped, bitwise.
+ * logits: device fp32 [t][n_experts] (n_experts <= 1024).  Other arguments as
+ * for moe_gemv_grouped. */
+int moe_forward(const qg_moe_desc* d, const uint16_t* x, const float* logits, int64_t t, float* y,
+                void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------ small-M prefill GEMM
  * Y[t][r] = bf16_rne(s_t * sum_c D[r][c] * X[t][c]) with D = e2m1 * e4m3

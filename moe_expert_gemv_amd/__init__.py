@@ -25,7 +25,7 @@ __all__ = [
     "qg_unpack_nvfp4", "qg_unpack_nvfp4_gate_up", "qg_unpack_q4_0", "qg_unpack_q8_0", "qg_dequant",
     "qgemv_q8_0", "qgemv_nvfp4", "qgemv_nvfp4_swiglu", "qg_quantize_q8_0_act",
     "qgemv_q4_0_a8", "moe_route_topk", "QgMoeDesc", "moe_workspace_bytes",
-    "moe_gemv_grouped", "qgemm_prefill", "EXPORTED_SYMBOLS",
+    "moe_gemv_grouped", "moe_forward", "qgemm_prefill", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
@@ -94,6 +94,7 @@ _SIGNATURES = {
     "moe_route_topk": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "moe_workspace_bytes": (_SZ, [ctypes.POINTER(QgMoeDesc), _I64]),
     "moe_gemv_grouped": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "moe_forward": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _I64, _P, _P, _SZ, _P]),
     "qgemm_prefill": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
@@ -291,6 +292,13 @@ def moe_gemv_grouped(desc: QgMoeDesc, x, ids, weights, t, y, ws, ws_bytes=None, 
     _check("moe_gemv_grouped",
            lib().moe_gemv_grouped(ctypes.byref(desc), _dptr(x), _dptr(ids), _dptr(weights), t,
                                   _dptr(y), _dptr(ws), nbytes, _stream(stream)))
+
+
+def moe_forward(desc: QgMoeDesc, x, logits, t, y, ws, ws_bytes=None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_forward",
+           lib().moe_forward(ctypes.byref(desc), _dptr(x), _dptr(logits), t, _dptr(y), _dptr(ws), nbytes,
+                             _stream(stream)))
 
 
 def qgemm_prefill(w, tensor_scale, n, k, x, m, y, stream=None) -> None:

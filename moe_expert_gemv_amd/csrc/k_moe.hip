@@ -36,65 +36,106 @@ constexpr int kMaxPairs = kMaxTokens * (kMaxTopK + 1);
 
 // ------------------------------------------------------------------ router
 
-// One wave per token; each lane holds PER lane logits (expert = i*64 + lane).
+// (value, index) pair order of the router: larger logit first, ties to the
+// lower expert index; index kNoExpert marks an empty slot (always last).
+constexpr int kNoExpert = 0x7fffffff;
+
+__device__ __forceinline__ bool route_better(float v, int i, float bv, int bi) {
+    return i != kNoExpert && (bi == kNoExpert || v > bv || (v == bv && i < bi));
+}
+
+template <int CTRL>
+__device__ __forceinline__ void route_step_dpp(float& bv, int& bi) {
+    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xf, 0xf, false));
+    const int oi = __builtin_amdgcn_update_dpp(kNoExpert, bi, CTRL, 0xf, 0xf, false);
+    if (route_better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+    }
+}
+
+// Wave-wide best (value, index): the same fixed butterfly as group_sum
+// (DPP within rows of 16, a swizzle across rows, then the two 32-lane halves);
+// every lane returns the winner.
+__device__ __forceinline__ void route_wave_best(float& bv, int& bi) {
+    route_step_dpp<0xB1>(bv, bi);   // lane ^ 1
+    route_step_dpp<0x4E>(bv, bi);   // lane ^ 2
+    route_step_dpp<0x141>(bv, bi);  // half-row mirror
+    route_step_dpp<0x140>(bv, bi);  // row mirror
+    {
+        const float ov = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(bv), 0x401F));
+        const int oi = __builtin_amdgcn_ds_swizzle(bi, 0x401F);
+        if (route_better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+    const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+    const int i0 = __builtin_amdgcn_readlane(bi, 0);
+    const float v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 32));
+    const int i1 = __builtin_amdgcn_readlane(bi, 32);
+    const bool second = route_better(v1, i1, v0, i0);
+    bv = second ? v1 : v0;
+    bi = second ? i1 : i0;
+}
+
+// Top-k of one token's e logits by the calling wave (e <= 64 * PER).  Lane s
+// (s < top_k) returns selection s: its logit in sel_v, its expert in sel_i and
+// its renormalised softmax weight in sel_w.  All lanes must call it.
 template <int PER>
-__global__ __launch_bounds__(kBlock) void k_route_topk(const float* __restrict__ logits, int t, int e,
-                                                       int top_k, int32_t* __restrict__ ids,
-                                                       float* __restrict__ wts) {
+__device__ __forceinline__ void route_one_token(const float* __restrict__ logits, int e, int top_k,
+                                                float& sel_v, int& sel_i, float& sel_w) {
     const int lane = lane_id();
-    const int tok = int(blockIdx.x) * (kBlock / kWave) + int(threadIdx.x) / kWave;
-    if (tok >= t) return;  // uniform per wave
     float v[PER];
     bool taken[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int ex = i * kWave + lane;
-        v[i] = ex < e ? logits[int64_t(tok) * e + ex] : 0.f;
+        const int exs = ex < e ? ex : 0;
+        v[i] = logits[exs];
         taken[i] = ex >= e;
     }
-    float sel_v[16];
-    int sel_i[16];
+    sel_v = 0.f;
+    sel_i = kNoExpert;
     for (int s = 0; s < top_k; ++s) {
-        // lane-local best among the untaken: larger value, then lower index
         float bv = 0.f;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int ex = i * kWave + lane;
-            if (!taken[i] && (bi == 0x7fffffff || v[i] > bv)) {
-                bv = v[i];
-                bi = ex;
-            }
-        }
-        // wave-wide best, same ordering (ties to the lower index)
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            const bool better = oi != 0x7fffffff &&
-                                (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
-            if (better) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        sel_v[s] = bv;
-        sel_i[s] = bi;
+        int bi = kNoExpert;
 #pragma unroll
         for (int i = 0; i < PER; ++i)
-            if (i * kWave + lane == bi) taken[i] = true;
+            if (!taken[i] && route_better(v[i], i * kWave + lane, bv, bi)) {
+                bv = v[i];
+                bi = i * kWave + lane;
+            }
+        route_wave_best(bv, bi);
+        if (lane == s) {
+            sel_v = bv;
+            sel_i = bi;
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) taken[i] = taken[i] || (i * kWave + lane == bi);
     }
-    if (lane == 0) {
-        float ex[16];
-        float sum = 0.f;
-        for (int s = 0; s < top_k; ++s) {
-            ex[s] = expf(sel_v[s] - sel_v[0]);
-            sum += ex[s];
-        }
-        for (int s = 0; s < top_k; ++s) {
-            ids[int64_t(tok) * top_k + s] = sel_i[s];
-            wts[int64_t(tok) * top_k + s] = ex[s] / sum;
-        }
+    // weights: exp(l - l_max) / sum over the selection, summed in slot order
+    const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
+    const float ex = lane < top_k ? expf(sel_v - vmax) : 0.f;
+    float sum = 0.f;
+    for (int s = 0; s < top_k; ++s) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), s));
+    sel_w = ex / sum;
+}
+
+// One wave per token.
+template <int PER>
+__global__ __launch_bounds__(kBlock) void k_route_topk(const float* __restrict__ logits, int t, int e,
+                                                       int top_k, int32_t* __restrict__ ids,
+                                                       float* __restrict__ wts) {
+    const int tok = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * (kBlock / kWave) + int(threadIdx.x) / kWave);
+    if (tok >= t) return;  // uniform per wave
+    float sv, sw;
+    int si;
+    route_one_token<PER>(logits + int64_t(tok) * e, e, top_k, sv, si, sw);
+    const int lane = lane_id();
+    if (lane < top_k) {
+        ids[int64_t(tok) * top_k + lane] = si;
+        wts[int64_t(tok) * top_k + lane] = sw;
     }
 }
 
@@ -174,14 +215,37 @@ struct MoeArgs {
 
 // blockIdx.y = expert group, blockIdx.x = tile of a-rows.  Each group of G
 // lanes owns RA a-rows (RA gate rows and the RA matching up rows).
-template <int MT, int G, int C, int RA>
+// ROUTE: the workgroup first routes every token itself from the logits
+// (route_one_token, one wave per token) into LDS; workgroup (0,0) publishes
+// the ids and weights in the workspace for the down kernel.
+template <int MT, int G, int C, int RA, bool ROUTE, int PER>
 __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_t* __restrict__ x,
-                                                        const int32_t* __restrict__ ids, int t,
+                                                        const int32_t* __restrict__ ids_in,
+                                                        const float* __restrict__ logits, int t,
                                                         MoeWorkspace ws) {
     __shared__ Csr c;
     __shared__ int s_e[kMaxPairs], s_first[kMaxPairs];
-    build_csr(ids, t, A.k, A.E, A.has_shared, c, s_e, s_first);
+    __shared__ int s_ids[kMaxTokens * kMaxTopK];
     const int tid = int(threadIdx.x);
+    const int32_t* ids = ids_in;
+    if constexpr (ROUTE) {
+        const int lane = lane_id();
+        for (int tok = tid / kWave; tok < t; tok += kBlock / kWave) {  // uniform per wave
+            float sv, sw;
+            int si;
+            route_one_token<PER>(logits + int64_t(tok) * A.E, A.E, A.k, sv, si, sw);
+            if (lane < A.k) {
+                s_ids[tok * A.k + lane] = si;
+                if (blockIdx.x == 0 && blockIdx.y == 0) {
+                    ws.ids[tok * A.k + lane] = si;
+                    ws.wts[tok * A.k + lane] = sw;
+                }
+            }
+        }
+        __syncthreads();
+        ids = s_ids;
+    }
+    build_csr(ids, t, A.k, A.E, A.has_shared, c, s_e, s_first);
     if (blockIdx.x == 0 && blockIdx.y == 0) {
         const int P = t * (A.k + A.has_shared);
         if (tid == 0) *ws.n_groups = c.n_groups;
@@ -341,13 +405,25 @@ __global__ __launch_bounds__(1024) void k_moe_down(MoeArgs A, const float* __res
 
 // C = 1 when a row fits in one chunk per lane, else the runtime chunk loop.
 template <int MT, int GU, int CU, int GD, int CD>
-hipError_t moe_go(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const float* w, int t,
-                  float* y, const MoeWorkspace& ws, hipStream_t s) {
+hipError_t moe_go(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const float* w, const float* logits,
+                  int t, float* y, const MoeWorkspace& ws, hipStream_t s) {
     constexpr int RA = 2;
     const int max_groups = t * A.k + (A.has_shared ? 1 : 0);
     const int a_rows_per_block = (kBlock / kWave) * (kWave / GU) * RA;
     const dim3 g1((A.I + a_rows_per_block - 1) / a_rows_per_block, max_groups);
-    hipLaunchKernelGGL((k_moe_gate_up<MT, GU, CU, RA>), g1, dim3(kBlock), 0, s, A, x, ids, t, ws);
+    if (logits) {
+        const int per = (A.E + kWave - 1) / kWave;
+        if (per <= 4)
+            hipLaunchKernelGGL((k_moe_gate_up<MT, GU, CU, RA, true, 4>), g1, dim3(kBlock), 0, s, A, x, nullptr,
+                               logits, t, ws);
+        else
+            hipLaunchKernelGGL((k_moe_gate_up<MT, GU, CU, RA, true, 16>), g1, dim3(kBlock), 0, s, A, x, nullptr,
+                               logits, t, ws);
+        w = ws.wts;
+    } else {
+        hipLaunchKernelGGL((k_moe_gate_up<MT, GU, CU, RA, false, 1>), g1, dim3(kBlock), 0, s, A, x, ids, nullptr,
+                           t, ws);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     constexpr int kRowsDown = kWave / GD;  // one row per lane group
@@ -358,25 +434,25 @@ hipError_t moe_go(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const
 }
 
 template <int MT, int GU, int CU>
-hipError_t moe_down_shape(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const float* w, int t,
-                          float* y, const MoeWorkspace& ws, hipStream_t s) {
+hipError_t moe_down_shape(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const float* w,
+                          const float* logits, int t, float* y, const MoeWorkspace& ws, hipStream_t s) {
     const int jd = A.I / 32;
     if (lanes_per_row(jd) == 64)
-        return jd <= 64 ? moe_go<MT, GU, CU, 64, 1>(A, x, ids, w, t, y, ws, s)
-                        : moe_go<MT, GU, CU, 64, 0>(A, x, ids, w, t, y, ws, s);
-    return jd <= 16 ? moe_go<MT, GU, CU, 16, 1>(A, x, ids, w, t, y, ws, s)
-                    : moe_go<MT, GU, CU, 16, 0>(A, x, ids, w, t, y, ws, s);
+        return jd <= 64 ? moe_go<MT, GU, CU, 64, 1>(A, x, ids, w, logits, t, y, ws, s)
+                        : moe_go<MT, GU, CU, 64, 0>(A, x, ids, w, logits, t, y, ws, s);
+    return jd <= 16 ? moe_go<MT, GU, CU, 16, 1>(A, x, ids, w, logits, t, y, ws, s)
+                    : moe_go<MT, GU, CU, 16, 0>(A, x, ids, w, logits, t, y, ws, s);
 }
 
 template <int MT>
-hipError_t moe_mt(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const float* w, int t,
-                  float* y, const MoeWorkspace& ws, hipStream_t s) {
+hipError_t moe_mt(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const float* w, const float* logits,
+                  int t, float* y, const MoeWorkspace& ws, hipStream_t s) {
     const int ju = A.H / 32;
     if (lanes_per_row(ju) == 64)
-        return ju <= 64 ? moe_down_shape<MT, 64, 1>(A, x, ids, w, t, y, ws, s)
-                        : moe_down_shape<MT, 64, 0>(A, x, ids, w, t, y, ws, s);
-    return ju <= 16 ? moe_down_shape<MT, 16, 1>(A, x, ids, w, t, y, ws, s)
-                    : moe_down_shape<MT, 16, 0>(A, x, ids, w, t, y, ws, s);
+        return ju <= 64 ? moe_down_shape<MT, 64, 1>(A, x, ids, w, logits, t, y, ws, s)
+                        : moe_down_shape<MT, 64, 0>(A, x, ids, w, logits, t, y, ws, s);
+    return ju <= 16 ? moe_down_shape<MT, 16, 1>(A, x, ids, w, logits, t, y, ws, s)
+                    : moe_down_shape<MT, 16, 0>(A, x, ids, w, logits, t, y, ws, s);
 }
 
 }  // namespace
@@ -413,6 +489,8 @@ size_t moe_workspace_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, v
     const int64_t o_a = take(2 * P * I);
     const int64_t o_h = (d->flags & QG_MOE_KEEP_H) ? take(4 * P * 2 * I) : -1;
     const int64_t o_o = take(4 * P * H);
+    const int64_t o_ids = take(4 * t * d->top_k);
+    const int64_t o_wts = take(4 * t * d->top_k);
     if (ws && base) {
         char* b = static_cast<char*>(base);
         ws->n_groups = reinterpret_cast<int32_t*>(b + o_ng);
@@ -423,12 +501,14 @@ size_t moe_workspace_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, v
         ws->a = reinterpret_cast<uint16_t*>(b + o_a);
         ws->h = o_h >= 0 ? reinterpret_cast<float*>(b + o_h) : nullptr;
         ws->o = reinterpret_cast<float*>(b + o_o);
+        ws->ids = reinterpret_cast<int32_t*>(b + o_ids);
+        ws->wts = reinterpret_cast<float*>(b + o_wts);
     }
     return size_t(off);
 }
 
 hipError_t launch_moe(const qg_moe_desc* d, const uint16_t* x, const int32_t* ids, const float* w,
-                      int t, float* y, const MoeWorkspace& ws, hipStream_t s) {
+                      const float* logits, int t, float* y, const MoeWorkspace& ws, hipStream_t s) {
     MoeArgs A;
     A.E = d->n_experts;
     A.k = d->top_k;
@@ -443,9 +523,9 @@ hipError_t launch_moe(const qg_moe_desc* d, const uint16_t* x, const int32_t* id
     A.gu_scale = d->gate_up_scale;
     A.dn_scale = d->down_scale;
     switch (token_class(t)) {
-        case 1: return moe_mt<1>(A, x, ids, w, t, y, ws, s);
-        case 4: return moe_mt<4>(A, x, ids, w, t, y, ws, s);
-        default: return moe_mt<16>(A, x, ids, w, t, y, ws, s);
+        case 1: return moe_mt<1>(A, x, ids, w, logits, t, y, ws, s);
+        case 4: return moe_mt<4>(A, x, ids, w, logits, t, y, ws, s);
+        default: return moe_mt<16>(A, x, ids, w, logits, t, y, ws, s);
     }
 }
 

@@ -154,7 +154,20 @@ int moe_gemv_grouped(const qg_moe_desc* d, const uint16_t* x, const int32_t* ids
     MoeWorkspace lay;
     const size_t need = moe_workspace_layout(d, t, &lay, ws);
     if (ws_bytes < need) return QG_ENOSPC;
-    return finish(launch_moe(d, x, ids, weights, int(t), y, lay, as_stream(stream)));
+    return finish(launch_moe(d, x, ids, weights, nullptr, int(t), y, lay, as_stream(stream)));
+}
+
+int moe_forward(const qg_moe_desc* d, const uint16_t* x, const float* logits, int64_t t, float* y, void* ws,
+                size_t ws_bytes, void* stream) {
+    if (int st = check_moe_desc(d)) return st;
+    if (!x || !logits || !y || !ws) return QG_EINVAL;
+    if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(y, 16) || !aligned(ws, 256)) return QG_EINVAL;
+    if (t < 1) return QG_EINVAL;
+    if (t > QG_MAX_M || d->n_experts > 1024) return QG_EUNSUPPORTED;
+    MoeWorkspace lay;
+    const size_t need = moe_workspace_layout(d, t, &lay, ws);
+    if (ws_bytes < need) return QG_ENOSPC;
+    return finish(launch_moe(d, x, nullptr, nullptr, logits, int(t), y, lay, as_stream(stream)));
 }
 
 int qgemm_prefill(const void* w, float tensor_scale, int64_t n, int64_t k, const uint16_t* x,

@@ -41,10 +41,14 @@ struct MoeWorkspace {
     uint16_t* a;
     float* h;       // nullable
     float* o;
+    int32_t* ids;   // routing written by the fused path (moe_forward)
+    float* wts;
 };
 size_t moe_workspace_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, void* base);
+// ids/w given: grouped GEMVs only.  logits given (ids, w null): routing is
+// done inside the gate/up kernel and written to ws.ids / ws.wts.
 hipError_t launch_moe(const qg_moe_desc* d, const uint16_t* x, const int32_t* ids, const float* w,
-                      int t, float* y, const MoeWorkspace& ws, hipStream_t s);
+                      const float* logits, int t, float* y, const MoeWorkspace& ws, hipStream_t s);
 
 hipError_t launch_prefill(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x,
                           int64_t m, uint16_t* y, hipStream_t s);

@@ -213,6 +213,16 @@ def test_moe_workspace_and_checks(L):
     assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 1, FAKE, FAKE + 16, ws1, None) == qg.QG_EINVAL
 
 
+def test_moe_forward_checks(L):
+    d = _desc()
+    ws1 = qg.moe_workspace_bytes(d, 1)
+    f = L.moe_forward
+    assert f(ctypes.byref(d), FAKE, FAKE, 1, FAKE, FAKE, ws1 - 256, None) == qg.QG_ENOSPC
+    assert f(ctypes.byref(d), FAKE, None, 1, FAKE, FAKE, ws1, None) == qg.QG_EINVAL
+    assert f(ctypes.byref(d), FAKE, FAKE, 0, FAKE, FAKE, ws1, None) == qg.QG_EINVAL
+    assert f(ctypes.byref(_desc(n_experts=2048)), FAKE, FAKE, 1, FAKE, FAKE, 1 << 30, None) == qg.QG_EUNSUPPORTED
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(qg, "LIB_PATH", str(tmp_path / "nope.so"))
     monkeypatch.setattr(qg, "_lib", None)

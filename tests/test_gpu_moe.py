@@ -193,6 +193,36 @@ def test_moe_batch_invariance_and_determinism():
         assert np.array_equal(y1.view(np.uint32), y4[t:t + 1].view(np.uint32)), t
 
 
+@pytest.mark.parametrize("t,E,k,shared", [(1, 256, 8, True), (4, 64, 8, True), (16, 300, 8, False), (3, 8, 2, True)])
+def test_moe_forward_matches_route_then_grouped(t, E, k, shared):
+    """The fused path (routing inside the gate/up kernel) gives bitwise the
+    same ids, weights and outputs as moe_route_topk + moe_gemv_grouped."""
+    import torch
+
+    require_gpu()
+    L = synth.moe_case(t=t, n_experts=E, top_k=k, hidden=256, inter=64, has_shared=shared, seed=E + t)
+    layer = Layer(L)
+    ids_d, w_d = route_gpu(L.logits, k)
+    y_split, _, _ = run_moe(layer, L.x, ids_d, w_d)
+    d = layer.desc()
+    nbytes = qg.moe_workspace_bytes(d, t)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    y = empty((t, L.hidden), torch.float32)
+    qg.moe_forward(d, dev(L.x), dev(L.logits), t, y, ws)
+    assert np.array_equal(host(y).view(np.uint32), y_split.view(np.uint32))
+    # the routing it wrote sits at the end of the workspace
+    wsh = host(ws)
+    P = t * (k + int(shared))
+    H, I = L.hidden, L.inter
+    off = 0
+    for nb in (4, 4 * P, 4 * (P + 1), 4 * P, 4 * P, 2 * P * I, 4 * P * 2 * I, 4 * P * H):
+        off = (off + nb + 255) // 256 * 256
+    ids = wsh[off:off + 4 * t * k].view(np.int32).reshape(t, k)
+    off = (off + 4 * t * k + 255) // 256 * 256
+    wts = wsh[off:off + 4 * t * k].view(np.float32).reshape(t, k)
+    assert np.array_equal(ids, host(ids_d)) and np.array_equal(wts.view(np.uint32), host(w_d).view(np.uint32))
+
+
 @pytest.fixture(scope="module")
 def full_layer():
     """The 35B-A3B-like layer: 256 routed experts + 1 shared, H=2048, I=512."""
