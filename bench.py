@@ -13,13 +13,21 @@ Measurement:
   * warmup and timed steps each run as one HIP-graph replay (the pages' decode
     is one graph replay per token); the timed replay is bracketed by
     synchronisations and HIP events;
-  * the dominant kernel is timed alone with HIP events around every launch on
-    its own stream, behind a long blocking copy so the GPU never waits on the
-    CPU between launches;
-  * the CPU baseline is the oracle (fp64 numpy) on a bounded sample of rows.
+  * the dominant kernel is timed alone: a graph of back-to-back launches of it
+    (on rotating weight copies) replayed on its own stream between two HIP
+    events; the launch duration is the region divided by the launch count;
+  * the CPU baseline is the oracle (fp64 numpy, one thread) running whole
+    steps of the same workload for a bounded time.
 
 Prints one JSON line.  ``--config`` selects the other workloads (Q8_0, W4A8,
 MoE, prefill) for design measurements.
+
+Two CPU-only modes turn rocprofv3 output (rocpd SQLite databases) into the
+text summaries and the per-launch HBM traffic kept with the sources:
+  ``--summarize-rocprof DB --command CMD``: per-kernel duration table;
+  ``--write-traffic --config C --fetch-db F --write-db W``: FETCH_SIZE and
+  WRITE_SIZE of the workload's dominant kernel(s), each scaled by what the same
+  counter read for the plain copy that ``--calibrate-copy`` adds to a run.
 """
 from __future__ import annotations
 
@@ -41,25 +49,31 @@ PEAK_BF16_TFLOPS = 2500.0
 ROTATE_BYTES = 1 << 30
 
 
-def source_digest() -> str:
+CSRC = "moe_expert_gemv_amd/csrc"
+_COMMON_SOURCES = ("qg_device.hpp", "qg_layout.hpp")
+COPY_CAL_BYTES = 256 << 20  # the plain copy that calibrates the byte counters
+
+
+def source_digest(files) -> str:
+    """Digest of the sources a kernel is built from (its .hip file, the headers
+    it includes); a committed counter summary is valid only for that digest."""
     h = hashlib.sha256()
-    for d in ("moe_expert_gemv_amd/csrc", "include"):
-        for name in sorted(os.listdir(os.path.join(ROOT, d))):
-            with open(os.path.join(ROOT, d, name), "rb") as f:
-                h.update(name.encode() + f.read())
+    for name in sorted(set(files) | set(_COMMON_SOURCES)):
+        with open(os.path.join(ROOT, CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel: str, launch_bytes_alg: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the summary is missing or the kernel sources changed since."""
+def traffic_from_profile(config: str, cls) -> int | None:
+    """HBM bytes per dominant launch from profiles/traffic.json, or None when
+    there is no entry or the kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    ent = data.get(kernel)
-    if not ent or ent.get("source_digest") != source_digest():
+    ent = data.get(config)
+    if not ent or ent.get("source_digest") != source_digest(cls.sources):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -70,6 +84,8 @@ class Workload:
     name = ""
     dominant = ""
     bound = "hbm"
+    sources: tuple = ()     # files under csrc/ the dominant kernel(s) are built from
+    kernel_re: tuple = ()   # one dominant launch = one dispatch of each of these kernels
 
     def step(self, i: int):  # enqueue step i on the current stream
         raise NotImplementedError
@@ -84,6 +100,9 @@ def _copies(unit_bytes: int) -> int:
 
 class DenseLayer(Workload):
     """gate+up [2I x H] + SwiGLU, then down [H x I], batch m."""
+
+    sources = ("k_gemv_nvfp4.hip", "qg_gemv_core.hpp")
+    kernel_re = (r"k_gemv_nvfp4\w*<[^>]*\btrue>",)
 
     def __init__(self, m=1):
         import torch
@@ -155,6 +174,9 @@ class DenseLayer(Workload):
 
 
 class Q8Gemv(Workload):
+    sources = ("k_gemv_q8.hip",)
+    kernel_re = (r"k_gemv_q8_0\b",)
+
     def __init__(self, m=1):
         import torch
         import moe_expert_gemv_amd as qg
@@ -181,6 +203,9 @@ class Q8Gemv(Workload):
 
 
 class W4A8Gemv(Workload):
+    sources = ("k_gemv_a8.hip",)
+    kernel_re = (r"k_gemv_q4_0_a8\b",)
+
     def __init__(self, m=1):
         import torch
         import moe_expert_gemv_amd as qg
@@ -214,6 +239,9 @@ class W4A8Gemv(Workload):
 
 
 class MoE(Workload):
+    sources = ("k_moe.hip", "qg_gemv_core.hpp")
+    kernel_re = (r"k_moe_gate_up\b", r"k_moe_down\b")
+
     def __init__(self, t=1):
         import torch
         import moe_expert_gemv_amd as qg
@@ -260,7 +288,7 @@ class MoE(Workload):
             u.append(len(set(ids.ravel().tolist())) + 1)
         self.mean_active = float(np.mean(u))
         self.alg_step = int(self.mean_active * (2 * I * H * 9 // 16 + H * I * 9 // 16)) + t * (2 * H + 4 * H)
-        self.dominant_bytes = int(self.mean_active * (2 * I * H * 9 // 16)) + t * 2 * H
+        self.dominant_bytes = self.alg_step  # the dominant launch is the whole moe_forward call
         self.flops_step = int(2 * t * 9 * (2 * I * H + H * I))
         self.name = (f"moe decode (35B-A3B-like): 256 routed + 1 shared experts, hidden {H}, inter {I}, "
                      f"top-8, {t} token(s), routing drawn per step")
@@ -275,6 +303,9 @@ class MoE(Workload):
 
 
 class Prefill(Workload):
+    sources = ("k_prefill.hip",)
+    kernel_re = (r"k_prefill\b",)
+
     def __init__(self, m=512):
         import torch
         import moe_expert_gemv_amd as qg
@@ -302,17 +333,17 @@ class Prefill(Workload):
     dominant_launch = step
 
 
-CONFIGS = {
-    "dense": lambda: DenseLayer(1),
-    "dense-m4": lambda: DenseLayer(4),
-    "q8": lambda: Q8Gemv(1),
-    "w4a8": lambda: W4A8Gemv(1),
-    "w4a8-m4": lambda: W4A8Gemv(4),
-    "moe": lambda: MoE(1),
-    "moe-t4": lambda: MoE(4),
-    "prefill64": lambda: Prefill(64),
-    "prefill128": lambda: Prefill(128),
-    "prefill512": lambda: Prefill(512),
+CONFIGS = {  # name -> (workload class, its size argument)
+    "dense": (DenseLayer, 1),
+    "dense-m4": (DenseLayer, 4),
+    "q8": (Q8Gemv, 1),
+    "w4a8": (W4A8Gemv, 1),
+    "w4a8-m4": (W4A8Gemv, 4),
+    "moe": (MoE, 1),
+    "moe-t4": (MoE, 4),
+    "prefill64": (Prefill, 64),
+    "prefill128": (Prefill, 128),
+    "prefill512": (Prefill, 512),
 }
 
 
@@ -370,26 +401,135 @@ def time_steps(wl: Workload, steps: int, warmup: int, use_graph: bool):
     return t0.elapsed_time(t1) / steps  # ms per step
 
 
-def time_dominant(wl: Workload, launches: int):
-    """Average duration of the dominant kernel: HIP events around each launch
-    on its own stream, queued behind a blocker so launches run back to back."""
+def time_dominant(wl: Workload, launches: int, reps: int = 3):
+    """Average duration of one dominant launch: a graph of `launches`
+    back-to-back launches (rotating weight copies) replayed on its own stream
+    between two HIP events recorded on that stream; best of `reps` replays."""
     import torch
 
     stream = torch.cuda.Stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
     with torch.cuda.stream(stream):
         wl.dominant_launch(0)
     torch.cuda.synchronize()
-    keep = _blocker(stream)
-    with torch.cuda.stream(stream):
-        for i, (a, b) in enumerate(ev):
-            a.record(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(launches):
             wl.dominant_launch(i + 1)
-            b.record(stream)
+    with torch.cuda.stream(stream):
+        g.replay()
     torch.cuda.synchronize()
-    del keep
-    d = np.array([a.elapsed_time(b) for a, b in ev])  # ms
-    return float(np.mean(d)), float(np.median(d))
+    per = []
+    for _ in range(reps):
+        keep = _blocker(stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        del keep
+        per.append(a.elapsed_time(b) / launches)  # ms
+    return float(min(per)), float(np.mean(per))
+
+
+def calibrate_copy():
+    """A plain device copy of COPY_CAL_BYTES (fp32 negation: every byte read
+    once, written once), run three times; the byte counters of a profiled run
+    are scaled by what they read for this kernel."""
+    import torch
+
+    n = COPY_CAL_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        flush.zero_()  # evict src from L2 / Infinity Cache
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- rocprofv3 summaries
+
+def _dispatches(db: str):
+    """(kernel display name, duration ns) of every dispatch in a rocpd database."""
+    import sqlite3
+
+    c = sqlite3.connect(db)
+    q = ("SELECT S.display_name, K.end - K.start FROM rocpd_kernel_dispatch K "
+         "JOIN rocpd_info_kernel_symbol S ON S.id = K.kernel_id AND S.guid = K.guid")
+    return c.execute(q).fetchall()
+
+
+def _short(name: str) -> str:
+    name = name.replace("void ", "", 1) if name.startswith("void ") else name
+    name = name.replace("qg::(anonymous namespace)::", "")
+    depth, out = 0, []
+    for ch in name:  # drop the argument list, keep template arguments
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out)[:110]
+
+
+def summarize_rocprof(db: str, command: str) -> str:
+    by = {}
+    for name, ns in _dispatches(db):
+        by.setdefault(name, []).append(ns / 1e3)
+    total = sum(sum(v) for v in by.values())
+    lines = ["rocprofv3 kernel trace summary (durations in microseconds)",
+             f"command: {command}", "",
+             f"{'calls':>6} {'avg':>9} {'median':>9} {'min':>9} {'max':>9} {'total%':>7}  kernel"]
+    for name, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(v)
+        lines.append(f"{len(a):6d} {a.mean():9.2f} {np.median(a):9.2f} {a.min():9.2f} {a.max():9.2f} "
+                     f"{100 * a.sum() / total:7.2f}  {_short(name)}")
+    return "\n".join(lines) + "\n"
+
+
+def _counter_avgs(db: str, counter: str, pattern: str):
+    """Mean counter value (KiB per dispatch) over dispatches whose name matches."""
+    import re
+    import sqlite3
+
+    c = sqlite3.connect(db)
+    rows = c.execute("SELECT kernel_name, dispatch_id, SUM(value) FROM counters_collection "
+                     "WHERE counter_name = ? GROUP BY dispatch_id, kernel_name", (counter,)).fetchall()
+    v = [val for name, _, val in rows if re.search(pattern, name)]
+    if not v:
+        raise SystemExit(f"no dispatch of /{pattern}/ with {counter} in {db}")
+    return float(np.mean(v)), len(v)
+
+
+def write_traffic(config: str, fetch_db: str, write_db: str, command: str):
+    cls = CONFIGS[config][0]
+    cal_kib = COPY_CAL_BYTES / 1024
+    f_cal, _ = _counter_avgs(fetch_db, "FETCH_SIZE", r"neg_kernel")
+    w_cal, _ = _counter_avgs(write_db, "WRITE_SIZE", r"neg_kernel")
+    f_scale, w_scale = cal_kib / f_cal, cal_kib / w_cal
+    fetch = write = 0.0
+    per_kernel = {}
+    for pat in cls.kernel_re:
+        f, nf = _counter_avgs(fetch_db, "FETCH_SIZE", pat)
+        w, nw = _counter_avgs(write_db, "WRITE_SIZE", pat)
+        per_kernel[pat] = {"fetch_kib_raw": f, "write_kib_raw": w, "dispatches": [nf, nw]}
+        fetch += f * f_scale * 1024
+        write += w * w_scale * 1024
+    ent = {"kernels": per_kernel, "fetch_scale": f_scale, "write_scale": w_scale,
+           "copy_calibration_bytes": COPY_CAL_BYTES, "fetch_bytes_per_launch": int(round(fetch)),
+           "write_bytes_per_launch": int(round(write)), "hbm_bytes_per_launch": int(round(fetch + write)),
+           "source_digest": source_digest(cls.sources), "sources": list(cls.sources), "command": command}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data[config] = ent
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({config: ent}))
 
 
 def main():
@@ -401,7 +541,21 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of a graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain copy of known size first (for byte-counter calibration)")
+    ap.add_argument("--summarize-rocprof", metavar="DB", help="print a kernel summary of a rocpd database")
+    ap.add_argument("--write-traffic", action="store_true", help="record the dominant kernel's HBM bytes")
+    ap.add_argument("--fetch-db")
+    ap.add_argument("--write-db")
+    ap.add_argument("--command", default="", help="the profiled command, recorded with a summary")
     args = ap.parse_args()
+
+    if args.summarize_rocprof:
+        sys.stdout.write(summarize_rocprof(args.summarize_rocprof, args.command))
+        return
+    if args.write_traffic:
+        write_traffic(args.config, args.fetch_db, args.write_db, args.command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode GEMV path runs on a single device (the "
@@ -417,11 +571,14 @@ def main():
 
     qg.lib()
     print(f"[bench] building workload {args.config}", file=sys.stderr, flush=True)
-    wl = CONFIGS[args.config]()
+    cls, size = CONFIGS[args.config]
+    wl = cls(size)
+    if args.calibrate_copy:
+        calibrate_copy()
     print(f"[bench] {wl.name}; {getattr(wl, 'R', 1)} weight copies; timing", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     ms = time_steps(wl, args.steps, args.warmup, not args.no_graph)
-    dom_mean, dom_median = time_dominant(wl, max(20, min(args.steps, 200)))
+    dom_best, dom_mean = time_dominant(wl, max(20, min(args.steps, 200)))
     value = wl.alg_step / (ms * 1e-3) / 1e9
 
     if wl.bound == "mfma":
@@ -432,10 +589,10 @@ def main():
         achieved = wl.dominant_bytes / (dom_mean * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
-    roof["traffic"] = traffic_from_profile(args.config, wl.dominant_bytes)
+    roof["traffic"] = traffic_from_profile(args.config, cls)
     roof["kernel"] = wl.dominant
     roof["us_per_launch"] = dom_mean * 1e3
-    roof["us_per_launch_median"] = dom_median * 1e3
+    roof["us_per_launch_best_replay"] = dom_best * 1e3
     roof["alg_bytes_per_launch"] = wl.dominant_bytes
 
     cpu = None
@@ -460,7 +617,8 @@ def main():
         "data": "synthetic (seeded generators; random codes/scales of the stated distributions)",
         "config": {"workload": wl.name, "alg_bytes_per_step": wl.alg_step,
                    "weight_copies_rotated": getattr(wl, "R", 1),
-                   "graph_replay": not args.no_graph, "source_digest": source_digest()},
+                   "graph_replay": not args.no_graph,
+                   "kernel_source_digest": source_digest(cls.sources)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

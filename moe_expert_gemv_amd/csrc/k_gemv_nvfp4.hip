@@ -1,9 +1,9 @@
 // Dense NVFP4 x bf16 GEMV for gfx950 (wave64), plain or with the SwiGLU
 // epilogue of a fused gate+up projection.
 //
-// The decode step streams every weight byte once and sits at the DRAM
-// bandwidth limit (memra README, known gaps: plain-decode margins at the DRAM
-// wall), so the kernel is shaped around HBM streaming:
+// The decode step streams every weight byte once, so its speed limit is HBM
+// bandwidth (memra README, known gaps), and the kernel is shaped around
+// streaming:
 //  * a group of G lanes (G = 64, or 16 for rows shorter than 2048 elements)
 //    owns R rows; each lane loads 16-byte code chunks c*G + l, c < C, so one
 //    wave-wide load reads 1 KB of a row contiguously (non-temporal);
