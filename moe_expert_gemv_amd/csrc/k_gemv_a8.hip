@@ -38,18 +38,20 @@ struct XBlock {
     int bsum8;  // 8 * sum of the block's q_x
 };
 
-// Block j of token t's activations (j must be a valid block); zeros when !ok.
+// Block j of token t's activations (j must be a valid block).  The token's
+// base addresses are wave-uniform; only the 32-bit block offset is per lane.
+// Without XS the block sum is formed from the codes.
+template <bool XS>
 __device__ __forceinline__ XBlock load_xblock(const int8_t* xq, const uint16_t* xd, const int32_t* xs, int64_t t,
-                                              int k, int nb, int j, bool ok) {
+                                              int k, int nb, uint32_t j) {
     XBlock b;
-    const int8_t* p = xq + t * k + 32 * j;
-    b.x0 = zero_unless(ok, ld16(p));
-    b.x1 = zero_unless(ok, ld16(p + 16));
-    const float dx = f16_to_f32(xd[t * nb + j]);
-    b.dx = ok ? dx : 0.f;
+    const int8_t* p = (xq + t * k) + 32u * j;
+    b.x0 = ld16(p);
+    b.x1 = ld16(p + 16);
+    b.dx = f16_to_f32((xd + t * nb)[j]);
     int s;
-    if (xs) {
-        s = xs[t * nb + j];
+    if constexpr (XS) {
+        s = (xs + t * nb)[j];
     } else {
         s = 0;
 #pragma unroll
@@ -58,12 +60,13 @@ __device__ __forceinline__ XBlock load_xblock(const int8_t* xq, const uint16_t* 
             s = dot4_i8(0x01010101u, b.x1[q], s);
         }
     }
-    b.bsum8 = ok ? 8 * s : 0;
+    b.bsum8 = 8 * s;
     return b;
 }
 
-// Chunk j of a row = Q4_0 block j: 16 code bytes and one fp16 scale.
-template <int R, int MT, int G, int C>
+// Chunk j of a row = Q4_0 block j: 16 code bytes and one fp16 scale.  XS:
+// the quantizer's int32 block sums are given (else formed from the codes).
+template <int R, int MT, int G, int C, bool XS>
 __global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restrict__ w, int64_t soff,
                                                          int n, int k,
                                                          const int8_t* __restrict__ xq,
@@ -72,8 +75,9 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restri
                                                          float* __restrict__ y) {
     constexpr int kGroups = kWave / G;
     const int lane = lane_id();
-    const int grp = lane / G, l = lane % G;
-    const int wave = int(blockIdx.x) * (kBlock / kWave) + int(threadIdx.x) / kWave;
+    const int grp = G == kWave ? 0 : lane / G;  // one group per wave: rows are wave-uniform
+    const int l = G == kWave ? lane : lane % G;
+    const int wave = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * (kBlock / kWave) + int(threadIdx.x) / kWave);
     const int unit = wave * kGroups + grp;
     const int64_t crow = k / 2, srow = (k / 32) * 2;
     const int nb = k / 32;
@@ -92,36 +96,61 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restri
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[r][t] = 0.f;
 
+    // Token slots past m read token 0 (valid addresses); their sums are dropped.
+    int64_t tok[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) tok[t] = t < m ? t : 0;
+
     if constexpr (C > 0) {
+        // Every code chunk and scale of the R*C blocks is loaded first, at a
+        // clamped (always valid) block index; lanes whose block c lies past
+        // the row end keep their sum unchanged.
         u32x4 cw[C][R];
-        float dw[C][R];
+        uint32_t sw[C][R];
+        bool okc[C];
+        uint32_t jc[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const int j = c * G + l;
-            const bool ok = j < nb;
-            const int js = ok ? j : 0;
+            okc[c] = j < nb;
+            jc[c] = okc[c] ? uint32_t(j) : 0u;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                cw[c][r] = zero_unless(ok, ld_stream16(codes[r] + 16 * js));
-                const float dv = f16_to_f32(ld<uint16_t>(scales[r] + 2 * js));
-                dw[c][r] = ok ? dv : 0.f;
+                cw[c][r] = ld_stream16(codes[r] + 16u * jc[c]);
+                sw[c][r] = ld<uint16_t>(scales[r] + 2u * jc[c]);
             }
         }
+        // Tokens in blocks of up to four: per block and chunk, the tokens'
+        // activation blocks are loaded and each row's codes unpacked once.
+        constexpr int TB = MT < 4 ? MT : 4;
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const int j = c * G + l;
-            const bool ok = j < nb;
-            const int js = ok ? j : 0;
+        for (int tb = 0; tb < MT; tb += TB) {
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                if (t < m) {
-                    const XBlock b = load_xblock(xq, xd, xs, t, k, nb, js, ok);
+            for (int c = 0; c < C; ++c) {
+                XBlock b[TB];
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const int isum = q4_block_dot(cw[c][r], b.x0, b.x1) - b.bsum8;
-                        acc[r][t] = fmaf(dw[c][r] * b.dx, float(isum), acc[r][t]);
+                for (int t = 0; t < TB; ++t) b[t] = load_xblock<XS>(xq, xd, xs, tok[tb + t], k, nb, jc[c]);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    uint32_t lo[4], hi[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) q4_unpack(cw[c][r][q], lo[q], hi[q]);
+                    const float dwr = f16_to_f32(sw[c][r]);
+#pragma unroll
+                    for (int t = 0; t < TB; ++t) {
+                        int isum = 0;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            isum = dot4_i8(lo[q], b[t].x0[q], isum);
+                            isum = dot4_i8(hi[q], b[t].x1[q], isum);
+                        }
+                        const float v = fmaf(dwr * b[t].dx, float(isum - b[t].bsum8), acc[r][tb + t]);
+                        acc[r][tb + t] = okc[c] ? v : acc[r][tb + t];
                     }
                 }
+                // Stage the activation loads per chunk and token block: hoisting
+                // them all above the arithmetic would not fit in registers.
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     } else {
@@ -136,7 +165,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restri
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 if (t < m) {
-                    const XBlock b = load_xblock(xq, xd, xs, t, k, nb, j, true);
+                    const XBlock b = load_xblock<XS>(xq, xd, xs, t, k, nb, uint32_t(j));
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
                         const int isum = q4_block_dot(cw[r], b.x0, b.x1) - b.bsum8;
@@ -218,13 +247,23 @@ struct Args {
 
 template <int G, int C, int MT>
 hipError_t go(const Args& A, hipStream_t s) {
-    constexpr int R = rows_per_group(C, MT);
-    const int64_t units = (int64_t(A.n) + R - 1) / R;
-    const int64_t per_block = (kBlock / kWave) * (kWave / G);
-    const dim3 grid(unsigned((units + per_block - 1) / per_block));
-    hipLaunchKernelGGL((k_gemv_q4_0_a8<R, MT, G, C>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.n, A.k, A.xq,
-                       A.xd, A.xs, A.m, A.y);
-    return hipGetLastError();
+    if constexpr (MT >= 16 && C > 4) {
+        // 16 tokens over long rows: the all-loads-first form does not fit in
+        // registers; use the block loop.
+        return go<G, 0, MT>(A, s);
+    } else {
+        constexpr int R = rows_per_group(C, MT);
+        const int64_t units = (int64_t(A.n) + R - 1) / R;
+        const int64_t per_block = (kBlock / kWave) * (kWave / G);
+        const dim3 grid(unsigned((units + per_block - 1) / per_block));
+        if (A.xs)
+            hipLaunchKernelGGL((k_gemv_q4_0_a8<R, MT, G, C, true>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.n,
+                               A.k, A.xq, A.xd, A.xs, A.m, A.y);
+        else
+            hipLaunchKernelGGL((k_gemv_q4_0_a8<R, MT, G, C, false>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.n,
+                               A.k, A.xq, A.xd, A.xs, A.m, A.y);
+        return hipGetLastError();
+    }
 }
 
 template <int G, int MT>

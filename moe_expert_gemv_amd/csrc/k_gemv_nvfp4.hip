@@ -52,8 +52,9 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4(const uint8_t* __restrict
                                                        float* __restrict__ h) {
     constexpr int kGroups = kWave / G;
     const int lane = lane_id();
-    const int grp = lane / G, l = lane % G;
-    const int wave = int(blockIdx.x) * (kBlock / kWave) + int(threadIdx.x) / kWave;
+    const int grp = G == kWave ? 0 : lane / G;  // one group per wave: rows are wave-uniform
+    const int l = G == kWave ? lane : lane % G;
+    const int wave = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * (kBlock / kWave) + int(threadIdx.x) / kWave);
     const int unit = wave * kGroups + grp;
     const int64_t crow = k / 2, srow = k / 16;
 
@@ -283,16 +284,23 @@ hipError_t go_stream(const Args& A, hipStream_t s) {
 
 template <int G, int C, int MT, bool SW>
 hipError_t go(const Args& A, hipStream_t s) {
-    if constexpr (MT == 1 && C > 0 && C <= 6) return go_stream<G, C, SW>(A, s);
-    constexpr int R0 = rows_per_group(C, MT);
-    constexpr int R = SW ? (R0 < 2 ? 2 : R0) : R0;
-    constexpr int per_unit = SW ? R / 2 : R;
-    const int64_t units = (int64_t(A.nout) + per_unit - 1) / per_unit;
-    const int64_t per_block = (kBlock / kWave) * (kWave / G);
-    const dim3 grid(unsigned((units + per_block - 1) / per_block));
-    hipLaunchKernelGGL((k_gemv_nvfp4<R, MT, G, C, SW>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.s_t,
-                       A.nout, A.k, A.x, A.m, A.y, A.a, A.h);
-    return hipGetLastError();
+    if constexpr (MT == 1 && C > 0 && C <= 6) {
+        return go_stream<G, C, SW>(A, s);
+    } else if constexpr (MT >= 16 && C > 4) {
+        // 16 tokens over long rows: the all-loads-first form does not fit in
+        // registers; use the chunk loop.
+        return go<G, 0, MT, SW>(A, s);
+    } else {
+        constexpr int R0 = rows_per_group(C, MT);
+        constexpr int R = SW ? (R0 < 2 ? 2 : R0) : R0;
+        constexpr int per_unit = SW ? R / 2 : R;
+        const int64_t units = (int64_t(A.nout) + per_unit - 1) / per_unit;
+        const int64_t per_block = (kBlock / kWave) * (kWave / G);
+        const dim3 grid(unsigned((units + per_block - 1) / per_block));
+        hipLaunchKernelGGL((k_gemv_nvfp4<R, MT, G, C, SW>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.s_t,
+                           A.nout, A.k, A.x, A.m, A.y, A.a, A.h);
+        return hipGetLastError();
+    }
 }
 
 template <int G, int MT, bool SW>

@@ -5,20 +5,21 @@
 // active expert's weights are streamed once for all its tokens (bw24 README,
 // MoE feature entry: expert-major CSR batching), and keep routing on the device
 // (bw24 README, CUDA-graph decode: a few bytes of host traffic per token).
-// Here a layer is three launches on one stream:
-//   1. k_route_topk       logits -> ids, weights (one wave per token)
-//   2. k_moe_gate_up      every workgroup rebuilds the CSR from ids in LDS (a
-//                         few hundred integer ops), then one (expert group x
-//                         row tile) of the grouped gate/up GEMV + SwiGLU;
-//                         workgroup (0,0) also publishes the CSR in the
-//                         workspace
-//   3. k_moe_down         one row tile of the grouped down GEMV, one wave per
-//                         expert group, then the weighted sum of the routed
-//                         outputs in slot order plus the shared expert, done
-//                         inside the workgroup through LDS
-// Grids are sized for the worst case (t * top_k + 1 groups); workgroups whose
-// group does not exist return at once.
+// A layer is two launches on one stream:
+//   1. gate/up: the routing (moe_forward: one wave per token, from the logits;
+//      moe_gemv_grouped: ids given) and the expert-major CSR are built inside
+//      every workgroup, in LDS, then the grouped gate/up GEMV + SwiGLU; the
+//      first workgroup publishes routing and CSR in the workspace;
+//   2. down: the grouped down GEMV, then the weighted sum of the routed
+//      outputs in slot order plus the shared expert, inside the workgroup
+//      through LDS (no synchronisation between workgroups).
+// One token: a workgroup per (expert group, row tile), grids sized for the
+// worst case (t * top_k + 1 groups), absent groups return at once.  Two to
+// four tokens: the tile path below, one workgroup per row tile holding every
+// group.  moe_route_topk is the routing alone.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "qg_device.hpp"
 #include "qg_gemv_core.hpp"
@@ -33,93 +34,121 @@ constexpr int kBlock = 256;
 constexpr int kMaxTokens = QG_MAX_M;
 constexpr int kMaxTopK = 8;
 constexpr int kMaxPairs = kMaxTokens * (kMaxTopK + 1);
+// Per-expert tensor scales are staged in LDS at kernel start (their load then
+// overlaps the routing instead of trailing the GEMV) for up to this many
+// experts including the shared one; larger rosters read them from memory.
+constexpr int kMaxScaleLds = 1025;
+static_assert(kMaxTokens * kMaxTopK <= kBlock, "build_csr gives each routed pair its own thread");
+static_assert(kMaxPairs % 4 == 0 && kMaxPairs >= kMaxTokens * kMaxTopK, "CSR scratch is read four entries at a time");
 
 // ------------------------------------------------------------------ router
 
-// (value, index) pair order of the router: larger logit first, ties to the
-// lower expert index; index kNoExpert marks an empty slot (always last).
-constexpr int kNoExpert = 0x7fffffff;
-
-__device__ __forceinline__ bool route_better(float v, int i, float bv, int bi) {
-    return i != kNoExpert && (bi == kNoExpert || v > bv || (v == bv && i < bi));
+// Router keys.  A logit v of expert i becomes the 64-bit key
+// (order(v) << 32) | ~i, where order() maps the fp32 bit pattern to an
+// unsigned integer with the same order as the values (-0 counts as +0, NaN
+// below every number); a larger key is a larger logit, ties going to the
+// lower expert index.  Key 0 marks an empty slot and loses to every logit.
+__device__ __forceinline__ uint64_t route_key(float v, int i) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;  // -0 == +0
+    uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    if (v != v) ord = 1u;          // NaN: below every number
+    return (uint64_t(ord) << 32) | uint64_t(~uint32_t(i));
 }
 
-template <int CTRL>
-__device__ __forceinline__ void route_step_dpp(float& bv, int& bi) {
-    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xf, 0xf, false));
-    const int oi = __builtin_amdgcn_update_dpp(kNoExpert, bi, CTRL, 0xf, 0xf, false);
-    if (route_better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-    }
+__device__ __forceinline__ float route_key_value(uint64_t key) {
+    const uint32_t ord = uint32_t(key >> 32);
+    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
 }
 
-// Wave-wide best (value, index): the same fixed butterfly as group_sum
-// (DPP within rows of 16, a swizzle across rows, then the two 32-lane halves);
-// every lane returns the winner.
-__device__ __forceinline__ void route_wave_best(float& bv, int& bi) {
-    route_step_dpp<0xB1>(bv, bi);   // lane ^ 1
-    route_step_dpp<0x4E>(bv, bi);   // lane ^ 2
-    route_step_dpp<0x141>(bv, bi);  // half-row mirror
-    route_step_dpp<0x140>(bv, bi);  // row mirror
-    {
-        const float ov = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(bv), 0x401F));
-        const int oi = __builtin_amdgcn_ds_swizzle(bi, 0x401F);
-        if (route_better(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-        }
-    }
-    const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
-    const int i0 = __builtin_amdgcn_readlane(bi, 0);
-    const float v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 32));
-    const int i1 = __builtin_amdgcn_readlane(bi, 32);
-    const bool second = route_better(v1, i1, v0, i0);
-    bv = second ? v1 : v0;
-    bi = second ? i1 : i0;
+__device__ __forceinline__ int route_key_index(uint64_t key) { return int(~uint32_t(key)); }
+
+// One DPP exchange of the wave-wide key maximum; rows outside ROW_MASK keep
+// their own key.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint64_t route_max_step(uint64_t k) {
+    const uint32_t lo = uint32_t(k), hi = uint32_t(k >> 32);
+    const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false);
+    const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false);
+    const uint64_t o = (uint64_t(ohi) << 32) | olo;
+    return o > k ? o : k;
 }
 
-// Top-k of one token's e logits by the calling wave (e <= 64 * PER).  Lane s
-// (s < top_k) returns selection s: its logit in sel_v, its expert in sel_i and
-// its renormalised softmax weight in sel_w.  All lanes must call it.
+// Largest key of the wave, returned to every lane: butterflies inside rows of
+// 16 lanes, then row broadcasts that leave the total in lane 63.
+__device__ __forceinline__ uint64_t route_wave_max(uint64_t k) {
+    k = route_max_step<0xB1>(k);        // quad_perm [1,0,3,2]
+    k = route_max_step<0x4E>(k);        // quad_perm [2,3,0,1]
+    k = route_max_step<0x141>(k);       // row_half_mirror
+    k = route_max_step<0x140>(k);       // row_mirror: every lane holds its row's maximum
+    k = route_max_step<0x142, 0xA>(k);  // row_bcast:15 into rows 1 and 3
+    k = route_max_step<0x143, 0xC>(k);  // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(k), 63);
+    const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(k >> 32), 63);
+    return (uint64_t(hi) << 32) | lo;
+}
+
+// Loads of one token's e logits for route_select (e <= 64 * PER): lane l
+// gets logits l, l + 64, ...  All loads are unconditional, at clamped (valid)
+// addresses, so they are in flight together.
 template <int PER>
-__device__ __forceinline__ void route_one_token(const float* __restrict__ logits, int e, int top_k,
-                                                float& sel_v, int& sel_i, float& sel_w) {
+__device__ __forceinline__ void route_load(const float* __restrict__ logits, int e, float (&v)[PER]) {
     const int lane = lane_id();
-    float v[PER];
-    bool taken[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = logits[min(i * kWave + lane, e - 1)];
+}
+
+// Top-k of one token's logits (loaded by route_load) by the calling wave.
+// Lane s (s < top_k) returns selection s: its logit in sel_v, its expert in
+// sel_i and its renormalised softmax weight in sel_w.  All lanes must call
+// it.  Each lane sorts its PER keys once; a round takes the wave maximum of
+// the lanes' leading keys and the winning lane moves to its next key.
+template <int PER>
+__device__ __forceinline__ void route_select(const float (&v)[PER], int e, int top_k, float& sel_v, int& sel_i,
+                                             float& sel_w) {
+    const int lane = lane_id();
+    uint64_t key[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int ex = i * kWave + lane;
-        const int exs = ex < e ? ex : 0;
-        v[i] = logits[exs];
-        taken[i] = ex >= e;
+        const uint64_t keep = ex < e ? ~0ull : 0ull;  // slots past e: key 0
+        key[i] = route_key(v[i], ex) & keep;
     }
-    sel_v = 0.f;
-    sel_i = kNoExpert;
-    for (int s = 0; s < top_k; ++s) {
-        float bv = 0.f;
-        int bi = kNoExpert;
+    // descending insertion sort of the lane's keys (a fixed network)
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (!taken[i] && route_better(v[i], i * kWave + lane, bv, bi)) {
-                bv = v[i];
-                bi = i * kWave + lane;
-            }
-        route_wave_best(bv, bi);
-        if (lane == s) {
-            sel_v = bv;
-            sel_i = bi;
+    for (int i = 1; i < PER; ++i)
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+            const uint64_t a = key[j - 1], b = key[j];
+            key[j - 1] = a > b ? a : b;
+            key[j] = a > b ? b : a;
         }
+    uint64_t mine = 0;
+    for (int s = 0; s < top_k; ++s) {
+        const uint64_t best = route_wave_max(key[0]);
+        if (lane == s) mine = best;
+        if (key[0] == best) {  // the winner (keys are distinct) moves to its next key
 #pragma unroll
-        for (int i = 0; i < PER; ++i) taken[i] = taken[i] || (i * kWave + lane == bi);
+            for (int i = 0; i + 1 < PER; ++i) key[i] = key[i + 1];
+            key[PER - 1] = 0;
+        }
     }
+    sel_v = route_key_value(mine);
+    sel_i = route_key_index(mine);
     // weights: exp(l - l_max) / sum over the selection, summed in slot order
     const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
     const float ex = lane < top_k ? expf(sel_v - vmax) : 0.f;
     float sum = 0.f;
     for (int s = 0; s < top_k; ++s) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), s));
     sel_w = ex / sum;
+}
+
+template <int PER>
+__device__ __forceinline__ void route_one_token(const float* __restrict__ logits, int e, int top_k,
+                                                float& sel_v, int& sel_i, float& sel_w) {
+    float v[PER];
+    route_load<PER>(logits, e, v);
+    route_select<PER>(v, e, top_k, sel_v, sel_i, sel_w);
 }
 
 // One wave per token.
@@ -152,39 +181,45 @@ struct Csr {
 // Expert-major CSR of the t*k routed pairs (pair p = token p/k, slot p%k):
 // active experts ascending, pairs inside an expert in ascending (token, slot)
 // order, then the shared expert with every token.  Ids are clamped into
-// [0, E) so that bad ids can never index outside the expert arrays.
+// [0, E) so that bad ids can never index outside the expert arrays.  Thread p
+// handles pair p (t*k <= kBlock); s_e and s_first hold at least t*k rounded up
+// to 4 entries, 16-byte aligned, and are read four at a time.
 __device__ void build_csr(const int32_t* __restrict__ ids, int t, int k, int E, int has_shared,
                           Csr& c, int* s_e, int* s_first) {
     const int P = t * k;
-    const int tid = int(threadIdx.x);
-    for (int p = tid; p < P; p += kBlock) s_e[p] = min(max(ids[p], 0), E - 1);
+    const int P4 = (P + 3) & ~3;
+    const int p = int(threadIdx.x);
+    const int e = p < P ? min(max(ids[p], 0), E - 1) : 0x7fffffff;  // padding sorts after every expert
+    if (p < P4) s_e[p] = e;
     __syncthreads();
-    for (int p = tid; p < P; p += kBlock) {
-        const int e = s_e[p];
-        int less = 0, before = 0;
-        for (int q = 0; q < P; ++q) {
-            const int eq = s_e[q];
-            less += eq < e;
-            before += (q < p) & (eq == e);
+    int less = 0, before = 0;  // pairs of a smaller expert; earlier pairs of the same expert
+    if (p < P) {
+#pragma unroll 4
+        for (int q = 0; q < P4; q += 4) {
+            const int4 v = *reinterpret_cast<const int4*>(s_e + q);
+            less += int(v.x < e) + int(v.y < e) + int(v.z < e) + int(v.w < e);
+            before += int(v.x == e && q < p) + int(v.y == e && q + 1 < p) + int(v.z == e && q + 2 < p) +
+                      int(v.w == e && q + 3 < p);
         }
         const int rank = less + before;
         c.tok[rank] = p / k;
         c.slot[rank] = p % k;
-        s_first[p] = (before == 0) ? less + 1 : 0;  // 1 + offset of the group, or 0
     }
-    __syncthreads();
-    for (int p = tid; p < P; p += kBlock) {
-        if (s_first[p]) {
-            const int e = s_e[p];
-            int g = 0;
-            for (int q = 0; q < P; ++q) g += (s_first[q] != 0) & (s_e[q] < e);
-            c.experts[g] = e;
-            c.offsets[g] = s_first[p] - 1;
+    const bool first = p < P && before == 0;  // the expert's first pair
+    if (p < P4) s_first[p] = first ? 1 : 0;
+    const int U = __syncthreads_count(first);  // active experts
+    if (first) {
+        int g = 0;  // active experts below e
+#pragma unroll 4
+        for (int q = 0; q < P4; q += 4) {
+            const int4 v = *reinterpret_cast<const int4*>(s_e + q);
+            const int4 f = *reinterpret_cast<const int4*>(s_first + q);
+            g += (f.x & int(v.x < e)) + (f.y & int(v.y < e)) + (f.z & int(v.z < e)) + (f.w & int(v.w < e));
         }
+        c.experts[g] = e;
+        c.offsets[g] = less;
     }
-    if (tid == 0) {
-        int U = 0;
-        for (int q = 0; q < P; ++q) U += s_first[q] != 0;
+    if (p == 0) {
         c.offsets[U] = P;
         if (has_shared) {
             c.experts[U] = E;
@@ -192,11 +227,10 @@ __device__ void build_csr(const int32_t* __restrict__ ids, int t, int k, int E, 
         }
         c.n_groups = U + (has_shared ? 1 : 0);
     }
-    if (has_shared)
-        for (int i = tid; i < t; i += kBlock) {
-            c.tok[P + i] = i;
-            c.slot[P + i] = k;
-        }
+    if (has_shared && p < t) {
+        c.tok[P + p] = p;
+        c.slot[P + p] = k;
+    }
     __syncthreads();
 }
 
@@ -224,10 +258,16 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
                                                         const float* __restrict__ logits, int t,
                                                         MoeWorkspace ws) {
     __shared__ Csr c;
-    __shared__ int s_e[kMaxPairs], s_first[kMaxPairs];
+    __shared__ __align__(16) int s_e[kMaxPairs];
+    __shared__ __align__(16) int s_first[kMaxPairs];
     __shared__ int s_ids[kMaxTokens * kMaxTopK];
+    __shared__ float s_scale[kMaxScaleLds];
     const int tid = int(threadIdx.x);
     const int32_t* ids = ids_in;
+    const int n_scales = A.E + A.has_shared;
+    const bool scales_in_lds = n_scales <= kMaxScaleLds;
+    if (scales_in_lds)
+        for (int i = tid; i < n_scales; i += kBlock) s_scale[i] = A.gu_scale[i];  // visible after the CSR barrier
     if constexpr (ROUTE) {
         const int lane = lane_id();
         for (int tok = tid / kWave; tok < t; tok += kBlock / kWave) {  // uniform per wave
@@ -272,7 +312,7 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
 
     const uint8_t* w = A.gate_up + int64_t(e) * A.gu_stride;
     const int64_t soff = scale_plane_offset(QG_NVFP4, 2 * int64_t(I), H);
-    const float s_t = A.gu_scale[e];
+    const float s_t = scales_in_lds ? s_scale[e] : A.gu_scale[e];
     // gate/up rows are interleaved in the packed matrix: R consecutive rows
     int rows[R];
 #pragma unroll
@@ -293,7 +333,7 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < MT; ++i) acc[r][i] = 0.f;
-    nvfp4_partial<R, MT, G, C>(codes, scales, xp, mg, H / 32, l, acc);
+    nvfp4_partial_m<R, MT, G, C>(codes, scales, xp, mg, H / 32, l, acc);
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -335,13 +375,21 @@ __global__ __launch_bounds__(1024) void k_moe_down(MoeArgs A, const float* __res
     __shared__ int s_exp[kMaxPairs];
     __shared__ int s_pair[kMaxTokens][kMaxTopK + 1];
     __shared__ float s_o[kMaxPairs][kRows];
+    __shared__ float s_scale[kMaxScaleLds];
     const int tid = int(threadIdx.x);
     const int nthreads = int(blockDim.x);
     const int nw = nthreads / kWave;
+    const int n_scales = A.E + A.has_shared;
+    const bool scales_in_lds = n_scales <= kMaxScaleLds;
+    if (scales_in_lds)
+        for (int i = tid; i < n_scales; i += nthreads) s_scale[i] = A.dn_scale[i];  // visible after the barrier below
+    // The CSR header is read up to the worst-case group count (the workspace
+    // holds that many entries), so these loads do not wait for n_groups.
     const int ng = *ws.n_groups;
     const int P = t * (A.k + A.has_shared);
-    for (int i = tid; i <= ng; i += nthreads) s_off[i] = ws.offsets[i];
-    for (int i = tid; i < ng; i += nthreads) s_exp[i] = ws.experts[i];
+    const int gmax = t * A.k + A.has_shared;
+    for (int i = tid; i <= gmax; i += nthreads) s_off[i] = ws.offsets[i];
+    for (int i = tid; i < gmax; i += nthreads) s_exp[i] = ws.experts[i];
     for (int i = tid; i < P; i += nthreads) s_pair[ws.pair_tok[i]][ws.pair_slot[i]] = i;
     __syncthreads();
 
@@ -355,7 +403,7 @@ __global__ __launch_bounds__(1024) void k_moe_down(MoeArgs A, const float* __res
         const int p0 = s_off[g];
         const int mg = s_off[g + 1] - p0;
         const uint8_t* w = A.down + int64_t(e) * A.dn_stride;
-        const float s_t = A.dn_scale[e];
+        const float s_t = scales_in_lds ? s_scale[e] : A.dn_scale[e];
         const uint8_t* codes[R];
         const uint8_t* scales[R];
 #pragma unroll
@@ -372,7 +420,7 @@ __global__ __launch_bounds__(1024) void k_moe_down(MoeArgs A, const float* __res
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int i = 0; i < MT; ++i) acc[r][i] = 0.f;
-        nvfp4_partial<R, MT, G, C>(codes, scales, xp, mg, I / 32, l, acc);
+        nvfp4_partial_m<R, MT, G, C>(codes, scales, xp, mg, I / 32, l, acc);
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -401,6 +449,376 @@ __global__ __launch_bounds__(1024) void k_moe_down(MoeArgs A, const float* __res
         if (A.has_shared) sum += s_o[s_pair[tt][A.k]][rr];
         y[int64_t(tt) * H + row] = sum;
     }
+}
+
+// ------------------------------------------------------------------ tile path (t <= 4)
+
+// For two to four tokens the layer runs as two launches of kTileBlock-thread
+// workgroups, one row tile per workgroup and every expert group in it: wave w
+// takes groups w, w + 8, w + 16, ... and issues the weight loads of all of
+// them before any arithmetic, while activations and per-expert scales sit in
+// LDS (loaded at kernel start, alongside the routing).  The routing and the
+// CSR are thus built once per workgroup rather than once per (group, tile),
+// and with one workgroup per CU the grid is resident at once.  Eight waves
+// per workgroup leave each wave up to 256 registers for the weights in
+// flight.
+constexpr int kTileBlock = 512;
+constexpr int kTileWaves = kTileBlock / kWave;
+constexpr int kStageBytes = 64 * 1024;  // LDS activation staging per workgroup
+constexpr int kStagePerThread = kStageBytes / 16 / kTileBlock;
+constexpr int kScalesPerThread = (kMaxScaleLds + kTileBlock - 1) / kTileBlock;
+static_assert(kMaxTokens * kMaxTopK <= kTileBlock, "build_csr gives each routed pair its own thread");
+
+// Copy n16 16-byte units (n16 >= 1, at most kStagePerThread * kTileBlock)
+// from global memory to LDS: every load is issued (at a clamped, valid index)
+// before the first LDS write, so they are all in flight together.
+__device__ __forceinline__ void stage16(u32x4* __restrict__ dst, const uint16_t* __restrict__ src, int n16) {
+    const int tid = int(threadIdx.x);
+    u32x4 v[kStagePerThread];
+#pragma unroll
+    for (int k = 0; k < kStagePerThread; ++k) v[k] = ld16(src + 8 * int64_t(min(tid + k * kTileBlock, n16 - 1)));
+#pragma unroll
+    for (int k = 0; k < kStagePerThread; ++k)
+        if (tid + k * kTileBlock < n16) dst[tid + k * kTileBlock] = v[k];
+}
+
+// Same for n fp32 scales (1 <= n <= kMaxScaleLds).
+__device__ __forceinline__ void stage_scales(float* __restrict__ dst, const float* __restrict__ src, int n) {
+    const int tid = int(threadIdx.x);
+    float v[kScalesPerThread];
+#pragma unroll
+    for (int k = 0; k < kScalesPerThread; ++k) v[k] = src[min(tid + k * kTileBlock, n - 1)];
+#pragma unroll
+    for (int k = 0; k < kScalesPerThread; ++k)
+        if (tid + k * kTileBlock < n) dst[tid + k * kTileBlock] = v[k];
+}
+
+// One expert group's weights for one wave: R rows x C chunks per lane.
+template <int C, int R>
+struct GroupW {
+    u32x4 cw[C][R];
+    uint32_t sw[C][R];
+};
+
+template <int C, int R>
+__device__ __forceinline__ void load_group_w(GroupW<C, R>& b, const uint8_t* const (&codes)[R],
+                                             const uint8_t* const (&scales)[R], const uint32_t (&jc)[C]) {
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            b.cw[c][r] = ld_stream16(codes[r] + 16u * jc[c]);
+            b.sw[c][r] = ld<uint16_t>(scales[r] + 2u * jc[c]);
+        }
+}
+
+// Row sums of one token from a group's preloaded weights; the token's bf16
+// activations at xl (LDS).  Same arithmetic and order per row as
+// nvfp4_partial: chunks ascending, each 16-element block summed, scaled and
+// added in order.  Tokens of a group are taken one at a time (the few groups
+// with several tokens decode their chunks once per token).
+template <int R, int C>
+__device__ __forceinline__ void nvfp4_token_dot(const GroupW<C, R>& b, const bool (&okc)[C], const uint32_t (&jc)[C],
+                                                const uint16_t* xl, float (&acc)[R]) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        u32x4 xv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[q] = ld16(xl + 32u * jc[c] + 8u * q);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float v = nvfp4_chunk_dot(b.cw[c][r], b.sw[c][r], xv, acc[r]);
+            acc[r] = okc[c] ? v : acc[r];
+        }
+    }
+}
+
+// Gate/up + SwiGLU, tile path.  blockIdx.x = tile of R consecutive packed
+// rows (R/2 a-rows; gate/up rows interleaved), every group; a row of H/32
+// chunks spread over the whole wave (G = 64).  ROUTE as in k_moe_gate_up.
+template <int C, int R, bool ROUTE, int PER, int GW>
+__global__ __launch_bounds__(kTileBlock) void k_moe_gate_up_tile(MoeArgs A, const uint16_t* __restrict__ x,
+                                                                 const int32_t* __restrict__ ids_in,
+                                                                 const float* __restrict__ logits, int t,
+                                                                 MoeWorkspace ws) {
+    static_assert(R % 2 == 0, "gate and up rows come in pairs");
+    __shared__ Csr c;
+    __shared__ __align__(16) int s_e[kMaxPairs];
+    __shared__ __align__(16) int s_first[kMaxPairs];
+    __shared__ int s_ids[kMaxTokens * kMaxTopK];
+    __shared__ float s_scale[kMaxScaleLds];
+    __shared__ __align__(16) uint16_t s_x[kStageBytes / 2];
+    const int tid = int(threadIdx.x);
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int H = A.H, I = A.I, E = A.E;
+
+    // 1. loads: this wave's token logits first, then scales and x into LDS
+    float lv[PER];
+    if constexpr (ROUTE)
+        if (wave < t) route_load<PER>(logits + int64_t(wave) * E, E, lv);
+    stage_scales(s_scale, A.gu_scale, E + A.has_shared);
+    stage16(reinterpret_cast<u32x4*>(s_x), x, t * H / 8);  // x [t][H]
+    // 2. routing (one wave per token), then the CSR
+    const int32_t* ids = ids_in;
+    if constexpr (ROUTE) {
+        if (wave < t) {
+            float sv, sw;
+            int si;
+            route_select<PER>(lv, E, A.k, sv, si, sw);
+            if (lane < A.k) {
+                s_ids[wave * A.k + lane] = si;
+                if (blockIdx.x == 0) {
+                    ws.ids[wave * A.k + lane] = si;
+                    ws.wts[wave * A.k + lane] = sw;
+                }
+            }
+        }
+        __syncthreads();
+        ids = s_ids;
+    }
+    build_csr(ids, t, A.k, E, A.has_shared, c, s_e, s_first);
+    if (blockIdx.x == 0) {
+        const int P = t * (A.k + A.has_shared);
+        if (tid == 0) *ws.n_groups = c.n_groups;
+        for (int i = tid; i < P; i += kTileBlock) {
+            ws.pair_tok[i] = c.tok[i];
+            ws.pair_slot[i] = c.slot[i];
+        }
+        for (int i = tid; i < c.n_groups; i += kTileBlock) ws.experts[i] = c.experts[i];
+        for (int i = tid; i <= c.n_groups; i += kTileBlock) ws.offsets[i] = c.offsets[i];
+    }
+
+    // 3. weight loads of all this wave's groups
+    const int ng = c.n_groups;
+    const int nv = min(GW, (ng - wave + kTileWaves - 1) / kTileWaves);  // groups of this wave (uniform)
+    if (nv <= 0) return;
+    const int nchunks = H / 32;
+    bool okc[C];
+    uint32_t jc[C];
+#pragma unroll
+    for (int cc = 0; cc < C; ++cc) {
+        const int j = cc * kWave + lane;
+        okc[cc] = j < nchunks;
+        jc[cc] = okc[cc] ? uint32_t(j) : 0u;
+    }
+    const int row0 = int(blockIdx.x) * R;
+    const int64_t soff = scale_plane_offset(QG_NVFP4, 2 * int64_t(I), H);
+    GroupW<C, R> gw[GW];
+#pragma unroll
+    for (int j = 0; j < GW; ++j) {
+        if (j < nv) {
+            const int e = c.experts[wave + kTileWaves * j];
+            const uint8_t* w = A.gate_up + int64_t(e) * A.gu_stride;
+            const uint8_t* codes[R];
+            const uint8_t* scales[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int64_t row = min(row0 + r, 2 * I - 1);
+                codes[r] = w + row * (H / 2);
+                scales[r] = w + soff + row * (H / 16);
+            }
+            load_group_w<C, R>(gw[j], codes, scales, jc);
+        }
+    }
+
+    // 4. per group: row sums, reduction, SwiGLU, store
+#pragma unroll
+    for (int j = 0; j < GW; ++j) {
+        if (j >= nv) break;
+        const int g = wave + kTileWaves * j;
+        const int e = c.experts[g];
+        const int p0 = c.offsets[g];
+        const int mg = c.offsets[g + 1] - p0;
+        const float s_t = s_scale[e];
+        for (int i = 0; i < mg; ++i) {  // the group's tokens, one at a time
+            const int p = p0 + i;
+            float acc[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = 0.f;
+            nvfp4_token_dot<R, C>(gw[j], okc, jc, s_x + c.tok[p] * H, acc);
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = group_sum<kWave>(acc[r]) * s_t;
+            if (lane == 0) {
+#pragma unroll
+                for (int r = 0; r < R / 2; ++r) {
+                    const int row = row0 / 2 + r;
+                    if (row >= I) break;
+                    const float gv = acc[2 * r], uv = acc[2 * r + 1];
+                    const float act = gv / (1.0f + expf(-gv)) * uv;
+                    ws.a[int64_t(p) * I + row] = uint16_t(f32_to_bf16_rne(act));
+                    if (ws.h) {
+                        ws.h[int64_t(p) * 2 * I + row] = gv;
+                        ws.h[int64_t(p) * 2 * I + I + row] = uv;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Down + combine, tile path.  blockIdx.x = tile of (64 / G) * R output rows,
+// every group; the SwiGLU outputs of all pairs are staged in LDS.  The
+// combine is the same fixed-order sum as in k_moe_down.
+template <int G, int C, int R, int GW>
+__global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const float* __restrict__ wts, int t,
+                                                              float* __restrict__ y, MoeWorkspace ws) {
+    constexpr int kGroups = kWave / G;
+    constexpr int kRows = kGroups * R;  // rows per tile
+    __shared__ int s_off[kMaxPairs + 1];
+    __shared__ int s_exp[kMaxPairs];
+    __shared__ int s_pair[kMaxTokens][kMaxTopK + 1];
+    __shared__ float s_o[kMaxPairs][kRows];
+    __shared__ float s_scale[kMaxScaleLds];
+    __shared__ __align__(16) uint16_t s_a[kStageBytes / 2];
+    const int tid = int(threadIdx.x);
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int I = A.I, H = A.H;
+    // header up to the worst-case group count, scales and a: one round of loads
+    const int ng = *ws.n_groups;
+    const int P = t * (A.k + A.has_shared);
+    const int gmax = t * A.k + A.has_shared;
+    {  // gmax < P < kTileBlock: one entry per thread, loads first
+        const int oo = ws.offsets[min(tid, gmax)];
+        const int ee = ws.experts[min(tid, gmax - 1)];
+        const int pt = ws.pair_tok[min(tid, P - 1)], ps = ws.pair_slot[min(tid, P - 1)];
+        stage_scales(s_scale, A.dn_scale, A.E + A.has_shared);
+        stage16(reinterpret_cast<u32x4*>(s_a), ws.a, P * I / 8);  // a [P][I]
+        if (tid <= gmax) s_off[tid] = oo;
+        if (tid < gmax) s_exp[tid] = ee;
+        if (tid < P) s_pair[pt][ps] = tid;
+    }
+    __syncthreads();
+
+    const int grp = lane / G, l = lane % G;
+    const int tile0 = int(blockIdx.x) * kRows;
+    const int nv = min(GW, (ng - wave + kTileWaves - 1) / kTileWaves);
+    if (nv > 0) {
+        const int nchunks = I / 32;
+        bool okc[C];
+        uint32_t jc[C];
+#pragma unroll
+        for (int cc = 0; cc < C; ++cc) {
+            const int j = cc * G + l;
+            okc[cc] = j < nchunks;
+            jc[cc] = okc[cc] ? uint32_t(j) : 0u;
+        }
+        const int64_t soff = scale_plane_offset(QG_NVFP4, H, I);
+        GroupW<C, R> gw[GW];
+#pragma unroll
+        for (int j = 0; j < GW; ++j) {
+            if (j < nv) {
+                const int e = s_exp[wave + kTileWaves * j];
+                const uint8_t* w = A.down + int64_t(e) * A.dn_stride;
+                const uint8_t* codes[R];
+                const uint8_t* scales[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int64_t row = min(tile0 + grp * R + r, H - 1);
+                    codes[r] = w + row * (I / 2);
+                    scales[r] = w + soff + row * (I / 16);
+                }
+                load_group_w<C, R>(gw[j], codes, scales, jc);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < GW; ++j) {
+            if (j >= nv) break;
+            const int g = wave + kTileWaves * j;
+            const int e = s_exp[g];
+            const int p0 = s_off[g];
+            const int mg = s_off[g + 1] - p0;
+            const float s_t = s_scale[e];
+            for (int i = 0; i < mg; ++i) {  // the group's pairs, one at a time
+                const int p = p0 + i;
+                float acc[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = 0.f;
+                nvfp4_token_dot<R, C>(gw[j], okc, jc, s_a + p * I, acc);
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = group_sum<G>(acc[r]) * s_t;
+                if (l == 0) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const int row = tile0 + grp * R + r;
+                        s_o[p][grp * R + r] = acc[r];
+                        if (row < H) ws.o[int64_t(p) * H + row] = acc[r];
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < t * kRows; idx += kTileBlock) {
+        const int tt = idx / kRows, rr = idx % kRows;
+        const int row = tile0 + rr;
+        if (row >= H) continue;
+        float sum = 0.f;
+        for (int s = 0; s < A.k; ++s) sum = fmaf(wts[int64_t(tt) * A.k + s], s_o[s_pair[tt][s]][rr], sum);
+        if (A.has_shared) sum += s_o[s_pair[tt][A.k]][rr];
+        y[int64_t(tt) * H + row] = sum;
+    }
+}
+
+// Launch of the tile path; false when the shapes are outside it.
+bool moe_tile_go(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const float* w, const float* logits,
+                 int t, float* y, const MoeWorkspace& ws, hipStream_t s, hipError_t& err) {
+    constexpr int RU = 4;  // packed gate/up rows per tile
+    constexpr int RD = 2;  // down rows per lane group
+    const int ju = A.H / 32, jd = A.I / 32;
+    const int gmax = t * A.k + A.has_shared;
+    const int P = t * (A.k + A.has_shared);
+    const int cu = chunks_per_lane(ju, 64);
+    const bool down16 = lanes_per_row(jd) == 16;
+    const int cd = chunks_per_lane(jd, down16 ? 16 : 64);
+    // one token: the per-(group, tile) kernels are as fast and need no staging
+    if (t < 2 || t > 4 || gmax > 5 * kTileWaves) return false;
+    if (lanes_per_row(ju) != 64 || (cu != 1 && cu != 2) || (cd != 1 && cd != 2)) return false;
+    if (int64_t(t) * A.H * 2 > kStageBytes || int64_t(P) * A.I * 2 > kStageBytes) return false;
+    if (A.E + A.has_shared > kMaxScaleLds) return false;
+    const bool gw1 = gmax <= 2 * kTileWaves;  // else up to 5 groups per wave
+    if (cu == 2 && !gw1) return false;         // too many registers: the general path
+    const dim3 g1((2 * A.I + RU - 1) / RU);
+    auto up = [&](auto cu_c, auto gw_c) {
+        constexpr int CU = decltype(cu_c)::value, GWc = decltype(gw_c)::value;
+        if (logits) {
+            if ((A.E + kWave - 1) / kWave <= 4)
+                hipLaunchKernelGGL((k_moe_gate_up_tile<CU, RU, true, 4, GWc>), g1, dim3(kTileBlock), 0, s, A, x,
+                                   nullptr, logits, t, ws);
+            else
+                hipLaunchKernelGGL((k_moe_gate_up_tile<CU, RU, true, 16, GWc>), g1, dim3(kTileBlock), 0, s, A,
+                                   x, nullptr, logits, t, ws);
+        } else {
+            hipLaunchKernelGGL((k_moe_gate_up_tile<CU, RU, false, 1, GWc>), g1, dim3(kTileBlock), 0, s, A, x,
+                               ids, nullptr, t, ws);
+        }
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I5 = std::integral_constant<int, 5>;
+    if (cu == 1) gw1 ? up(I1{}, I2{}) : up(I1{}, I5{});
+    else gw1 ? up(I2{}, I2{}) : up(I2{}, I5{});
+    err = hipGetLastError();
+    if (err != hipSuccess) return true;
+    if (logits) w = ws.wts;
+    auto down = [&](auto g_c, auto cd_c, auto gw_c) {
+        constexpr int GD = decltype(g_c)::value, CD = decltype(cd_c)::value, GWc = decltype(gw_c)::value;
+        constexpr int kRowsDown = (kWave / GD) * RD;
+        const dim3 g2((A.H + kRowsDown - 1) / kRowsDown);
+        hipLaunchKernelGGL((k_moe_down_tile<GD, CD, RD, GWc>), g2, dim3(kTileBlock), 0, s, A, w, t, y, ws);
+    };
+    using I16 = std::integral_constant<int, 16>;
+    using I64 = std::integral_constant<int, 64>;
+    if (down16) {
+        if (cd == 1) gw1 ? down(I16{}, I1{}, I2{}) : down(I16{}, I1{}, I5{});
+        else gw1 ? down(I16{}, I2{}, I2{}) : down(I16{}, I2{}, I5{});
+    } else {
+        if (cd == 1) gw1 ? down(I64{}, I1{}, I2{}) : down(I64{}, I1{}, I5{});
+        else gw1 ? down(I64{}, I2{}, I2{}) : down(I64{}, I2{}, I5{});
+    }
+    err = hipGetLastError();
+    return true;
 }
 
 // C = 1 when a row fits in one chunk per lane, else the runtime chunk loop.
@@ -522,9 +940,14 @@ hipError_t launch_moe(const qg_moe_desc* d, const uint16_t* x, const int32_t* id
     A.dn_stride = d->down_stride;
     A.gu_scale = d->gate_up_scale;
     A.dn_scale = d->down_scale;
+    hipError_t err = hipSuccess;
     switch (token_class(t)) {
-        case 1: return moe_mt<1>(A, x, ids, w, logits, t, y, ws, s);
-        case 4: return moe_mt<4>(A, x, ids, w, logits, t, y, ws, s);
+        case 1:
+            if (moe_tile_go(A, x, ids, w, logits, t, y, ws, s, err)) return err;
+            return moe_mt<1>(A, x, ids, w, logits, t, y, ws, s);
+        case 4:
+            if (moe_tile_go(A, x, ids, w, logits, t, y, ws, s, err)) return err;
+            return moe_mt<4>(A, x, ids, w, logits, t, y, ws, s);
         default: return moe_mt<16>(A, x, ids, w, logits, t, y, ws, s);
     }
 }

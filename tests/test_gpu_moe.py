@@ -161,6 +161,36 @@ def test_moe_small(t, E, k, H, I, shared):
     check_moe(L, Layer(L), t)
 
 
+@pytest.mark.parametrize("t,E,k,H,I,shared", [(2, 16, 4, 4096, 256, True),   # gate/up 2 chunks per lane
+                                              (3, 8, 2, 2048, 2048, True),   # down rows over 64 lanes
+                                              (2, 8, 2, 2048, 4096, False),  # down 2 chunks per lane
+                                              (4, 64, 8, 2048, 512, True),   # up to 5 groups per wave
+                                              (2, 40, 8, 2048, 512, True)])  # 17 groups
+def test_moe_tile_path(t, E, k, H, I, shared):
+    """Two to four tokens run the row-tile kernels: every launch shape they
+    take, against the oracle."""
+    require_gpu()
+    print(f"[moe tile t={t} E={E} k={k} H={H} I={I} shared={shared}]", flush=True)
+    L = synth.moe_case(t=t, n_experts=E, top_k=k, hidden=H, inter=I, has_shared=shared, seed=t * 1000 + E + H)
+    check_moe(L, Layer(L), t)
+
+
+def test_moe_tile_path_batch_invariance():
+    """Token rows of a 4-token call (row-tile kernels) equal the same tokens
+    run alone (per-group kernels) bitwise, at the full layer width."""
+    require_gpu()
+    L = synth.moe_case(t=4, n_experts=32, top_k=8, hidden=2048, inter=512, has_shared=True, seed=91)
+    layer = Layer(L)
+    ids_d, w_d = route_gpu(L.logits, 8)
+    y4, _, _ = run_moe(layer, L.x, ids_d, w_d)
+    for t in range(4):
+        y1, _, _ = run_moe(layer, L.x[t:t + 1], ids_d[t:t + 1].contiguous(), w_d[t:t + 1].contiguous())
+        assert np.array_equal(y1.view(np.uint32), y4[t:t + 1].view(np.uint32)), t
+    for t in (2, 3):  # 2- and 3-token prefixes, also on the row-tile kernels
+        yt, _, _ = run_moe(layer, L.x[:t], ids_d[:t].contiguous(), w_d[:t].contiguous())
+        assert np.array_equal(yt.view(np.uint32), y4[:t].view(np.uint32)), t
+
+
 def test_moe_single_expert_matches_dense_kernels():
     """E=1, top-1, no shared expert: the grouped path equals the dense
     gate+up/SwiGLU and down kernels bitwise."""
@@ -193,14 +223,16 @@ def test_moe_batch_invariance_and_determinism():
         assert np.array_equal(y1.view(np.uint32), y4[t:t + 1].view(np.uint32)), t
 
 
-@pytest.mark.parametrize("t,E,k,shared", [(1, 256, 8, True), (4, 64, 8, True), (16, 300, 8, False), (3, 8, 2, True)])
-def test_moe_forward_matches_route_then_grouped(t, E, k, shared):
+@pytest.mark.parametrize("t,E,k,shared,H,I", [(1, 256, 8, True, 256, 64), (4, 64, 8, True, 256, 64),
+                                              (16, 300, 8, False, 256, 64), (3, 8, 2, True, 256, 64),
+                                              (4, 128, 8, True, 2048, 512), (2, 300, 8, False, 2048, 256)])
+def test_moe_forward_matches_route_then_grouped(t, E, k, shared, H, I):
     """The fused path (routing inside the gate/up kernel) gives bitwise the
     same ids, weights and outputs as moe_route_topk + moe_gemv_grouped."""
     import torch
 
     require_gpu()
-    L = synth.moe_case(t=t, n_experts=E, top_k=k, hidden=256, inter=64, has_shared=shared, seed=E + t)
+    L = synth.moe_case(t=t, n_experts=E, top_k=k, hidden=H, inter=I, has_shared=shared, seed=E + t)
     layer = Layer(L)
     ids_d, w_d = route_gpu(L.logits, k)
     y_split, _, _ = run_moe(layer, L.x, ids_d, w_d)
@@ -213,7 +245,6 @@ def test_moe_forward_matches_route_then_grouped(t, E, k, shared):
     # the routing it wrote sits at the end of the workspace
     wsh = host(ws)
     P = t * (k + int(shared))
-    H, I = L.hidden, L.inter
     off = 0
     for nb in (4, 4 * P, 4 * (P + 1), 4 * P, 4 * P, 2 * P * I, 4 * P * 2 * I, 4 * P * H):
         off = (off + nb + 255) // 256 * 256
