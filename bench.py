@@ -333,6 +333,29 @@ class Prefill(Workload):
     dominant_launch = step
 
 
+class PrefillWs(Prefill):
+    """m <= 128: the workspace variant (k split into slices of 1024 over
+    workgroups, then a fixed-order sum of the slices' partials)."""
+
+    kernel_re = (r"k_prefill_sk\b", r"k_prefill_reduce\b")
+
+    def __init__(self, m=64):
+        import torch
+
+        super().__init__(m)
+        self.ws_bytes = self.qg.qgemm_prefill_workspace_bytes(self.N, self.K, m)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        # the partial sums make a round trip through memory
+        self.name += f"; k split in {self.K // 1024} slices, fp32 partials {self.ws_bytes} B"
+        self.dominant = "prefill MFMA GEMM (k-split kernel + slice sum)"
+
+    def step(self, i):
+        self.qg.qgemm_prefill_ws(self.w[i % self.R], 0.01, self.N, self.K, self.x, self.m, self.y, self.ws,
+                                 self.ws_bytes)
+
+    dominant_launch = step
+
+
 CONFIGS = {  # name -> (workload class, its size argument)
     "dense": (DenseLayer, 1),
     "dense-m4": (DenseLayer, 4),
@@ -341,8 +364,8 @@ CONFIGS = {  # name -> (workload class, its size argument)
     "w4a8-m4": (W4A8Gemv, 4),
     "moe": (MoE, 1),
     "moe-t4": (MoE, 4),
-    "prefill64": (Prefill, 64),
-    "prefill128": (Prefill, 128),
+    "prefill64": (PrefillWs, 64),
+    "prefill128": (PrefillWs, 128),
     "prefill512": (Prefill, 512),
 }
 

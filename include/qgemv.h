@@ -273,6 +273,25 @@ int moe_forward(const qg_moe_desc* d, const uint16_t* x, const float* logits, in
 int qgemm_prefill(const void* w, float tensor_scale, int64_t n, int64_t k, const uint16_t* x,
                   int64_t m, uint16_t* y, void* stream);
 
+/* Device workspace bytes that qgemm_prefill_ws needs for this shape: nonzero
+ * for m <= 128 (ceil(k / 1024) * m * n fp32 partial sums), 0 when the shape
+ * runs without one (m > 128), and 0 for invalid arguments. */
+size_t qgemm_prefill_workspace_bytes(int64_t n, int64_t k, int64_t m);
+
+/* The same product as qgemm_prefill, with a caller-owned device workspace.
+ * For m <= 128 the k range is split into slices of 1024 handled by separate
+ * workgroups (each reads only its slice of x, the dominant memory traffic of
+ * a small-m product); their fp32 partial sums go to ws and a second launch
+ * adds them in slice order and rounds once.  ws: device, 256-byte aligned,
+ * ws_bytes >= qgemm_prefill_workspace_bytes(n, k, m) (else QG_EINVAL for a
+ * null or misaligned ws, QG_ENOSPC for too few bytes); ignored (may be null)
+ * when that size is 0.  The library reads and writes ws only during the call
+ * (stream-ordered); calls that share a workspace must not overlap.  A row's
+ * result does not depend on the other rows or on m within m <= 128; it
+ * agrees with qgemm_prefill to rounding (the summation order differs). */
+int qgemm_prefill_ws(const void* w, float tensor_scale, int64_t n, int64_t k, const uint16_t* x,
+                     int64_t m, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,8 @@ __all__ = [
     "qg_unpack_nvfp4", "qg_unpack_nvfp4_gate_up", "qg_unpack_q4_0", "qg_unpack_q8_0", "qg_dequant",
     "qgemv_q8_0", "qgemv_nvfp4", "qgemv_nvfp4_swiglu", "qg_quantize_q8_0_act",
     "qgemv_q4_0_a8", "moe_route_topk", "QgMoeDesc", "moe_workspace_bytes",
-    "moe_gemv_grouped", "moe_forward", "qgemm_prefill", "EXPORTED_SYMBOLS",
+    "moe_gemv_grouped", "moe_forward", "qgemm_prefill", "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
+    "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
@@ -96,6 +97,8 @@ _SIGNATURES = {
     "moe_gemv_grouped": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "moe_forward": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _I64, _P, _P, _SZ, _P]),
     "qgemm_prefill": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P]),
+    "qgemm_prefill_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "qgemm_prefill_ws": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -304,3 +307,18 @@ def moe_forward(desc: QgMoeDesc, x, logits, t, y, ws, ws_bytes=None, stream=None
 def qgemm_prefill(w, tensor_scale, n, k, x, m, y, stream=None) -> None:
     _check("qgemm_prefill",
            lib().qgemm_prefill(_dptr(w), tensor_scale, n, k, _dptr(x), m, _dptr(y), _stream(stream)))
+
+
+def qgemm_prefill_workspace_bytes(n, k, m) -> int:
+    return int(lib().qgemm_prefill_workspace_bytes(n, k, m))
+
+
+def qgemm_prefill_ws(w, tensor_scale, n, k, x, m, y, ws, ws_bytes=None, stream=None) -> None:
+    if ws is None:
+        ptr, nbytes = 0, 0 if ws_bytes is None else ws_bytes
+    else:
+        ptr = _dptr(ws)
+        nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("qgemm_prefill_ws",
+           lib().qgemm_prefill_ws(_dptr(w), tensor_scale, n, k, _dptr(x), m, _dptr(y), ptr, nbytes,
+                                  _stream(stream)))

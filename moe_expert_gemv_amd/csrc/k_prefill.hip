@@ -7,10 +7,27 @@
 // gaps), which is why the block-scaled FP4 MFMA of gfx950 is not used: its
 // E8M0-per-32 scales and low-precision activations would change the result.
 //
-// Workgroup tile: 64 tokens x 64 weight rows, k-step 64, 4 waves in a 2x2
-// arrangement, each wave a 32x32 sub-tile (2x2 MFMA tiles).  Per k-step the
-// workgroup stages the X tile (bf16) and the decoded W tile (bf16) in LDS.
+// Layout of the work:
+//  * W is the streamed operand (0.5625 byte per weight, read once) and X the
+//    reused one, so every wave owns distinct weight rows and decodes them
+//    straight into MFMA B fragments in registers (no LDS round trip for W),
+//    several stages ahead of use; X tiles go through LDS, double-buffered.
+//  * Inside a 128-element slab, lane group g (lanes 16g..16g+15) covers 32
+//    consecutive k, so one 16-byte code load per lane feeds 4 MFMA steps;
+//    step s of the MFMA sums, for lane group g, the k range
+//    slab + 32g + 8s .. +8 on both operands (A and B use the same permutation
+//    of k, so the contraction is unchanged).
+//  * Two shapes.  M <= 128: workgroups of 64 tokens x 48 weight rows (N =
+//    12288 gives 256 per 64 tokens); slab j of k goes to wave j mod 4, each
+//    wave chains its slabs through the MFMAs in ascending order, and the four
+//    partial sums are added in wave order through LDS.  M > 128: workgroups
+//    of 128 tokens x 192 weight rows, each wave 48 rows over all k in one
+//    ascending MFMA chain.  Within a shape the summation order of an output
+//    does not depend on M or on the other rows, so a row's result does not
+//    depend on the batch it came in (the two shapes agree to rounding).
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "qg_device.hpp"
 #include "qg_internal.hpp"
@@ -21,109 +38,572 @@ namespace qg {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int BM = 64, BN = 64, BK = 64;
-constexpr int kPad = 8;  // bf16 elements of padding per LDS row
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ floatx4 mfma_16x16x32_bf16(const u32x4& a, const u32x4& b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(kBlock) void k_prefill(const uint8_t* __restrict__ w, int64_t soff,
-                                                    float s_t, int n, int k,
-                                                    const uint16_t* __restrict__ x, int m,
+// Eight E2M1 codes (one dword, low nibble first) times the fp32 block scale s,
+// as eight bf16 (exact: at most 6 significant bits).
+template <int B>
+__device__ __forceinline__ uint32_t decode2_scaled(uint32_t codes, float s) {
+    f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, B);  // byte B: two codes
+    f = f * s;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
+}
+
+__device__ __forceinline__ u32x4 decode8_scaled(uint32_t codes, float s) {
+    return u32x4{decode2_scaled<0>(codes, s), decode2_scaled<1>(codes, s), decode2_scaled<2>(codes, s),
+                 decode2_scaled<3>(codes, s)};
+}
+
+// 4 x 4 transpose of dwords across the four 16-lane groups of a wave: on
+// return, d[q] of lane group g holds what d[g] of lane group q held (same
+// position inside the group).  v_permlane32_swap exchanges its first
+// operand's lanes 32..63 with its second operand's lanes 0..31,
+// v_permlane16_swap the first operand's odd 16-lane rows with the second's
+// even rows.
+__device__ __forceinline__ void transpose4_lane_groups(uint32_t (&d)[4]) {
+    auto s32 = [](uint32_t& a, uint32_t& b) {
+        const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+        a = r[0];
+        b = r[1];
+    };
+    auto s16 = [](uint32_t& a, uint32_t& b) {
+        const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+        a = r[0];
+        b = r[1];
+    };
+    s32(d[0], d[2]);
+    s32(d[1], d[3]);
+    s16(d[0], d[1]);
+    s16(d[2], d[3]);
+}
+
+// MB: 16-token blocks per wave; NB: 16-row blocks of W per wave; WN x WK = 4
+// waves along W rows x along k; WD: stages of W loads in flight.
+constexpr int KW = 128;  // k per wave per stage: one slab
+
+template <int MB, int NB, int WN, int WK, int WD>
+struct PrefillShape {
+    static constexpr int BM = 16 * MB;            // tokens per workgroup
+    static constexpr int BN = 16 * NB * WN;       // weight rows per workgroup
+    static constexpr int BK = KW * WK;            // k per stage
+    static constexpr int SPS = KW / 32;           // MFMA steps per slab
+    static constexpr int CPR = BK / 8;            // 16-byte X chunks per LDS row
+    static constexpr int NCH = BM * CPR / kBlock; // X chunks staged per thread
+    static_assert(WN * WK == 4 && (WK == 1 || WK == 4), "four waves, k split 1 or 4 ways");
+    static_assert(CPR >= 16 && (CPR & (CPR - 1)) == 0, "X rows of a power-of-two count of 16 chunks");
+    static_assert((BM * CPR) % kBlock == 0, "X tile split evenly over the threads");
+};
+
+// One stage of one wave's W rows: codes and scales of its NB row blocks.
+template <int NB>
+struct WStage {
+    uint32_t c[NB][4];
+    uint32_t s[NB];  // the two scale bytes in the low half
+};
+
+template <int MB, int NB, int WN, int WK, int WD>
+__global__ __launch_bounds__(kBlock) void k_prefill(const uint8_t* __restrict__ w, int64_t soff, float s_t,
+                                                    int n, int k, const uint16_t* __restrict__ x, int m,
                                                     uint16_t* __restrict__ y) {
-    __shared__ __attribute__((aligned(16))) uint16_t Xs[BM][BK + kPad];
-    __shared__ __attribute__((aligned(16))) uint16_t Ws[BN][BK + kPad];
+    using S = PrefillShape<MB, NB, WN, WK, WD>;
+    constexpr int BM = S::BM, BN = S::BN, BK = S::BK, CPR = S::CPR, NCH = S::NCH, SPS = S::SPS;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * BK];
 
     const int tid = int(threadIdx.x);
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = int(blockIdx.y) * BM, n0 = int(blockIdx.x) * BN;
-    // loader role: one row and one 16-element segment of each tile
-    const int lr = tid >> 2, lc = tid & 3;
-    const bool x_ok = m0 + lr < m, w_ok = n0 + lr < n;
-    const uint16_t* xrow = x + int64_t(x_ok ? m0 + lr : 0) * k;
-    const uint8_t* crow = w + int64_t(w_ok ? n0 + lr : 0) * (k / 2);
-    const uint8_t* srow = w + soff + int64_t(w_ok ? n0 + lr : 0) * (k / 16);
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave % WN, wk = wave / WN;
+    const int lr = lane & 15, lg = lane >> 4;  // fragment row / column, lane group
+    const int m0 = int(blockIdx.y) * BM;
+    const int n0 = int(blockIdx.x) * BN + wn * 16 * NB;
+    const int nst = (k + BK - 1) / BK;
+    const int64_t crow = k / 2, srow = k / 16;
 
-    floatx4 acc[2][2];
+    // ---- X staging: thread t moves chunks p = t + 256 j of the BM x BK tile;
+    // chunk (row, c) lands at row * CPR + (c ^ (row & 15)) (bank-conflict-free
+    // fragment reads: 16 lanes reading one column of 16 rows hit 16 slots).
+    u32x4 xr[NCH];
+    auto x_load = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    for (int k0 = 0; k0 < k; k0 += BK) {
-        const int kc = k0 + 16 * lc;  // first element of this thread's segment
-        const bool k_ok = kc < k;
-        u32x4 xa = {0, 0, 0, 0}, xb = {0, 0, 0, 0};
-        if (x_ok && k_ok) {
-            xa = ld16(xrow + kc);
-            xb = ld16(xrow + kc + 8);
+        for (int j = 0; j < NCH; ++j) {
+            const int p = tid + kBlock * j;
+            const int row = p / CPR, c = p % CPR;
+            const int kk = st * BK + 8 * c;
+            const bool ok = kk < k;
+            const int64_t gr = min(m0 + row, m - 1);
+            const u32x4 v = ld16(x + gr * k + (ok ? kk : 0));
+            xr[j] = ok ? v : u32x4{0u, 0u, 0u, 0u};
         }
-        u32x4 wa = {0, 0, 0, 0}, wb = {0, 0, 0, 0};
-        if (w_ok && k_ok) {
-            const u32x2 c = *reinterpret_cast<const u32x2*>(crow + kc / 2);
-            const float s = e4m3_to_f32<0>(srow[kc / 16]);
-            uint32_t o[8];
+    };
+    auto x_store = [&](int buf) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const bf16x2 p[4] = {e2m1x2_to_bf16x2<0>(c[q]), e2m1x2_to_bf16x2<1>(c[q]),
-                                     e2m1x2_to_bf16x2<2>(c[q]), e2m1x2_to_bf16x2<3>(c[q])};
+        for (int j = 0; j < NCH; ++j) {
+            const int p = tid + kBlock * j;
+            const int row = p / CPR, c = p % CPR;
+            *reinterpret_cast<u32x4*>(&xs[buf][8 * (row * CPR + (c ^ (row & 15)))]) = xr[j];
+        }
+    };
+
+    // ---- W: this wave's rows n0 + 16 nb + lr, k range of lane group lg
+    const uint8_t* wc[NB];
+    const uint8_t* ws[NB];
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    // e2m1 * e4m3 has at most 6 significant bits: exact in bf16
-                    const uint32_t lo = f32_to_bf16_rne(bf16x2_lo(p[b]) * s);
-                    const uint32_t hi = f32_to_bf16_rne(bf16x2_hi(p[b]) * s);
-                    o[4 * q + b] = lo | (hi << 16);
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t row = min(n0 + 16 * nb + lr, n - 1);
+        wc[nb] = w + row * crow;
+        ws[nb] = w + soff + row * srow;
+    }
+    auto k_lane = [&](int st) { return st * BK + wk * KW + lg * (KW / 4); };
+    auto w_load = [&](WStage<NB>& b, int st) {
+        const int kl = k_lane(st);
+        const int kc = kl < k ? kl : 0;  // lanes past the end read the row start
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const u32x4 v = ld_stream16(wc[nb] + kc / 2);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
+            b.s[nb] = ld<uint16_t>(ws[nb] + kc / 16);
+        }
+    };
+
+    floatx4 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // ---- prologue.  Every load in the loop is unconditional (stages past
+    // the end read clamped addresses and contribute zeros), so the loop body
+    // has no branches and the compiler's load counting stays exact: a branch
+    // around a load would make it wait for every load in flight.
+    WStage<NB> wr[WD];
+#pragma unroll
+    for (int d = 0; d < WD; ++d) w_load(wr[d], d);
+    x_load(0);
+    x_store(0);
+    x_load(1);
+    __syncthreads();
+
+    // ---- main loop, unrolled by WD so the W ring index is static; runs a
+    // whole number of ring rounds (stages past nst multiply zeros)
+    for (int st0 = 0; st0 < nst; st0 += WD) {
+#pragma unroll
+        for (int d = 0; d < WD; ++d) {
+            const int st = st0 + d;
+            const int buf = st & 1;
+            // per MFMA step: decode this stage's W for the step into B
+            // fragments, then the step's MFMAs with A from the swizzled X tile
+            const bool okw = k_lane(st) < k;
+            const uint16_t* xb = xs[buf];
+            WStage<NB> cur = wr[d];
+            // refill this ring slot with stage st + WD (its codes are in cur)
+            w_load(wr[d], st + WD);
+#pragma unroll
+            for (int s = 0; s < SPS; ++s) {
+                u32x4 bfr[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float sc = (s < 2) ? e4m3_to_f32<0>(cur.s[nb]) : e4m3_to_f32<1>(cur.s[nb]);
+                    const u32x4 v = decode8_scaled(cur.c[nb][s], sc);
+                    bfr[nb] = okw ? v : u32x4{0u, 0u, 0u, 0u};
+                }
+                const int c = (wk * KW + lg * (KW / 4) + 8 * s) / 8;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int row = 16 * mb + lr;
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(&xb[8 * (row * CPR + (c ^ (row & 15)))]);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[mb][nb] = mfma_16x16x32_bf16(a, bfr[nb], acc[mb][nb]);
                 }
             }
-            wa = u32x4{o[0], o[1], o[2], o[3]};
-            wb = u32x4{o[4], o[5], o[6], o[7]};
-        }
-        __syncthreads();  // previous k-step's fragment reads are done
-        *reinterpret_cast<u32x4*>(&Xs[lr][16 * lc]) = xa;
-        *reinterpret_cast<u32x4*>(&Xs[lr][16 * lc + 8]) = xb;
-        *reinterpret_cast<u32x4*>(&Ws[lr][16 * lc]) = wa;
-        *reinterpret_cast<u32x4*>(&Ws[lr][16 * lc + 8]) = wb;
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-            u32x4 af[2], bf[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const u32x4*>(&Xs[wm * 32 + i * 16 + (lane & 15)][kk + 8 * (lane >> 4)]);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bf[j] = *reinterpret_cast<const u32x4*>(&Ws[wn * 32 + j * 16 + (lane & 15)][kk + 8 * (lane >> 4)]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma_16x16x32_bf16(af[i], bf[j], acc[i][j]);
+            // stage st + 1 into the other buffer (last read in stage st - 1,
+            // before the barrier that closed it), then prefetch st + 2
+            x_store(buf ^ 1);
+            x_load(st + 2);
+            __syncthreads();
         }
     }
-    // D[i][j] of a 16x16 tile: lane holds rows 4*(lane/16)+v, column lane%16
+
+    // ---- epilogue: D of a 16x16 tile: lane holds rows 4*(lane/16)+v, column lane%16
+    if constexpr (WK == 1) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int row = m0 + 16 * mb + 4 * lg + v;
+                    const int col = n0 + 16 * nb + lr;
+                    if (row < m && col < n)
+                        y[int64_t(row) * n + col] = uint16_t(f32_to_bf16_rne(acc[mb][nb][v] * s_t));
+                }
+    } else {
+        // the four waves' partials through LDS, added in order; the X
+        // buffers are free after the loop's last barrier
+        static_assert(WN == 1, "k split across all four waves");
+        float* red = reinterpret_cast<float*>(&xs[0][0]);
+        static_assert(sizeof(float) * WK * BM * BN <= sizeof(xs), "reduction fits in the X buffers");
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    red[(wk * BM + 16 * mb + 4 * lg + v) * BN + 16 * nb + lr] = acc[mb][nb][v];
+        __syncthreads();
+        for (int idx = tid; idx < BM * BN; idx += kBlock) {
+            const int r = idx / BN, c = idx % BN;
+            float sum = red[r * BN + c];
+#pragma unroll
+            for (int q = 1; q < WK; ++q) sum += red[(q * BM + r) * BN + c];
+            const int row = m0 + r, col = int(blockIdx.x) * BN + c;
+            if (row < m && col < n) y[int64_t(row) * n + col] = uint16_t(f32_to_bf16_rne(sum * s_t));
+        }
+    }
+}
+
+// M <= 128: the k range is split over the four waves (slab j of 128 k to
+// wave j mod 4), so a wave's X operand is its own: A fragments are loaded
+// from global memory (L2) straight into registers, two slabs ahead, and W
+// four slabs ahead; the main loop has no LDS traffic and no barrier.  The
+// four partial sums meet in LDS at the end and are added in wave order.
+// Inside a slab, MFMA step q of lane group g takes k = 32q + 8g .. +8, so an
+// A load reads 64 contiguous bytes of each of 16 rows; W is loaded as 16
+// contiguous bytes per lane (k = 32g .. 32g+31) and redistributed across the
+// lane groups by a 4 x 4 transpose.  Workgroup: 16*MB tokens x 16*NB rows.
+template <int MB, int NB>
+__global__ __launch_bounds__(kBlock) void k_prefill_ks(const uint8_t* __restrict__ w, int64_t soff, float s_t,
+                                                       int n, int k, const uint16_t* __restrict__ x, int m,
+                                                       uint16_t* __restrict__ y) {
+    constexpr int BM = 16 * MB, BN = 16 * NB;
+    constexpr int AD = 2, WD = 4, U = 4;  // ring depths (slabs) and the unroll that makes them static
+    __shared__ float red[4 * BM * BN];
+
+    const int tid = int(threadIdx.x);
+    const int lane = tid & 63;
+    const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int m0 = int(blockIdx.y) * BM, n0 = int(blockIdx.x) * BN;
+    const int nslab = (k + KW - 1) / KW;
+    const int nw = (nslab - wk + 3) / 4;            // slabs wk, wk + 4, ... of this wave
+    const int ilast = nw > 0 ? nw - 1 : 0;
+
+    const uint16_t* xrow[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) xrow[mb] = x + int64_t(min(m0 + 16 * mb + lr, m - 1)) * k;
+    const uint8_t* wc[NB];
+    const uint8_t* ws[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t row = min(n0 + 16 * nb + lr, n - 1);
+        wc[nb] = w + row * (k / 2);
+        ws[nb] = w + soff + row * (k / 16);
+    }
+    // first k of the wave's i-th slab (clamped to a valid slab)
+    auto slab_k = [&](int i) { return KW * (wk + 4 * min(i, ilast)); };
+
+    u32x4 ar[AD][MB][4];
+    WStage<NB> wr[WD];
+    auto a_load = [&](u32x4 (&a)[MB][4], int i) {
+        const int k0 = slab_k(i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int kq = k0 + 32 * q;            // step q is valid for all lanes or none
+            const int kc = (kq < k ? kq : 0) + 8 * lg;  // past the end: a valid address, zeroed at use
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) a[mb][q] = ld16(xrow[mb] + kc);
+        }
+    };
+    auto w_load = [&](WStage<NB>& b, int i) {
+        const int kb = slab_k(i) + 32 * lg;
+        const int kc = kb < k ? kb : 0;  // past the end: the row's own first block
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const u32x4 v = ld_stream16(wc[nb] + kc / 2);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
+            b.s[nb] = ld<uint16_t>(ws[nb] + kc / 16);  // blocks of k = kc .. kc+31
+        }
+    };
+
+    floatx4 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int d = 0; d < WD; ++d) w_load(wr[d], d);
+#pragma unroll
+    for (int d = 0; d < AD; ++d) a_load(ar[d], d);
+
+    for (int i0 = 0; i0 < nw; i0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u;
+            if (i < nw) {  // wave-uniform: compute slab i (no load inside)
+                const int k0 = KW * (wk + 4 * i);
+                if (k0 + KW > k) {  // the last slab runs past k: zero its X there
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            ar[u % AD][mb][q] = k0 + 32 * q < k ? ar[u % AD][mb][q] : u32x4{0u, 0u, 0u, 0u};
+                }
+                // W to step-major order: codes, and the scale byte of each step
+                // (lane group g, step q: block 2q + g/2 of the slab)
+                uint32_t cq[NB][4], sq[NB][4];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) cq[nb][q] = wr[u % WD].c[nb][q];
+                    transpose4_lane_groups(cq[nb]);
+                    const uint32_t s2 = wr[u % WD].s[nb];  // this lane group's blocks 2g, 2g+1
+                    sq[nb][0] = sq[nb][1] = s2 & 0xffu;
+                    sq[nb][2] = sq[nb][3] = s2 >> 8;
+                    transpose4_lane_groups(sq[nb]);  // sq[q] = block 2q + g/2 (from lane group q)
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    u32x4 bfr[NB];
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) bfr[nb] = decode8_scaled(cq[nb][q], e4m3_to_f32<0>(sq[nb][q]));
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc[mb][nb] = mfma_16x16x32_bf16(ar[u % AD][mb][q], bfr[nb], acc[mb][nb]);
+                }
+            }
+            // refill both ring slots (unconditional: clamped slab index)
+            a_load(ar[u % AD], i + AD);
+            w_load(wr[u % WD], i + WD);
+        }
+    }
+
+    // partial sums through LDS, added in wave order
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[(wk * BM + 16 * mb + 4 * lg + v) * BN + 16 * nb + lr] = acc[mb][nb][v];
+    __syncthreads();
+    for (int idx = tid; idx < BM * BN; idx += kBlock) {
+        const int r = idx / BN, c = idx % BN;
+        float sum = red[r * BN + c];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) sum += red[(q * BM + r) * BN + c];
+        const int row = m0 + r, col = n0 + c;
+        if (row < m && col < n) y[int64_t(row) * n + col] = uint16_t(f32_to_bf16_rne(sum * s_t));
+    }
+}
+
+// M <= 128 with a workspace: the k range is split over several workgroups
+// (kSkRange each), so a workgroup reads only its slice of X -- 64 tokens x
+// 1024 k, 128 KB, copied into LDS once by gfx950's direct global-to-LDS loads
+// -- instead of all of X.  Its four waves each take 48 weight rows over the
+// slice.  The copy completes at the barrier that publishes it (the compiler
+// waits there for every load in flight), so the weight loads are issued
+// after it: all eight slabs at once, and slab j's MFMAs wait only for the
+// first j + 1 slabs (loads complete in order), which overlaps the weight
+// stream with the arithmetic.  The fp32 partial sums go to the workspace;
+// k_prefill_reduce adds them in range order.
+constexpr int kSkRange = 1024;             // k per workgroup
+constexpr int kSkSlabs = kSkRange / KW;    // 8
+constexpr int kSkDepth = 4;                // weight slabs in flight
+constexpr int kSkRows = 64;                // tokens per workgroup
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+template <int NB>
+__global__ __launch_bounds__(kBlock) void k_prefill_sk(const uint8_t* __restrict__ w, int64_t soff, int n, int k,
+                                                       const uint16_t* __restrict__ x, int m,
+                                                       float* __restrict__ part) {
+    constexpr int MB = kSkRows / 16, BN = 16 * NB * 4;
+    constexpr int CPR = kSkRange / 8;  // 16-byte chunks per X row
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kSkRows * kSkRange];
+
+    const int tid = int(threadIdx.x);
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int m0 = int(blockIdx.y) * kSkRows;
+    const int n0 = int(blockIdx.x) * BN + wave * 16 * NB;
+    const int kz = int(blockIdx.z) * kSkRange;
+
+    // 1. X slice into LDS: chunk slot p holds X[row][kz + 8c], row = p / CPR,
+    // c = (p % CPR) ^ (row & 15) (fragment reads hit 16 distinct slots per 16
+    // lanes).  One copy instruction fills 64 consecutive slots, lane i slot
+    // base + i, so each lane fetches the chunk its slot holds (rows past m
+    // repeat row m-1; chunks past k are zeroed below).
+    {
+        constexpr int kCopies = kSkRows * CPR / kWave;  // per workgroup
+        for (int cp = wave; cp < kCopies; cp += kBlock / kWave) {
+            const int p = cp * kWave + lane;
+            const int row = p / CPR, c = (p % CPR) ^ (row & 15);
+            const int kk = kz + 8 * c;
+            const uint16_t* src = x + int64_t(min(m0 + row, m - 1)) * k + (kk < k ? kk : 0);
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(xs + 8 * cp * kWave), 16, 0, 0);
+        }
+    }
+    __syncthreads();  // the compiler completes the copies before the barrier
+    if (kz + kSkRange > k) {  // range runs past k: zero those X chunks
+        for (int p = tid; p < kSkRows * CPR; p += kBlock) {
+            const int row = p / CPR, c = (p % CPR) ^ (row & 15);
+            if (kz + 8 * c >= k) *reinterpret_cast<u32x4*>(&xs[8 * p]) = u32x4{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+    }
+
+    // 2. weight slabs of this wave's rows (past k: the row's own first block),
+    // kSkDepth slabs ahead of the arithmetic: slab j + kSkDepth is requested
+    // before slab j is computed, so the stream drains while the MFMAs run
+    const uint8_t* wc[NB];
+    const uint8_t* ws[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t row = min(n0 + 16 * nb + lr, n - 1);
+        wc[nb] = w + row * (k / 2);
+        ws[nb] = w + soff + row * (k / 16);
+    }
+    auto w_load = [&](WStage<NB>& b, int j) {
+        const int kb = kz + KW * j + 32 * lg;
+        const int kc = kb < k ? kb : 0;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const u32x4 v = ld_stream16(wc[nb] + kc / 2);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
+            b.s[nb] = ld<uint16_t>(ws[nb] + kc / 16);
+        }
+    };
+    WStage<NB> wr[kSkDepth];
+#pragma unroll
+    for (int j = 0; j < kSkDepth; ++j) w_load(wr[j], j);
+
+    // 3. MFMAs, slab by slab: all kSkSlabs slabs, without a runtime branch
+    // (a branch would let the compiler sink each slab's loads down to their
+    // use); slabs past the range meet zeroed X and add nothing
+    floatx4 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kSkSlabs; ++j) {
+        const WStage<NB> cur = wr[j % kSkDepth];
+        if (j + kSkDepth < kSkSlabs) w_load(wr[j % kSkDepth], j + kSkDepth);
+        __builtin_amdgcn_sched_barrier(0);  // the refill is issued before slab j's arithmetic
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            u32x4 bfr[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float sc = (q < 2) ? e4m3_to_f32<0>(cur.s[nb]) : e4m3_to_f32<1>(cur.s[nb]);
+                bfr[nb] = decode8_scaled(cur.c[nb][q], sc);
+            }
+            const int c = 16 * j + 4 * lg + q;  // k = 128 j + 32 lg + 8 q
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int row = 16 * mb + lr;
+                const u32x4 a = *reinterpret_cast<const u32x4*>(&xs[8 * (row * CPR + (c ^ (row & 15)))]);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32_bf16(a, bfr[nb], acc[mb][nb]);
+            }
+        }
+    }
+    // 4. partial sums of this range: part[z][row][col]
+    float* pz = part + int64_t(blockIdx.z) * m * n;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int row = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + v;
-                const int col = n0 + wn * 32 + j * 16 + (lane & 15);
-                if (row < m && col < n)
-                    y[int64_t(row) * n + col] = uint16_t(f32_to_bf16_rne(acc[i][j][v] * s_t));
+                const int row = m0 + 16 * mb + 4 * lg + v, col = n0 + 16 * nb + lr;
+                if (row < m && col < n) pz[int64_t(row) * n + col] = acc[mb][nb][v];
             }
+}
+
+// y = bf16_rne(s_t * sum over the nz ranges of part[z]), ranges in order.
+// Four outputs per thread when count % 4 == 0 (every slice then starts
+// 16-byte aligned), else one.
+__global__ __launch_bounds__(kBlock) void k_prefill_reduce(const float* __restrict__ part, int nz, int64_t count,
+                                                           float s_t, uint16_t* __restrict__ y) {
+    const int64_t n4 = count % 4 == 0 ? count / 4 : 0;
+    for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < n4; i += int64_t(gridDim.x) * kBlock) {
+        floatx4 sum = *reinterpret_cast<const floatx4*>(part + 4 * i);
+        for (int z = 1; z < nz; ++z) {
+            const floatx4 v = *reinterpret_cast<const floatx4*>(part + z * count + 4 * i);
+            sum[0] += v[0];
+            sum[1] += v[1];
+            sum[2] += v[2];
+            sum[3] += v[3];
+        }
+        const uint32_t lo = f32_to_bf16_rne(sum[0] * s_t) | (f32_to_bf16_rne(sum[1] * s_t) << 16);
+        const uint32_t hi = f32_to_bf16_rne(sum[2] * s_t) | (f32_to_bf16_rne(sum[3] * s_t) << 16);
+        *reinterpret_cast<u32x2*>(y + 4 * i) = u32x2{lo, hi};
+    }
+    for (int64_t i = 4 * n4 + int64_t(blockIdx.x) * kBlock + threadIdx.x; i < count;
+         i += int64_t(gridDim.x) * kBlock) {
+        float sum = part[i];
+        for (int z = 1; z < nz; ++z) sum += part[z * count + i];
+        y[i] = uint16_t(f32_to_bf16_rne(sum * s_t));
+    }
+}
+
+template <int MB, int NB, int WN, int WK, int WD>
+hipError_t go(const uint8_t* w, int64_t soff, float s_t, int64_t n, int64_t k, const uint16_t* x, int64_t m,
+              uint16_t* y, hipStream_t s) {
+    using S = PrefillShape<MB, NB, WN, WK, WD>;
+    const dim3 grid(unsigned((n + S::BN - 1) / S::BN), unsigned((m + S::BM - 1) / S::BM));
+    hipLaunchKernelGGL((k_prefill<MB, NB, WN, WK, WD>), grid, dim3(kBlock), 0, s, w, soff, s_t, int(n),
+                       int(k), x, int(m), y);
+    return hipGetLastError();
 }
 
 }  // namespace
 
+size_t prefill_workspace_bytes(int64_t n, int64_t k, int64_t m) {
+    if (m > 128) return 0;
+    const int64_t nz = (k + kSkRange - 1) / kSkRange;
+    return size_t(nz * m * n * 4);
+}
+
+hipError_t launch_prefill_ws(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x, int64_t m,
+                             uint16_t* y, float* ws, hipStream_t s) {
+    if (m > 128) return launch_prefill(w, s_t, n, k, x, m, y, s);
+    const int64_t soff = scale_plane_offset(QG_NVFP4, n, k);
+    constexpr int NB = 3;
+    const int nz = int((k + kSkRange - 1) / kSkRange);
+    const dim3 grid(unsigned((n + 64 * NB - 1) / (64 * NB)), unsigned((m + kSkRows - 1) / kSkRows), unsigned(nz));
+    hipLaunchKernelGGL((k_prefill_sk<NB>), grid, dim3(kBlock), 0, s, w, soff, int(n), int(k), x, int(m), ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t count = m * n;
+    const unsigned blocks = unsigned(std::max<int64_t>(1, std::min<int64_t>((count / 4 + kBlock - 1) / kBlock, 4096)));
+    hipLaunchKernelGGL(k_prefill_reduce, dim3(blocks), dim3(kBlock), 0, s, ws, nz, count, s_t, y);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x,
                           int64_t m, uint16_t* y, hipStream_t s) {
     const int64_t soff = scale_plane_offset(QG_NVFP4, n, k);
-    const dim3 grid(unsigned((n + BN - 1) / BN), unsigned((m + BM - 1) / BM));
-    hipLaunchKernelGGL(k_prefill, grid, dim3(kBlock), 0, s, w, soff, s_t, int(n), int(k), x, int(m), y);
-    return hipGetLastError();
+    if (m <= 128) {
+        constexpr int MB = 4, NB = 3;
+        const dim3 grid(unsigned((n + 16 * NB - 1) / (16 * NB)), unsigned((m + 16 * MB - 1) / (16 * MB)));
+        hipLaunchKernelGGL((k_prefill_ks<MB, NB>), grid, dim3(kBlock), 0, s, w, soff, s_t, int(n), int(k), x,
+                           int(m), y);
+        return hipGetLastError();
+    }
+    return go<8, 3, 4, 1, 4>(w, soff, s_t, n, k, x, m, y, s);
 }
 
 }  // namespace qg

@@ -178,4 +178,22 @@ int qgemm_prefill(const void* w, float tensor_scale, int64_t n, int64_t k, const
                                  as_stream(stream)));
 }
 
+size_t qgemm_prefill_workspace_bytes(int64_t n, int64_t k, int64_t m) {
+    if (!valid_shape(n, k) || m < 1 || m > (int64_t(65535) * 64)) return 0;
+    return prefill_workspace_bytes(n, k, m);
+}
+
+int qgemm_prefill_ws(const void* w, float tensor_scale, int64_t n, int64_t k, const uint16_t* x,
+                     int64_t m, uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+    if (!w || !x || !y || !aligned(w, 256) || !aligned(x, 16) || !aligned(y, 16)) return QG_EINVAL;
+    if (!valid_shape(n, k) || m < 1 || m > (int64_t(65535) * 64)) return QG_EINVAL;
+    const size_t need = prefill_workspace_bytes(n, k, m);
+    if (need > 0) {
+        if (!ws || !aligned(ws, 256)) return QG_EINVAL;
+        if (ws_bytes < need) return QG_ENOSPC;
+    }
+    return finish(launch_prefill_ws(static_cast<const uint8_t*>(w), tensor_scale, n, k, x, m, y,
+                                    static_cast<float*>(ws), as_stream(stream)));
+}
+
 }  // extern "C"

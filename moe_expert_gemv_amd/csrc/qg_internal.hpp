@@ -52,5 +52,9 @@ hipError_t launch_moe(const qg_moe_desc* d, const uint16_t* x, const int32_t* id
 
 hipError_t launch_prefill(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x,
                           int64_t m, uint16_t* y, hipStream_t s);
+// Workspace bytes of launch_prefill_ws (0: the single-pass kernel, no workspace).
+size_t prefill_workspace_bytes(int64_t n, int64_t k, int64_t m);
+hipError_t launch_prefill_ws(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x, int64_t m,
+                             uint16_t* y, float* ws, hipStream_t s);
 
 }  // namespace qg

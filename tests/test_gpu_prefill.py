@@ -22,8 +22,21 @@ def run_prefill(w, x_bits):
     return host(y).view(np.uint16)
 
 
-def check(w, x, rows=None, cols=None, what=""):
-    got_bits = run_prefill(w, x)
+def run_prefill_ws(w, x_bits):
+    """The workspace variant (k split over workgroups for m <= 128)."""
+    import torch
+
+    n, k = w["codes"].shape
+    m = x_bits.shape[0]
+    y = empty((m, n), torch.int16)
+    nbytes = qg.qgemm_prefill_workspace_bytes(n, k, m)
+    ws = empty((max(nbytes, 256) // 4,), torch.float32)
+    qg.qgemm_prefill_ws(pack_dev(w), float(w["tensor_scale"]), n, k, dev(x_bits), m, y, ws, nbytes)
+    return host(y).view(np.uint16)
+
+
+def check(w, x, rows=None, cols=None, what="", run=run_prefill):
+    got_bits = run(w, x)
     if rows is not None:
         got_bits = got_bits[np.ix_(rows, cols)]
     got = oracle.decode_bf16(got_bits)
@@ -60,6 +73,33 @@ def test_random(m, n, k):
     check(w, x, what=f"prefill {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m,n,k", [(1, 1, 32), (3, 17, 64), (64, 64, 64), (65, 130, 96), (100, 300, 512),
+                                   (128, 200, 4096), (7, 1000, 2080), (37, 193, 1056), (128, 385, 3072),
+                                   (513, 129, 160)])
+def test_random_workspace(m, n, k):
+    """qgemm_prefill_ws: k slices of 1024 (a partial last slice, a k tail
+    inside a slice), rows of 64, columns of 192 with ragged ends."""
+    require_gpu()
+    print(f"[prefill ws m={m} n={n} k={k}]", flush=True)
+    g = synth.rng(m * 11 + n * 5 + k)
+    w = synth.nvfp4_weights(g, n, k)
+    x = synth.x_bf16(g, m, k)
+    check(w, x, what=f"prefill ws {m}x{n}x{k}", run=run_prefill_ws)
+
+
+def test_workspace_rows_are_independent():
+    """With the workspace, a row's result does not depend on the other rows
+    or on m (m <= 128)."""
+    require_gpu()
+    g = synth.rng(19)
+    w = synth.nvfp4_weights(g, 256, 2080)
+    x = synth.x_bf16(g, 128, 2080)
+    full = run_prefill_ws(w, x)
+    assert np.array_equal(run_prefill_ws(w, x[64:65]), full[64:65])
+    assert np.array_equal(run_prefill_ws(w, x[:5]), full[:5])
+    assert np.array_equal(run_prefill_ws(w, x[27:127]), full[27:127])
+
+
 def test_one_hot_rows_are_exact():
     require_gpu()
     g = synth.rng(8)
@@ -76,22 +116,29 @@ def test_one_hot_rows_are_exact():
 
 
 def test_rows_are_independent():
+    """A row's result does not depend on the other rows of the batch, nor on
+    M inside each of the two shapes (M <= 128 and M > 128); across the two
+    shapes results agree to rounding (the parity tests)."""
     require_gpu()
     g = synth.rng(9)
     w = synth.nvfp4_weights(g, 256, 1024)
-    x = synth.x_bf16(g, 130, 1024)
-    full = run_prefill(w, x)
-    assert np.array_equal(run_prefill(w, x[64:65]), full[64:65])
-    assert np.array_equal(run_prefill(w, x[:5]), full[:5])
+    x = synth.x_bf16(g, 260, 1024)
+    small = run_prefill(w, x[:100])
+    assert np.array_equal(run_prefill(w, x[64:65]), small[64:65])
+    assert np.array_equal(run_prefill(w, x[:5]), small[:5])
+    assert np.array_equal(run_prefill(w, x[36:128])[:64], small[36:100])
+    large = run_prefill(w, x)
+    assert np.array_equal(run_prefill(w, x[1:130]), large[1:130])
+    assert np.array_equal(run_prefill(w, x[100:260]), large[100:260])
 
 
-@pytest.mark.parametrize("m", [64, 128, 512])
-def test_full_size_sampled(m):
+@pytest.mark.parametrize("m,ws", [(64, False), (128, False), (512, False), (64, True), (128, True)])
+def test_full_size_sampled(m, ws):
     """X [m x 4096] times the 9B-class [12288 x 4096] NVFP4 matrix."""
     require_gpu()
-    print(f"[prefill full m={m}]", flush=True)
+    print(f"[prefill full m={m} ws={ws}]", flush=True)
     case = synth.prefill_case(m=m)
     n = case.w["codes"].shape[0]
     rows = np.unique(np.concatenate([[0, m - 1], synth.rng(4).integers(0, m, 14)]))
     cols = np.unique(np.concatenate([np.arange(4), np.arange(n - 4, n), synth.rng(5).integers(0, n, 120)]))
-    check(case.w, case.x, rows, cols, f"prefill full m={m}")
+    check(case.w, case.x, rows, cols, f"prefill full m={m}", run=run_prefill_ws if ws else run_prefill)
