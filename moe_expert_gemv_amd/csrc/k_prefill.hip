@@ -408,63 +408,66 @@ __global__ __launch_bounds__(kBlock) void k_prefill_ks(const uint8_t* __restrict
 
 // M <= 128 with a workspace: the k range is split over several workgroups
 // (kSkRange each), so a workgroup reads only its slice of X -- 64 tokens x
-// 1024 k, 128 KB, copied into LDS once by gfx950's direct global-to-LDS loads
-// -- instead of all of X.  Its four waves each take 48 weight rows over the
-// slice.  The copy completes at the barrier that publishes it (the compiler
-// waits there for every load in flight), so the weight loads are issued
-// after it: all eight slabs at once, and slab j's MFMAs wait only for the
-// first j + 1 slabs (loads complete in order), which overlaps the weight
-// stream with the arithmetic.  The fp32 partial sums go to the workspace;
-// k_prefill_reduce adds them in range order.
-constexpr int kSkRange = 1024;             // k per workgroup
-constexpr int kSkSlabs = kSkRange / KW;    // 8
-constexpr int kSkDepth = 4;                // weight slabs in flight
-constexpr int kSkRows = 64;                // tokens per workgroup
-typedef __attribute__((address_space(3))) void* lds_ptr;
+// 1024 k, 128 KB, staged into LDS once -- instead of all of X.  Eight waves,
+// two per SIMD: waves w and w + 4 take the same 48 weight rows, w the even
+// 128-k slabs of the range and w + 4 the odd ones, so one wave's weight
+// decode (VALU) runs while the other's MFMAs do.  The X loads are requested
+// first and return first (a wave's vector-memory operations complete in
+// order); kSkEarly weight slabs follow them before X is published and the
+// rest right after, so the weight stream starts early without queueing the
+// X data behind it.  The two halves are added through LDS at the end, the
+// fp32 partial sums go to the workspace, and k_prefill_reduce adds them in
+// range order.
+constexpr int kSkRange = 1024;                   // k per workgroup
+constexpr int kSkBlock = 512;                    // threads per workgroup
+constexpr int kSkHalves = 2;                     // waves sharing a row set
+constexpr int kSkSlabs = kSkRange / KW / kSkHalves;  // slabs per wave: 4
+constexpr int kSkRows = 64;                      // tokens per workgroup
+constexpr int kSkEarly = 1;                      // slabs requested before X is published
 
-template <int NB>
-__global__ __launch_bounds__(kBlock) void k_prefill_sk(const uint8_t* __restrict__ w, int64_t soff, int n, int k,
-                                                       const uint16_t* __restrict__ x, int m,
-                                                       float* __restrict__ part) {
-    constexpr int MB = kSkRows / 16, BN = 16 * NB * 4;
+template <int NB, bool TAIL, int EARLY>
+__global__ __launch_bounds__(kSkBlock) void k_prefill_sk(const uint8_t* __restrict__ w, int64_t soff, int n, int k,
+                                                         const uint16_t* __restrict__ x, int m,
+                                                         float* __restrict__ part) {
+    constexpr int MB = kSkRows / 16;
+    constexpr int RW = kSkBlock / kWave / kSkHalves;  // row sets per workgroup: 4
+    constexpr int BN = 16 * NB * RW;
     constexpr int CPR = kSkRange / 8;  // 16-byte chunks per X row
+    constexpr int kAccFloats = MB * NB * 4;
+    static_assert(RW * kAccFloats * kWave * 4 <= kSkRows * kSkRange * 2, "halves combine in the X buffer");
     __shared__ __attribute__((aligned(16))) uint16_t xs[kSkRows * kSkRange];
 
     const int tid = int(threadIdx.x);
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rs = wave % RW, half = wave / RW;
     const int lr = lane & 15, lg = lane >> 4;
     const int m0 = int(blockIdx.y) * kSkRows;
-    const int n0 = int(blockIdx.x) * BN + wave * 16 * NB;
+    const int n0 = int(blockIdx.x) * BN + rs * 16 * NB;
     const int kz = int(blockIdx.z) * kSkRange;
 
-    // 1. X slice into LDS: chunk slot p holds X[row][kz + 8c], row = p / CPR,
-    // c = (p % CPR) ^ (row & 15) (fragment reads hit 16 distinct slots per 16
-    // lanes).  One copy instruction fills 64 consecutive slots, lane i slot
-    // base + i, so each lane fetches the chunk its slot holds (rows past m
-    // repeat row m-1; chunks past k are zeroed below).
-    {
-        constexpr int kCopies = kSkRows * CPR / kWave;  // per workgroup
-        for (int cp = wave; cp < kCopies; cp += kBlock / kWave) {
-            const int p = cp * kWave + lane;
-            const int row = p / CPR, c = (p % CPR) ^ (row & 15);
-            const int kk = kz + 8 * c;
-            const uint16_t* src = x + int64_t(min(m0 + row, m - 1)) * k + (kk < k ? kk : 0);
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(xs + 8 * cp * kWave), 16, 0, 0);
-        }
+    // 1. X slice, requested first: this lane's kCopies chunks go to registers
+    // now and to LDS once they arrive.  Chunk slot p of the LDS tile holds
+    // X[row][kz + 8c], row = p / CPR, c = (p % CPR) ^ (row & 15) (fragment
+    // reads then hit 16 distinct slots per 16 lanes); lane i of copy step cp
+    // fills slot cp * 64 + i.  Rows past m repeat row m-1; chunks past k are
+    // zeroed below.
+    constexpr int kCopies = kSkRows * CPR / kSkBlock;  // per lane
+    u32x4 xr[kCopies];
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+        const int cp = wave + (kSkBlock / kWave) * i;
+        const int p = cp * kWave + lane;
+        const int row = p / CPR, c = (p % CPR) ^ (row & 15);
+        const int kk = kz + 8 * c;
+        xr[i] = ld16(x + int64_t(min(m0 + row, m - 1)) * k + (kk < k ? kk : 0));
     }
-    __syncthreads();  // the compiler completes the copies before the barrier
-    if (kz + kSkRange > k) {  // range runs past k: zero those X chunks
-        for (int p = tid; p < kSkRows * CPR; p += kBlock) {
-            const int row = p / CPR, c = (p % CPR) ^ (row & 15);
-            if (kz + 8 * c >= k) *reinterpret_cast<u32x4*>(&xs[8 * p]) = u32x4{0u, 0u, 0u, 0u};
-        }
-        __syncthreads();
-    }
-
-    // 2. weight slabs of this wave's rows (past k: the row's own first block),
-    // kSkDepth slabs ahead of the arithmetic: slab j + kSkDepth is requested
-    // before slab j is computed, so the stream drains while the MFMAs run
+    // 2. this wave's weight slabs (past k: the row's own first block); slab j
+    // covers k = kz + 128 (2 j + half) + [0, 128).  The first EARLY slabs are
+    // requested right behind the X loads -- after a bare barrier (it waits for
+    // no memory), so every wave's X loads are ahead of them -- and the rest
+    // once X is in LDS.
+    WStage<NB> wr[kSkSlabs];
     const uint8_t* wc[NB];
     const uint8_t* ws[NB];
 #pragma unroll
@@ -473,24 +476,59 @@ __global__ __launch_bounds__(kBlock) void k_prefill_sk(const uint8_t* __restrict
         wc[nb] = w + row * (k / 2);
         ws[nb] = w + soff + row * (k / 16);
     }
-    auto w_load = [&](WStage<NB>& b, int j) {
-        const int kb = kz + KW * j + 32 * lg;
+    auto w_load = [&](int j) {
+        const int kb = kz + KW * (kSkHalves * j + half) + 32 * lg;
         const int kc = kb < k ? kb : 0;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const u32x4 v = ld_stream16(wc[nb] + kc / 2);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
-            b.s[nb] = ld<uint16_t>(ws[nb] + kc / 16);
+            for (int q = 0; q < 4; ++q) wr[j].c[nb][q] = v[q];
+            wr[j].s[nb] = ld<uint16_t>(ws[nb] + kc / 16);
         }
     };
-    WStage<NB> wr[kSkDepth];
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (EARLY > 0) {
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < kSkDepth; ++j) w_load(wr[j], j);
+        for (int j = 0; j < EARLY; ++j) w_load(j);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
-    // 3. MFMAs, slab by slab: all kSkSlabs slabs, without a runtime branch
-    // (a branch would let the compiler sink each slab's loads down to their
-    // use); slabs past the range meet zeroed X and add nothing
+    // Publish the X slice: the X loads complete before the weight loads
+    // issued after them (the compiler's wait for xr leaves those in flight),
+    // and an LDS-only release/acquire around the barrier waits for the LDS
+    // writes alone.
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+        const int cp = wave + (kSkBlock / kWave) * i;
+        *reinterpret_cast<u32x4*>(&xs[8 * (cp * kWave + lane)]) = xr[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    __builtin_amdgcn_sched_barrier(0);  // no decode is hoisted above the barrier
+#pragma unroll
+    for (int j = EARLY; j < kSkSlabs; ++j) w_load(j);
+    __builtin_amdgcn_sched_barrier(0);
+    // TAIL (k not a multiple of kSkRange): the last range zeroes its X chunks
+    // past k.  Without it the kernel is one basic block, which keeps each
+    // weight load's zero-extension next to the load (across a branch the
+    // compiler moves them all to the join, where they would wait for every
+    // slab at once).
+    if constexpr (TAIL) {
+        if (kz + kSkRange > k) {
+            for (int p = tid; p < kSkRows * CPR; p += kSkBlock) {
+                const int row = p / CPR, c = (p % CPR) ^ (row & 15);
+                if (kz + 8 * c >= k) *reinterpret_cast<u32x4*>(&xs[8 * p]) = u32x4{0u, 0u, 0u, 0u};
+            }
+            __syncthreads();
+        }
+    }
+
+    // 3. MFMAs, slab by slab, without a runtime branch (slabs past the range
+    // meet zeroed X and add nothing)
     floatx4 acc[MB][NB];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -498,18 +536,15 @@ __global__ __launch_bounds__(kBlock) void k_prefill_sk(const uint8_t* __restrict
         for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kSkSlabs; ++j) {
-        const WStage<NB> cur = wr[j % kSkDepth];
-        if (j + kSkDepth < kSkSlabs) w_load(wr[j % kSkDepth], j + kSkDepth);
-        __builtin_amdgcn_sched_barrier(0);  // the refill is issued before slab j's arithmetic
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             u32x4 bfr[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const float sc = (q < 2) ? e4m3_to_f32<0>(cur.s[nb]) : e4m3_to_f32<1>(cur.s[nb]);
-                bfr[nb] = decode8_scaled(cur.c[nb][q], sc);
+                const float sc = (q < 2) ? e4m3_to_f32<0>(wr[j].s[nb]) : e4m3_to_f32<1>(wr[j].s[nb]);
+                bfr[nb] = decode8_scaled(wr[j].c[nb][q], sc);
             }
-            const int c = 16 * j + 4 * lg + q;  // k = 128 j + 32 lg + 8 q
+            const int c = 16 * (kSkHalves * j + half) + 4 * lg + q;  // k = 128 slab + 32 lg + 8 q
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = 16 * mb + lr;
@@ -519,17 +554,33 @@ __global__ __launch_bounds__(kBlock) void k_prefill_sk(const uint8_t* __restrict
             }
         }
     }
-    // 4. partial sums of this range: part[z][row][col]
-    float* pz = part + int64_t(blockIdx.z) * m * n;
+
+    // 4. odd half + even half (in that fixed order) through the X buffer, then
+    // the partial sums of this range: part[z][row][col]
+    float* red = reinterpret_cast<float*>(xs) + rs * kAccFloats * kWave;
+    __syncthreads();  // every wave is done with X
+    if (half == 1) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = m0 + 16 * mb + 4 * lg + v, col = n0 + 16 * nb + lr;
-                if (row < m && col < n) pz[int64_t(row) * n + col] = acc[mb][nb][v];
-            }
+                for (int v = 0; v < 4; ++v) red[((mb * NB + nb) * 4 + v) * kWave + lane] = acc[mb][nb][v];
+    }
+    __syncthreads();
+    if (half == 0) {
+        float* pz = part + int64_t(blockIdx.z) * m * n;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float sum = red[((mb * NB + nb) * 4 + v) * kWave + lane] + acc[mb][nb][v];
+                    const int row = m0 + 16 * mb + 4 * lg + v, col = n0 + 16 * nb + lr;
+                    if (row < m && col < n) pz[int64_t(row) * n + col] = sum;
+                }
+    }
 }
 
 // y = bf16_rne(s_t * sum over the nz ranges of part[z]), ranges in order.
@@ -583,8 +634,14 @@ hipError_t launch_prefill_ws(const uint8_t* w, float s_t, int64_t n, int64_t k, 
     const int64_t soff = scale_plane_offset(QG_NVFP4, n, k);
     constexpr int NB = 3;
     const int nz = int((k + kSkRange - 1) / kSkRange);
-    const dim3 grid(unsigned((n + 64 * NB - 1) / (64 * NB)), unsigned((m + kSkRows - 1) / kSkRows), unsigned(nz));
-    hipLaunchKernelGGL((k_prefill_sk<NB>), grid, dim3(kBlock), 0, s, w, soff, int(n), int(k), x, int(m), ws);
+    constexpr int BN = 16 * NB * (kSkBlock / kWave / kSkHalves);
+    const dim3 grid(unsigned((n + BN - 1) / BN), unsigned((m + kSkRows - 1) / kSkRows), unsigned(nz));
+    if (k % kSkRange == 0)
+        hipLaunchKernelGGL((k_prefill_sk<NB, false, kSkEarly>), grid, dim3(kSkBlock), 0, s, w, soff, int(n), int(k), x, int(m),
+                           ws);
+    else
+        hipLaunchKernelGGL((k_prefill_sk<NB, true, kSkEarly>), grid, dim3(kSkBlock), 0, s, w, soff, int(n), int(k), x, int(m),
+                           ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t count = m * n;
