@@ -240,7 +240,7 @@ class W4A8Gemv(Workload):
 
 class MoE(Workload):
     sources = ("k_moe.hip", "qg_gemv_core.hpp")
-    kernel_re = (r"k_moe_gate_up\b", r"k_moe_down\b")
+    kernel_re = (r"k_moe_gate_up(?:_tile)?\b", r"k_moe_down(?:_tile)?\b")
 
     def __init__(self, t=1):
         import torch
