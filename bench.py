@@ -35,6 +35,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -54,13 +55,22 @@ _COMMON_SOURCES = ("qg_device.hpp", "qg_layout.hpp")
 COPY_CAL_BYTES = 256 << 20  # the plain copy that calibrates the byte counters
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines (edits to comments do not
+    change the kernel a counter summary was taken on)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_digest(files) -> str:
-    """Digest of the sources a kernel is built from (its .hip file, the headers
-    it includes); a committed counter summary is valid only for that digest."""
+    """Digest of the code of the sources a kernel is built from (its .hip file,
+    the headers it includes); a committed counter summary is valid only for
+    that digest."""
     h = hashlib.sha256()
     for name in sorted(set(files) | set(_COMMON_SOURCES)):
-        with open(os.path.join(ROOT, CSRC, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(ROOT, CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

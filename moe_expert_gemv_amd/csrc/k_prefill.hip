@@ -17,14 +17,17 @@
 //    step s of the MFMA sums, for lane group g, the k range
 //    slab + 32g + 8s .. +8 on both operands (A and B use the same permutation
 //    of k, so the contraction is unchanged).
-//  * Two shapes.  M <= 128: workgroups of 64 tokens x 48 weight rows (N =
-//    12288 gives 256 per 64 tokens); slab j of k goes to wave j mod 4, each
+//  * Three shapes.  M <= 128 without a workspace (k_prefill_ks): workgroups
+//    of 64 tokens x 48 weight rows; slab j of k goes to wave j mod 4, each
 //    wave chains its slabs through the MFMAs in ascending order, and the four
-//    partial sums are added in wave order through LDS.  M > 128: workgroups
-//    of 128 tokens x 192 weight rows, each wave 48 rows over all k in one
-//    ascending MFMA chain.  Within a shape the summation order of an output
-//    does not depend on M or on the other rows, so a row's result does not
-//    depend on the batch it came in (the two shapes agree to rounding).
+//    partial sums are added in wave order through LDS.  M <= 128 with a
+//    workspace (k_prefill_sk + k_prefill_reduce): k is also split over
+//    workgroups, 1024 per workgroup, whose fp32 partials are added in range
+//    order by a second kernel.  M > 128 (k_prefill): workgroups of 128
+//    tokens x 192 weight rows, each wave 48 rows over all k in one ascending
+//    MFMA chain.  Within a shape the summation order of an output does not
+//    depend on M or on the other rows, so a row's result does not depend on
+//    the batch it came in (the shapes agree with each other to rounding).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -185,12 +185,14 @@ inline constexpr int lanes_per_row(int64_t nchunks) { return nchunks >= 64 ? 64 
 inline constexpr int token_class(int m) { return m <= 1 ? 1 : m <= 4 ? 4 : 16; }
 
 // Rows per lane group: about 8 KB of weight loads in flight per wave (R*C
-// chunks of 1 KB per wave-wide load); with several tokens at least 2 rows so
-// that each activation load feeds more than one row, and at most 2 rows at 16
-// tokens to bound the accumulators.
+// chunks of 1 KB per wave-wide load); with several tokens at least 4 rows (2
+// for rows of more than 4 chunks per lane) so that each activation load feeds
+// several rows -- activations for 4 tokens are as many bytes per row as the
+// weights -- and at most 2 rows at 16 tokens to bound the accumulators.
 inline constexpr int rows_per_group(int C, int MT) {
     const int c = C == 0 ? 8 : C;
     int r = 8 / c;
+    if (MT > 1 && r < 4 && C > 0 && C <= 4) r = 4;
     if (MT > 1 && r < 2) r = 2;
     if (MT >= 16 && r > 2) r = 2;
     return r >= 8 ? 8 : r >= 4 ? 4 : r >= 2 ? 2 : 1;
