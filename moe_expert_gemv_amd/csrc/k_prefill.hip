@@ -23,11 +23,13 @@
 //    partial sums are added in wave order through LDS.  M <= 128 with a
 //    workspace (k_prefill_sk + k_prefill_reduce): k is also split over
 //    workgroups, 1024 per workgroup, whose fp32 partials are added in range
-//    order by a second kernel.  M > 128 (k_prefill): workgroups of 128
-//    tokens x 192 weight rows, each wave 48 rows over all k in one ascending
-//    MFMA chain.  Within a shape the summation order of an output does not
-//    depend on M or on the other rows, so a row's result does not depend on
-//    the batch it came in (the shapes agree with each other to rounding).
+//    order by a second kernel.  M > 128: workgroups of 128 tokens x 192
+//    weight rows; with k a multiple of 256 eight waves (k_prefill8, two
+//    chains per output, added in a fixed order), otherwise four
+//    (k_prefill, each wave 48 rows over all k in one ascending MFMA chain).
+//    Within a shape the summation order of an output does not depend on M or
+//    on the other rows, so a row's result does not depend on the batch it
+//    came in (the shapes agree with each other to rounding).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -90,6 +92,16 @@ __device__ __forceinline__ void transpose4_lane_groups(uint32_t (&d)[4]) {
 // waves along W rows x along k; WD: stages of W loads in flight.
 constexpr int KW = 128;  // k per wave per stage: one slab
 
+// Workgroup barrier that publishes LDS only: waits for this wave's LDS
+// accesses (not its global loads, so weight prefetches stay in flight), then
+// s_barrier.  __syncthreads() would also wait for every outstanding global
+// load.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int MB, int NB, int WN, int WK, int WD>
 struct PrefillShape {
     static constexpr int BM = 16 * MB;            // tokens per workgroup
@@ -131,6 +143,9 @@ __global__ __launch_bounds__(kBlock) void k_prefill(const uint8_t* __restrict__ 
     // ---- X staging: thread t moves chunks p = t + 256 j of the BM x BK tile;
     // chunk (row, c) lands at row * CPR + (c ^ (row & 15)) (bank-conflict-free
     // fragment reads: 16 lanes reading one column of 16 rows hit 16 slots).
+    // Chunks past k are zeroed when stored, not when loaded: a use right
+    // after the prefetch would make the compiler wait for it (and, loads
+    // completing in order, for every load issued before it).
     u32x4 xr[NCH];
     auto x_load = [&](int st) {
 #pragma unroll
@@ -138,18 +153,18 @@ __global__ __launch_bounds__(kBlock) void k_prefill(const uint8_t* __restrict__ 
             const int p = tid + kBlock * j;
             const int row = p / CPR, c = p % CPR;
             const int kk = st * BK + 8 * c;
-            const bool ok = kk < k;
             const int64_t gr = min(m0 + row, m - 1);
-            const u32x4 v = ld16(x + gr * k + (ok ? kk : 0));
-            xr[j] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+            xr[j] = ld16(x + gr * k + (kk < k ? kk : 0));
         }
     };
-    auto x_store = [&](int buf) {
+    auto x_store = [&](int buf, int st) {
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const int p = tid + kBlock * j;
             const int row = p / CPR, c = p % CPR;
-            *reinterpret_cast<u32x4*>(&xs[buf][8 * (row * CPR + (c ^ (row & 15)))]) = xr[j];
+            const bool ok = st * BK + 8 * c < k;
+            *reinterpret_cast<u32x4*>(&xs[buf][8 * (row * CPR + (c ^ (row & 15)))]) =
+                ok ? xr[j] : u32x4{0u, 0u, 0u, 0u};
         }
     };
 
@@ -189,9 +204,9 @@ __global__ __launch_bounds__(kBlock) void k_prefill(const uint8_t* __restrict__ 
 #pragma unroll
     for (int d = 0; d < WD; ++d) w_load(wr[d], d);
     x_load(0);
-    x_store(0);
+    x_store(0, 0);
     x_load(1);
-    __syncthreads();
+    lds_barrier();
 
     // ---- main loop, unrolled by WD so the W ring index is static; runs a
     // whole number of ring rounds (stages past nst multiply zeros)
@@ -228,9 +243,9 @@ __global__ __launch_bounds__(kBlock) void k_prefill(const uint8_t* __restrict__ 
             }
             // stage st + 1 into the other buffer (last read in stage st - 1,
             // before the barrier that closed it), then prefetch st + 2
-            x_store(buf ^ 1);
+            x_store(buf ^ 1, st + 1);
             x_load(st + 2);
-            __syncthreads();
+            lds_barrier();  // the W ring stays in flight across it
         }
     }
 
@@ -269,6 +284,147 @@ __global__ __launch_bounds__(kBlock) void k_prefill(const uint8_t* __restrict__ 
             const int row = m0 + r, col = int(blockIdx.x) * BN + c;
             if (row < m && col < n) y[int64_t(row) * n + col] = uint16_t(f32_to_bf16_rne(sum * s_t));
         }
+    }
+}
+
+// M > 128 with k a multiple of 256, eight waves (two per SIMD, so one wave's
+// weight decode and LDS reads overlap the other's MFMAs): waves w and w + 4
+// take the same 48 weight rows, w the first 128-k slab of each 256-k stage and
+// w + 4 the second.  The X tile of a stage (BM tokens x 256 k) is
+// double-buffered in LDS and filled by gfx950's direct global-to-LDS loads,
+// which hold no registers; each wave's weight slab for the next stage is
+// loaded into registers at the start of the current one.  Everything a stage
+// requests is needed at the start of the next, so one full wait before the
+// stage's closing barrier covers both.  At the end the second half's sums go
+// through LDS and are added to the first half's in that fixed order.
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+template <int MB, int NB>
+__global__ __launch_bounds__(512) void k_prefill8(const uint8_t* __restrict__ w, int64_t soff, float s_t, int n,
+                                                  int k, const uint16_t* __restrict__ x, int m,
+                                                  uint16_t* __restrict__ y) {
+    constexpr int NT = 512, WN = 4;
+    constexpr int BM = 16 * MB, BN = 16 * NB * WN, BK = 2 * KW;
+    constexpr int CPR = BK / 8;                 // 16-byte X chunks per LDS row
+    constexpr int NCP = BM * CPR / NT;          // copy instructions per wave per stage
+    constexpr int SPS = KW / 32;                // MFMA steps per slab
+    static_assert((BM * CPR) % NT == 0, "X tile split evenly over the threads");
+    static_assert(sizeof(float) * BM * BN <= 2 * BM * BK * 2, "second-half sums fit in the X buffers");
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * BK];
+
+    const int tid = int(threadIdx.x);
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave % WN, wk = wave / WN;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int m0 = int(blockIdx.y) * BM;
+    const int n0 = int(blockIdx.x) * BN + wn * 16 * NB;
+    const int nst = k / BK;
+    const int64_t crow = k / 2, srow = k / 16;
+
+    // X tile of stage st into buffer buf: slot p holds X[row][st BK + 8c],
+    // row = p / CPR, c = (p % CPR) ^ (row & 15) (fragment reads hit 16
+    // distinct slots per 16 lanes); copy instruction i of this wave fills the
+    // 64 consecutive slots from (wave + 8 i) * 64, lane j the j-th.  Rows past
+    // m repeat row m - 1.
+    auto x_copy = [&](int buf, int st) {
+#pragma unroll
+        for (int i = 0; i < NCP; ++i) {
+            const int cp = wave + (NT / kWave) * i;
+            const int p = cp * kWave + lane;
+            const int row = p / CPR, c = (p % CPR) ^ (row & 15);
+            const uint16_t* src = x + int64_t(min(m0 + row, m - 1)) * k + st * BK + 8 * c;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(xs[buf] + 8 * cp * kWave), 16, 0, 0);
+        }
+    };
+
+    const uint8_t* wc[NB];
+    const uint8_t* ws[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t row = min(n0 + 16 * nb + lr, n - 1);
+        wc[nb] = w + row * crow;
+        ws[nb] = w + soff + row * srow;
+    }
+    // stages past the end reread stage 0 (a valid address; never used)
+    auto w_load = [&](WStage<NB>& b, int st) {
+        const int kl = (st < nst ? st : 0) * BK + wk * KW + lg * (KW / 4);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const u32x4 v = ld_stream16(wc[nb] + kl / 2);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
+            b.s[nb] = ld<uint16_t>(ws[nb] + kl / 16);
+        }
+    };
+
+    floatx4 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    WStage<NB> wr;
+    w_load(wr, 0);
+    x_copy(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stage's copies and weights have landed
+    lds_barrier();
+
+    for (int st = 0; st < nst; ++st) {
+        const int buf = st & 1;
+        const uint16_t* xb = xs[buf];
+        const WStage<NB> cur = wr;
+        w_load(wr, st + 1);
+        // the last stage recopies its own tile into the idle buffer: no branch
+        // (a join after the copies would make the compiler wait for them at
+        // the first use of any loaded register)
+        x_copy(buf ^ 1, st + 1 < nst ? st + 1 : st);
+        __builtin_amdgcn_sched_barrier(0);  // the next stage's loads are issued before this stage's work
+#pragma unroll
+        for (int s = 0; s < SPS; ++s) {
+            u32x4 bfr[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float sc = (s < 2) ? e4m3_to_f32<0>(cur.s[nb]) : e4m3_to_f32<1>(cur.s[nb]);
+                bfr[nb] = decode8_scaled(cur.c[nb][s], sc);
+            }
+            const int c = (wk * KW + lg * (KW / 4) + 8 * s) / 8;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int row = 16 * mb + lr;
+                const u32x4 a = *reinterpret_cast<const u32x4*>(&xb[8 * (row * CPR + (c ^ (row & 15)))]);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32_bf16(a, bfr[nb], acc[mb][nb]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next stage's copies and weights
+        lds_barrier();
+    }
+
+    // second half's sums through LDS (the X buffers are free after the last
+    // barrier), added to the first half's in that order
+    float* red = reinterpret_cast<float*>(&xs[0][0]) + wn * (MB * NB * 4 * kWave);
+    if (wk == 1) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) red[((mb * NB + nb) * 4 + v) * kWave + lane] = acc[mb][nb][v];
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float sum = acc[mb][nb][v] + red[((mb * NB + nb) * 4 + v) * kWave + lane];
+                    const int row = m0 + 16 * mb + 4 * lg + v;
+                    const int col = n0 + 16 * nb + lr;
+                    if (row < m && col < n) y[int64_t(row) * n + col] = uint16_t(f32_to_bf16_rne(sum * s_t));
+                }
     }
 }
 
@@ -661,6 +817,12 @@ hipError_t launch_prefill(const uint8_t* w, float s_t, int64_t n, int64_t k, con
         const dim3 grid(unsigned((n + 16 * NB - 1) / (16 * NB)), unsigned((m + 16 * MB - 1) / (16 * MB)));
         hipLaunchKernelGGL((k_prefill_ks<MB, NB>), grid, dim3(kBlock), 0, s, w, soff, s_t, int(n), int(k), x,
                            int(m), y);
+        return hipGetLastError();
+    }
+    if (k % (2 * KW) == 0) {
+        constexpr int MB = 8, NB = 3, BN = 16 * NB * 4, BM = 16 * MB;
+        const dim3 grid(unsigned((n + BN - 1) / BN), unsigned((m + BM - 1) / BM));
+        hipLaunchKernelGGL((k_prefill8<MB, NB>), grid, dim3(512), 0, s, w, soff, s_t, int(n), int(k), x, int(m), y);
         return hipGetLastError();
     }
     return go<8, 3, 4, 1, 4>(w, soff, s_t, n, k, x, m, y, s);

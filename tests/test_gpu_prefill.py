@@ -63,7 +63,11 @@ def test_worked_example():
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 32), (3, 17, 64), (64, 64, 64), (65, 130, 96), (100, 300, 512),
-                                   (128, 64, 4096), (7, 1000, 2080), (513, 129, 160)])
+                                   (128, 64, 4096), (7, 1000, 2080), (513, 129, 160),
+                                   # M > 128, k a multiple of 256 (eight-wave kernel), ragged m and n
+                                   (129, 193, 256), (300, 200, 768), (257, 385, 2048),
+                                   # M > 128, other k (four-wave kernel)
+                                   (200, 100, 1056)])
 def test_random(m, n, k):
     require_gpu()
     print(f"[prefill m={m} n={n} k={k}]", flush=True)
@@ -117,8 +121,8 @@ def test_one_hot_rows_are_exact():
 
 def test_rows_are_independent():
     """A row's result does not depend on the other rows of the batch, nor on
-    M inside each of the two shapes (M <= 128 and M > 128); across the two
-    shapes results agree to rounding (the parity tests)."""
+    M inside each shape (M <= 128; M > 128, here with k a multiple of 256);
+    across shapes results agree to rounding (the parity tests)."""
     require_gpu()
     g = synth.rng(9)
     w = synth.nvfp4_weights(g, 256, 1024)
