@@ -268,6 +268,7 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
     const bool scales_in_lds = n_scales <= kMaxScaleLds;
     if (scales_in_lds)
         for (int i = tid; i < n_scales; i += kBlock) s_scale[i] = A.gu_scale[i];  // visible after the CSR barrier
+    bool csr_done = false;
     if constexpr (ROUTE) {
         const int lane = lane_id();
         for (int tok = tid / kWave; tok < t; tok += kBlock / kWave) {  // uniform per wave
@@ -281,11 +282,35 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
                     ws.wts[tok * A.k + lane] = sw;
                 }
             }
+            if (t == 1) {
+                // One token: its k experts are distinct, so the CSR is their
+                // ascending order, one pair each (what build_csr produces),
+                // written by this wave -- one barrier instead of four.
+                int rank = 0;
+                for (int j = 0; j < A.k; ++j) rank += int(__builtin_amdgcn_readlane(si, j) < si);
+                if (lane < A.k) {
+                    c.experts[rank] = si;
+                    c.offsets[rank] = rank;
+                    c.tok[rank] = 0;
+                    c.slot[rank] = lane;
+                }
+                if (lane == 0) {
+                    c.offsets[A.k] = A.k;
+                    if (A.has_shared) {
+                        c.experts[A.k] = A.E;
+                        c.offsets[A.k + 1] = A.k + 1;
+                        c.tok[A.k] = 0;
+                        c.slot[A.k] = A.k;
+                    }
+                    c.n_groups = A.k + A.has_shared;
+                }
+            }
         }
         __syncthreads();
         ids = s_ids;
+        csr_done = t == 1;
     }
-    build_csr(ids, t, A.k, A.E, A.has_shared, c, s_e, s_first);
+    if (!csr_done) build_csr(ids, t, A.k, A.E, A.has_shared, c, s_e, s_first);
     if (blockIdx.x == 0 && blockIdx.y == 0) {
         const int P = t * (A.k + A.has_shared);
         if (tid == 0) *ws.n_groups = c.n_groups;

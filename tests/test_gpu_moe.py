@@ -225,10 +225,13 @@ def test_moe_batch_invariance_and_determinism():
 
 @pytest.mark.parametrize("t,E,k,shared,H,I", [(1, 256, 8, True, 256, 64), (4, 64, 8, True, 256, 64),
                                               (16, 300, 8, False, 256, 64), (3, 8, 2, True, 256, 64),
-                                              (4, 128, 8, True, 2048, 512), (2, 300, 8, False, 2048, 256)])
+                                              (4, 128, 8, True, 2048, 512), (2, 300, 8, False, 2048, 256),
+                                              (1, 300, 8, False, 256, 64), (1, 8, 2, True, 256, 64)])
 def test_moe_forward_matches_route_then_grouped(t, E, k, shared, H, I):
     """The fused path (routing inside the gate/up kernel) gives bitwise the
-    same ids, weights and outputs as moe_route_topk + moe_gemv_grouped."""
+    same ids, weights and outputs as moe_route_topk + moe_gemv_grouped, and
+    publishes the oracle's expert-major grouping (at t = 1 it is built
+    directly from the routing wave)."""
     import torch
 
     require_gpu()
@@ -252,6 +255,11 @@ def test_moe_forward_matches_route_then_grouped(t, E, k, shared, H, I):
     off = (off + 4 * t * k + 255) // 256 * 256
     wts = wsh[off:off + 4 * t * k].view(np.float32).reshape(t, k)
     assert np.array_equal(ids, host(ids_d)) and np.array_equal(wts.view(np.uint32), host(w_d).view(np.uint32))
+    W = read_workspace(wsh, L, t)
+    csr = oracle.group_by_expert(ids, E, shared)
+    assert W["n_groups"] == len(csr["experts"])
+    for key in ("experts", "offsets", "tok", "slot"):
+        assert np.array_equal(W[key], csr[key]), key
 
 
 @pytest.fixture(scope="module")
