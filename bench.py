@@ -212,6 +212,42 @@ class Q8Gemv(Workload):
     dominant_launch = step
 
 
+class Fp8Gemv(Workload):
+    """FP8 E4M3 weight GEMV with block-128 scales at the gate+up shape of the
+    9B-class layer (the pages' 9B model runs FP8 weights)."""
+
+    sources = ("k_gemv_fp8.hip",)
+    kernel_re = (r"k_gemv_fp8\b",)
+
+    def __init__(self, m=1):
+        import torch
+        import moe_expert_gemv_amd as qg
+        import synth
+
+        self.qg, self.m = qg, m
+        self.N, self.K = 24576, 4096
+        g = synth.rng(synth.seed_for(6))
+        w = synth.fp8_weights(g, self.N, self.K, tiled=True)
+        buf = qg.qg_pack_fp8(qg.QG_FP8_B128, w["codes"], w["scales"])
+        self.R = _copies(buf.nbytes)
+        self.w = torch.from_numpy(buf).cuda().repeat(self.R, 1)
+        x = synth.x_bf16(g, m, self.K)
+        self.x = torch.from_numpy(x.view(np.int16).copy()).cuda()
+        self.y = torch.empty((m, self.N), dtype=torch.float32, device="cuda")
+        scales = w["scales"].size * 4
+        self.alg_step = self.N * self.K + scales + 2 * m * self.K + 4 * m * self.N
+        self.dominant_bytes = self.alg_step
+        self.flops_step = 2 * m * self.N * self.K
+        self.name = (f"FP8 E4M3 GEMV {self.N}x{self.K} (9B-class gate+up), block-128 fp32 scales, "
+                     f"bf16 activations, batch {m}")
+        self.dominant = "FP8 GEMV"
+
+    def step(self, i):
+        self.qg.qgemv_fp8(self.qg.QG_FP8_B128, self.w[i % self.R], self.N, self.K, self.x, self.m, self.y)
+
+    dominant_launch = step
+
+
 class W4A8Gemv(Workload):
     sources = ("k_gemv_a8.hip",)
     kernel_re = (r"k_gemv_q4_0_a8\b",)
@@ -372,6 +408,7 @@ CONFIGS = {  # name -> (workload class, its size argument)
     "q8": (Q8Gemv, 1),
     "w4a8": (W4A8Gemv, 1),
     "w4a8-m4": (W4A8Gemv, 4),
+    "fp8": (Fp8Gemv, 1),
     "moe": (MoE, 1),
     "moe-t4": (MoE, 4),
     "prefill64": (PrefillWs, 64),

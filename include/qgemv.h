@@ -15,6 +15,10 @@
  *          scale per tensor.  w = e2m1(c) * e4m3(s_b) * s_t.
  *   Q8_0   32-element blocks; int8 codes, one fp16 scale.  w = d * q.
  *   Q4_0   32-element blocks; 4-bit codes, one fp16 scale.  w = d * (q - 8).
+ *   FP8    E4M3 codes (OCP OFP8 v1.0, the variant without infinities), one
+ *          byte per weight, with fp32 scales: one per tensor (QG_FP8_TENSOR)
+ *          or one per 128 x 128 tile of W (QG_FP8_B128, the "block-128" FP8
+ *          checkpoints of the memra README, loaders entry).  w = e4m3(c) * s.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -62,6 +66,8 @@ extern "C" {
 #define QG_NVFP4 1
 #define QG_Q8_0  2
 #define QG_Q4_0  3
+#define QG_FP8_TENSOR 4
+#define QG_FP8_B128   5
 
 #define QG_ABI_VERSION    1
 #define QG_LAYOUT_VERSION 1  /* packed device layout described below */
@@ -92,6 +98,10 @@ int qg_last_hip_error(void);
  *          32b+16+i (high nibble).
  *          scales: n rows of k/32 fp16 bit patterns.
  *   Q8_0   codes: n rows of k int8.  scales: n rows of k/32 fp16 bit patterns.
+ *   FP8    codes: n rows of k E4M3 bytes.  scales: fp32; QG_FP8_TENSOR one
+ *          value, QG_FP8_B128 a row-major grid [ceil(n/128)][ceil(k/128)]
+ *          whose entry (i, j) scales rows [128i, 128i+128) x columns
+ *          [128j, 128j+128) (the last tiles may be partial).
  *
  * Every row of every plane starts 16-byte aligned when k % 32 == 0.
  */
@@ -132,12 +142,22 @@ int qg_unpack_q4_0(const void* src, size_t src_bytes, int64_t n, int64_t k,
 int qg_unpack_q8_0(const void* src, size_t src_bytes, int64_t n, int64_t k,
                    int8_t* codes, uint16_t* scales_f16);
 
+/* FP8 packer / unpacker.  fmt: QG_FP8_TENSOR or QG_FP8_B128 (else
+ * QG_EINVAL).  codes: E4M3 bit patterns, row-major [n][k]; scales: fp32, 1
+ * value (tensor) or the [ceil(n/128)][ceil(k/128)] grid (block-128).  Any
+ * bit pattern is accepted (NaN codes decode to NaN).  Exact inverses. */
+int qg_pack_fp8(int fmt, const uint8_t* codes, const float* scales, int64_t n, int64_t k,
+                void* dst, size_t dst_bytes);
+int qg_unpack_fp8(int fmt, const void* src, size_t src_bytes, int64_t n, int64_t k,
+                  uint8_t* codes, float* scales);
+
 /* ------------------------------------------------------ dequantization
  * out[r][c] = the weight value, fp32 (device, [n][k]).  NVFP4: e2m1*e4m3 is
  * exact and the product with tensor_scale is rounded once (to nearest even);
  * Q4_0 and Q8_0 values are exact in fp32.  Runs the same device decode code
  * as the GEMV kernels; meant for verification, not for the decode path.
- * tensor_scale is ignored for Q4_0 / Q8_0. */
+ * tensor_scale is ignored for Q4_0 / Q8_0 / FP8 (FP8 values e4m3 * s are
+ * rounded once to fp32). */
 int qg_dequant(int fmt, const void* w, float tensor_scale, int64_t n, int64_t k,
                float* out, void* stream);
 
@@ -157,6 +177,16 @@ int qgemv_q8_0(const void* w, int64_t n, int64_t k, const float* x, int64_t m,
  * each row sum. */
 int qgemv_nvfp4(const void* w, float tensor_scale, int64_t n, int64_t k,
                 const uint16_t* x, int64_t m, float* y, void* stream);
+
+/* FP8 (E4M3) x bf16 activations (LumenLLM README: native FP8 weights; its
+ * 9B model runs FP8).  fmt: QG_FP8_TENSOR or QG_FP8_B128; w: device packed
+ * FP8 [n][k]; x: device bf16 bit patterns [m][k]; y: device fp32 [m][n].
+ * Each 16-element chunk of a row is summed in fp32 (exact products of bf16
+ * and e4m3), then added into the row sum as fma(s, chunk_sum, acc) with its
+ * tile's scale (block-128), or the row sum is multiplied by the tensor scale
+ * once (tensor). */
+int qgemv_fp8(int fmt, const void* w, int64_t n, int64_t k, const uint16_t* x, int64_t m, float* y,
+              void* stream);
 
 /* NVFP4 fused gate+up GEMV with the SwiGLU epilogue of an MLP.  w_gu: device
  * fused gate/up matrix packed by qg_pack_nvfp4_gate_up (logical rows

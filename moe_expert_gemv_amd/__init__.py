@@ -19,10 +19,11 @@ import numpy as np
 
 __all__ = [
     "QGError", "QGLibraryMissing", "LIB_PATH", "lib", "loaded",
-    "QG_NVFP4", "QG_Q8_0", "QG_Q4_0", "QG_MAX_M", "QG_MOE_KEEP_H",
+    "QG_NVFP4", "QG_Q8_0", "QG_Q4_0", "QG_FP8_TENSOR", "QG_FP8_B128", "QG_MAX_M", "QG_MOE_KEEP_H",
     "qg_abi_version", "qg_layout_version", "qg_status_string", "qg_packed_bytes",
     "qg_scale_plane_offset", "qg_pack_nvfp4", "qg_pack_nvfp4_gate_up", "qg_pack_q4_0", "qg_pack_q8_0",
-    "qg_unpack_nvfp4", "qg_unpack_nvfp4_gate_up", "qg_unpack_q4_0", "qg_unpack_q8_0", "qg_dequant",
+    "qg_unpack_nvfp4", "qg_unpack_nvfp4_gate_up", "qg_unpack_q4_0", "qg_unpack_q8_0", "qg_pack_fp8",
+    "qg_unpack_fp8", "qgemv_fp8", "fp8_scale_shape", "qg_dequant",
     "qgemv_q8_0", "qgemv_nvfp4", "qgemv_nvfp4_swiglu", "qg_quantize_q8_0_act",
     "qgemv_q4_0_a8", "moe_route_topk", "QgMoeDesc", "moe_workspace_bytes",
     "moe_gemv_grouped", "moe_forward", "qgemm_prefill", "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
@@ -32,7 +33,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
 
 QG_OK, QG_EINVAL, QG_EUNSUPPORTED, QG_ENOSPC, QG_EHIP = 0, -1, -2, -4, -5
-QG_NVFP4, QG_Q8_0, QG_Q4_0 = 1, 2, 3
+QG_NVFP4, QG_Q8_0, QG_Q4_0, QG_FP8_TENSOR, QG_FP8_B128 = 1, 2, 3, 4, 5
 QG_MAX_M = 16
 QG_MOE_KEEP_H = 1
 
@@ -86,6 +87,9 @@ _SIGNATURES = {
     "qg_unpack_nvfp4_gate_up": (_I32, [_P, _SZ, _I64, _I64, _P, _P]),
     "qg_unpack_q4_0": (_I32, [_P, _SZ, _I64, _I64, _P, _P]),
     "qg_unpack_q8_0": (_I32, [_P, _SZ, _I64, _I64, _P, _P]),
+    "qg_pack_fp8": (_I32, [_I32, _P, _P, _I64, _I64, _P, _SZ]),
+    "qg_unpack_fp8": (_I32, [_I32, _P, _SZ, _I64, _I64, _P, _P]),
+    "qgemv_fp8": (_I32, [_I32, _P, _I64, _I64, _P, _I64, _P, _P]),
     "qg_dequant": (_I32, [_I32, _P, _F32, _I64, _I64, _P, _P]),
     "qgemv_q8_0": (_I32, [_P, _I64, _I64, _P, _I64, _P, _P]),
     "qgemv_nvfp4": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P]),
@@ -248,6 +252,39 @@ def qg_unpack_q8_0(buf, n, k):
     return _unpack("qg_unpack_q8_0", buf, n, k, np.int8, np.uint16, 32)
 
 
+def fp8_scale_shape(fmt, n, k):
+    """Shape of the fp32 scales of an FP8 matrix: (1, 1) per tensor, the
+    [ceil(n/128), ceil(k/128)] tile grid for block-128."""
+    if fmt == QG_FP8_TENSOR:
+        return (1, 1)
+    if fmt == QG_FP8_B128:
+        return ((n + 127) // 128, (k + 127) // 128)
+    raise QGError("fp8_scale_shape", QG_EINVAL)
+
+
+def qg_pack_fp8(fmt, codes, scales) -> np.ndarray:
+    """E4M3 codes [n][k] (bit patterns) and fp32 scales (fp8_scale_shape) -> packed."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    n, k = codes.shape
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    if scales.size != int(np.prod(fp8_scale_shape(fmt, n, k))):
+        raise QGError("qg_pack_fp8", QG_EINVAL)
+    size = qg_packed_bytes(fmt, n, k)
+    if size == 0:
+        raise QGError("qg_pack_fp8", QG_EINVAL)
+    out = np.empty(size, dtype=np.uint8)
+    _check("qg_pack_fp8", lib().qg_pack_fp8(fmt, _hptr(codes), _hptr(scales), n, k, _hptr(out), size))
+    return out
+
+
+def qg_unpack_fp8(fmt, buf, n, k):
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    codes = np.empty((n, k), dtype=np.uint8)
+    scales = np.empty(fp8_scale_shape(fmt, n, k), dtype=np.float32)
+    _check("qg_unpack_fp8", lib().qg_unpack_fp8(fmt, _hptr(buf), buf.nbytes, n, k, _hptr(codes), _hptr(scales)))
+    return codes, scales
+
+
 # ---------------------------------------------------------------- device entry points
 
 def qg_dequant(fmt, w, tensor_scale, n, k, out, stream=None) -> None:
@@ -261,6 +298,10 @@ def qgemv_q8_0(w, n, k, x, m, y, stream=None) -> None:
 def qgemv_nvfp4(w, tensor_scale, n, k, x, m, y, stream=None) -> None:
     _check("qgemv_nvfp4",
            lib().qgemv_nvfp4(_dptr(w), tensor_scale, n, k, _dptr(x), m, _dptr(y), _stream(stream)))
+
+
+def qgemv_fp8(fmt, w, n, k, x, m, y, stream=None) -> None:
+    _check("qgemv_fp8", lib().qgemv_fp8(fmt, _dptr(w), n, k, _dptr(x), m, _dptr(y), _stream(stream)))
 
 
 def qgemv_nvfp4_swiglu(w_gu, tensor_scale, inter, k, x, m, a, h=None, stream=None) -> None:

@@ -67,8 +67,17 @@ int qg_dequant(int fmt, const void* w, float tensor_scale, int64_t n, int64_t k,
                void* stream) {
     if (!valid_fmt(fmt) || !w || !out || !aligned(w, 256) || !aligned(out, 16)) return QG_EINVAL;
     if (!valid_shape(n, k)) return QG_EINVAL;
+    if (is_fp8(fmt))
+        return finish(launch_dequant_fp8(fmt, static_cast<const uint8_t*>(w), n, k, out, as_stream(stream)));
     return finish(launch_dequant(fmt, static_cast<const uint8_t*>(w), tensor_scale, n, k, out,
                                  as_stream(stream)));
+}
+
+int qgemv_fp8(int fmt, const void* w, int64_t n, int64_t k, const uint16_t* x, int64_t m, float* y,
+              void* stream) {
+    if (!is_fp8(fmt)) return QG_EINVAL;
+    if (int st = check_gemv(w, n, k, x, m, y)) return st;
+    return finish(launch_gemv_fp8(fmt, static_cast<const uint8_t*>(w), n, k, x, int(m), y, as_stream(stream)));
 }
 
 int qgemv_q8_0(const void* w, int64_t n, int64_t k, const float* x, int64_t m, float* y,

@@ -30,6 +30,14 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t w) {
     return __builtin_amdgcn_cvt_f32_fp8(int(w), B);
 }
 
+// E4M3 bytes 2W and 2W+1 of w -> two bf16 (lower byte first).  Every E4M3
+// value, subnormals included, is exact in bf16; NaN stays NaN.  gfx950's
+// packed FP8 conversion with a unit scale.
+template <int W>
+__device__ __forceinline__ bf16x2 e4m3x2_to_bf16x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, W != 0);
+}
+
 // IEEE binary16 bits -> fp32 (exact, subnormals included).
 __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
     return float(__builtin_bit_cast(_Float16, uint16_t(bits)));

@@ -188,4 +188,27 @@ int qg_unpack_q8_0(const void* src, size_t src_bytes, int64_t n, int64_t k, int8
     return QG_OK;
 }
 
+int qg_pack_fp8(int fmt, const uint8_t* codes, const float* scales, int64_t n, int64_t k, void* dst,
+                size_t dst_bytes) {
+    if (!qg::is_fp8(fmt)) return QG_EINVAL;
+    int st = check_pack_args(fmt, codes, scales, n, k, dst, dst_bytes);
+    if (st) return st;
+    uint8_t* out = static_cast<uint8_t*>(dst);
+    std::memset(out, 0, size_t(qg::packed_bytes(fmt, n, k)));
+    std::memcpy(out, codes, size_t(n * k));
+    std::memcpy(out + qg::scale_plane_offset(fmt, n, k), scales, size_t(qg::scale_plane_bytes(fmt, n, k)));
+    return QG_OK;
+}
+
+int qg_unpack_fp8(int fmt, const void* src, size_t src_bytes, int64_t n, int64_t k, uint8_t* codes,
+                  float* scales) {
+    if (!qg::is_fp8(fmt)) return QG_EINVAL;
+    int st = check_pack_args(fmt, codes, scales, n, k, src, src_bytes);
+    if (st) return st;
+    const uint8_t* in = static_cast<const uint8_t*>(src);
+    std::memcpy(codes, in, size_t(n * k));
+    std::memcpy(scales, in + qg::scale_plane_offset(fmt, n, k), size_t(qg::scale_plane_bytes(fmt, n, k)));
+    return QG_OK;
+}
+
 }  // extern "C"

@@ -80,8 +80,30 @@ def dequant_q4_0(w: dict, rows=None) -> np.ndarray:
     return (q.reshape(n, k // Q_BLOCK, Q_BLOCK) * d[:, :, None]).reshape(n, k)
 
 
+FP8_TILE = 128
+
+
+def dequant_fp8(w: dict, rows=None) -> np.ndarray:
+    """FP8 weight values: e4m3(code) times an fp32 scale, exact in fp64.
+
+    E4M3 weights (LumenLLM README, feature list "Quantization": native FP8
+    (E4M3); model table: its 9B model runs FP8).  Scales: one per tensor, or
+    one per 128 x 128 tile of W when ``w["tiled"]`` (the block-128 FP8
+    checkpoints of the memra README, feature list "Loaders"); tile (i, j)
+    scales rows [128 i, 128 i + 128) and columns [128 j, 128 j + 128).
+    """
+    r = _rows(w, rows)
+    v = decode_e4m3(w["codes"][r])
+    s = np.asarray(w["scales"], dtype=np.float32).astype(np.float64)
+    if not w["tiled"]:
+        return v * s.reshape(-1)[0]
+    k = v.shape[1]
+    cols = np.arange(k) // FP8_TILE
+    return v * s[(r // FP8_TILE)[:, None], cols[None, :]]
+
+
 def dequant(w: dict, rows=None) -> np.ndarray:
-    f = {"nvfp4": dequant_nvfp4, "q8_0": dequant_q8_0, "q4_0": dequant_q4_0}[w["fmt"]]
+    f = {"nvfp4": dequant_nvfp4, "q8_0": dequant_q8_0, "q4_0": dequant_q4_0, "fp8": dequant_fp8}[w["fmt"]]
     return f(w, rows)
 
 

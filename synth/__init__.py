@@ -40,6 +40,8 @@ BASE_SEED = 20261202
 NVFP4 = "nvfp4"
 Q8_0 = "q8_0"
 Q4_0 = "q4_0"
+FP8 = "fp8"
+FP8_TILE = 128  # side of an FP8 block-128 scale tile
 
 
 def seed_for(cfg: int, tensor_index: int = 0) -> int:
@@ -91,6 +93,24 @@ def nvfp4_weights(g: np.random.Generator, n: int, k: int, tensor_scale: float = 
         "scales": to_e4m3_bits(sc),
         "tensor_scale": np.float32(tensor_scale),
     }
+
+
+def fp8_weights(g: np.random.Generator, n: int, k: int, tiled: bool = True, std: float = 0.02) -> dict:
+    """FP8 E4M3 weights the way FP8 checkpoints are made: w ~ N(0, std) in
+    fp32, one fp32 scale per 128 x 128 tile (tiled) or per tensor equal to the
+    tile's max |w| / 448, codes = E4M3 of w / scale (torch's cast)."""
+    w = (g.standard_normal(size=(n, k)) * std).astype(np.float32)
+    if tiled:
+        tn, tk = (n + FP8_TILE - 1) // FP8_TILE, (k + FP8_TILE - 1) // FP8_TILE
+        pad = np.zeros((tn * FP8_TILE, tk * FP8_TILE), np.float32)
+        pad[:n, :k] = np.abs(w)
+        amax = pad.reshape(tn, FP8_TILE, tk, FP8_TILE).max(axis=(1, 3))
+    else:
+        amax = np.array([[np.abs(w).max()]], np.float32)
+    scales = np.maximum(amax, np.float32(1e-30)).astype(np.float32) / np.float32(448.0)
+    full = np.repeat(np.repeat(scales, FP8_TILE, axis=0), FP8_TILE, axis=1)[:n, :k] if tiled else scales[0, 0]
+    codes = to_e4m3_bits(w / full)
+    return {"fmt": FP8, "tiled": tiled, "n": n, "k": k, "codes": codes, "scales": scales.astype(np.float32)}
 
 
 def q8_0_weights(g: np.random.Generator, n: int, k: int) -> dict:

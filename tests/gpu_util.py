@@ -52,12 +52,18 @@ def empty(shape, dtype):
     return torch.empty(shape, dtype=dtype, device="cuda")
 
 
+def fp8_fmt(w: dict) -> int:
+    return qg.QG_FP8_B128 if w["tiled"] else qg.QG_FP8_TENSOR
+
+
 def pack_dev(w: dict):
     """Pack a logical weight dict with the library's packer and upload it."""
     if w["fmt"] == "nvfp4":
         buf = qg.qg_pack_nvfp4(w["codes"], w["scales"])
     elif w["fmt"] == "q4_0":
         buf = qg.qg_pack_q4_0(w["codes"], w["scales"])
+    elif w["fmt"] == "fp8":
+        buf = qg.qg_pack_fp8(fp8_fmt(w), w["codes"], w["scales"])
     else:
         buf = qg.qg_pack_q8_0(w["codes"], w["scales"])
     return dev_u8(buf)

@@ -245,3 +245,42 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(qg, "_lib", None)
     with pytest.raises(qg.QGLibraryMissing):
         qg.qg_abi_version()
+
+
+# ---------------------------------------------------------------- FP8
+
+@pytest.mark.parametrize("fmt,n,k,scales", [(qg.QG_FP8_TENSOR, 3, 64, 4), (qg.QG_FP8_B128, 3, 64, 4),
+                                            (qg.QG_FP8_B128, 300, 384, 3 * 3 * 4),
+                                            (qg.QG_FP8_B128, 24576, 4096, 192 * 32 * 4)])
+def test_fp8_packed_sizes(L, fmt, n, k, scales):
+    off = qg.qg_scale_plane_offset(fmt, n, k)
+    assert off % 256 == 0 and off >= n * k and off - n * k < 256
+    total = qg.qg_packed_bytes(fmt, n, k)
+    assert total % 256 == 0 and total - off >= scales and total - off - scales < 256
+
+
+@pytest.mark.parametrize("n,k,tiled", [(1, 32, True), (3, 64, False), (130, 160, True), (300, 384, True)])
+def test_fp8_pack_roundtrip_and_layout(L, n, k, tiled):
+    g = synth.rng(n * 7 + k)
+    w = synth.fp8_weights(g, n, k, tiled=tiled)
+    fmt = qg.QG_FP8_B128 if tiled else qg.QG_FP8_TENSOR
+    buf = qg.qg_pack_fp8(fmt, w["codes"], w["scales"])
+    c, s = qg.qg_unpack_fp8(fmt, buf, n, k)
+    assert np.array_equal(c, w["codes"]) and np.array_equal(s, w["scales"])
+    # codes plane: row-major bytes; scale plane: the fp32 grid, row-major
+    assert np.array_equal(buf[:n * k].reshape(n, k), w["codes"])
+    off = qg.qg_scale_plane_offset(fmt, n, k)
+    assert np.array_equal(buf[off:off + 4 * w["scales"].size].view(np.float32).reshape(w["scales"].shape),
+                          w["scales"])
+
+
+def test_fp8_argument_checks(L):
+    codes = np.zeros((4, 64), np.uint8)
+    with pytest.raises(qg.QGError):
+        qg.qg_pack_fp8(qg.QG_NVFP4, codes, np.ones((1, 1), np.float32))  # not an FP8 format
+    with pytest.raises(qg.QGError):
+        qg.qg_pack_fp8(qg.QG_FP8_B128, codes, np.ones((2, 2), np.float32))  # wrong grid size
+    assert L.qgemv_fp8(qg.QG_NVFP4, 256, 4, 64, 256, 1, 256, None) == qg.QG_EINVAL  # bad format
+    assert L.qgemv_fp8(qg.QG_FP8_B128, 256, 4, 48, 256, 1, 256, None) == qg.QG_EINVAL  # k % 32
+    assert L.qgemv_fp8(qg.QG_FP8_B128, 256, 4, 64, 256, 17, 256, None) == qg.QG_EUNSUPPORTED  # m > 16
+    assert L.qgemv_fp8(qg.QG_FP8_TENSOR, 0, 4, 64, 256, 1, 256, None) == qg.QG_EINVAL  # null w

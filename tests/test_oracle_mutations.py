@@ -7,6 +7,7 @@ import oracle
 from oracle import formats as F
 from oracle import ops as O
 from tests import test_oracle_a8 as A8
+from tests import test_oracle_fp8 as TF8
 from tests import test_oracle_formats as TF
 from tests import test_oracle_gemv as TG
 from tests import test_oracle_moe as TM
@@ -90,6 +91,28 @@ def _gemv_transposed_x(w, x, rows=None):
     return X[:, ::-1] @ W.T
 
 
+def _fp8_tiles(transpose=False, tile=128, columns=True):
+    def dq(w, rows=None):
+        r = O._rows(w, rows)
+        v = F.decode_e4m3(w["codes"][r])
+        s = np.asarray(w["scales"], np.float64)
+        if not w["tiled"]:
+            return v * s.reshape(-1)[0]
+        ri = (r // tile)[:, None]
+        ci = (np.arange(v.shape[1]) // tile)[None, :] if columns else np.zeros((1, v.shape[1]), np.int64)
+        if transpose:
+            ri, ci = ci, ri
+        ri = np.minimum(ri, s.shape[0] - 1)
+        ci = np.minimum(ci, s.shape[1] - 1)
+        return v * s[ri, ci]
+    return dq
+
+
+def _fp8_pins():
+    return [lambda: TF8.test_dequant_matches_torch_decode_and_tile_lookup(300, 384, True),
+            TF8.test_gemv_exact_brute_force_across_tiles]
+
+
 MUTATIONS = [
     ("e2m1 exponent bias dropped", [(F, "decode_e2m1", _e2m1_wrong_bias), (O, "decode_e2m1", _e2m1_wrong_bias),
                                     (oracle, "decode_e2m1", _e2m1_wrong_bias)],
@@ -113,6 +136,9 @@ MUTATIONS = [
      [TM.test_ex5_router_tie_to_lower_index]),
     ("gate and up swapped", [(O, "swiglu", _swiglu_swapped), (oracle, "swiglu", _swiglu_swapped)],
      [TM.test_swiglu_gate_is_first_half]),
+    ("FP8 scale grid transposed", [(O, "dequant_fp8", _fp8_tiles(transpose=True))], _fp8_pins()),
+    ("FP8 tiles of 64", [(O, "dequant_fp8", _fp8_tiles(tile=64))], _fp8_pins()),
+    ("FP8 column tiles ignored", [(O, "dequant_fp8", _fp8_tiles(columns=False))], _fp8_pins()),
 ]
 
 
