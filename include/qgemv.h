@@ -292,6 +292,28 @@ int moe_gemv_grouped(const qg_moe_desc* d, const uint16_t* x, const int32_t* ids
 int moe_forward(const qg_moe_desc* d, const uint16_t* x, const float* logits, int64_t t, float* y,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------ MoE prefill
+ * The same MoE layer as moe_forward (same routing, grouping, SwiGLU and
+ * combine definitions and the same result up to rounding) for many tokens:
+ * the grouped NVFP4 MoE GEMM of the LumenLLM README's prefill (feature list
+ * "Kernels").  The expert matmuls run on the matrix cores over tiles of up to
+ * 32 pairs of one expert: bf16 activations times exactly decoded weights,
+ * fp32 accumulation (two partial sums per output added in a fixed order),
+ * then the tensor scale; a = bf16_rne(silu(g) * u).  A pair's products do not
+ * depend on which tile it lands in, so results are bitwise reproducible and a
+ * token's output does not depend on the other tokens of the call.
+ * 1 <= t <= 65536, top_k <= 8, n_experts <= 1024; hidden and inter each one
+ * of 512, 1024, 2048 (else QG_EUNSUPPORTED).  The workspace starts with the
+ * moe_gemv_grouped / moe_forward layout above for these P = t * (top_k +
+ * has_shared) pairs (the CSR, a, h with QG_MOE_KEEP_H, o, ids, weights),
+ * followed by int32 tile_start[P + 2], int32 counts[n_experts] and int32
+ * pair_pos[t][top_k + 1] (each region 256-byte aligned).  Six launches on
+ * the stream: routing, pair counts, pair placement, gate/up + SwiGLU, down,
+ * combine. */
+size_t moe_prefill_workspace_bytes(const qg_moe_desc* d, int64_t t);
+int moe_prefill(const qg_moe_desc* d, const uint16_t* x, const float* logits, int64_t t, float* y,
+                void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------ small-M prefill GEMM
  * Y[t][r] = bf16_rne(s_t * sum_c D[r][c] * X[t][c]) with D = e2m1 * e4m3
  * (exact in bf16), bf16 matrix-core products and fp32 accumulation; the

@@ -26,7 +26,7 @@ __all__ = [
     "qg_unpack_fp8", "qgemv_fp8", "fp8_scale_shape", "qg_dequant",
     "qgemv_q8_0", "qgemv_nvfp4", "qgemv_nvfp4_swiglu", "qg_quantize_q8_0_act",
     "qgemv_q4_0_a8", "moe_route_topk", "QgMoeDesc", "moe_workspace_bytes",
-    "moe_gemv_grouped", "moe_forward", "qgemm_prefill", "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
+    "moe_gemv_grouped", "moe_forward", "moe_prefill_workspace_bytes", "moe_prefill", "qgemm_prefill", "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -100,6 +100,8 @@ _SIGNATURES = {
     "moe_workspace_bytes": (_SZ, [ctypes.POINTER(QgMoeDesc), _I64]),
     "moe_gemv_grouped": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "moe_forward": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _I64, _P, _P, _SZ, _P]),
+    "moe_prefill_workspace_bytes": (_SZ, [ctypes.POINTER(QgMoeDesc), _I64]),
+    "moe_prefill": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _I64, _P, _P, _SZ, _P]),
     "qgemm_prefill": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P]),
     "qgemm_prefill_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "qgemm_prefill_ws": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]),
@@ -342,6 +344,17 @@ def moe_forward(desc: QgMoeDesc, x, logits, t, y, ws, ws_bytes=None, stream=None
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check("moe_forward",
            lib().moe_forward(ctypes.byref(desc), _dptr(x), _dptr(logits), t, _dptr(y), _dptr(ws), nbytes,
+                             _stream(stream)))
+
+
+def moe_prefill_workspace_bytes(desc: QgMoeDesc, t: int) -> int:
+    return lib().moe_prefill_workspace_bytes(ctypes.byref(desc), t)
+
+
+def moe_prefill(desc: QgMoeDesc, x, logits, t, y, ws, ws_bytes=None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_prefill",
+           lib().moe_prefill(ctypes.byref(desc), _dptr(x), _dptr(logits), t, _dptr(y), _dptr(ws), nbytes,
                              _stream(stream)))
 
 

@@ -1,0 +1,370 @@
+// MoE over many tokens (prefill) on gfx950 matrix cores: route, group the
+// (token, expert) pairs expert-major, grouped gate/up GEMM with the SwiGLU
+// epilogue, grouped down GEMM, weighted combine.
+//
+// The LumenLLM README prefills its MoE models with a grouped NVFP4 MoE GEMM
+// on tensor cores (feature list "Kernels"); the bw24 README groups routed
+// pairs expert-major so each active expert's weights are read once for all
+// its tokens (MoE feature entry).  Same layer and same results definition as
+// the decode path (k_moe.hip), for any token count:
+//   1. routing: k_route_topk, one wave per token;
+//   2. grouping: k_mpf_count counts each expert's pairs, k_mpf_place writes
+//      the expert-major CSR (active experts ascending, then the shared
+//      expert; inside an expert, pairs in (token, slot) order -- a stable
+//      placement, so the CSR is exactly the decode path's) and the tile table
+//      of the GEMMs (kPfPairs pairs per tile);
+//   3. k_mpf_gemm<SWIGLU>: one workgroup per (tile, block of 192 weight
+//      rows): the tile's activation rows are gathered into LDS, the expert's
+//      NVFP4 rows decoded straight into MFMA fragments (eight waves, two per
+//      SIMD, on alternate 128-k slabs, added through LDS in a fixed order);
+//      gate/up rows are interleaved, so SwiGLU pairs adjacent columns;
+//   4. k_mpf_combine: y = sum over slots of w * o, then + o_shared, in that
+//      order (the decode path's order).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "qg_device.hpp"
+#include "qg_internal.hpp"
+#include "qg_layout.hpp"
+#include "qg_mfma.hpp"
+
+namespace qg {
+
+namespace {
+
+constexpr int kPfPairs = 32;    // pairs per GEMM tile (two 16-row MFMA blocks)
+constexpr int kPfBlock = 512;   // GEMM workgroup: eight waves
+constexpr int kPfNB = 3;        // 16-row weight blocks per wave
+constexpr int kPfBN = 16 * kPfNB * 4;  // weight rows per GEMM workgroup: 192
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// counts[e] = number of routed pairs of expert e.  One wave per expert.
+__global__ __launch_bounds__(64) void k_mpf_count(const int32_t* __restrict__ ids, int pr,
+                                                  int32_t* __restrict__ counts) {
+    const int e = int(blockIdx.x), lane = int(threadIdx.x);
+    int c = 0;
+    for (int i = lane; i < pr; i += 64) c += int(ids[i] == e);
+    c = wave_sum_i(c);
+    if (lane == 0) counts[e] = c;
+}
+
+// Workgroup e < E places expert e's pairs; workgroup E places the shared
+// expert's (if any) and writes the end entries.
+__global__ __launch_bounds__(64) void k_mpf_place(const int32_t* __restrict__ ids, int t, int k, int E,
+                                                  int has_shared, const int32_t* __restrict__ counts,
+                                                  MoeWorkspace ws, int32_t* __restrict__ tile_off,
+                                                  int32_t* __restrict__ pair_pos) {
+    const int e = int(blockIdx.x), lane = int(threadIdx.x);
+    const int pr = t * k;
+    int off = 0, grp = 0, tiles = 0;  // over the experts before e
+    for (int j = lane; j < e; j += 64) {
+        const int c = counts[j];
+        off += c;
+        grp += int(c > 0);
+        tiles += (c + kPfPairs - 1) / kPfPairs;
+    }
+    off = wave_sum_i(off);
+    grp = wave_sum_i(grp);
+    tiles = wave_sum_i(tiles);
+    if (e < E) {
+        if (counts[e] == 0) return;
+        if (lane == 0) {
+            ws.experts[grp] = e;
+            ws.offsets[grp] = off;
+            tile_off[grp] = tiles;
+        }
+        int base = off;
+        for (int i0 = 0; i0 < pr; i0 += 64) {
+            const int i = i0 + lane;
+            const bool hit = i < pr && ids[i] == e;
+            const uint64_t mask = __ballot(hit);
+            if (hit) {
+                const int pos = base + __popcll(mask & ((uint64_t(1) << lane) - 1));
+                const int tok = i / k, s = i % k;
+                ws.pair_tok[pos] = tok;
+                ws.pair_slot[pos] = s;
+                pair_pos[tok * (k + 1) + s] = pos;
+            }
+            base += __popcll(mask);
+        }
+    } else {
+        int g = grp;
+        if (has_shared) {
+            if (lane == 0) {
+                ws.experts[g] = E;
+                ws.offsets[g] = pr;
+                tile_off[g] = tiles;
+            }
+            for (int tok = lane; tok < t; tok += 64) {
+                ws.pair_tok[pr + tok] = tok;
+                ws.pair_slot[pr + tok] = k;
+                pair_pos[tok * (k + 1) + k] = pr + tok;
+            }
+            ++g;
+            tiles += (t + kPfPairs - 1) / kPfPairs;
+        }
+        if (lane == 0) {
+            ws.offsets[g] = pr + (has_shared ? t : 0);
+            tile_off[g] = tiles;
+            *ws.n_groups = g;
+        }
+    }
+}
+
+struct GemmArgs {
+    const uint8_t* w;        // expert e's matrix at w + e * stride
+    int64_t stride, soff;    // bytes per expert; scale plane offset inside a matrix
+    const float* scale;      // per-expert tensor scales
+    int n;                   // weight rows (2I packed gate/up, or H)
+    const uint16_t* src;     // activation rows: x (gathered by token) or a (by pair)
+    uint16_t* a_out;         // SwiGLU output [P][n/2] bf16
+    float* h_out;            // nullable [P][n] (g then u)
+    float* o_out;            // plain output [P][n] fp32
+};
+
+// One tile of up to kPfPairs pairs of one expert x kPfBN weight rows, over
+// K = 256 * KS (KS >= 2: the halves' sums must fit in the tile's LDS).  SWIGLU: activations gathered by token, output a (and h);
+// else activations are the pairs' own rows of a, output o.
+template <int KS, bool SWIGLU>
+__global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace ws,
+                                                       const int32_t* __restrict__ tile_off) {
+    constexpr int K = 2 * KW * KS;          // reduction length
+    constexpr int MB = kPfPairs / 16, NB = kPfNB;
+    constexpr int CPR = K / 8;              // 16-byte chunks per LDS row
+    constexpr int NCP = kPfPairs * CPR / kPfBlock;  // activation chunks per thread
+    constexpr int WD = KS < 4 ? KS : 4;     // weight slabs in flight per wave
+    static_assert(CPR >= 16 && (CPR & (CPR - 1)) == 0, "rows of a power-of-two count of 16 chunks");
+    static_assert(sizeof(float) * 4 * MB * NB * 4 * kWave <= kPfPairs * K * 2, "halves combine in the tile");
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kPfPairs * K];
+
+    const int tid = int(threadIdx.x);
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rs = wave % 4, half = wave / 4;
+    const int lr = lane & 15, lg = lane >> 4;
+
+    // tile -> expert group (largest g with tile_off[g] <= ty)
+    const int ty = int(blockIdx.y);
+    const int ng = *ws.n_groups;
+    if (ty >= tile_off[ng]) return;
+    int lo = 0, hi = ng - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (tile_off[mid] <= ty) lo = mid;
+        else hi = mid - 1;
+    }
+    const int g = lo;
+    const int e = ws.experts[g];
+    const int p0 = ws.offsets[g] + (ty - tile_off[g]) * kPfPairs;
+    const int np = min(kPfPairs, ws.offsets[g + 1] - p0);  // >= 1
+    const int n0 = int(blockIdx.x) * kPfBN + rs * 16 * NB;
+    const uint8_t* w = A.w + int64_t(e) * A.stride;
+    const float s_t = A.scale[e];
+
+    // 1. activation rows into registers (rows past np repeat the last pair)
+    u32x4 xr[NCP];
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+        const int p = (wave + 8 * i) * kWave + lane;
+        const int row = p / CPR, c = (p % CPR) ^ (row & 15);
+        const int pos = p0 + min(row, np - 1);
+        const int srow = SWIGLU ? ws.pair_tok[pos] : pos;
+        xr[i] = ld16(A.src + int64_t(srow) * K + 8 * c);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. weight slabs: slab j of this wave covers k = 128 (2 j + half) + [0, 128)
+    const uint8_t* wc[NB];
+    const uint8_t* wsc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t row = min(n0 + 16 * nb + lr, A.n - 1);
+        wc[nb] = w + row * (K / 2);
+        wsc[nb] = w + A.soff + row * (K / 16);
+    }
+    auto w_load = [&](WStage<NB>& b, int j) {
+        const int kb = KW * (2 * j + half) + 32 * lg;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const u32x4 v = ld_stream16(wc[nb] + kb / 2);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
+            b.s[nb] = ld<uint16_t>(wsc[nb] + kb / 16);
+        }
+    };
+    WStage<NB> wr[WD];
+#pragma unroll
+    for (int j = 0; j < WD; ++j) w_load(wr[j], j);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. publish the activation tile (the loads complete in order, ahead of
+    // the weight loads; the LDS-only barrier leaves those in flight)
+#pragma unroll
+    for (int i = 0; i < NCP; ++i)
+        *reinterpret_cast<u32x4*>(&xs[8 * ((wave + 8 * i) * kWave + lane)]) = xr[i];
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    floatx4 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        const WStage<NB> cur = wr[j % WD];
+        if (j + WD < KS) w_load(wr[j % WD], j + WD);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            u32x4 bfr[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float sc = (q < 2) ? e4m3_to_f32<0>(cur.s[nb]) : e4m3_to_f32<1>(cur.s[nb]);
+                bfr[nb] = decode8_scaled(cur.c[nb][q], sc);
+            }
+            const int c = 16 * (2 * j + half) + 4 * lg + q;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int row = 16 * mb + lr;
+                const u32x4 a = *reinterpret_cast<const u32x4*>(&xs[8 * (row * CPR + (c ^ (row & 15)))]);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32_bf16(a, bfr[nb], acc[mb][nb]);
+            }
+        }
+    }
+
+    // 4. second half + first half, in that order, through the tile's LDS
+    float* red = reinterpret_cast<float*>(xs) + rs * (MB * NB * 4 * kWave);
+    __syncthreads();
+    if (half == 1) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) red[((mb * NB + nb) * 4 + v) * kWave + lane] = acc[mb][nb][v];
+    }
+    __syncthreads();
+    if (half != 0) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float sum = (acc[mb][nb][v] + red[((mb * NB + nb) * 4 + v) * kWave + lane]) * s_t;
+                const int row = 16 * mb + 4 * lg + v;  // pair of the tile
+                const int col = n0 + 16 * nb + lr;     // weight row
+                if constexpr (SWIGLU) {
+                    // packed rows 2i (gate) and 2i+1 (up) sit in neighbouring lanes
+                    const float other = __shfl_xor(sum, 1);
+                    if ((lr & 1) == 0 && row < np && col < A.n) {
+                        const int64_t pos = p0 + row;
+                        const int I = A.n / 2, i = col / 2;
+                        const float gv = sum, uv = other;
+                        A.a_out[pos * I + i] = uint16_t(f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv));
+                        if (A.h_out) {
+                            A.h_out[pos * 2 * I + i] = gv;
+                            A.h_out[pos * 2 * I + I + i] = uv;
+                        }
+                    }
+                } else {
+                    if (row < np && col < A.n) A.o_out[int64_t(p0 + row) * A.n + col] = sum;
+                }
+            }
+}
+
+// y[t][h] = sum_s w[t][s] * o[pair (t, s)][h] (slots ascending), + o[pair
+// (t, shared)][h].
+__global__ __launch_bounds__(256) void k_mpf_combine(const float* __restrict__ o, const float* __restrict__ wts,
+                                                     const int32_t* __restrict__ pair_pos, int k, int has_shared,
+                                                     int H, float* __restrict__ y) {
+    const int tok = int(blockIdx.x);
+    const int h = int(blockIdx.y) * 256 + int(threadIdx.x);
+    if (h >= H) return;
+    float sum = 0.f;
+    for (int s = 0; s < k; ++s)
+        sum = fmaf(wts[int64_t(tok) * k + s], o[int64_t(pair_pos[tok * (k + 1) + s]) * H + h], sum);
+    if (has_shared) sum += o[int64_t(pair_pos[tok * (k + 1) + k]) * H + h];
+    y[int64_t(tok) * H + h] = sum;
+}
+
+template <int KS, bool SW>
+hipError_t gemm(const GemmArgs& A, const MoeWorkspace& ws, const int32_t* tile_off, int max_tiles,
+                hipStream_t s) {
+    const dim3 grid(unsigned((A.n + kPfBN - 1) / kPfBN), unsigned(max_tiles));
+    hipLaunchKernelGGL((k_mpf_gemm<KS, SW>), grid, dim3(kPfBlock), 0, s, A, ws, tile_off);
+    return hipGetLastError();
+}
+
+template <bool SW>
+hipError_t gemm_k(int64_t K, const GemmArgs& A, const MoeWorkspace& ws, const int32_t* tile_off, int max_tiles,
+                  hipStream_t s) {
+    switch (K) {
+        case 512: return gemm<2, SW>(A, ws, tile_off, max_tiles, s);
+        case 1024: return gemm<4, SW>(A, ws, tile_off, max_tiles, s);
+        default: return gemm<8, SW>(A, ws, tile_off, max_tiles, s);
+    }
+}
+
+}  // namespace
+
+bool moe_prefill_shape_ok(int64_t hidden, int64_t inter) {
+    auto ok = [](int64_t v) { return v == 512 || v == 1024 || v == 2048; };
+    return ok(hidden) && ok(inter);
+}
+
+size_t moe_prefill_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, MoePrefillExtra* ex, void* base) {
+    // the decode path's fields first (same layout), then the prefill's own
+    size_t off = moe_workspace_layout(d, t, ws, base);
+    const int64_t P = t * (d->top_k + (d->has_shared ? 1 : 0));
+    auto take = [&](int64_t bytes) {
+        const size_t at = off;
+        off = size_t(align_up(int64_t(off) + bytes, kPlaneAlign));
+        return at;
+    };
+    const size_t o_tiles = take(4 * (P + 2));
+    const size_t o_cnt = take(4 * int64_t(d->n_experts));
+    const size_t o_pos = take(4 * t * (d->top_k + 1));
+    if (ex && base) {
+        char* b = static_cast<char*>(base);
+        ex->tile_off = reinterpret_cast<int32_t*>(b + o_tiles);
+        ex->counts = reinterpret_cast<int32_t*>(b + o_cnt);
+        ex->pair_pos = reinterpret_cast<int32_t*>(b + o_pos);
+    }
+    return off;
+}
+
+hipError_t launch_moe_prefill(const qg_moe_desc* d, const uint16_t* x, const float* logits, int t, float* y,
+                              const MoeWorkspace& ws, const MoePrefillExtra& ex, hipStream_t s) {
+    const int E = d->n_experts, k = d->top_k, hs = d->has_shared ? 1 : 0;
+    const int H = int(d->hidden), I = int(d->inter);
+    const int pr = t * k;
+    hipError_t err = launch_route_topk(logits, t, E, k, ws.ids, ws.wts, s);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_mpf_count, dim3(unsigned(E)), dim3(64), 0, s, ws.ids, pr, ex.counts);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_mpf_place, dim3(unsigned(E + 1)), dim3(64), 0, s, ws.ids, t, k, E, hs, ex.counts, ws,
+                       ex.tile_off, ex.pair_pos);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // tiles: at most one partial tile per active expert (and the shared one)
+    const int max_tiles = (pr + kPfPairs - 1) / kPfPairs + std::min(E, pr) + (hs ? (t + kPfPairs - 1) / kPfPairs : 0);
+    GemmArgs gu{static_cast<const uint8_t*>(d->gate_up), d->gate_up_stride, scale_plane_offset(QG_NVFP4, 2 * int64_t(I), H), d->gate_up_scale,
+                2 * I, x, ws.a, ws.h, nullptr};
+    if ((err = gemm_k<true>(H, gu, ws, ex.tile_off, max_tiles, s)) != hipSuccess) return err;
+    GemmArgs dn{static_cast<const uint8_t*>(d->down), d->down_stride, scale_plane_offset(QG_NVFP4, int64_t(H), I), d->down_scale,
+                H, ws.a, nullptr, nullptr, ws.o};
+    if ((err = gemm_k<false>(I, dn, ws, ex.tile_off, max_tiles, s)) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_mpf_combine, dim3(unsigned(t), unsigned((H + 255) / 256)), dim3(256), 0, s, ws.o, ws.wts,
+                       ex.pair_pos, k, hs, H, y);
+    return hipGetLastError();
+}
+
+}  // namespace qg

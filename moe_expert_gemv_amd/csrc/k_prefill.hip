@@ -35,6 +35,7 @@
 #include <algorithm>
 
 #include "qg_device.hpp"
+#include "qg_mfma.hpp"
 #include "qg_internal.hpp"
 #include "qg_layout.hpp"
 
@@ -43,28 +44,6 @@ namespace qg {
 namespace {
 
 constexpr int kBlock = 256;
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ floatx4 mfma_16x16x32_bf16(const u32x4& a, const u32x4& b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// Eight E2M1 codes (one dword, low nibble first) times the fp32 block scale s,
-// as eight bf16 (exact: at most 6 significant bits).
-template <int B>
-__device__ __forceinline__ uint32_t decode2_scaled(uint32_t codes, float s) {
-    f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, B);  // byte B: two codes
-    f = f * s;
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
-}
-
-__device__ __forceinline__ u32x4 decode8_scaled(uint32_t codes, float s) {
-    return u32x4{decode2_scaled<0>(codes, s), decode2_scaled<1>(codes, s), decode2_scaled<2>(codes, s),
-                 decode2_scaled<3>(codes, s)};
-}
-
 // 4 x 4 transpose of dwords across the four 16-lane groups of a wave: on
 // return, d[q] of lane group g holds what d[g] of lane group q held (same
 // position inside the group).  v_permlane32_swap exchanges its first
@@ -90,17 +69,6 @@ __device__ __forceinline__ void transpose4_lane_groups(uint32_t (&d)[4]) {
 
 // MB: 16-token blocks per wave; NB: 16-row blocks of W per wave; WN x WK = 4
 // waves along W rows x along k; WD: stages of W loads in flight.
-constexpr int KW = 128;  // k per wave per stage: one slab
-
-// Workgroup barrier that publishes LDS only: waits for this wave's LDS
-// accesses (not its global loads, so weight prefetches stay in flight), then
-// s_barrier.  __syncthreads() would also wait for every outstanding global
-// load.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 template <int MB, int NB, int WN, int WK, int WD>
 struct PrefillShape {
@@ -113,13 +81,6 @@ struct PrefillShape {
     static_assert(WN * WK == 4 && (WK == 1 || WK == 4), "four waves, k split 1 or 4 ways");
     static_assert(CPR >= 16 && (CPR & (CPR - 1)) == 0, "X rows of a power-of-two count of 16 chunks");
     static_assert((BM * CPR) % kBlock == 0, "X tile split evenly over the threads");
-};
-
-// One stage of one wave's W rows: codes and scales of its NB row blocks.
-template <int NB>
-struct WStage {
-    uint32_t c[NB][4];
-    uint32_t s[NB];  // the two scale bytes in the low half
 };
 
 template <int MB, int NB, int WN, int WK, int WD>

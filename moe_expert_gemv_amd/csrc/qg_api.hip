@@ -47,6 +47,9 @@ inline int finish(hipError_t e) {
     return QG_EHIP;
 }
 
+// Largest token count of moe_prefill (grid and index ranges stay well inside int).
+constexpr int64_t kMoePrefillMaxT = 65536;
+
 // Checks shared by the GEMV entry points.
 inline int check_gemv(const void* w, int64_t n, int64_t k, const void* x, int64_t m, const void* y) {
     if (!w || !x || !y) return QG_EINVAL;
@@ -177,6 +180,27 @@ int moe_forward(const qg_moe_desc* d, const uint16_t* x, const float* logits, in
     const size_t need = moe_workspace_layout(d, t, &lay, ws);
     if (ws_bytes < need) return QG_ENOSPC;
     return finish(launch_moe(d, x, nullptr, nullptr, logits, int(t), y, lay, as_stream(stream)));
+}
+
+size_t moe_prefill_workspace_bytes(const qg_moe_desc* d, int64_t t) {
+    if (check_moe_desc(d) || t < 1 || t > kMoePrefillMaxT) return 0;
+    if (!moe_prefill_shape_ok(d->hidden, d->inter) || d->n_experts > 1024) return 0;
+    return moe_prefill_layout(d, t, nullptr, nullptr, nullptr);
+}
+
+int moe_prefill(const qg_moe_desc* d, const uint16_t* x, const float* logits, int64_t t, float* y, void* ws,
+                size_t ws_bytes, void* stream) {
+    if (int st = check_moe_desc(d)) return st;
+    if (!x || !logits || !y || !ws) return QG_EINVAL;
+    if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(y, 16) || !aligned(ws, 256)) return QG_EINVAL;
+    if (t < 1) return QG_EINVAL;
+    if (t > kMoePrefillMaxT || d->n_experts > 1024 || !moe_prefill_shape_ok(d->hidden, d->inter))
+        return QG_EUNSUPPORTED;
+    MoeWorkspace lay;
+    MoePrefillExtra ex;
+    const size_t need = moe_prefill_layout(d, t, &lay, &ex, ws);
+    if (ws_bytes < need) return QG_ENOSPC;
+    return finish(launch_moe_prefill(d, x, logits, int(t), y, lay, ex, as_stream(stream)));
 }
 
 int qgemm_prefill(const void* w, float tensor_scale, int64_t n, int64_t k, const uint16_t* x,

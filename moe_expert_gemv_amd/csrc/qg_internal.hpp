@@ -53,6 +53,17 @@ size_t moe_workspace_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, v
 hipError_t launch_moe(const qg_moe_desc* d, const uint16_t* x, const int32_t* ids, const float* w,
                       const float* logits, int t, float* y, const MoeWorkspace& ws, hipStream_t s);
 
+// MoE over many tokens: the decode workspace fields, then these.
+struct MoePrefillExtra {
+    int32_t* tile_off;  // [P + 2] first GEMM tile of each group
+    int32_t* counts;    // [n_experts] routed pairs per expert
+    int32_t* pair_pos;  // [t * (top_k + 1)] CSR position of pair (token, slot)
+};
+bool moe_prefill_shape_ok(int64_t hidden, int64_t inter);
+size_t moe_prefill_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, MoePrefillExtra* ex, void* base);
+hipError_t launch_moe_prefill(const qg_moe_desc* d, const uint16_t* x, const float* logits, int t, float* y,
+                              const MoeWorkspace& ws, const MoePrefillExtra& ex, hipStream_t s);
+
 hipError_t launch_prefill(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x,
                           int64_t m, uint16_t* y, hipStream_t s);
 // Workspace bytes of launch_prefill_ws (0: the single-pass kernel, no workspace).
