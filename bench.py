@@ -288,6 +288,8 @@ class MoE(Workload):
     sources = ("k_moe.hip", "qg_gemv_core.hpp")
     kernel_re = (r"k_moe_gate_up(?:_tile)?\b", r"k_moe_down(?:_tile)?\b")
 
+    routing_samples = 64  # routings drawn (one per step, cycled)
+
     def __init__(self, t=1):
         import torch
         import moe_expert_gemv_amd as qg
@@ -310,7 +312,7 @@ class MoE(Workload):
         self.scales = torch.full((E,), 0.01, dtype=torch.float32, device="cuda")
         self.L = L
         # a fresh routing per step (logits drawn per step) so steps touch different experts
-        self.S = 64
+        self.S = self.routing_samples
         g = synth.rng(synth.seed_for(4, 900))
         logits = synth.logits_f32(g, self.S * t, L.n_experts)
         self.logits = torch.from_numpy(logits).cuda().view(self.S, t, L.n_experts)
@@ -325,7 +327,7 @@ class MoE(Workload):
                              down_stride=ds, gate_up_scale=self.scales.data_ptr(),
                              down_scale=self.scales.data_ptr())
             self.descs.append(d)
-        self.ws_bytes = qg.moe_workspace_bytes(self.descs[0], t)
+        self.ws_bytes = self.workspace_bytes(self.descs[0], t)
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device="cuda")
         # algorithmic bytes: the active experts' packed weights + activations
         u = []
@@ -340,6 +342,9 @@ class MoE(Workload):
                      f"top-8, {t} token(s), routing drawn per step")
         self.dominant = "moe_forward: routing + grouped gate/up + SwiGLU, grouped down + combine (2 kernels)"
 
+    def workspace_bytes(self, desc, t):
+        return self.qg.moe_workspace_bytes(desc, t)
+
     def step(self, i):
         # routing + grouped expert GEMVs + combine: two launches
         self.qg.moe_forward(self.descs[i % self.R], self.x, self.logits[i % self.S], self.t, self.y, self.ws,
@@ -348,9 +353,35 @@ class MoE(Workload):
     dominant_launch = step
 
 
+class MoEPrefill(MoE):
+    """The same layer over a prompt of t tokens (grouped NVFP4 MoE GEMM on the
+    matrix cores): at t = 512 every expert is active, so a step streams all
+    257 experts' weights once."""
+
+    sources = ("k_moe_prefill.hip", "k_moe.hip", "qg_mfma.hpp")
+    kernel_re = (r"k_route_topk\b", r"k_mpf_count\b", r"k_mpf_place\b", r"k_mpf_gemm\w*<[^>]*\btrue>",
+                 r"k_mpf_gemm\w*<[^>]*\bfalse>", r"k_mpf_combine\b")
+    routing_samples = 8
+
+    def __init__(self, t=512):
+        super().__init__(t)
+        self.name = (f"moe prefill (35B-A3B-like): 256 routed + 1 shared experts, hidden {self.L.hidden}, "
+                     f"inter {self.L.inter}, top-8, {t} tokens, routing drawn per step")
+        self.dominant = "moe_prefill: routing, grouping, grouped gate/up + SwiGLU and down GEMMs, combine (6 kernels)"
+
+    def workspace_bytes(self, desc, t):
+        return self.qg.moe_prefill_workspace_bytes(desc, t)
+
+    def step(self, i):
+        self.qg.moe_prefill(self.descs[i % self.R], self.x, self.logits[i % self.S], self.t, self.y, self.ws,
+                            self.ws_bytes)
+
+    dominant_launch = step
+
+
 class Prefill(Workload):
     sources = ("k_prefill.hip",)
-    kernel_re = (r"k_prefill\b",)
+    kernel_re = (r"k_prefill8?\b",)
 
     def __init__(self, m=512):
         import torch
@@ -411,6 +442,7 @@ CONFIGS = {  # name -> (workload class, its size argument)
     "fp8": (Fp8Gemv, 1),
     "moe": (MoE, 1),
     "moe-t4": (MoE, 4),
+    "moe-prefill": (MoEPrefill, 512),
     "prefill64": (PrefillWs, 64),
     "prefill128": (PrefillWs, 128),
     "prefill512": (Prefill, 512),

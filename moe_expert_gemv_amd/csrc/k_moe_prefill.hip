@@ -38,70 +38,131 @@ constexpr int kPfBlock = 512;   // GEMM workgroup: eight waves
 constexpr int kPfNB = 3;        // 16-row weight blocks per wave
 constexpr int kPfBN = 16 * kPfNB * 4;  // weight rows per GEMM workgroup: 192
 
+constexpr int kGroupThreads = 256;  // count / place workgroups
+constexpr int kIdsPerPass = 4 * kGroupThreads;  // ids a workgroup reads per pass (four per thread)
+
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     return v;
 }
 
-// counts[e] = number of routed pairs of expert e.  One wave per expert.
-__global__ __launch_bounds__(64) void k_mpf_count(const int32_t* __restrict__ ids, int pr,
-                                                  int32_t* __restrict__ counts) {
-    const int e = int(blockIdx.x), lane = int(threadIdx.x);
-    int c = 0;
-    for (int i = lane; i < pr; i += 64) c += int(ids[i] == e);
-    c = wave_sum_i(c);
-    if (lane == 0) counts[e] = c;
+// Sum of v over the workgroup, returned to every thread.
+__device__ __forceinline__ int block_sum_i(int v, int* s_tmp) {
+    v = wave_sum_i(v);
+    const int wave = int(threadIdx.x) / kWave;
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) s_tmp[wave] = v;
+    __syncthreads();
+    int r = 0;
+#pragma unroll
+    for (int w = 0; w < kGroupThreads / kWave; ++w) r += s_tmp[w];
+    return r;
 }
 
-// Workgroup e < E places expert e's pairs; workgroup E places the shared
-// expert's (if any) and writes the end entries.
-__global__ __launch_bounds__(64) void k_mpf_place(const int32_t* __restrict__ ids, int t, int k, int E,
-                                                  int has_shared, const int32_t* __restrict__ counts,
-                                                  MoeWorkspace ws, int32_t* __restrict__ tile_off,
-                                                  int32_t* __restrict__ pair_pos) {
-    const int e = int(blockIdx.x), lane = int(threadIdx.x);
+// Exclusive prefix of v over the workgroup's threads (in thread order); the
+// total goes to *total.
+__device__ __forceinline__ int block_exclusive_i(int v, int* s_tmp, int* total) {
+    const int lane = int(threadIdx.x) & (kWave - 1), wave = int(threadIdx.x) / kWave;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int u = __shfl_up(inc, o);
+        if (lane >= o) inc += u;
+    }
+    __syncthreads();
+    if (lane == kWave - 1) s_tmp[wave] = inc;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kGroupThreads / kWave; ++w) {
+        const int c = s_tmp[w];
+        before += w < wave ? c : 0;
+        all += c;
+    }
+    *total = all;
+    return before + inc - v;
+}
+
+// Four ids starting at i (i % 4 == 0); entries at or past pr read as -1.
+__device__ __forceinline__ int4 ids4(const int32_t* __restrict__ ids, int i, int pr) {
+    if (i + 3 < pr) return *reinterpret_cast<const int4*>(ids + i);
+    int4 v{-1, -1, -1, -1};
+    if (i < pr) v.x = ids[i];
+    if (i + 1 < pr) v.y = ids[i + 1];
+    if (i + 2 < pr) v.z = ids[i + 2];
+    return v;
+}
+
+// counts[e] = number of routed pairs of expert e.  One workgroup per expert;
+// every thread reads four ids per 16-byte load, all loads of a pass at once.
+__global__ __launch_bounds__(kGroupThreads) void k_mpf_count(const int32_t* __restrict__ ids, int pr,
+                                                             int32_t* __restrict__ counts) {
+    __shared__ int s_tmp[kGroupThreads / kWave];
+    const int e = int(blockIdx.x);
+    int c = 0;
+#pragma unroll 4
+    for (int i = 4 * int(threadIdx.x); i < pr; i += kIdsPerPass) {
+        const int4 v = ids4(ids, i, pr);
+        c += int(v.x == e) + int(v.y == e) + int(v.z == e) + int(v.w == e);
+    }
+    c = block_sum_i(c, s_tmp);
+    if (threadIdx.x == 0) counts[e] = c;
+}
+
+// Workgroup e < E places expert e's pairs in pair-index order; workgroup E
+// places the shared expert's (if any) and writes the end entries.
+__global__ __launch_bounds__(kGroupThreads) void k_mpf_place(const int32_t* __restrict__ ids, int t, int k, int E,
+                                                             int has_shared, const int32_t* __restrict__ counts,
+                                                             MoeWorkspace ws, int32_t* __restrict__ tile_off,
+                                                             int32_t* __restrict__ pair_pos) {
+    __shared__ int s_tmp[kGroupThreads / kWave];
+    const int e = int(blockIdx.x), tid = int(threadIdx.x);
     const int pr = t * k;
     int off = 0, grp = 0, tiles = 0;  // over the experts before e
-    for (int j = lane; j < e; j += 64) {
+    for (int j = tid; j < e; j += kGroupThreads) {
         const int c = counts[j];
         off += c;
         grp += int(c > 0);
         tiles += (c + kPfPairs - 1) / kPfPairs;
     }
-    off = wave_sum_i(off);
-    grp = wave_sum_i(grp);
-    tiles = wave_sum_i(tiles);
+    off = block_sum_i(off, s_tmp);
+    grp = block_sum_i(grp, s_tmp);
+    tiles = block_sum_i(tiles, s_tmp);
     if (e < E) {
-        if (counts[e] == 0) return;
-        if (lane == 0) {
+        if (counts[e] == 0) return;  // uniform
+        if (tid == 0) {
             ws.experts[grp] = e;
             ws.offsets[grp] = off;
             tile_off[grp] = tiles;
         }
         int base = off;
-        for (int i0 = 0; i0 < pr; i0 += 64) {
-            const int i = i0 + lane;
-            const bool hit = i < pr && ids[i] == e;
-            const uint64_t mask = __ballot(hit);
-            if (hit) {
-                const int pos = base + __popcll(mask & ((uint64_t(1) << lane) - 1));
-                const int tok = i / k, s = i % k;
-                ws.pair_tok[pos] = tok;
-                ws.pair_slot[pos] = s;
-                pair_pos[tok * (k + 1) + s] = pos;
-            }
-            base += __popcll(mask);
+        for (int i0 = 0; i0 < pr; i0 += kIdsPerPass) {  // uniform trip count
+            const int i = i0 + 4 * tid;
+            const int4 v = ids4(ids, i, pr);
+            const int hit[4] = {int(v.x == e), int(v.y == e), int(v.z == e), int(v.w == e)};
+            int total;
+            int pos = base + block_exclusive_i(hit[0] + hit[1] + hit[2] + hit[3], s_tmp, &total);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (hit[q]) {
+                    const int tok = (i + q) / k, sl = (i + q) % k;
+                    ws.pair_tok[pos] = tok;
+                    ws.pair_slot[pos] = sl;
+                    pair_pos[tok * (k + 1) + sl] = pos;
+                    ++pos;
+                }
+            base += total;
         }
     } else {
         int g = grp;
         if (has_shared) {
-            if (lane == 0) {
+            if (tid == 0) {
                 ws.experts[g] = E;
                 ws.offsets[g] = pr;
                 tile_off[g] = tiles;
             }
-            for (int tok = lane; tok < t; tok += 64) {
+            for (int tok = tid; tok < t; tok += kGroupThreads) {
                 ws.pair_tok[pr + tok] = tok;
                 ws.pair_slot[pr + tok] = k;
                 pair_pos[tok * (k + 1) + k] = pr + tok;
@@ -109,7 +170,7 @@ __global__ __launch_bounds__(64) void k_mpf_place(const int32_t* __restrict__ id
             ++g;
             tiles += (t + kPfPairs - 1) / kPfPairs;
         }
-        if (lane == 0) {
+        if (tid == 0) {
             ws.offsets[g] = pr + (has_shared ? t : 0);
             tile_off[g] = tiles;
             *ws.n_groups = g;
@@ -140,8 +201,8 @@ __global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace 
     constexpr int NCP = kPfPairs * CPR / kPfBlock;  // activation chunks per thread
     constexpr int WD = KS < 4 ? KS : 4;     // weight slabs in flight per wave
     static_assert(CPR >= 16 && (CPR & (CPR - 1)) == 0, "rows of a power-of-two count of 16 chunks");
-    static_assert(sizeof(float) * 4 * MB * NB * 4 * kWave <= kPfPairs * K * 2, "halves combine in the tile");
     __shared__ __attribute__((aligned(16))) uint16_t xs[kPfPairs * K];
+    __shared__ float red_s[4 * MB * NB * 4 * kWave];  // the second half's sums (own region: one barrier)
 
     const int tid = int(threadIdx.x);
     const int lane = tid & 63;
@@ -198,9 +259,11 @@ __global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace 
             b.s[nb] = ld<uint16_t>(wsc[nb] + kb / 16);
         }
     };
+    // one slab right behind the activation loads, the rest once the tile is
+    // published (requested all up front, the weight stream delays the
+    // activation data, which returns in order behind it)
     WStage<NB> wr[WD];
-#pragma unroll
-    for (int j = 0; j < WD; ++j) w_load(wr[j], j);
+    w_load(wr[0], 0);
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. publish the activation tile (the loads complete in order, ahead of
@@ -209,6 +272,9 @@ __global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace 
     for (int i = 0; i < NCP; ++i)
         *reinterpret_cast<u32x4*>(&xs[8 * ((wave + 8 * i) * kWave + lane)]) = xr[i];
     lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 1; j < WD; ++j) w_load(wr[j], j);
     __builtin_amdgcn_sched_barrier(0);
 
     floatx4 acc[MB][NB];
@@ -240,9 +306,8 @@ __global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace 
         }
     }
 
-    // 4. second half + first half, in that order, through the tile's LDS
-    float* red = reinterpret_cast<float*>(xs) + rs * (MB * NB * 4 * kWave);
-    __syncthreads();
+    // 4. second half + first half, in that order, through LDS
+    float* red = red_s + rs * (MB * NB * 4 * kWave);
     if (half == 1) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -349,10 +414,10 @@ hipError_t launch_moe_prefill(const qg_moe_desc* d, const uint16_t* x, const flo
     const int pr = t * k;
     hipError_t err = launch_route_topk(logits, t, E, k, ws.ids, ws.wts, s);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_mpf_count, dim3(unsigned(E)), dim3(64), 0, s, ws.ids, pr, ex.counts);
+    hipLaunchKernelGGL(k_mpf_count, dim3(unsigned(E)), dim3(kGroupThreads), 0, s, ws.ids, pr, ex.counts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(k_mpf_place, dim3(unsigned(E + 1)), dim3(64), 0, s, ws.ids, t, k, E, hs, ex.counts, ws,
-                       ex.tile_off, ex.pair_pos);
+    hipLaunchKernelGGL(k_mpf_place, dim3(unsigned(E + 1)), dim3(kGroupThreads), 0, s, ws.ids, t, k, E, hs,
+                       ex.counts, ws, ex.tile_off, ex.pair_pos);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // tiles: at most one partial tile per active expert (and the shared one)
     const int max_tiles = (pr + kPfPairs - 1) / kPfPairs + std::min(E, pr) + (hs ? (t + kPfPairs - 1) / kPfPairs : 0);
