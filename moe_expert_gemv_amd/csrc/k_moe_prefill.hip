@@ -37,6 +37,11 @@ constexpr int kPfPairs = 32;    // pairs per GEMM tile (two 16-row MFMA blocks)
 constexpr int kPfBlock = 512;   // GEMM workgroup: eight waves
 constexpr int kPfNB = 3;        // 16-row weight blocks per wave
 constexpr int kPfBN = 16 * kPfNB * 4;  // weight rows per GEMM workgroup: 192
+// Workgroups are dealt to the XCDs round-robin by launch index, and each XCD
+// has an L2 of its own; the GEMM grid is remapped so that neighbouring work
+// items (the row blocks of one tile, which gather the same activation rows)
+// run one after another on the same XCD.  Results do not depend on it.
+constexpr int kXcds = 8;
 
 constexpr int kGroupThreads = 256;  // count / place workgroups
 constexpr int kIdsPerPass = 4 * kGroupThreads;  // ids a workgroup reads per pass (four per thread)
@@ -190,11 +195,11 @@ struct GemmArgs {
 };
 
 // One tile of up to kPfPairs pairs of one expert x kPfBN weight rows, over
-// K = 256 * KS (KS >= 2: the halves' sums must fit in the tile's LDS).  SWIGLU: activations gathered by token, output a (and h);
+// K = 256 * KS.  SWIGLU: activations gathered by token, output a (and h);
 // else activations are the pairs' own rows of a, output o.
 template <int KS, bool SWIGLU>
-__global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace ws,
-                                                       const int32_t* __restrict__ tile_off) {
+__global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace ws, const int32_t* __restrict__ tile_off,
+                                                       int n_blocks, int items) {
     constexpr int K = 2 * KW * KS;          // reduction length
     constexpr int MB = kPfPairs / 16, NB = kPfNB;
     constexpr int CPR = K / 8;              // 16-byte chunks per LDS row
@@ -210,10 +215,17 @@ __global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace 
     const int rs = wave % 4, half = wave / 4;
     const int lr = lane & 15, lg = lane >> 4;
 
-    // tile -> expert group (largest g with tile_off[g] <= ty)
-    const int ty = int(blockIdx.y);
+    // work item (XCD-contiguous over the real items, so every XCD gets an
+    // equal share) -> (tile ty, row block); tile -> expert group (largest g
+    // with tile_off[g] <= ty).  The grid is sized for the worst case; the
+    // surplus workgroups come last in launch order and exit.
     const int ng = *ws.n_groups;
-    if (ty >= tile_off[ng]) return;
+    const int real_items = min(tile_off[ng] * n_blocks, items);
+    const int per_xcd = (real_items + kXcds - 1) / kXcds;
+    if (int(blockIdx.x) / kXcds >= per_xcd) return;
+    const int item = int(blockIdx.x) % kXcds * per_xcd + int(blockIdx.x) / kXcds;
+    if (item >= real_items) return;
+    const int ty = item / n_blocks, nblk = item % n_blocks;
     int lo = 0, hi = ng - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) / 2;
@@ -224,7 +236,7 @@ __global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace 
     const int e = ws.experts[g];
     const int p0 = ws.offsets[g] + (ty - tile_off[g]) * kPfPairs;
     const int np = min(kPfPairs, ws.offsets[g + 1] - p0);  // >= 1
-    const int n0 = int(blockIdx.x) * kPfBN + rs * 16 * NB;
+    const int n0 = nblk * kPfBN + rs * 16 * NB;
     const uint8_t* w = A.w + int64_t(e) * A.stride;
     const float s_t = A.scale[e];
 
@@ -364,8 +376,11 @@ __global__ __launch_bounds__(256) void k_mpf_combine(const float* __restrict__ o
 template <int KS, bool SW>
 hipError_t gemm(const GemmArgs& A, const MoeWorkspace& ws, const int32_t* tile_off, int max_tiles,
                 hipStream_t s) {
-    const dim3 grid(unsigned((A.n + kPfBN - 1) / kPfBN), unsigned(max_tiles));
-    hipLaunchKernelGGL((k_mpf_gemm<KS, SW>), grid, dim3(kPfBlock), 0, s, A, ws, tile_off);
+    const int n_blocks = (A.n + kPfBN - 1) / kPfBN;
+    const int64_t items = int64_t(n_blocks) * max_tiles;
+    const int64_t per_xcd = (items + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL((k_mpf_gemm<KS, SW>), dim3(unsigned(per_xcd * kXcds)), dim3(kPfBlock), 0, s, A, ws, tile_off,
+                       n_blocks, int(items));
     return hipGetLastError();
 }
 
@@ -421,11 +436,11 @@ hipError_t launch_moe_prefill(const qg_moe_desc* d, const uint16_t* x, const flo
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // tiles: at most one partial tile per active expert (and the shared one)
     const int max_tiles = (pr + kPfPairs - 1) / kPfPairs + std::min(E, pr) + (hs ? (t + kPfPairs - 1) / kPfPairs : 0);
-    GemmArgs gu{static_cast<const uint8_t*>(d->gate_up), d->gate_up_stride, scale_plane_offset(QG_NVFP4, 2 * int64_t(I), H), d->gate_up_scale,
-                2 * I, x, ws.a, ws.h, nullptr};
+    GemmArgs gu{static_cast<const uint8_t*>(d->gate_up), d->gate_up_stride,
+                scale_plane_offset(QG_NVFP4, 2 * int64_t(I), H), d->gate_up_scale, 2 * I, x, ws.a, ws.h, nullptr};
     if ((err = gemm_k<true>(H, gu, ws, ex.tile_off, max_tiles, s)) != hipSuccess) return err;
-    GemmArgs dn{static_cast<const uint8_t*>(d->down), d->down_stride, scale_plane_offset(QG_NVFP4, int64_t(H), I), d->down_scale,
-                H, ws.a, nullptr, nullptr, ws.o};
+    GemmArgs dn{static_cast<const uint8_t*>(d->down), d->down_stride, scale_plane_offset(QG_NVFP4, int64_t(H), I),
+                d->down_scale, H, ws.a, nullptr, nullptr, ws.o};
     if ((err = gemm_k<false>(I, dn, ws, ex.tile_off, max_tiles, s)) != hipSuccess) return err;
     hipLaunchKernelGGL(k_mpf_combine, dim3(unsigned(t), unsigned((H + 255) / 256)), dim3(256), 0, s, ws.o, ws.wts,
                        ex.pair_pos, k, hs, H, y);

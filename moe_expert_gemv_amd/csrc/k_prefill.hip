@@ -757,11 +757,11 @@ hipError_t launch_prefill_ws(const uint8_t* w, float s_t, int64_t n, int64_t k, 
     constexpr int BN = 16 * NB * (kSkBlock / kWave / kSkHalves);
     const dim3 grid(unsigned((n + BN - 1) / BN), unsigned((m + kSkRows - 1) / kSkRows), unsigned(nz));
     if (k % kSkRange == 0)
-        hipLaunchKernelGGL((k_prefill_sk<NB, false, kSkEarly>), grid, dim3(kSkBlock), 0, s, w, soff, int(n), int(k), x, int(m),
-                           ws);
+        hipLaunchKernelGGL((k_prefill_sk<NB, false, kSkEarly>), grid, dim3(kSkBlock), 0, s, w, soff, int(n), int(k),
+                           x, int(m), ws);
     else
-        hipLaunchKernelGGL((k_prefill_sk<NB, true, kSkEarly>), grid, dim3(kSkBlock), 0, s, w, soff, int(n), int(k), x, int(m),
-                           ws);
+        hipLaunchKernelGGL((k_prefill_sk<NB, true, kSkEarly>), grid, dim3(kSkBlock), 0, s, w, soff, int(n), int(k),
+                           x, int(m), ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t count = m * n;
