@@ -32,6 +32,12 @@ here are the public ones:
   scale per tensor; value = e2m1(code) * e4m3(block scale) * tensor scale.
 * Q8_0: 32-element blocks of int8 codes with one fp16 scale; value = d * q.
 * Q4_0: 32-element blocks of 4-bit codes with one fp16 scale; value = d*(q-8).
+* FP8: E4M3 codes with fp32 scales per tensor or per 128 x 128 tile.
+* K-quants (Q4_K, Q5_K, Q6_K) and IQ4_XS: 256-element super-blocks with fp16
+  scales and 6-bit or int8 sub-block scales (the GGUF definitions, stated on
+  logical values in ``ops.py``).  The pages name these formats but define
+  none of them; the IQ4_XS codebook values are pinned only by their own
+  fixture (parity unpinned for the codebook).
 
 Every reading taken where the pages are silent is listed in the repository's
 design notes and in the docstring of the function that takes it.
@@ -62,6 +68,12 @@ from .ops import (  # noqa: F401
     quantize_q8_0_act,
     gemv_q4_0_a8,
     gemv_q4_0_a8_abs,
+    dequant_q4_k,
+    dequant_q6_k,
+    dequant_iq4_xs,
+    act_q8_0_values,
+    gemv_a8,
+    gemv_a8_abs,
     block_isums_q4_0_a8,
     route_topk,
     group_by_expert,

@@ -102,8 +102,73 @@ def dequant_fp8(w: dict, rows=None) -> np.ndarray:
     return v * s[(r // FP8_TILE)[:, None], cols[None, :]]
 
 
+# ---------------------------------------------------------------------------
+# K-quants and IQ4_XS (super-blocks of 256 elements)
+#
+# The pages name these formats without defining them: K-quant split-plane
+# matvecs (memra README, feature list "Decode kernels"), GGUF models in
+# Q4_K / Q5_K / Q6_K and a 35B MoE in IQ4_XS (bw24 README, requirements and
+# model list; memra README, model table).  The definitions below are the
+# public GGUF ones, stated on the logical values (codes and scales), not on
+# GGUF's byte packing:
+#
+# * Q4_K / Q5_K: per 256 elements an fp16 scale d and an fp16 scale dmin; per
+#   32-element sub-block j a 6-bit scale sc_j and a 6-bit min m_j; 4-bit
+#   (Q4_K) or 5-bit (Q5_K) codes q:  w = d * sc_j * q - dmin * m_j.
+# * Q6_K: per 256 elements an fp16 scale d; per 16-element sub-block j an
+#   int8 scale sc_j; 6-bit codes q:  w = d * sc_j * (q - 32).
+# * IQ4_XS: per 256 elements an fp16 scale d; per 32-element sub-block j a
+#   6-bit scale ls_j; 4-bit indices q into the fixed non-linear 16-entry
+#   codebook T (the IQ4_NL values):  w = d * (ls_j - 32) * T[q].
+# ---------------------------------------------------------------------------
+
+KQ_SUPER = 256
+IQ4_NL_VALUES = np.array([-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113],
+                         dtype=np.float64)
+
+
+def _per_column(v: np.ndarray, width: int) -> np.ndarray:
+    """Spread per-(sub-)block values over the columns they scale."""
+    return np.repeat(np.asarray(v, dtype=np.float64), width, axis=1)
+
+
+def dequant_q4_k(w: dict, rows=None) -> np.ndarray:
+    """Q4_K / Q5_K values d*sc_j*q - dmin*m_j (same rule; Q5_K codes go to 31).
+
+    Each product is exact in fp64 (at most 22 significant bits); the
+    difference is exact whenever d and dmin lie within 2^30 of each other,
+    which every realistic scale pair (and every generated one) does.
+    """
+    r = _rows(w, rows)
+    q = w["codes"][r].astype(np.float64)
+    d = _per_column(decode_f16(w["d"][r]), KQ_SUPER)
+    dmin = _per_column(decode_f16(w["dmin"][r]), KQ_SUPER)
+    sc = _per_column(w["sub"][r], 32)
+    mn = _per_column(w["mins"][r], 32)
+    return d * sc * q - dmin * mn
+
+
+def dequant_q6_k(w: dict, rows=None) -> np.ndarray:
+    """Q6_K values d*sc_j*(q - 32), sc_j int8 per 16 elements (exact: <= 24 bits)."""
+    r = _rows(w, rows)
+    q = w["codes"][r].astype(np.float64) - 32.0
+    d = _per_column(decode_f16(w["d"][r]), KQ_SUPER)
+    sc = _per_column(w["sub"][r].astype(np.int8), 16)
+    return d * sc * q
+
+
+def dequant_iq4_xs(w: dict, rows=None) -> np.ndarray:
+    """IQ4_XS values d*(ls_j - 32)*T[q] (exact: <= 24 significant bits)."""
+    r = _rows(w, rows)
+    t = IQ4_NL_VALUES[w["codes"][r]]
+    d = _per_column(decode_f16(w["d"][r]), KQ_SUPER)
+    ls = _per_column(w["sub"][r], 32) - 32.0
+    return d * ls * t
+
+
 def dequant(w: dict, rows=None) -> np.ndarray:
-    f = {"nvfp4": dequant_nvfp4, "q8_0": dequant_q8_0, "q4_0": dequant_q4_0, "fp8": dequant_fp8}[w["fmt"]]
+    f = {"nvfp4": dequant_nvfp4, "q8_0": dequant_q8_0, "q4_0": dequant_q4_0, "fp8": dequant_fp8,
+         "q4_k": dequant_q4_k, "q5_k": dequant_q4_k, "q6_k": dequant_q6_k, "iq4_xs": dequant_iq4_xs}[w["fmt"]]
     return f(w, rows)
 
 
@@ -216,6 +281,29 @@ def gemv_q4_0_a8_abs(w: dict, xq, xd, rows=None) -> np.ndarray:
     dw = np.abs(decode_f16(w["scales"][r]))
     dx = np.abs(decode_f16(np.asarray(xd)))
     return np.einsum("mnb,nb,mb->mn", s.astype(np.float64), dw, dx)
+
+
+def act_q8_0_values(xq, xd) -> np.ndarray:
+    """The dequantized Q8_0 activation x_hat = d_x * q_x, exact in fp64."""
+    qx = np.asarray(xq).astype(np.float64)
+    m, k = qx.shape
+    return qx * _per_column(decode_f16(np.asarray(xd)), Q_BLOCK)
+
+
+def gemv_a8(w: dict, xq, xd, rows=None) -> np.ndarray:
+    """y[m, n] = sum_k w[n, k] * x_hat[m, k] with x_hat the Q8_0 activation.
+
+    The K-quant and IQ4_XS matvecs take Q8_0 activations, as the W4A8 path
+    does (memra README, "Decode kernels": K-quant split-plane matvecs with
+    warp-level dp4a, an int8 dot that needs int8 activations).  Plain
+    definition: both operands dequantized exactly, one fp64 matmul.
+    """
+    return act_q8_0_values(xq, xd) @ dequant(w, rows).T
+
+
+def gemv_a8_abs(w: dict, xq, xd, rows=None) -> np.ndarray:
+    """sum_k |w[n, k] * x_hat[m, k]|, the scale of the rounding error."""
+    return np.abs(act_q8_0_values(xq, xd)) @ np.abs(dequant(w, rows)).T
 
 
 # ---------------------------------------------------------------------------

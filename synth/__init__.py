@@ -21,6 +21,7 @@ layer); the distributions are:
   scale 0.01.
 * Q4_0 weights: 4-bit codes uniform in 0..15; one fp16 scale per 32-element
   block drawn as |N(0,1)| * 0.01.
+* K-quant / IQ4_XS weights: see ``kquant_weights``.
 * Activations: N(0,1), as fp32 or rounded to bf16.
 * Router logits: fp32 N(0,1).
 
@@ -42,6 +43,12 @@ Q8_0 = "q8_0"
 Q4_0 = "q4_0"
 FP8 = "fp8"
 FP8_TILE = 128  # side of an FP8 block-128 scale tile
+Q4_K = "q4_k"
+Q5_K = "q5_k"
+Q6_K = "q6_k"
+IQ4_XS = "iq4_xs"
+KQ_SUPER = 256  # elements per super-block of the K-quant and IQ4_XS formats
+KQUANTS = (Q4_K, Q5_K, Q6_K, IQ4_XS)
 
 
 def seed_for(cfg: int, tensor_index: int = 0) -> int:
@@ -111,6 +118,34 @@ def fp8_weights(g: np.random.Generator, n: int, k: int, tiled: bool = True, std:
     full = np.repeat(np.repeat(scales, FP8_TILE, axis=0), FP8_TILE, axis=1)[:n, :k] if tiled else scales[0, 0]
     codes = to_e4m3_bits(w / full)
     return {"fmt": FP8, "tiled": tiled, "n": n, "k": k, "codes": codes, "scales": scales.astype(np.float32)}
+
+
+def kquant_weights(g: np.random.Generator, fmt: str, n: int, k: int) -> dict:
+    """K-quant / IQ4_XS weights in logical form, one super-block of 256
+    elements per fp16 scale d (and fp16 dmin for Q4_K / Q5_K):
+
+    * codes uniform over the format's range (Q4_K and IQ4_XS 0..15, Q5_K
+      0..31, Q6_K 0..63);
+    * d = fp16 of |N(0,1)| * 1e-3 (Q4_K, Q5_K), * 2e-4 (Q6_K), * 1e-4 (IQ4_XS);
+      dmin = fp16 of |N(0,1)| * 7.5e-3 (Q4_K, Q5_K);
+    * sub-block scales ``sub``: Q4_K / Q5_K / IQ4_XS one 6-bit value (0..63)
+      per 32 elements, Q6_K one int8 per 16 elements (uniform -128..127);
+      ``mins`` (Q4_K / Q5_K) one 6-bit value per 32 elements.
+    """
+    assert fmt in KQUANTS and k % KQ_SUPER == 0
+    hi = {Q4_K: 16, Q5_K: 32, Q6_K: 64, IQ4_XS: 16}[fmt]
+    codes = g.integers(0, hi, size=(n, k), dtype=np.uint8)
+    ns = k // KQ_SUPER
+    dscale = {Q4_K: 1e-3, Q5_K: 1e-3, Q6_K: 2e-4, IQ4_XS: 1e-4}[fmt]
+    w = {"fmt": fmt, "n": n, "k": k, "codes": codes, "d": to_f16_bits(np.abs(g.standard_normal(size=(n, ns))) * dscale)}
+    if fmt == Q6_K:
+        w["sub"] = g.integers(-128, 128, size=(n, k // 16), dtype=np.int16).astype(np.int8)
+    else:
+        w["sub"] = g.integers(0, 64, size=(n, k // 32), dtype=np.uint8)
+    if fmt in (Q4_K, Q5_K):
+        w["dmin"] = to_f16_bits(np.abs(g.standard_normal(size=(n, ns))) * 7.5e-3)
+        w["mins"] = g.integers(0, 64, size=(n, k // 32), dtype=np.uint8)
+    return w
 
 
 def q8_0_weights(g: np.random.Generator, n: int, k: int) -> dict:
@@ -185,6 +220,15 @@ class W4A8:
 def w4a8_case(n: int = 17408, k: int = 5120, m: int = 1, seed: int | None = None) -> W4A8:
     s = seed_for(3) if seed is None else seed
     w = q4_0_weights(rng(s), n, k)
+    x = x_f32(rng(s + 1), m, k)
+    return W4A8(w=w, x=x)
+
+
+def kquant_case(fmt: str, n: int = 17408, k: int = 5120, m: int = 1, seed: int | None = None) -> W4A8:
+    """K-quant / IQ4_XS weights times Q8_0-quantized fp32 activations (the
+    27B-class [17408 x 5120] projection by default)."""
+    s = seed_for(8, 10 * KQUANTS.index(fmt)) if seed is None else seed
+    w = kquant_weights(rng(s), fmt, n, k)
     x = x_f32(rng(s + 1), m, k)
     return W4A8(w=w, x=x)
 

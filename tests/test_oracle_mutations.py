@@ -4,12 +4,14 @@ import numpy as np
 import pytest
 
 import oracle
+import synth
 from oracle import formats as F
 from oracle import ops as O
 from tests import test_oracle_a8 as A8
 from tests import test_oracle_fp8 as TF8
 from tests import test_oracle_formats as TF
 from tests import test_oracle_gemv as TG
+from tests import test_oracle_kquants as TK
 from tests import test_oracle_moe as TM
 
 pytestmark = pytest.mark.cpu
@@ -108,6 +110,44 @@ def _fp8_tiles(transpose=False, tile=128, columns=True):
     return dq
 
 
+def _kq_min_added(w, rows=None):
+    r = O._rows(w, rows)
+    q = w["codes"][r].astype(np.float64)
+    d = O._per_column(F.decode_f16(w["d"][r]), 256)
+    dmin = O._per_column(F.decode_f16(w["dmin"][r]), 256)
+    return d * O._per_column(w["sub"][r], 32) * q + dmin * O._per_column(w["mins"][r], 32)
+
+
+def _kq_fifth_bit_dropped(w, rows=None):
+    return ORIG_Q4K(dict(w, codes=w["codes"] & 15), rows)
+
+
+def _q6k_no_offset(w, rows=None):
+    r = O._rows(w, rows)
+    d = O._per_column(F.decode_f16(w["d"][r]), 256)
+    return d * O._per_column(w["sub"][r].astype(np.int8), 16) * w["codes"][r].astype(np.float64)
+
+
+def _q6k_sub_blocks_of_32(w, rows=None):
+    r = O._rows(w, rows)
+    k = w["codes"].shape[1]
+    d = O._per_column(F.decode_f16(w["d"][r]), 256)
+    sc = O._per_column(w["sub"][r][:, :k // 32].astype(np.int8), 32)
+    return d * sc * (w["codes"][r].astype(np.float64) - 32.0)
+
+
+def _iq4_no_scale_offset(w, rows=None):
+    return ORIG_IQ4(dict(w, sub=w["sub"].astype(np.int16) + 32), rows)
+
+
+def _iq4_codebook_reversed(w, rows=None):
+    return ORIG_IQ4(dict(w, codes=15 - w["codes"]), rows)
+
+
+ORIG_Q4K = O.dequant_q4_k
+ORIG_IQ4 = O.dequant_iq4_xs
+
+
 def _fp8_pins():
     return [lambda: TF8.test_dequant_matches_torch_decode_and_tile_lookup(300, 384, True),
             TF8.test_gemv_exact_brute_force_across_tiles]
@@ -139,6 +179,15 @@ MUTATIONS = [
     ("FP8 scale grid transposed", [(O, "dequant_fp8", _fp8_tiles(transpose=True))], _fp8_pins()),
     ("FP8 tiles of 64", [(O, "dequant_fp8", _fp8_tiles(tile=64))], _fp8_pins()),
     ("FP8 column tiles ignored", [(O, "dequant_fp8", _fp8_tiles(columns=False))], _fp8_pins()),
+    ("K-quant min added", [(O, "dequant_q4_k", _kq_min_added)], [TK.test_q4_k_reduces_to_q4_0]),
+    ("Q5_K fifth bit dropped", [(O, "dequant_q4_k", _kq_fifth_bit_dropped)], [TK.test_q5_k_uses_the_fifth_bit]),
+    ("Q6_K offset of 32 dropped", [(O, "dequant_q6_k", _q6k_no_offset)], [TK.test_q6_k_reduces_to_q8_0]),
+    ("Q6_K sub-blocks of 32", [(O, "dequant_q6_k", _q6k_sub_blocks_of_32)],
+     [lambda: TK.test_one_hot_sub_block(synth.Q6_K)]),
+    ("IQ4_XS scale offset dropped", [(O, "dequant_iq4_xs", _iq4_no_scale_offset)],
+     [TK.test_iq4_xs_codebook_and_scale_offset]),
+    ("IQ4_XS codebook reversed", [(O, "dequant_iq4_xs", _iq4_codebook_reversed)],
+     [TK.test_iq4_xs_codebook_and_scale_offset]),
 ]
 
 
