@@ -19,6 +19,21 @@
  *          byte per weight, with fp32 scales: one per tensor (QG_FP8_TENSOR)
  *          or one per 128 x 128 tile of W (QG_FP8_B128, the "block-128" FP8
  *          checkpoints of the memra README, loaders entry).  w = e4m3(c) * s.
+ *   Q4_K, Q5_K, Q6_K, IQ4_XS  (the K-quant and IQ4_XS formats the pages run
+ *          their GGUF models in: memra README, feature list "Decode kernels"
+ *          and model table; bw24 README, requirements.  The pages do not
+ *          define them; these are the public GGUF definitions, on logical
+ *          values.)  256-element super-blocks with an fp16 scale d:
+ *          Q4_K / Q5_K  fp16 dmin per super-block, 6-bit scale sc_j and 6-bit
+ *                 min m_j per 32 elements, 4- / 5-bit codes q:
+ *                 w = d * sc_j * q - dmin * m_j.
+ *          Q6_K   int8 scale sc_j per 16 elements, 6-bit codes q:
+ *                 w = d * sc_j * (q - 32).
+ *          IQ4_XS 6-bit scale ls_j per 32 elements, 4-bit indices q into the
+ *                 IQ4_NL codebook T = {-127, -104, -83, -65, -49, -35, -22,
+ *                 -10, 1, 13, 25, 38, 53, 69, 89, 113}:
+ *                 w = d * (ls_j - 32) * T[q].
+ *          k must be a multiple of 256 for these formats.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -68,6 +83,10 @@ extern "C" {
 #define QG_Q4_0  3
 #define QG_FP8_TENSOR 4
 #define QG_FP8_B128   5
+#define QG_Q4_K   6
+#define QG_Q5_K   7
+#define QG_Q6_K   8
+#define QG_IQ4_XS 9
 
 #define QG_ABI_VERSION    1
 #define QG_LAYOUT_VERSION 1  /* packed device layout described below */
@@ -102,7 +121,20 @@ int qg_last_hip_error(void);
  *          value, QG_FP8_B128 a row-major grid [ceil(n/128)][ceil(k/128)]
  *          whose entry (i, j) scales rows [128i, 128i+128) x columns
  *          [128j, 128j+128) (the last tiles may be partial).
- *
+ *   K-quants / IQ4_XS, with S = k/256 super-blocks and B = k/32 blocks per row:
+ *          codes: n rows of k/2 bytes in the Q4_0 nibble order (the low four
+ *          code bits), then for Q5_K k/8 bytes (one dword per block b: bit
+ *          8*(e%4) + e/4 holds bit 4 of element 32b+e) or for Q6_K k/4
+ *          bytes (two dwords per block: the first for elements e < 16, the
+ *          second for e >= 16; with e' = e % 16, bits 8*(e'%4) + 2*(e'/4)
+ *          and the next hold bits 4..5 of the code).  Placing four
+ *          elements' high bits one byte apart lets the kernel rebuild four
+ *          codes with one shift and one mask.
+ *          scales: n rows of: the super-block part (Q4_K / Q5_K: S dwords,
+ *          d in the low and dmin in the high half; Q6_K / IQ4_XS: S fp16 d),
+ *          then the block part (Q4_K / Q5_K: B uint16, sc_b in the low and
+ *          m_b in the high byte; Q6_K: the k/16 int8 scales in order;
+ *          IQ4_XS: B bytes ls_b).
  * Every row of every plane starts 16-byte aligned when k % 32 == 0.
  */
 
@@ -151,13 +183,27 @@ int qg_pack_fp8(int fmt, const uint8_t* codes, const float* scales, int64_t n, i
 int qg_unpack_fp8(int fmt, const void* src, size_t src_bytes, int64_t n, int64_t k,
                   uint8_t* codes, float* scales);
 
+/* K-quant / IQ4_XS packer and unpacker.  fmt: QG_Q4_K, QG_Q5_K, QG_Q6_K or
+ * QG_IQ4_XS; k % 256 == 0.  codes: one per byte, row-major [n][k] (Q4_K and
+ * IQ4_XS 0..15, Q5_K 0..31, Q6_K 0..63, else QG_EINVAL).  d: fp16 bits
+ * [n][k/256].  dmin: fp16 bits [n][k/256] (Q4_K / Q5_K; ignored otherwise,
+ * may be NULL).  sub: Q4_K / Q5_K / IQ4_XS [n][k/32] values 0..63 (else
+ * QG_EINVAL), Q6_K [n][k/16] int8 bit patterns.  mins: [n][k/32] 0..63
+ * (Q4_K / Q5_K; ignored otherwise, may be NULL).  Exact inverses. */
+int qg_pack_kquant(int fmt, const uint8_t* codes, const uint16_t* d, const uint16_t* dmin,
+                   const uint8_t* sub, const uint8_t* mins, int64_t n, int64_t k, void* dst,
+                   size_t dst_bytes);
+int qg_unpack_kquant(int fmt, const void* src, size_t src_bytes, int64_t n, int64_t k, uint8_t* codes,
+                     uint16_t* d, uint16_t* dmin, uint8_t* sub, uint8_t* mins);
+
 /* ------------------------------------------------------ dequantization
  * out[r][c] = the weight value, fp32 (device, [n][k]).  NVFP4: e2m1*e4m3 is
  * exact and the product with tensor_scale is rounded once (to nearest even);
  * Q4_0 and Q8_0 values are exact in fp32.  Runs the same device decode code
  * as the GEMV kernels; meant for verification, not for the decode path.
- * tensor_scale is ignored for Q4_0 / Q8_0 / FP8 (FP8 values e4m3 * s are
- * rounded once to fp32). */
+ * tensor_scale is ignored for Q4_0 / Q8_0 / FP8 / K-quants (FP8 values
+ * e4m3 * s, and Q4_K / Q5_K values d*sc*q - dmin*m, are rounded once to
+ * fp32; Q6_K and IQ4_XS values are exact in fp32). */
 int qg_dequant(int fmt, const void* w, float tensor_scale, int64_t n, int64_t k,
                float* out, void* stream);
 
@@ -213,6 +259,23 @@ int qg_quantize_q8_0_act(const float* x, int64_t m, int64_t k, int8_t* xq, uint1
  * sums are recomputed in the kernel); y: device fp32 [m][n]. */
 int qgemv_q4_0_a8(const void* w, int64_t n, int64_t k, const int8_t* xq, const uint16_t* xd,
                   const int32_t* xs, int64_t m, float* y, void* stream);
+
+/* K-quant / IQ4_XS weights x Q8_0 activations (memra README, feature list
+ * "Decode kernels": K-quant split-plane matvecs with dp4a).  Per 32-element
+ * block b of a row, with the block's activation scale d_x, codes q_x and
+ * their sum s_x (all from qg_quantize_q8_0_act), exact int32 dots first:
+ *   Q4_K / Q5_K  i = sum q * q_x;
+ *                y += d_x * fma(d*sc_b, i, -((dmin*m_b) * s_x));
+ *   Q6_K         h = sum of q_x over the block's first 16 elements;
+ *                v = sc_2b * (sum_lo q*q_x - 32 h)
+ *                  + sc_2b+1 * (sum_hi q*q_x - 32 (s_x - h));
+ *                y += (d * d_x) * v;
+ *   IQ4_XS       v = (ls_b - 32) * sum T[q] * q_x;  y += (d * d_x) * v;
+ * blocks in ascending order, then the fixed lane butterfly (fp32).
+ * w: device packed [n][k] (k % 256 == 0); xq / xd / xs: device, as written
+ * by qg_quantize_q8_0_act (xs is required here); y: device fp32 [m][n]. */
+int qgemv_kquant_a8(int fmt, const void* w, int64_t n, int64_t k, const int8_t* xq, const uint16_t* xd,
+                    const int32_t* xs, int64_t m, float* y, void* stream);
 
 /* ------------------------------------------------------ MoE decode
  * Router: for each of t tokens pick the top_k largest of n_experts fp32

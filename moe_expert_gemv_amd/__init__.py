@@ -20,13 +20,16 @@ import numpy as np
 __all__ = [
     "QGError", "QGLibraryMissing", "LIB_PATH", "lib", "loaded",
     "QG_NVFP4", "QG_Q8_0", "QG_Q4_0", "QG_FP8_TENSOR", "QG_FP8_B128", "QG_MAX_M", "QG_MOE_KEEP_H",
+    "QG_Q4_K", "QG_Q5_K", "QG_Q6_K", "QG_IQ4_XS", "KQUANT_FORMATS", "qg_pack_kquant", "qg_unpack_kquant",
+    "qgemv_kquant_a8",
     "qg_abi_version", "qg_layout_version", "qg_status_string", "qg_packed_bytes",
     "qg_scale_plane_offset", "qg_pack_nvfp4", "qg_pack_nvfp4_gate_up", "qg_pack_q4_0", "qg_pack_q8_0",
     "qg_unpack_nvfp4", "qg_unpack_nvfp4_gate_up", "qg_unpack_q4_0", "qg_unpack_q8_0", "qg_pack_fp8",
     "qg_unpack_fp8", "qgemv_fp8", "fp8_scale_shape", "qg_dequant",
     "qgemv_q8_0", "qgemv_nvfp4", "qgemv_nvfp4_swiglu", "qg_quantize_q8_0_act",
     "qgemv_q4_0_a8", "moe_route_topk", "QgMoeDesc", "moe_workspace_bytes",
-    "moe_gemv_grouped", "moe_forward", "moe_prefill_workspace_bytes", "moe_prefill", "qgemm_prefill", "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
+    "moe_gemv_grouped", "moe_forward", "moe_prefill_workspace_bytes", "moe_prefill", "qgemm_prefill",
+    "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -34,6 +37,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so
 
 QG_OK, QG_EINVAL, QG_EUNSUPPORTED, QG_ENOSPC, QG_EHIP = 0, -1, -2, -4, -5
 QG_NVFP4, QG_Q8_0, QG_Q4_0, QG_FP8_TENSOR, QG_FP8_B128 = 1, 2, 3, 4, 5
+QG_Q4_K, QG_Q5_K, QG_Q6_K, QG_IQ4_XS = 6, 7, 8, 9
+KQUANT_FORMATS = (QG_Q4_K, QG_Q5_K, QG_Q6_K, QG_IQ4_XS)
 QG_MAX_M = 16
 QG_MOE_KEEP_H = 1
 
@@ -96,6 +101,9 @@ _SIGNATURES = {
     "qgemv_nvfp4_swiglu": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P, _P]),
     "qg_quantize_q8_0_act": (_I32, [_P, _I64, _I64, _P, _P, _P, _P]),
     "qgemv_q4_0_a8": (_I32, [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
+    "qg_pack_kquant": (_I32, [_I32, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ]),
+    "qg_unpack_kquant": (_I32, [_I32, _P, _SZ, _I64, _I64, _P, _P, _P, _P, _P]),
+    "qgemv_kquant_a8": (_I32, [_I32, _P, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
     "moe_route_topk": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "moe_workspace_bytes": (_SZ, [ctypes.POINTER(QgMoeDesc), _I64]),
     "moe_gemv_grouped": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _P, _I64, _P, _P, _SZ, _P]),
@@ -287,6 +295,57 @@ def qg_unpack_fp8(fmt, buf, n, k):
     return codes, scales
 
 
+def _kq_has_min(fmt):
+    return fmt in (QG_Q4_K, QG_Q5_K)
+
+
+def qg_pack_kquant(fmt, codes, d, sub, dmin=None, mins=None) -> np.ndarray:
+    """K-quant / IQ4_XS logical arrays -> packed host buffer.  codes [n][k]
+    uint8; d (and dmin) fp16 bits [n][k/256]; sub [n][k/32] (Q6_K: int8
+    [n][k/16]); mins [n][k/32] (Q4_K / Q5_K)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    n, k = codes.shape
+    size = qg_packed_bytes(fmt, n, k)
+    if size == 0:
+        raise QGError("qg_pack_kquant", QG_EINVAL)
+    d = np.ascontiguousarray(d, dtype=np.uint16)
+    sub = np.ascontiguousarray(sub).view(np.uint8) if np.asarray(sub).dtype == np.int8 else \
+        np.ascontiguousarray(sub, dtype=np.uint8)
+    want_sub = n * (k // 16 if fmt == QG_Q6_K else k // 32)
+    if d.size != n * (k // 256) or sub.size != want_sub:
+        raise QGError("qg_pack_kquant", QG_EINVAL)
+    dm = mn = None
+    if _kq_has_min(fmt):
+        if dmin is None or mins is None:
+            raise QGError("qg_pack_kquant", QG_EINVAL)
+        dm = np.ascontiguousarray(dmin, dtype=np.uint16)
+        mn = np.ascontiguousarray(mins, dtype=np.uint8)
+        if dm.size != d.size or mn.size != n * (k // 32):
+            raise QGError("qg_pack_kquant", QG_EINVAL)
+    out = np.empty(size, dtype=np.uint8)
+    _check("qg_pack_kquant", lib().qg_pack_kquant(fmt, _hptr(codes), _hptr(d), None if dm is None else _hptr(dm),
+                                                  _hptr(sub), None if mn is None else _hptr(mn), n, k,
+                                                  _hptr(out), size))
+    return out
+
+
+def qg_unpack_kquant(fmt, buf, n, k) -> dict:
+    """Inverse of qg_pack_kquant: {"codes", "d", "sub"[, "dmin", "mins"]}."""
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    codes = np.empty((n, k), dtype=np.uint8)
+    d = np.empty((n, k // 256), dtype=np.uint16)
+    sub = np.empty((n, k // 16 if fmt == QG_Q6_K else k // 32), dtype=np.uint8)
+    dm = np.empty_like(d) if _kq_has_min(fmt) else None
+    mn = np.empty((n, k // 32), dtype=np.uint8) if _kq_has_min(fmt) else None
+    _check("qg_unpack_kquant",
+           lib().qg_unpack_kquant(fmt, _hptr(buf), buf.nbytes, n, k, _hptr(codes), _hptr(d),
+                                  None if dm is None else _hptr(dm), _hptr(sub), None if mn is None else _hptr(mn)))
+    out = {"codes": codes, "d": d, "sub": sub.view(np.int8) if fmt == QG_Q6_K else sub}
+    if dm is not None:
+        out["dmin"], out["mins"] = dm, mn
+    return out
+
+
 # ---------------------------------------------------------------- device entry points
 
 def qg_dequant(fmt, w, tensor_scale, n, k, out, stream=None) -> None:
@@ -321,6 +380,12 @@ def qgemv_q4_0_a8(w, n, k, xq, xd, xs, m, y, stream=None) -> None:
     _check("qgemv_q4_0_a8",
            lib().qgemv_q4_0_a8(_dptr(w), n, k, _dptr(xq), _dptr(xd), _dptr(xs), m, _dptr(y),
                                _stream(stream)))
+
+
+def qgemv_kquant_a8(fmt, w, n, k, xq, xd, xs, m, y, stream=None) -> None:
+    _check("qgemv_kquant_a8",
+           lib().qgemv_kquant_a8(fmt, _dptr(w), n, k, _dptr(xq), _dptr(xd), _dptr(xs), m, _dptr(y),
+                                 _stream(stream)))
 
 
 def moe_route_topk(logits, t, n_experts, top_k, ids, weights, stream=None) -> None:

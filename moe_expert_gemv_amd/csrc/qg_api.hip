@@ -69,7 +69,9 @@ extern "C" {
 int qg_dequant(int fmt, const void* w, float tensor_scale, int64_t n, int64_t k, float* out,
                void* stream) {
     if (!valid_fmt(fmt) || !w || !out || !aligned(w, 256) || !aligned(out, 16)) return QG_EINVAL;
-    if (!valid_shape(n, k)) return QG_EINVAL;
+    if (!valid_fmt_shape(fmt, n, k)) return QG_EINVAL;
+    if (is_kquant(fmt))
+        return finish(launch_dequant_kquant(fmt, static_cast<const uint8_t*>(w), n, k, out, as_stream(stream)));
     if (is_fp8(fmt))
         return finish(launch_dequant_fp8(fmt, static_cast<const uint8_t*>(w), n, k, out, as_stream(stream)));
     return finish(launch_dequant(fmt, static_cast<const uint8_t*>(w), tensor_scale, n, k, out,
@@ -121,6 +123,16 @@ int qgemv_q4_0_a8(const void* w, int64_t n, int64_t k, const int8_t* xq, const u
     if (!xd || !aligned(xd, 2) || (xs && !aligned(xs, 4))) return QG_EINVAL;
     return finish(launch_gemv_q4_0_a8(static_cast<const uint8_t*>(w), n, k, xq, xd, xs, int(m), y,
                                       as_stream(stream)));
+}
+
+int qgemv_kquant_a8(int fmt, const void* w, int64_t n, int64_t k, const int8_t* xq, const uint16_t* xd,
+                    const int32_t* xs, int64_t m, float* y, void* stream) {
+    if (!is_kquant(fmt)) return QG_EINVAL;
+    if (int st = check_gemv(w, n, k, xq, m, y)) return st;
+    if (k % kKqSuper != 0) return QG_EINVAL;
+    if (!xd || !xs || !aligned(xd, 2) || !aligned(xs, 4)) return QG_EINVAL;
+    return finish(launch_gemv_kquant_a8(fmt, static_cast<const uint8_t*>(w), n, k, xq, xd, xs, int(m), y,
+                                        as_stream(stream)));
 }
 
 int moe_route_topk(const float* logits, int64_t t, int64_t n_experts, int64_t top_k, int32_t* ids,

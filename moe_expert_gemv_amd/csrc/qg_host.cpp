@@ -32,12 +32,12 @@ const char* qg_status_string(int status) {
 }
 
 size_t qg_packed_bytes(int fmt, int64_t n, int64_t k) {
-    if (!qg::valid_fmt(fmt) || !qg::valid_shape(n, k)) return 0;
+    if (!qg::valid_fmt(fmt) || !qg::valid_fmt_shape(fmt, n, k)) return 0;
     return size_t(qg::packed_bytes(fmt, n, k));
 }
 
 size_t qg_scale_plane_offset(int fmt, int64_t n, int64_t k) {
-    if (!qg::valid_fmt(fmt) || !qg::valid_shape(n, k)) return 0;
+    if (!qg::valid_fmt(fmt) || !qg::valid_fmt_shape(fmt, n, k)) return 0;
     return size_t(qg::scale_plane_offset(fmt, n, k));
 }
 
@@ -46,7 +46,7 @@ size_t qg_scale_plane_offset(int fmt, int64_t n, int64_t k) {
 static int check_pack_args(int fmt, const void* a, const void* b, int64_t n, int64_t k,
                            const void* buf, size_t bytes) {
     if (!a || !b || !buf) return QG_EINVAL;
-    if (!qg::valid_shape(n, k)) return QG_EINVAL;
+    if (!qg::valid_fmt_shape(fmt, n, k)) return QG_EINVAL;
     if (bytes < size_t(qg::packed_bytes(fmt, n, k))) return QG_ENOSPC;
     return QG_OK;
 }
@@ -208,6 +208,128 @@ int qg_unpack_fp8(int fmt, const void* src, size_t src_bytes, int64_t n, int64_t
     const uint8_t* in = static_cast<const uint8_t*>(src);
     std::memcpy(codes, in, size_t(n * k));
     std::memcpy(scales, in + qg::scale_plane_offset(fmt, n, k), size_t(qg::scale_plane_bytes(fmt, n, k)));
+    return QG_OK;
+}
+
+// ---------------------------------------------------------------- K-quants
+
+static int kq_code_limit(int fmt) { return fmt == QG_Q5_K ? 32 : fmt == QG_Q6_K ? 64 : 16; }
+static bool kq_has_min(int fmt) { return fmt == QG_Q4_K || fmt == QG_Q5_K; }
+// Bit position of the high code bits of element e (0..31) of a block in its
+// dword: Q5_K one bit, Q6_K two bits (e < 16 in the first dword, else the
+// second).  Four consecutive elements land one byte apart.
+static int kq5_bit(int e) { return 8 * (e % 4) + e / 4; }
+static int kq6_bit(int e) { return 8 * (e % 16 % 4) + 2 * (e % 16 / 4); }
+
+static int check_kquant_args(int fmt, const void* codes, const void* d, const void* dmin, const void* sub,
+                             const void* mins, int64_t n, int64_t k, const void* buf, size_t bytes) {
+    if (!qg::is_kquant(fmt) || !codes || !d || !sub || !buf) return QG_EINVAL;
+    if (kq_has_min(fmt) && (!dmin || !mins)) return QG_EINVAL;
+    if (!qg::valid_fmt_shape(fmt, n, k)) return QG_EINVAL;
+    if (bytes < size_t(qg::packed_bytes(fmt, n, k))) return QG_ENOSPC;
+    return QG_OK;
+}
+
+int qg_pack_kquant(int fmt, const uint8_t* codes, const uint16_t* d, const uint16_t* dmin, const uint8_t* sub,
+                   const uint8_t* mins, int64_t n, int64_t k, void* dst, size_t dst_bytes) {
+    int st = check_kquant_args(fmt, codes, d, dmin, sub, mins, n, k, dst, dst_bytes);
+    if (st) return st;
+    const int lim = kq_code_limit(fmt);
+    for (int64_t i = 0; i < n * k; ++i)
+        if (codes[i] >= lim) return QG_EINVAL;
+    if (fmt != QG_Q6_K)
+        for (int64_t i = 0; i < n * (k / 32); ++i)
+            if (sub[i] > 63 || (kq_has_min(fmt) && mins[i] > 63)) return QG_EINVAL;
+    uint8_t* out = static_cast<uint8_t*>(dst);
+    std::memset(out, 0, size_t(qg::packed_bytes(fmt, n, k)));
+    const int64_t crow = qg::code_row_bytes(fmt, k), srow = qg::scale_row_bytes(fmt, k);
+    const int64_t S = k / qg::kKqSuper, B = k / 32, sup = qg::kq_super_bytes(fmt, k);
+    uint8_t* splane = out + qg::scale_plane_offset(fmt, n, k);
+    for (int64_t r = 0; r < n; ++r) {
+        const uint8_t* c = codes + r * k;
+        uint8_t* o = out + r * crow;
+        uint8_t* hb = o + k / 2;
+        for (int64_t b = 0; b < B; ++b) {
+            for (int i = 0; i < 16; ++i)
+                o[16 * b + i] = uint8_t((c[32 * b + i] & 15) | ((c[32 * b + 16 + i] & 15) << 4));
+            if (fmt == QG_Q5_K) {
+                uint32_t h = 0;
+                for (int e = 0; e < 32; ++e) h |= uint32_t(c[32 * b + e] >> 4) << kq5_bit(e);
+                std::memcpy(hb + 4 * b, &h, 4);
+            } else if (fmt == QG_Q6_K) {
+                uint32_t h[2] = {0, 0};
+                for (int e = 0; e < 32; ++e) h[e / 16] |= uint32_t(c[32 * b + e] >> 4) << kq6_bit(e);
+                std::memcpy(hb + 8 * b, h, 8);
+            }
+        }
+        uint8_t* so = splane + r * srow;
+        for (int64_t s = 0; s < S; ++s) {
+            if (kq_has_min(fmt)) {
+                const uint32_t v = uint32_t(d[r * S + s]) | (uint32_t(dmin[r * S + s]) << 16);
+                std::memcpy(so + 4 * s, &v, 4);
+            } else {
+                std::memcpy(so + 2 * s, &d[r * S + s], 2);
+            }
+        }
+        if (kq_has_min(fmt)) {
+            for (int64_t b = 0; b < B; ++b) {
+                so[sup + 2 * b] = sub[r * B + b];
+                so[sup + 2 * b + 1] = mins[r * B + b];
+            }
+        } else {
+            std::memcpy(so + sup, sub + r * qg::kq_sub_bytes(fmt, k), size_t(qg::kq_sub_bytes(fmt, k)));
+        }
+    }
+    return QG_OK;
+}
+
+int qg_unpack_kquant(int fmt, const void* src, size_t src_bytes, int64_t n, int64_t k, uint8_t* codes,
+                     uint16_t* d, uint16_t* dmin, uint8_t* sub, uint8_t* mins) {
+    int st = check_kquant_args(fmt, codes, d, dmin, sub, mins, n, k, src, src_bytes);
+    if (st) return st;
+    const uint8_t* in = static_cast<const uint8_t*>(src);
+    const int64_t crow = qg::code_row_bytes(fmt, k), srow = qg::scale_row_bytes(fmt, k);
+    const int64_t S = k / qg::kKqSuper, B = k / 32, sup = qg::kq_super_bytes(fmt, k);
+    const uint8_t* splane = in + qg::scale_plane_offset(fmt, n, k);
+    for (int64_t r = 0; r < n; ++r) {
+        const uint8_t* o = in + r * crow;
+        const uint8_t* hb = o + k / 2;
+        uint8_t* c = codes + r * k;
+        for (int64_t b = 0; b < B; ++b) {
+            for (int i = 0; i < 16; ++i) {
+                c[32 * b + i] = o[16 * b + i] & 15;
+                c[32 * b + 16 + i] = o[16 * b + i] >> 4;
+            }
+            if (fmt == QG_Q5_K) {
+                uint32_t h;
+                std::memcpy(&h, hb + 4 * b, 4);
+                for (int e = 0; e < 32; ++e) c[32 * b + e] |= uint8_t(((h >> kq5_bit(e)) & 1) << 4);
+            } else if (fmt == QG_Q6_K) {
+                uint32_t h[2];
+                std::memcpy(h, hb + 8 * b, 8);
+                for (int e = 0; e < 32; ++e) c[32 * b + e] |= uint8_t(((h[e / 16] >> kq6_bit(e)) & 3) << 4);
+            }
+        }
+        const uint8_t* so = splane + r * srow;
+        for (int64_t s = 0; s < S; ++s) {
+            if (kq_has_min(fmt)) {
+                uint32_t v;
+                std::memcpy(&v, so + 4 * s, 4);
+                d[r * S + s] = uint16_t(v & 0xFFFF);
+                dmin[r * S + s] = uint16_t(v >> 16);
+            } else {
+                std::memcpy(&d[r * S + s], so + 2 * s, 2);
+            }
+        }
+        if (kq_has_min(fmt)) {
+            for (int64_t b = 0; b < B; ++b) {
+                sub[r * B + b] = so[sup + 2 * b];
+                mins[r * B + b] = so[sup + 2 * b + 1];
+            }
+        } else {
+            std::memcpy(sub + r * qg::kq_sub_bytes(fmt, k), so + sup, size_t(qg::kq_sub_bytes(fmt, k)));
+        }
+    }
     return QG_OK;
 }
 

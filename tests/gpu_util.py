@@ -52,6 +52,9 @@ def empty(shape, dtype):
     return torch.empty(shape, dtype=dtype, device="cuda")
 
 
+KQ_FMT = {"q4_k": qg.QG_Q4_K, "q5_k": qg.QG_Q5_K, "q6_k": qg.QG_Q6_K, "iq4_xs": qg.QG_IQ4_XS}
+
+
 def fp8_fmt(w: dict) -> int:
     return qg.QG_FP8_B128 if w["tiled"] else qg.QG_FP8_TENSOR
 
@@ -64,6 +67,8 @@ def pack_dev(w: dict):
         buf = qg.qg_pack_q4_0(w["codes"], w["scales"])
     elif w["fmt"] == "fp8":
         buf = qg.qg_pack_fp8(fp8_fmt(w), w["codes"], w["scales"])
+    elif w["fmt"] in KQ_FMT:
+        buf = qg.qg_pack_kquant(KQ_FMT[w["fmt"]], w["codes"], w["d"], w["sub"], w.get("dmin"), w.get("mins"))
     else:
         buf = qg.qg_pack_q8_0(w["codes"], w["scales"])
     return dev_u8(buf)

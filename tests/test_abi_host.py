@@ -284,3 +284,75 @@ def test_fp8_argument_checks(L):
     assert L.qgemv_fp8(qg.QG_FP8_B128, 256, 4, 48, 256, 1, 256, None) == qg.QG_EINVAL  # k % 32
     assert L.qgemv_fp8(qg.QG_FP8_B128, 256, 4, 64, 256, 17, 256, None) == qg.QG_EUNSUPPORTED  # m > 16
     assert L.qgemv_fp8(qg.QG_FP8_TENSOR, 0, 4, 64, 256, 1, 256, None) == qg.QG_EINVAL  # null w
+
+
+# ---------------------------------------------------------------- K-quants
+
+KQ = {synth.Q4_K: qg.QG_Q4_K, synth.Q5_K: qg.QG_Q5_K, synth.Q6_K: qg.QG_Q6_K, synth.IQ4_XS: qg.QG_IQ4_XS}
+
+
+def _kq_pack(w):
+    return qg.qg_pack_kquant(KQ[w["fmt"]], w["codes"], w["d"], w["sub"], w.get("dmin"), w.get("mins"))
+
+
+@pytest.mark.parametrize("fmt", synth.KQUANTS)
+@pytest.mark.parametrize("n,k", [(1, 256), (7, 768), (33, 5120)])
+def test_kquant_pack_roundtrip_and_sizes(L, fmt, n, k):
+    w = synth.kquant_weights(synth.rng(n + k), fmt, n, k)
+    buf = _kq_pack(w)
+    high = {synth.Q5_K: k // 8, synth.Q6_K: k // 4}.get(fmt, 0)
+    scale_row = {synth.Q4_K: 20, synth.Q5_K: 20, synth.Q6_K: 18, synth.IQ4_XS: 10}[fmt] * (k // 256)
+    align = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    assert buf.nbytes == align(n * (k // 2 + high)) + align(n * scale_row)
+    assert qg.qg_scale_plane_offset(KQ[fmt], n, k) == align(n * (k // 2 + high))
+    u = qg.qg_unpack_kquant(KQ[fmt], buf, n, k)
+    for key, v in u.items():
+        assert np.array_equal(v.view(np.uint8), np.asarray(w[key]).view(np.uint8)), key
+
+
+@pytest.mark.parametrize("fmt", [synth.Q5_K, synth.Q6_K])
+def test_kquant_high_bits_sit_one_byte_apart(L, fmt):
+    """The documented placement: for dword q of a block's 4-bit plane, one
+    shift and one mask of the high-bit word give the high bits of elements
+    4q..4q+3 (and of 16+4q..16+4q+3), one per byte."""
+    n, k = 3, 512
+    w = synth.kquant_weights(synth.rng(5), fmt, n, k)
+    buf = _kq_pack(w)
+    row = k // 2 + (k // 8 if fmt == synth.Q5_K else k // 4)
+    for r in range(n):
+        base = r * row + k // 2
+        for b in range(k // 32):
+            if fmt == synth.Q5_K:
+                h0 = h1 = int(buf[base + 4 * b:base + 4 * b + 4].view(np.uint32)[0])
+            else:
+                h0, h1 = (int(v) for v in buf[base + 8 * b:base + 8 * b + 8].view(np.uint32))
+            for q in range(4):
+                for i in range(4):
+                    e_lo, e_hi = 32 * b + 4 * q + i, 32 * b + 16 + 4 * q + i
+                    if fmt == synth.Q5_K:
+                        lo, hi = (h0 >> q) >> (8 * i) & 1, (h1 >> (4 + q)) >> (8 * i) & 1
+                    else:
+                        lo, hi = (h0 >> (2 * q)) >> (8 * i) & 3, (h1 >> (2 * q)) >> (8 * i) & 3
+                    assert lo == w["codes"][r, e_lo] >> 4 and hi == w["codes"][r, e_hi] >> 4
+
+
+def test_kquant_argument_checks(L):
+    w = synth.kquant_weights(synth.rng(6), synth.Q4_K, 2, 256)
+    bad = dict(w, codes=w["codes"].copy())
+    bad["codes"][1, 7] = 16
+    with pytest.raises(qg.QGError):
+        _kq_pack(bad)  # Q4_K code out of range
+    bad = dict(w, sub=w["sub"].copy())
+    bad["sub"][0, 3] = 64
+    with pytest.raises(qg.QGError):
+        _kq_pack(bad)  # 6-bit scale out of range
+    with pytest.raises(qg.QGError):
+        qg.qg_pack_kquant(qg.QG_Q4_K, w["codes"], w["d"], w["sub"])  # Q4_K needs dmin and mins
+    assert qg.qg_packed_bytes(qg.QG_Q6_K, 4, 224) == 0  # k % 256
+    w6 = synth.kquant_weights(synth.rng(7), synth.Q6_K, 2, 256)
+    w6["sub"][:] = -128  # any int8 is a valid Q6_K scale
+    _kq_pack(w6)
+    assert L.qgemv_kquant_a8(qg.QG_Q4_0, 256, 4, 256, 256, 256, 256, 1, 256, None) == qg.QG_EINVAL  # format
+    assert L.qgemv_kquant_a8(qg.QG_Q4_K, 256, 4, 224, 256, 256, 256, 1, 256, None) == qg.QG_EINVAL  # k % 256
+    assert L.qgemv_kquant_a8(qg.QG_Q4_K, 256, 4, 256, 256, 256, None, 1, 256, None) == qg.QG_EINVAL  # xs required
+    assert L.qgemv_kquant_a8(qg.QG_Q4_K, 256, 4, 256, 256, 256, 256, 17, 256, None) == qg.QG_EUNSUPPORTED
