@@ -284,6 +284,67 @@ class W4A8Gemv(Workload):
         self.qg.qgemv_q4_0_a8(self.w[i % self.R], self.N, self.K, self.xq, self.xd, self.xs, self.m, self.y)
 
 
+class KQuantGemv(Workload):
+    """K-quant / IQ4_XS weights x Q8_0 activations at the 27B-class
+    projection shape [17408 x 5120] (the shape the pages' 27B runs in Q4_K /
+    Q5_K / Q6_K use)."""
+    sources = ("k_gemv_kquant.hip",)
+    kernel_re = (r"k_gemv_kquant\b",)
+    fmt = ""
+
+    def __init__(self, m=1):
+        import torch
+        import moe_expert_gemv_amd as qg
+        import synth
+
+        self.qg, self.m = qg, m
+        self.N, self.K = 17408, 5120
+        self.code = {"q4_k": qg.QG_Q4_K, "q5_k": qg.QG_Q5_K, "q6_k": qg.QG_Q6_K, "iq4_xs": qg.QG_IQ4_XS}[self.fmt]
+        case = synth.kquant_case(self.fmt, m=m)
+        w = case.w
+        buf = qg.qg_pack_kquant(self.code, w["codes"], w["d"], w["sub"], w.get("dmin"), w.get("mins"))
+        self.R = _copies(buf.nbytes)
+        self.w = torch.from_numpy(buf).cuda().repeat(self.R, 1)
+        self.x = torch.from_numpy(case.x).cuda()
+        N, K = self.N, self.K
+        self.xq = torch.empty((m, K), dtype=torch.int8, device="cuda")
+        self.xd = torch.empty((m, K // 32), dtype=torch.int16, device="cuda")
+        self.xs = torch.empty((m, K // 32), dtype=torch.int32, device="cuda")
+        self.y = torch.empty((m, N), dtype=torch.float32, device="cuda")
+        # packed codes + scales (bytes of the layout, not of its padding)
+        high = {"q5_k": K // 8, "q6_k": K // 4}.get(self.fmt, 0)
+        srow = {"q4_k": 20, "q5_k": 20, "q6_k": 18, "iq4_xs": 10}[self.fmt] * (K // 256)
+        self.dominant_bytes = N * (K // 2 + high + srow) + m * (K + K // 32 * 6) + 4 * m * N
+        self.alg_step = self.dominant_bytes + m * K * 4 + m * (K + K // 32 * 6)
+        self.flops_step = 2 * m * N * K
+        self.name = f"{self.fmt} x q8_0 GEMV {N}x{K} (27B-class), batch {m}"
+        self.dominant = f"{self.fmt} GEMV"
+
+    def step(self, i):
+        self.qg.qg_quantize_q8_0_act(self.x, self.m, self.K, self.xq, self.xd, self.xs)
+        self.dominant_launch(i)
+
+    def dominant_launch(self, i):
+        self.qg.qgemv_kquant_a8(self.code, self.w[i % self.R], self.N, self.K, self.xq, self.xd, self.xs, self.m,
+                                self.y)
+
+
+class Q4KGemv(KQuantGemv):
+    fmt = "q4_k"
+
+
+class Q5KGemv(KQuantGemv):
+    fmt = "q5_k"
+
+
+class Q6KGemv(KQuantGemv):
+    fmt = "q6_k"
+
+
+class IQ4XSGemv(KQuantGemv):
+    fmt = "iq4_xs"
+
+
 class MoE(Workload):
     sources = ("k_moe.hip", "qg_gemv_core.hpp")
     kernel_re = (r"k_moe_gate_up(?:_tile)?\b", r"k_moe_down(?:_tile)?\b")
@@ -440,6 +501,10 @@ CONFIGS = {  # name -> (workload class, its size argument)
     "w4a8": (W4A8Gemv, 1),
     "w4a8-m4": (W4A8Gemv, 4),
     "fp8": (Fp8Gemv, 1),
+    "q4k": (Q4KGemv, 1),
+    "q5k": (Q5KGemv, 1),
+    "q6k": (Q6KGemv, 1),
+    "iq4xs": (IQ4XSGemv, 1),
     "moe": (MoE, 1),
     "moe-t4": (MoE, 4),
     "moe-prefill": (MoEPrefill, 512),

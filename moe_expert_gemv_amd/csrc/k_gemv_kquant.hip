@@ -33,14 +33,16 @@ constexpr uint32_t kIq4T1 = 0xF6EADDCFu;  //  -49,  -35,  -22,  -10
 constexpr uint32_t kIq4T2 = 0x26190D01u;  //    1,   13,   25,   38
 constexpr uint32_t kIq4T3 = 0x71594535u;  //   53,   69,   89,  113
 
-// Four 4-bit indices (one per byte) -> their four codebook bytes.
+// Four 4-bit indices (one per byte) -> their four codebook bytes.  Byte
+// permutes take selectors 0..7 as byte indices (and other values as
+// constants), so the first permute is right for indices 0..7, the second
+// (index ^ 8) for 8..15, and a third takes byte i from the first or the
+// second by bit 3 of index i (selector i or i + 4).
 __device__ __forceinline__ uint32_t iq4_lookup(uint32_t idx) {
-    const uint32_t sel = idx & 0x07070707u;
-    const uint32_t lo = __builtin_amdgcn_perm(kIq4T1, kIq4T0, sel);  // entries 0..7
-    const uint32_t hi = __builtin_amdgcn_perm(kIq4T3, kIq4T2, sel);  // entries 8..15
-    const uint32_t b = (idx >> 3) & 0x01010101u;
-    const uint32_t m = (b << 8) - b;  // 0xFF in every byte whose index is >= 8
-    return (hi & m) | (lo & ~m);
+    const uint32_t lo = __builtin_amdgcn_perm(kIq4T1, kIq4T0, idx);                // entries 0..7
+    const uint32_t hi = __builtin_amdgcn_perm(kIq4T3, kIq4T2, idx ^ 0x08080808u);  // entries 8..15
+    const uint32_t pick = ((idx >> 1) & 0x04040404u) | 0x03020100u;
+    return __builtin_amdgcn_perm(hi, lo, pick);
 }
 
 // The raw data of one 32-element block of a row.
