@@ -260,6 +260,20 @@ int qg_quantize_q8_0_act(const float* x, int64_t m, int64_t k, int8_t* xq, uint1
 int qgemv_q4_0_a8(const void* w, int64_t n, int64_t k, const int8_t* xq, const uint16_t* xd,
                   const int32_t* xs, int64_t m, float* y, void* stream);
 
+/* W4A8 prefill: Q4_0 weights x Q8_0 activations for any number of tokens
+ * on the matrix cores (bw24 README, feature list: the int8 W4A8 tensor-core
+ * GEMM for prefill and the int8 expert GEMM).  The same product as
+ * qgemv_q4_0_a8 -- per 32-element block the exact int32 dot
+ * isum = sum (q_w - 8) * q_x, then acc = fma(d_w * d_x, isum, acc) in fp32,
+ * blocks in ascending order -- for m >= 1 (not limited to QG_MAX_M).  Each
+ * output depends only on its own token and row: bitwise reproducible and
+ * batch-invariant; it agrees with qgemv_q4_0_a8 to rounding (that kernel
+ * splits the blocks of a row over lanes).  w: device packed Q4_0 [n][k];
+ * xq / xd: device, from qg_quantize_q8_0_act ([m][k] int8, [m][k/32] fp16
+ * bits); y: device fp32 [m][n].  m up to 2^24 (else QG_EUNSUPPORTED). */
+int qgemm_prefill_a8(const void* w, int64_t n, int64_t k, const int8_t* xq, const uint16_t* xd, int64_t m,
+                     float* y, void* stream);
+
 /* K-quant / IQ4_XS weights x Q8_0 activations (memra README, feature list
  * "Decode kernels": K-quant split-plane matvecs with dp4a).  Per 32-element
  * block b of a row, with the block's activation scale d_x, codes q_x and

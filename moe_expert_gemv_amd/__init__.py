@@ -21,7 +21,7 @@ __all__ = [
     "QGError", "QGLibraryMissing", "LIB_PATH", "lib", "loaded",
     "QG_NVFP4", "QG_Q8_0", "QG_Q4_0", "QG_FP8_TENSOR", "QG_FP8_B128", "QG_MAX_M", "QG_MOE_KEEP_H",
     "QG_Q4_K", "QG_Q5_K", "QG_Q6_K", "QG_IQ4_XS", "KQUANT_FORMATS", "qg_pack_kquant", "qg_unpack_kquant",
-    "qgemv_kquant_a8",
+    "qgemv_kquant_a8", "qgemm_prefill_a8",
     "qg_abi_version", "qg_layout_version", "qg_status_string", "qg_packed_bytes",
     "qg_scale_plane_offset", "qg_pack_nvfp4", "qg_pack_nvfp4_gate_up", "qg_pack_q4_0", "qg_pack_q8_0",
     "qg_unpack_nvfp4", "qg_unpack_nvfp4_gate_up", "qg_unpack_q4_0", "qg_unpack_q8_0", "qg_pack_fp8",
@@ -104,6 +104,7 @@ _SIGNATURES = {
     "qg_pack_kquant": (_I32, [_I32, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ]),
     "qg_unpack_kquant": (_I32, [_I32, _P, _SZ, _I64, _I64, _P, _P, _P, _P, _P]),
     "qgemv_kquant_a8": (_I32, [_I32, _P, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
+    "qgemm_prefill_a8": (_I32, [_P, _I64, _I64, _P, _P, _I64, _P, _P]),
     "moe_route_topk": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "moe_workspace_bytes": (_SZ, [ctypes.POINTER(QgMoeDesc), _I64]),
     "moe_gemv_grouped": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _P, _I64, _P, _P, _SZ, _P]),
@@ -386,6 +387,11 @@ def qgemv_kquant_a8(fmt, w, n, k, xq, xd, xs, m, y, stream=None) -> None:
     _check("qgemv_kquant_a8",
            lib().qgemv_kquant_a8(fmt, _dptr(w), n, k, _dptr(xq), _dptr(xd), _dptr(xs), m, _dptr(y),
                                  _stream(stream)))
+
+
+def qgemm_prefill_a8(w, n, k, xq, xd, m, y, stream=None) -> None:
+    _check("qgemm_prefill_a8",
+           lib().qgemm_prefill_a8(_dptr(w), n, k, _dptr(xq), _dptr(xd), m, _dptr(y), _stream(stream)))
 
 
 def moe_route_topk(logits, t, n_experts, top_k, ids, weights, stream=None) -> None:

@@ -35,7 +35,8 @@ HIP_FLAGS = [
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
 
 HIP_SOURCES = ["qg_api.hip", "k_gemv_nvfp4.hip", "k_gemv_q8.hip", "k_gemv_a8.hip", "k_gemv_fp8.hip",
-               "k_gemv_kquant.hip", "k_dequant.hip", "k_moe.hip", "k_moe_prefill.hip", "k_prefill.hip"]
+               "k_gemv_kquant.hip", "k_dequant.hip", "k_moe.hip", "k_moe_prefill.hip", "k_prefill.hip",
+               "k_prefill_a8.hip"]
 CXX_SOURCES = ["qg_host.cpp"]
 
 

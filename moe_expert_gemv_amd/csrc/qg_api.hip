@@ -125,6 +125,15 @@ int qgemv_q4_0_a8(const void* w, int64_t n, int64_t k, const int8_t* xq, const u
                                       as_stream(stream)));
 }
 
+int qgemm_prefill_a8(const void* w, int64_t n, int64_t k, const int8_t* xq, const uint16_t* xd, int64_t m,
+                     float* y, void* stream) {
+    if (!w || !xq || !xd || !y) return QG_EINVAL;
+    if (!aligned(w, 256) || !aligned(xq, 16) || !aligned(xd, 2) || !aligned(y, 16)) return QG_EINVAL;
+    if (!valid_shape(n, k) || m < 1) return QG_EINVAL;
+    if (!prefill_a8_shape_ok(n, k, m)) return QG_EUNSUPPORTED;
+    return finish(launch_prefill_a8(static_cast<const uint8_t*>(w), n, k, xq, xd, m, y, as_stream(stream)));
+}
+
 int qgemv_kquant_a8(int fmt, const void* w, int64_t n, int64_t k, const int8_t* xq, const uint16_t* xd,
                     const int32_t* xs, int64_t m, float* y, void* stream) {
     if (!is_kquant(fmt)) return QG_EINVAL;

@@ -28,6 +28,9 @@ hipError_t launch_dequant_fp8(int fmt, const uint8_t* w, int64_t n, int64_t k, f
 hipError_t launch_gemv_kquant_a8(int fmt, const uint8_t* w, int64_t n, int64_t k, const int8_t* xq,
                                  const uint16_t* xd, const int32_t* xs, int m, float* y, hipStream_t s);
 hipError_t launch_dequant_kquant(int fmt, const uint8_t* w, int64_t n, int64_t k, float* out, hipStream_t s);
+bool prefill_a8_shape_ok(int64_t n, int64_t k, int64_t m);
+hipError_t launch_prefill_a8(const uint8_t* w, int64_t n, int64_t k, const int8_t* xq, const uint16_t* xd,
+                             int64_t m, float* y, hipStream_t s);
 hipError_t launch_gemv_nvfp4_swiglu(const uint8_t* w, float s_t, int64_t inter, int64_t k,
                                     const uint16_t* x, int m, uint16_t* a, float* h, hipStream_t s);
 hipError_t launch_quantize_q8_0(const float* x, int64_t m, int64_t k, int8_t* xq, uint16_t* xd,

@@ -356,3 +356,11 @@ def test_kquant_argument_checks(L):
     assert L.qgemv_kquant_a8(qg.QG_Q4_K, 256, 4, 224, 256, 256, 256, 1, 256, None) == qg.QG_EINVAL  # k % 256
     assert L.qgemv_kquant_a8(qg.QG_Q4_K, 256, 4, 256, 256, 256, None, 1, 256, None) == qg.QG_EINVAL  # xs required
     assert L.qgemv_kquant_a8(qg.QG_Q4_K, 256, 4, 256, 256, 256, 256, 17, 256, None) == qg.QG_EUNSUPPORTED
+
+
+def test_prefill_a8_argument_checks(L):
+    assert L.qgemm_prefill_a8(0, 4, 64, 256, 256, 1, 256, None) == qg.QG_EINVAL          # null w
+    assert L.qgemm_prefill_a8(256, 4, 48, 256, 256, 1, 256, None) == qg.QG_EINVAL        # k % 32
+    assert L.qgemm_prefill_a8(256, 4, 64, 256, 256, 0, 256, None) == qg.QG_EINVAL        # m < 1
+    assert L.qgemm_prefill_a8(264, 4, 64, 256, 256, 1, 256, None) == qg.QG_EINVAL        # w misaligned
+    assert L.qgemm_prefill_a8(256, 4, 64, 256, 256, 1 << 25, 256, None) == qg.QG_EUNSUPPORTED
