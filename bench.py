@@ -47,6 +47,7 @@ sys.path.insert(0, ROOT)
 METRIC = "quantized GEMV achieved HBM GB/s (% of ~8 TB/s) + µs/call, batch 1"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_INT8_TOPS = 5000.0
 ROTATE_BYTES = 1 << 30
 
 
@@ -94,6 +95,7 @@ class Workload:
     name = ""
     dominant = ""
     bound = "hbm"
+    mfma_peak = (PEAK_BF16_TFLOPS, "TFLOP/s")  # dense peak of the contraction's dtype
     sources: tuple = ()     # files under csrc/ the dominant kernel(s) are built from
     kernel_re: tuple = ()   # one dominant launch = one dispatch of each of these kernels
 
@@ -471,6 +473,44 @@ class Prefill(Workload):
     dominant_launch = step
 
 
+class PrefillA8(Workload):
+    """W4A8 prefill on the int8 matrix cores: Q8_0-quantized fp32 activations
+    [m x 5120] times the 27B-class Q4_0 projection [17408 x 5120], fp32 out."""
+    sources = ("k_prefill_a8.hip",)
+    kernel_re = (r"k_prefill_a8\b",)
+    bound = "mfma"
+    mfma_peak = (PEAK_INT8_TOPS, "TOP/s")
+
+    def __init__(self, m=512):
+        import torch
+        import moe_expert_gemv_amd as qg
+        import synth
+
+        self.qg, self.m = qg, m
+        self.N, self.K = 17408, 5120
+        case = synth.w4a8_case(m=m)
+        buf = qg.qg_pack_q4_0(case.w["codes"], case.w["scales"])
+        self.R = _copies(buf.nbytes)
+        self.w = torch.from_numpy(buf).cuda().repeat(self.R, 1)
+        self.x = torch.from_numpy(case.x).cuda()
+        N, K = self.N, self.K
+        self.xq = torch.empty((m, K), dtype=torch.int8, device="cuda")
+        self.xd = torch.empty((m, K // 32), dtype=torch.int16, device="cuda")
+        self.y = torch.empty((m, N), dtype=torch.float32, device="cuda")
+        self.dominant_bytes = N * K // 2 + N * (K // 32) * 2 + m * (K + K // 32 * 2) + 4 * m * N
+        self.alg_step = self.dominant_bytes + m * K * 4 + m * (K + K // 32 * 2)
+        self.flops_step = 2 * m * N * K
+        self.name = f"W4A8 prefill (int8 MFMA): q8_0 X [{m}x{K}] x q4_0 W [{N}x{K}] (27B-class), fp32 out"
+        self.dominant = "W4A8 prefill int8 MFMA GEMM"
+
+    def step(self, i):
+        self.qg.qg_quantize_q8_0_act(self.x, self.m, self.K, self.xq, self.xd, None)
+        self.dominant_launch(i)
+
+    def dominant_launch(self, i):
+        self.qg.qgemm_prefill_a8(self.w[i % self.R], self.N, self.K, self.xq, self.xd, self.m, self.y)
+
+
 class PrefillWs(Prefill):
     """m <= 128: the workspace variant (k split into slices of 1024 over
     workgroups, then a fixed-order sum of the slices' partials)."""
@@ -511,6 +551,7 @@ CONFIGS = {  # name -> (workload class, its size argument)
     "prefill64": (PrefillWs, 64),
     "prefill128": (PrefillWs, 128),
     "prefill512": (Prefill, 512),
+    "w4a8-prefill512": (PrefillA8, 512),
 }
 
 
@@ -750,8 +791,8 @@ def main():
 
     if wl.bound == "mfma":
         achieved = wl.flops_step / (dom_mean * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS}
+        peak, unit = wl.mfma_peak
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak}
     else:
         achieved = wl.dominant_bytes / (dom_mean * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",

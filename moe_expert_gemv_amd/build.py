@@ -38,6 +38,10 @@ HIP_SOURCES = ["qg_api.hip", "k_gemv_nvfp4.hip", "k_gemv_q8.hip", "k_gemv_a8.hip
                "k_gemv_kquant.hip", "k_dequant.hip", "k_moe.hip", "k_moe_prefill.hip", "k_prefill.hip",
                "k_prefill_a8.hip"]
 CXX_SOURCES = ["qg_host.cpp"]
+# Per-source compiler options.  The int8 prefill reads every MFMA result back
+# into VALU arithmetic; the VGPR form of the MFMA saves a v_accvgpr_read per
+# output per block.
+HIP_FILE_FLAGS = {"k_prefill_a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _run(cmd: list[str]) -> None:
@@ -57,7 +61,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     cmds, objs = [], []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        cmds.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *HIP_FLAGS, *HIP_FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".cpp", ".host.o"))

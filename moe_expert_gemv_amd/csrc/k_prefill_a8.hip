@@ -42,9 +42,12 @@ constexpr int kMB = 4;                    // 16-token tiles per wave
 constexpr int kNB = 2;                    // 16-row tiles per wave
 constexpr int kTM = 16 * kMB;             // tokens per workgroup
 constexpr int kTN = 16 * kNB * kWaves;    // rows per workgroup
-constexpr int kChunk = 128;               // blocks whose activation scales sit in LDS at once
-constexpr int kPitch = kTM + 4;           // LDS floats per block (padded, keeps 16-byte alignment)
+constexpr int kS = 4;                     // 32-element blocks per stage
+constexpr int kAL = kTM * 2 * kS / kThreads;  // 16-byte activation loads per thread per stage
+constexpr int kBL = kTN * kS / kThreads;      // 16-byte weight loads per thread per stage
 constexpr int kXcds = 8;
+static_assert(kAL * kThreads == kTM * 2 * kS && kBL * kThreads == kTN * kS, "whole loads per thread");
+static_assert(kS == 4 && kTN + kTM <= kThreads, "scale loads: one thread per row or token, two dwords of 2 blocks");
 
 // Four Q4_0 codes (bytes 0..15) -> the int8 values q - 8.
 __device__ __forceinline__ uint32_t q4_to_s8(uint32_t q) {
@@ -52,18 +55,28 @@ __device__ __forceinline__ uint32_t q4_to_s8(uint32_t q) {
     return (q & 0x07070707u) | neg;
 }
 
-// One block's operands of one wave.
-struct Stage {
-    uint64_t a[kMB];       // activation codes, 8 per lane per token tile
-    uint32_t b[kNB][2];    // 8 raw code bytes per lane per row tile
-    uint32_t dw[kNB];      // weight scale (fp16 bits)
+// One stage of the workgroup's operands in LDS, block-major.
+struct Tile {
+    uint8_t a[kS][kTM][32];   // activation codes: block, token, 32 bytes
+    uint8_t b[kS][kTN][16];   // weight codes: block, row, the block's 16 bytes
+    float dx[kS][kTM];        // activation scales (fp32)
+    uint16_t dw[kS][kTN];     // weight scales (fp16 bits; 0 for blocks past k)
+};
+
+// The global loads of one stage, held in registers between the load and
+// the LDS store (all 16-byte loads are whole-line reads of contiguous runs).
+struct Regs {
+    u32x4 a[kAL];
+    u32x4 b[kBL];
+    uint16_t dx[kS];
+    uint32_t dw[2];
 };
 
 __global__ __launch_bounds__(kThreads) void k_prefill_a8(const uint8_t* __restrict__ w, int64_t soff, int n,
                                                          int k, const int8_t* __restrict__ xq,
                                                          const uint16_t* __restrict__ xd, int m,
                                                          float* __restrict__ y, int m_blocks, int items) {
-    __shared__ __attribute__((aligned(16))) float xd_s[kChunk * kPitch];
+    __shared__ Tile tile[2];
 
     // work item -> (row block, token block): each XCD takes a contiguous run
     // of items, so the token blocks of one row block share its L2
@@ -71,38 +84,68 @@ __global__ __launch_bounds__(kThreads) void k_prefill_a8(const uint8_t* __restri
     const int item = int(blockIdx.x) % kXcds * per_xcd + int(blockIdx.x) / kXcds;
     if (item >= items) return;
     const int t0 = item % m_blocks * kTM;
-    const int rblk = item / m_blocks;
+    const int n0 = item / m_blocks * kTN;
 
     const int tid = int(threadIdx.x);
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lr = lane & 15, g = lane >> 4;
     const int nb = k / 32;
-    const int r0 = rblk * kTN + wave * 16 * kNB;
+    const int nst = (nb + kS - 1) / kS;
+    const int64_t crow = k / 2, srow = k / 16;
 
-    const uint8_t* crow[kNB];
-    const uint8_t* srow[kNB];
+    // stage loads: activations (token, 16-byte part), weights (row, block),
+    // the weight scales of 4 blocks of one row (one 8-byte run, read as two
+    // dwords), the activation scales of one token (4 fp16)
+    auto gload = [&](Regs& r, int st) {
+        const int b0 = st * kS;
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) {
-        const int64_t row = min(r0 + 16 * j + lr, n - 1);
-        crow[j] = w + row * (k / 2) + 8 * (g & 1);
-        srow[j] = w + soff + row * (k / 16);
-    }
-    const int8_t* arow[kMB];
-#pragma unroll
-    for (int i = 0; i < kMB; ++i) arow[i] = xq + int64_t(min(t0 + 16 * i + lr, m - 1)) * k + 8 * g;
-    const int shift = 4 * (g >> 1);
-
-    auto load = [&](Stage& s, int blk) {
-#pragma unroll
-        for (int j = 0; j < kNB; ++j) {
-            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(crow[j] + 16 * blk));
-            s.b[j][0] = v[0];
-            s.b[j][1] = v[1];
-            s.dw[j] = ld<uint16_t>(srow[j] + 2 * blk);
+        for (int i = 0; i < kAL; ++i) {
+            const int c = tid + kThreads * i;
+            const int tok = c / (2 * kS), part = c % (2 * kS);
+            const int blk = min(b0 + part / 2, nb - 1);
+            r.a[i] = ld16(xq + int64_t(min(t0 + tok, m - 1)) * k + 32 * blk + 16 * (part % 2));
         }
 #pragma unroll
-        for (int i = 0; i < kMB; ++i) s.a[i] = ld<uint64_t>(arow[i] + 32 * blk);
+        for (int i = 0; i < kBL; ++i) {
+            const int c = tid + kThreads * i;
+            const int row = c / kS, blk = min(b0 + c % kS, nb - 1);
+            r.b[i] = ld_stream16(w + int64_t(min(n0 + row, n - 1)) * crow + 16 * blk);
+        }
+        if (tid < kTN) {
+            const uint8_t* sp = w + soff + int64_t(min(n0 + tid, n - 1)) * srow;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int ba = min(b0 + 2 * h, nb - 1), bb = min(b0 + 2 * h + 1, nb - 1);
+                r.dw[h] = uint32_t(ld<uint16_t>(sp + 2 * ba)) | (uint32_t(ld<uint16_t>(sp + 2 * bb)) << 16);
+            }
+        } else if (tid < kTN + kTM) {
+            const uint16_t* xp = xd + int64_t(min(t0 + tid - kTN, m - 1)) * nb;
+#pragma unroll
+            for (int j = 0; j < kS; ++j) r.dx[j] = xp[min(b0 + j, nb - 1)];
+        }
+    };
+    auto lstore = [&](Tile& T, const Regs& r, int st) {
+        const int b0 = st * kS;
+#pragma unroll
+        for (int i = 0; i < kAL; ++i) {
+            const int c = tid + kThreads * i;
+            const int tok = c / (2 * kS), part = c % (2 * kS);
+            *reinterpret_cast<u32x4*>(&T.a[part / 2][tok][16 * (part % 2)]) = r.a[i];
+        }
+#pragma unroll
+        for (int i = 0; i < kBL; ++i) {
+            const int c = tid + kThreads * i;
+            *reinterpret_cast<u32x4*>(&T.b[c % kS][c / kS][0]) = r.b[i];
+        }
+        if (tid < kTN) {
+#pragma unroll
+            for (int j = 0; j < kS; ++j)  // blocks past k scale by zero
+                T.dw[j][tid] = b0 + j < nb ? uint16_t(r.dw[j / 2] >> (16 * (j % 2))) : uint16_t(0);
+        } else if (tid < kTN + kTM) {
+#pragma unroll
+            for (int j = 0; j < kS; ++j) T.dx[j][tid - kTN] = f16_to_f32(r.dx[j]);
+        }
     };
 
     floatx4 acc[kMB][kNB];
@@ -111,66 +154,66 @@ __global__ __launch_bounds__(kThreads) void k_prefill_a8(const uint8_t* __restri
 #pragma unroll
         for (int j = 0; j < kNB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const Stage& s, int jj) {
-        uint64_t bf[kNB];
-        float dwf[kNB];
-#pragma unroll
-        for (int j = 0; j < kNB; ++j) {
-            const uint32_t lo = q4_to_s8((s.b[j][0] >> shift) & 0x0F0F0F0Fu);
-            const uint32_t hi = q4_to_s8((s.b[j][1] >> shift) & 0x0F0F0F0Fu);
-            bf[j] = uint64_t(lo) | (uint64_t(hi) << 32);
-            dwf[j] = f16_to_f32(s.dw[j]);
-        }
-#pragma unroll
-        for (int i = 0; i < kMB; ++i) {
-            const floatx4 dx = *reinterpret_cast<const floatx4*>(&xd_s[jj * kPitch + 16 * i + 4 * g]);
+    const int rw = wave * 16 * kNB;  // this wave's first row in the tile
+    const int shift = 4 * (g >> 1);
+    // One stage: per block the eight tile products first (independent, so
+    // the matrix core pipelines them), then the scale steps.
+    auto compute = [&](const Tile& T) {
+#pragma unroll 1
+        for (int t = 0; t < kS; ++t) {
+            uint64_t bf[kNB];
+            float dwf[kNB];
 #pragma unroll
             for (int j = 0; j < kNB; ++j) {
-                const i32x4 isum = __builtin_amdgcn_mfma_i32_16x16x32_i8(long(s.a[i]), long(bf[j]),
-                                                                         i32x4{0, 0, 0, 0}, 0, 0, 0);
+                const int row = rw + 16 * j + lr;
+                const u32x2 v = *reinterpret_cast<const u32x2*>(&T.b[t][row][8 * (g & 1)]);
+                const uint32_t lo = q4_to_s8((v[0] >> shift) & 0x0F0F0F0Fu);
+                const uint32_t hi = q4_to_s8((v[1] >> shift) & 0x0F0F0F0Fu);
+                bf[j] = uint64_t(lo) | (uint64_t(hi) << 32);
+                dwf[j] = f16_to_f32(T.dw[t][row]);
+            }
+            i32x4 isum[kMB][kNB];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(dwf[j] * dx[v], float(isum[v]), acc[i][j][v]);
+            for (int i = 0; i < kMB; ++i) {
+                const uint64_t a = *reinterpret_cast<const uint64_t*>(&T.a[t][16 * i + lr][8 * g]);
+#pragma unroll
+                for (int j = 0; j < kNB; ++j)
+                    isum[i][j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(long(a), long(bf[j]), i32x4{0, 0, 0, 0},
+                                                                       0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < kMB; ++i) {
+                const floatx4 dx = *reinterpret_cast<const floatx4*>(&T.dx[t][16 * i + 4 * g]);
+#pragma unroll
+                for (int j = 0; j < kNB; ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[i][j][v] = fmaf(dwf[j] * dx[v], float(isum[i][j][v]), acc[i][j][v]);
             }
         }
     };
 
-    for (int c0 = 0; c0 < nb; c0 += kChunk) {
-        const int len = min(kChunk, nb - c0);
-        // activation scales of this chunk into LDS, block-major (tokens past
-        // m repeat the last token; their outputs are not stored)
-        if (c0 > 0) __syncthreads();
-        for (int i = tid; i < kTM * len; i += kThreads) {
-            const int tok = i / len, jj = i % len;
-            const int t = min(t0 + tok, m - 1);
-            xd_s[jj * kPitch + tok] = f16_to_f32(xd[int64_t(t) * nb + c0 + jj]);
-        }
+    // double-buffered stages: the next stage's global loads are in flight
+    // while this one computes; one barrier per stage
+    Regs r;
+    gload(r, 0);
+    lstore(tile[0], r, 0);
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+        const int nx = min(st + 1, nst - 1);  // the last stage reloads itself into the idle buffer
+        gload(r, nx);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(tile[st & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(tile[(st + 1) & 1], r, nx);
         __syncthreads();
-
-        // four blocks of operands in flight; block indices past the chunk
-        // load the chunk's last block again (valid) and are not computed
-        Stage s0, s1, s2, s3;
-        const int last = c0 + len - 1;
-        load(s0, c0);
-        load(s1, min(c0 + 1, last));
-        load(s2, min(c0 + 2, last));
-        load(s3, min(c0 + 3, last));
-        for (int jj = 0; jj < len; jj += 4) {
-            compute(s0, jj);
-            load(s0, min(c0 + jj + 4, last));
-            if (jj + 1 < len) compute(s1, jj + 1);
-            load(s1, min(c0 + jj + 5, last));
-            if (jj + 2 < len) compute(s2, jj + 2);
-            load(s2, min(c0 + jj + 6, last));
-            if (jj + 3 < len) compute(s3, jj + 3);
-            load(s3, min(c0 + jj + 7, last));
-        }
     }
 
 #pragma unroll
     for (int i = 0; i < kMB; ++i)
 #pragma unroll
         for (int j = 0; j < kNB; ++j) {
-            const int row = r0 + 16 * j + lr;
+            const int row = n0 + rw + 16 * j + lr;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int t = t0 + 16 * i + 4 * g + v;
