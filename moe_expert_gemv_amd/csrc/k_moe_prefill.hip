@@ -198,16 +198,26 @@ struct GemmArgs {
 // K = 256 * KS.  SWIGLU: activations gathered by token, output a (and h);
 // else activations are the pairs' own rows of a, output o.
 template <int KS, bool SWIGLU>
-__global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace ws, const int32_t* __restrict__ tile_off,
+__global__ __launch_bounds__(kPfBlock, KS == 8 ? 4 : 2) void k_mpf_gemm(GemmArgs A, MoeWorkspace ws, const int32_t* __restrict__ tile_off,
                                                        int n_blocks, int items) {
     constexpr int K = 2 * KW * KS;          // reduction length
     constexpr int MB = kPfPairs / 16, NB = kPfNB;
-    constexpr int CPR = K / 8;              // 16-byte chunks per LDS row
-    constexpr int NCP = kPfPairs * CPR / kPfBlock;  // activation chunks per thread
-    constexpr int WD = KS < 4 ? KS : 4;     // weight slabs in flight per wave
+    // K >= 1024 is gathered in passes of 512 k through the same LDS (and the
+    // halves' sums are exchanged in that space afterwards): 32 KB and few
+    // staging registers, so two workgroups share a CU and one's gathers and
+    // epilogue overlap the other's weight stream.
+    constexpr int NP = KS >= 4 ? KS / 2 : 1;  // activation passes (512 k each from K = 1024)
+    constexpr int KP = K / NP;              // k per pass
+    constexpr int SP = KS / NP;             // weight stages (256 k) per pass
+    constexpr int CPR = KP / 8;             // 16-byte chunks per LDS row
+    constexpr int NCP = kPfPairs * CPR / kPfBlock;  // activation chunks per thread per pass
+    constexpr int WD = 2;                    // weight slabs in flight per wave
+    constexpr int RED = 4 * MB * NB * 4 * kWave;  // floats of the second half's sums
     static_assert(CPR >= 16 && (CPR & (CPR - 1)) == 0, "rows of a power-of-two count of 16 chunks");
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kPfPairs * K];
-    __shared__ float red_s[4 * MB * NB * 4 * kWave];  // the second half's sums (own region: one barrier)
+    static_assert(NP == 1 || 2 * RED <= kPfPairs * KP, "the sums fit in the activation tile's space");
+    static_assert(KS % NP == 0 && SP >= 1, "whole weight stages per pass");
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kPfPairs * KP];
+    __shared__ float red_own[NP == 1 ? RED : 1];  // one pass: a region of its own (one barrier)
 
     const int tid = int(threadIdx.x);
     const int lane = tid & 63;
@@ -242,14 +252,22 @@ __global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace 
 
     // 1. activation rows into registers (rows past np repeat the last pair)
     u32x4 xr[NCP];
+    auto x_load = [&](int pass) {
 #pragma unroll
-    for (int i = 0; i < NCP; ++i) {
-        const int p = (wave + 8 * i) * kWave + lane;
-        const int row = p / CPR, c = (p % CPR) ^ (row & 15);
-        const int pos = p0 + min(row, np - 1);
-        const int srow = SWIGLU ? ws.pair_tok[pos] : pos;
-        xr[i] = ld16(A.src + int64_t(srow) * K + 8 * c);
-    }
+        for (int i = 0; i < NCP; ++i) {
+            const int p = (wave + 8 * i) * kWave + lane;
+            const int row = p / CPR, c = (p % CPR) ^ (row & 15);
+            const int pos = p0 + min(row, np - 1);
+            const int srow = SWIGLU ? ws.pair_tok[pos] : pos;
+            xr[i] = ld16(A.src + int64_t(srow) * K + pass * KP + 8 * c);
+        }
+    };
+    auto x_store = [&]() {
+#pragma unroll
+        for (int i = 0; i < NCP; ++i)
+            *reinterpret_cast<u32x4*>(&xs[8 * ((wave + 8 * i) * kWave + lane)]) = xr[i];
+    };
+    x_load(0);
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. weight slabs: slab j of this wave covers k = 128 (2 j + half) + [0, 128)
@@ -280,9 +298,7 @@ __global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace 
 
     // 3. publish the activation tile (the loads complete in order, ahead of
     // the weight loads; the LDS-only barrier leaves those in flight)
-#pragma unroll
-    for (int i = 0; i < NCP; ++i)
-        *reinterpret_cast<u32x4*>(&xs[8 * ((wave + 8 * i) * kWave + lane)]) = xr[i];
+    x_store();
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -296,6 +312,16 @@ __global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace 
         for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
+        if (NP > 1 && j > 0 && j % SP == 0) {
+            // next pass: every wave is done with the previous part of the
+            // tile; gather the next part into the same space
+            __builtin_amdgcn_sched_barrier(0);
+            x_load(j / SP);
+            lds_barrier();
+            x_store();
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        }
         const WStage<NB> cur = wr[j % WD];
         if (j + WD < KS) w_load(wr[j % WD], j + WD);
         __builtin_amdgcn_sched_barrier(0);
@@ -307,7 +333,7 @@ __global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace 
                 const float sc = (q < 2) ? e4m3_to_f32<0>(cur.s[nb]) : e4m3_to_f32<1>(cur.s[nb]);
                 bfr[nb] = decode8_scaled(cur.c[nb][q], sc);
             }
-            const int c = 16 * (2 * j + half) + 4 * lg + q;
+            const int c = 16 * (2 * (j % SP) + half) + 4 * lg + q;  // chunk within the pass
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = 16 * mb + lr;
@@ -319,7 +345,8 @@ __global__ __launch_bounds__(kPfBlock) void k_mpf_gemm(GemmArgs A, MoeWorkspace 
     }
 
     // 4. second half + first half, in that order, through LDS
-    float* red = red_s + rs * (MB * NB * 4 * kWave);
+    float* red = (NP == 1 ? red_own : reinterpret_cast<float*>(xs)) + rs * (MB * NB * 4 * kWave);
+    if constexpr (NP > 1) lds_barrier();  // every wave is done reading the tile
     if (half == 1) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
