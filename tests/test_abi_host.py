@@ -364,3 +364,16 @@ def test_prefill_a8_argument_checks(L):
     assert L.qgemm_prefill_a8(256, 4, 64, 256, 256, 0, 256, None) == qg.QG_EINVAL        # m < 1
     assert L.qgemm_prefill_a8(264, 4, 64, 256, 256, 1, 256, None) == qg.QG_EINVAL        # w misaligned
     assert L.qgemm_prefill_a8(256, 4, 64, 256, 256, 1 << 25, 256, None) == qg.QG_EUNSUPPORTED
+
+
+def test_new_entry_points_reject_empty_and_null(L):
+    """Zero tokens, zero rows and null activation scales are argument errors
+    (checked on the host before anything is enqueued)."""
+    assert L.qgemv_kquant_a8(qg.QG_Q6_K, 256, 4, 256, 256, 256, 256, 0, 256, None) == qg.QG_EINVAL  # m = 0
+    assert L.qgemv_kquant_a8(qg.QG_Q6_K, 256, 0, 256, 256, 256, 256, 1, 256, None) == qg.QG_EINVAL  # n = 0
+    assert L.qgemv_kquant_a8(qg.QG_IQ4_XS, 256, 4, 256, 256, None, 256, 1, 256, None) == qg.QG_EINVAL  # xd
+    assert L.qgemm_prefill_a8(256, 0, 64, 256, 256, 4, 256, None) == qg.QG_EINVAL  # n = 0
+    assert L.qgemm_prefill_a8(256, 4, 64, 256, None, 4, 256, None) == qg.QG_EINVAL  # xd
+    assert L.qgemm_prefill_a8(256, 4, 64, 256, 256, 4, None, None) == qg.QG_EINVAL  # y
+    for fmt in qg.KQUANT_FORMATS:
+        assert qg.qg_packed_bytes(fmt, 1, 128) == 0 and qg.qg_packed_bytes(fmt, 1, 256) > 0
