@@ -13,11 +13,12 @@
 //      expert; inside an expert, pairs in (token, slot) order -- a stable
 //      placement, so the CSR is exactly the decode path's) and the tile table
 //      of the GEMMs (kPfPairs pairs per tile);
-//   3. k_mpf_gemm<SWIGLU>: one workgroup per (tile, block of 192 weight
-//      rows): the tile's activation rows are gathered into LDS, the expert's
-//      NVFP4 rows decoded straight into MFMA fragments (eight waves, two per
-//      SIMD, on alternate 128-k slabs, added through LDS in a fixed order);
-//      gate/up rows are interleaved, so SwiGLU pairs adjacent columns;
+//   3. k_mpf_gemm<SWIGLU>: one workgroup per (tile, block of 256 weight
+//      rows): the tile's activation rows are gathered into LDS (in passes of
+//      512 k), the expert's NVFP4 rows decoded straight into MFMA fragments
+//      (eight waves, each on 32 rows over the whole k range, one MFMA chain
+//      per output); gate/up rows are interleaved, so SwiGLU pairs adjacent
+//      columns;
 //   4. k_mpf_combine: y = sum over slots of w * o, then + o_shared, in that
 //      order (the decode path's order).
 #include <hip/hip_runtime.h>
@@ -35,8 +36,8 @@ namespace {
 
 constexpr int kPfPairs = 32;    // pairs per GEMM tile (two 16-row MFMA blocks)
 constexpr int kPfBlock = 512;   // GEMM workgroup: eight waves
-constexpr int kPfNB = 3;        // 16-row weight blocks per wave
-constexpr int kPfBN = 16 * kPfNB * 4;  // weight rows per GEMM workgroup: 192
+constexpr int kPfNB = 2;        // 16-row weight blocks per wave
+constexpr int kPfBN = 16 * kPfNB * (kPfBlock / 64);  // weight rows per GEMM workgroup: 256
 // Workgroups are dealt to the XCDs round-robin by launch index, and each XCD
 // has an L2 of its own; the GEMM grid is remapped so that neighbouring work
 // items (the row blocks of one tile, which gather the same activation rows)
@@ -198,31 +199,28 @@ struct GemmArgs {
 // K = 256 * KS.  SWIGLU: activations gathered by token, output a (and h);
 // else activations are the pairs' own rows of a, output o.
 template <int KS, bool SWIGLU>
-__global__ __launch_bounds__(kPfBlock, KS == 8 ? 4 : 2) void k_mpf_gemm(GemmArgs A, MoeWorkspace ws, const int32_t* __restrict__ tile_off,
-                                                       int n_blocks, int items) {
+__global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspace ws,
+                                                          const int32_t* __restrict__ tile_off, int n_blocks,
+                                                          int items) {
     constexpr int K = 2 * KW * KS;          // reduction length
+    constexpr int NS = K / KW;              // 128-k weight slabs
     constexpr int MB = kPfPairs / 16, NB = kPfNB;
-    // K >= 1024 is gathered in passes of 512 k through the same LDS (and the
-    // halves' sums are exchanged in that space afterwards): 32 KB and few
-    // staging registers, so two workgroups share a CU and one's gathers and
-    // epilogue overlap the other's weight stream.
-    constexpr int NP = KS >= 4 ? KS / 2 : 1;  // activation passes (512 k each from K = 1024)
-    constexpr int KP = K / NP;              // k per pass
-    constexpr int SP = KS / NP;             // weight stages (256 k) per pass
+    // The tile's activations are gathered in passes of 512 k through the same
+    // 32 KB of LDS, so two workgroups share a CU and one's gathers overlap
+    // the other's weight stream.
+    constexpr int KP = K < 512 ? K : 512;   // k per pass
+    constexpr int NP = K / KP;              // passes
+    constexpr int SPP = KP / KW;            // slabs per pass
     constexpr int CPR = KP / 8;             // 16-byte chunks per LDS row
     constexpr int NCP = kPfPairs * CPR / kPfBlock;  // activation chunks per thread per pass
-    constexpr int WD = 2;                    // weight slabs in flight per wave
-    constexpr int RED = 4 * MB * NB * 4 * kWave;  // floats of the second half's sums
+    constexpr int WD = KS >= 8 ? 3 : 4;     // weight slabs in flight per wave (within 128 VGPRs)
     static_assert(CPR >= 16 && (CPR & (CPR - 1)) == 0, "rows of a power-of-two count of 16 chunks");
-    static_assert(NP == 1 || 2 * RED <= kPfPairs * KP, "the sums fit in the activation tile's space");
-    static_assert(KS % NP == 0 && SP >= 1, "whole weight stages per pass");
+    static_assert(K % KP == 0 && NCP * kPfBlock == kPfPairs * CPR && NS >= WD, "pass and slab shapes");
     __shared__ __attribute__((aligned(16))) uint16_t xs[kPfPairs * KP];
-    __shared__ float red_own[NP == 1 ? RED : 1];  // one pass: a region of its own (one barrier)
 
     const int tid = int(threadIdx.x);
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rs = wave % 4, half = wave / 4;
     const int lr = lane & 15, lg = lane >> 4;
 
     // work item (XCD-contiguous over the real items, so every XCD gets an
@@ -246,7 +244,7 @@ __global__ __launch_bounds__(kPfBlock, KS == 8 ? 4 : 2) void k_mpf_gemm(GemmArgs
     const int e = ws.experts[g];
     const int p0 = ws.offsets[g] + (ty - tile_off[g]) * kPfPairs;
     const int np = min(kPfPairs, ws.offsets[g + 1] - p0);  // >= 1
-    const int n0 = nblk * kPfBN + rs * 16 * NB;
+    const int n0 = nblk * kPfBN + wave * 16 * NB;           // this wave's first weight row
     const uint8_t* w = A.w + int64_t(e) * A.stride;
     const float s_t = A.scale[e];
 
@@ -270,7 +268,7 @@ __global__ __launch_bounds__(kPfBlock, KS == 8 ? 4 : 2) void k_mpf_gemm(GemmArgs
     x_load(0);
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. weight slabs: slab j of this wave covers k = 128 (2 j + half) + [0, 128)
+    // 2. weight slabs: slab s covers k = 128 s + [0, 128) of this wave's rows
     const uint8_t* wc[NB];
     const uint8_t* wsc[NB];
 #pragma unroll
@@ -279,8 +277,8 @@ __global__ __launch_bounds__(kPfBlock, KS == 8 ? 4 : 2) void k_mpf_gemm(GemmArgs
         wc[nb] = w + row * (K / 2);
         wsc[nb] = w + A.soff + row * (K / 16);
     }
-    auto w_load = [&](WStage<NB>& b, int j) {
-        const int kb = KW * (2 * j + half) + 32 * lg;
+    auto w_load = [&](WStage<NB>& b, int sl) {
+        const int kb = KW * sl + 32 * lg;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const u32x4 v = ld_stream16(wc[nb] + kb / 2);
@@ -305,25 +303,26 @@ __global__ __launch_bounds__(kPfBlock, KS == 8 ? 4 : 2) void k_mpf_gemm(GemmArgs
     for (int j = 1; j < WD; ++j) w_load(wr[j], j);
     __builtin_amdgcn_sched_barrier(0);
 
+    // 4. one MFMA chain per output over the slabs in order
     floatx4 acc[MB][NB];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
-        if (NP > 1 && j > 0 && j % SP == 0) {
+    for (int sl = 0; sl < NS; ++sl) {
+        if (NP > 1 && sl > 0 && sl % SPP == 0) {
             // next pass: every wave is done with the previous part of the
             // tile; gather the next part into the same space
             __builtin_amdgcn_sched_barrier(0);
-            x_load(j / SP);
+            x_load(sl / SPP);
             lds_barrier();
             x_store();
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
         }
-        const WStage<NB> cur = wr[j % WD];
-        if (j + WD < KS) w_load(wr[j % WD], j + WD);
+        const WStage<NB> cur = wr[sl % WD];
+        if (sl + WD < NS) w_load(wr[sl % WD], sl + WD);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -333,7 +332,7 @@ __global__ __launch_bounds__(kPfBlock, KS == 8 ? 4 : 2) void k_mpf_gemm(GemmArgs
                 const float sc = (q < 2) ? e4m3_to_f32<0>(cur.s[nb]) : e4m3_to_f32<1>(cur.s[nb]);
                 bfr[nb] = decode8_scaled(cur.c[nb][q], sc);
             }
-            const int c = 16 * (2 * (j % SP) + half) + 4 * lg + q;  // chunk within the pass
+            const int c = 16 * (sl % SPP) + 4 * lg + q;  // chunk within the pass
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = 16 * mb + lr;
@@ -344,26 +343,14 @@ __global__ __launch_bounds__(kPfBlock, KS == 8 ? 4 : 2) void k_mpf_gemm(GemmArgs
         }
     }
 
-    // 4. second half + first half, in that order, through LDS
-    float* red = (NP == 1 ? red_own : reinterpret_cast<float*>(xs)) + rs * (MB * NB * 4 * kWave);
-    if constexpr (NP > 1) lds_barrier();  // every wave is done reading the tile
-    if (half == 1) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) red[((mb * NB + nb) * 4 + v) * kWave + lane] = acc[mb][nb][v];
-    }
-    __syncthreads();
-    if (half != 0) return;
+    // 5. epilogue, per wave: tensor scale, then SwiGLU or the plain output
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const float sum = (acc[mb][nb][v] + red[((mb * NB + nb) * 4 + v) * kWave + lane]) * s_t;
+                const float sum = acc[mb][nb][v] * s_t;
                 const int row = 16 * mb + 4 * lg + v;  // pair of the tile
                 const int col = n0 + 16 * nb + lr;     // weight row
                 if constexpr (SWIGLU) {
