@@ -443,7 +443,7 @@ class MoEPrefill(MoE):
 
 
 class Prefill(Workload):
-    sources = ("k_prefill.hip",)
+    sources = ("k_prefill.hip", "qg_mfma.hpp")
     kernel_re = (r"k_prefill8?\b",)
 
     def __init__(self, m=512):
@@ -476,7 +476,7 @@ class Prefill(Workload):
 class PrefillA8(Workload):
     """W4A8 prefill on the int8 matrix cores: Q8_0-quantized fp32 activations
     [m x 5120] times the 27B-class Q4_0 projection [17408 x 5120], fp32 out."""
-    sources = ("k_prefill_a8.hip",)
+    sources = ("k_prefill_a8.hip", "qg_mfma.hpp")
     kernel_re = (r"k_prefill_a8\b",)
     bound = "mfma"
     mfma_peak = (PEAK_INT8_TOPS, "TOP/s")

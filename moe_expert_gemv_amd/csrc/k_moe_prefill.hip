@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
         const int kb = KW * sl + 32 * lg;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const u32x4 v = ld_stream16(wc[nb] + kb / 2);
+            const u32x4 v = ld16(wc[nb] + kb / 2);  // fragment-shaped: ordinary loads (see k_prefill.hip)
 #pragma unroll
             for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
             b.s[nb] = ld<uint16_t>(wsc[nb] + kb / 16);

@@ -41,6 +41,11 @@
 
 namespace qg {
 
+// Weight reads here are fragment-shaped (16 rows x 64 bytes per wave
+// instruction), so each 128-byte line is read in two parts by different
+// instructions: ordinary loads keep the line for the second part (the
+// non-temporal form the GEMVs use measured about 10% slower here).
+
 namespace {
 
 constexpr int kBlock = 256;
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(kBlock) void k_prefill(const uint8_t* __restrict__ 
         const int kc = kl < k ? kl : 0;  // lanes past the end read the row start
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const u32x4 v = ld_stream16(wc[nb] + kc / 2);
+            const u32x4 v = ld16(wc[nb] + kc / 2);
 #pragma unroll
             for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
             b.s[nb] = ld<uint16_t>(ws[nb] + kc / 16);
@@ -312,7 +317,7 @@ __global__ __launch_bounds__(512) void k_prefill8(const uint8_t* __restrict__ w,
         const int kl = (st < nst ? st : 0) * BK + wk * KW + lg * (KW / 4);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const u32x4 v = ld_stream16(wc[nb] + kl / 2);
+            const u32x4 v = ld16(wc[nb] + kl / 2);
 #pragma unroll
             for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
             b.s[nb] = ld<uint16_t>(ws[nb] + kl / 16);
@@ -446,7 +451,7 @@ __global__ __launch_bounds__(kBlock) void k_prefill_ks(const uint8_t* __restrict
         const int kc = kb < k ? kb : 0;  // past the end: the row's own first block
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const u32x4 v = ld_stream16(wc[nb] + kc / 2);
+            const u32x4 v = ld16(wc[nb] + kc / 2);
 #pragma unroll
             for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
             b.s[nb] = ld<uint16_t>(ws[nb] + kc / 16);  // blocks of k = kc .. kc+31
@@ -601,7 +606,7 @@ __global__ __launch_bounds__(kSkBlock) void k_prefill_sk(const uint8_t* __restri
         const int kc = kb < k ? kb : 0;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const u32x4 v = ld_stream16(wc[nb] + kc / 2);
+            const u32x4 v = ld16(wc[nb] + kc / 2);
 #pragma unroll
             for (int q = 0; q < 4; ++q) wr[j].c[nb][q] = v[q];
             wr[j].s[nb] = ld<uint16_t>(ws[nb] + kc / 16);

@@ -110,7 +110,9 @@ __global__ __launch_bounds__(kThreads) void k_prefill_a8(const uint8_t* __restri
         for (int i = 0; i < kBL; ++i) {
             const int c = tid + kThreads * i;
             const int row = c / kS, blk = min(b0 + c % kS, nb - 1);
-            r.b[i] = ld_stream16(w + int64_t(min(n0 + row, n - 1)) * crow + 16 * blk);
+            // 64 bytes of a row per stage, the line's other half next stage:
+            // an ordinary load keeps the line in the cache
+            r.b[i] = ld16(w + int64_t(min(n0 + row, n - 1)) * crow + 16 * blk);
         }
         if (tid < kTN) {
             const uint8_t* sp = w + soff + int64_t(min(n0 + tid, n - 1)) * srow;
