@@ -113,8 +113,8 @@ def _copies(unit_bytes: int) -> int:
 class DenseLayer(Workload):
     """gate+up [2I x H] + SwiGLU, then down [H x I], batch m."""
 
-    sources = ("k_gemv_nvfp4.hip", "qg_gemv_core.hpp")
-    kernel_re = (r"k_gemv_nvfp4\w*<[^>]*\btrue>",)
+    sources = ("k_gemv_nvfp4.hip", "qg_gemv_core.hpp", "qg_mfma.hpp")
+    kernel_re = (r"k_gemv_nvfp4\w*<(?:\d+, ){4}true\b",)  # the SwiGLU instance (fifth argument)
 
     def __init__(self, m=1):
         import torch
