@@ -40,8 +40,9 @@ template <int C>
 constexpr int kStreamRows = C <= 2 ? 4 : 2;
 constexpr int kStreamUnitsDefault = 1;
 // Activations staged in LDS once per workgroup (rather than loaded by every
-// lane from L1/L2) for rows of three or more chunks per lane: measured on
-// MI355X, the 4096 x 12288 down projection went from 7.35 to 7.0 us, while
+// lane from L1/L2) for rows of three or more chunks per lane that fill every
+// lane's chunk slots (k == 2048 * C; other rows keep the per-lane loads): measured on
+// MI355X, the 4096 x 12288 down projection went from 7.35 to 6.9 us, while
 // at two chunks per lane (4096-element rows) the staging's extra registers
 // cost occupancy and time.
 template <int G, int C, int U>
@@ -163,13 +164,14 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4_stream(const uint8_t* __r
     const int nchunks = k / 32;
 
     // Lanes whose chunk c lies past the end of a row load chunk 0 instead (a
-    // valid address) and drop the result.
+    // valid address) and drop the result.  The LDSX instances are launched
+    // only for rows that fill every chunk slot (k == 32 * C * G).
     bool okc[C];
     uint32_t jc[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int j = c * G + l;
-        okc[c] = j < nchunks;
+        okc[c] = LDSX || j < nchunks;
         jc[c] = okc[c] ? uint32_t(j) : 0u;
     }
     // Activations: per lane from global memory (its C chunks, 64 bytes
@@ -179,13 +181,11 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4_stream(const uint8_t* __r
     // (consecutive j) then hit distinct banks, for the reads below and for
     // the staging stores.
     __shared__ u32x4 xs[LDSX ? C * 256 : 1];
-    const int nxu = k / 8;  // 16-byte units of x
     u32x4 xv[C][4];
     u32x4 xg[LDSX ? C : 1];
     if constexpr (LDSX) {
-        // clamped, branch-free: a clamped thread re-stores the last unit
 #pragma unroll
-        for (int s = 0; s < C; ++s) xg[s] = ld16(x + 8u * min(int(threadIdx.x) + kBlock * s, nxu - 1));
+        for (int s = 0; s < C; ++s) xg[s] = ld16(x + 8u * (threadIdx.x + kBlock * s));
     } else {
 #pragma unroll
         for (int c = 0; c < C; ++c)
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4_stream(const uint8_t* __r
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < C; ++s) {
-            const uint32_t u = uint32_t(min(int(threadIdx.x) + kBlock * s, nxu - 1));
+            const uint32_t u = threadIdx.x + kBlock * s;
             xs[4 * (u >> 2) + (((u & 3u) + (u >> 3)) & 3u)] = xg[s];
         }
         lds_barrier();
@@ -306,7 +306,7 @@ hipError_t go_stream_u(const Args& A, int64_t wunits, hipStream_t s) {
     constexpr int R = SW ? (R0 < 2 ? 2 : R0) : R0;
     const int64_t waves = (wunits + U - 1) / U;
     const dim3 grid(unsigned((waves + kBlock / kWave - 1) / (kBlock / kWave)));
-    if constexpr (kStreamLdsX<G, C, U>)
+    if (kStreamLdsX<G, C, U> && A.k == 32 * C * G)
         hipLaunchKernelGGL((k_gemv_nvfp4_stream<R, G, C, U, SW, true>), grid, dim3(kBlock), 0, s, A.w, A.soff,
                            A.s_t, A.nout, A.k, A.x, A.y, A.a, A.h, int(wunits));
     else
