@@ -197,3 +197,21 @@ def test_nvfp4_full_size_layer_sampled(which):
     rows = np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n), synth.rng(1).integers(0, n, 240)]))
     assert_within(got[:, rows], oracle.gemv(w, x, rows), oracle.gemv_abs(w, x, rows), f"nvfp4 {which}")
     assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("k", [6144, 8192, 12288, 16384, 5120, 7168, 10240])
+def test_nvfp4_batch1_long_rows(k):
+    """Batch-1 rows of three or more chunks per lane: the full ones (k a
+    multiple of 2048) stage the activations in LDS, the ragged ones load them
+    per lane.  Both against the oracle, and bitwise against the batch-2
+    kernel (same per-row order)."""
+    require_gpu()
+    print(f"[nvfp4 batch-1 k={k}]", flush=True)
+    g = synth.rng(k + 5)
+    n = 333
+    w = synth.nvfp4_weights(g, n, k)
+    x = synth.x_bf16(g, 2, k)
+    y1 = run_nvfp4(w, x[:1])
+    assert_within(y1, oracle.gemv(w, x[:1]), oracle.gemv_abs(w, x[:1]), f"nvfp4 {n}x{k} m=1")
+    y2 = run_nvfp4(w, x)
+    assert np.array_equal(y1.view(np.uint32), y2[:1].view(np.uint32)), k

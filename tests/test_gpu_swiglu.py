@@ -89,3 +89,17 @@ def test_dense_layer_full_size_stagewise():
     y_ref = oracle.ops.act_values(a_ref) @ oracle.ops.dequant(L.down).T
     rel = np.linalg.norm(yy - y_ref) / np.linalg.norm(y_ref)
     print(f"dense layer end-to-end relative L2 error vs fp64 chain: {rel:.3e}")
+
+
+@pytest.mark.parametrize("k", [6144, 12288])
+def test_swiglu_batch1_long_rows(k):
+    """The SwiGLU epilogue on the LDS-staged batch-1 kernel (full rows)."""
+    require_gpu()
+    print(f"[swiglu batch-1 k={k}]", flush=True)
+    g = synth.rng(k + 11)
+    inter = 96
+    w = synth.nvfp4_weights(g, 2 * inter, k)
+    x = synth.x_bf16(g, 2, k)
+    a1, h1 = check_swiglu_stage(w, x[:1], inter)
+    a2, h2 = run_swiglu(w, x, inter)
+    assert np.array_equal(a1, a2[:1]) and np.array_equal(h1.view(np.uint32), h2[:1].view(np.uint32))
