@@ -105,6 +105,39 @@ class Workload:
     def dominant_launch(self, i: int):
         raise NotImplementedError
 
+    # The CPU baseline: the oracle run on `cpu_parts` slices of the step (row
+    # slices of the weights, or routings / token groups for MoE), one slice
+    # at a time until the time budget is used; each slice reports the
+    # algorithmic bytes of the step it accounts for.
+    cpu_parts = 1
+
+    def cpu_part_desc(self) -> str:
+        return f"the oracle on 1/{self.cpu_parts} of the weight rows"
+
+    def cpu_part_steps(self) -> float:  # fraction of a step one part is
+        return 1.0 / self.cpu_parts
+
+    def cpu_sample(self, part: int, parts: int) -> float:
+        raise NotImplementedError
+
+    def cpu_baseline(self, budget_s=12.0):
+        from threadpoolctl import threadpool_limits
+
+        total, done, n = 0.0, 0.0, 0
+        with threadpool_limits(limits=1):
+            while total < budget_s and n < 1_000_000:
+                t1 = time.perf_counter()
+                done += self.cpu_sample(n % self.cpu_parts, self.cpu_parts)
+                total += time.perf_counter() - t1
+                n += 1
+        return {"value": done / total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} samples, each {self.cpu_part_desc()} ({n * self.cpu_part_steps():.3f} steps in "
+                          f"all) in {total:.1f} s, fp64 numpy, 1 thread"}
+
+
+def _slice(part: int, parts: int, n: int) -> np.ndarray:
+    return np.arange(part * n // parts, (part + 1) * n // parts)
+
 
 def _copies(unit_bytes: int) -> int:
     return max(2, int(np.ceil(ROTATE_BYTES / unit_bytes)))
@@ -208,6 +241,15 @@ class Q8Gemv(Workload):
         self.name = f"q8_0 GEMV 1024x1024, fp32 activations, batch {m}"
         self.dominant = "Q8_0 GEMV"
 
+    cpu_parts = 4
+
+    def cpu_sample(self, part, parts):
+        import oracle
+
+        rows = _slice(part, parts, 1024)
+        oracle.gemv(self.case.w, self.case.x, rows)
+        return self.alg_step * len(rows) / 1024
+
     def step(self, i):
         self.qg.qgemv_q8_0(self.w[i % self.R], 1024, 1024, self.x, self.m, self.y)
 
@@ -234,6 +276,7 @@ class Fp8Gemv(Workload):
         self.R = _copies(buf.nbytes)
         self.w = torch.from_numpy(buf).cuda().repeat(self.R, 1)
         x = synth.x_bf16(g, m, self.K)
+        self.w_log, self.x_log = w, x
         self.x = torch.from_numpy(x.view(np.int16).copy()).cuda()
         self.y = torch.empty((m, self.N), dtype=torch.float32, device="cuda")
         scales = w["scales"].size * 4
@@ -243,6 +286,15 @@ class Fp8Gemv(Workload):
         self.name = (f"FP8 E4M3 GEMV {self.N}x{self.K} (9B-class gate+up), block-128 fp32 scales, "
                      f"bf16 activations, batch {m}")
         self.dominant = "FP8 GEMV"
+
+    cpu_parts = 24
+
+    def cpu_sample(self, part, parts):
+        import oracle
+
+        rows = _slice(part, parts, self.N)
+        oracle.gemv(self.w_log, self.x_log, rows)
+        return self.alg_step * len(rows) / self.N
 
     def step(self, i):
         self.qg.qgemv_fp8(self.qg.QG_FP8_B128, self.w[i % self.R], self.N, self.K, self.x, self.m, self.y)
@@ -262,6 +314,7 @@ class W4A8Gemv(Workload):
         self.qg, self.m = qg, m
         self.N, self.K = 17408, 5120
         case = synth.w4a8_case(m=m)
+        self.case = case
         buf = qg.qg_pack_q4_0(case.w["codes"], case.w["scales"])
         self.R = _copies(buf.nbytes)
         self.w = torch.from_numpy(buf).cuda().repeat(self.R, 1)
@@ -277,6 +330,16 @@ class W4A8Gemv(Workload):
         self.flops_step = 2 * m * N * K
         self.name = f"q4_0 x q8_0 (W4A8) GEMV {N}x{K} (27B-class), batch {m}"
         self.dominant = "W4A8 GEMV"
+
+    cpu_parts = 17
+
+    def cpu_sample(self, part, parts):
+        import oracle
+
+        rows = _slice(part, parts, self.N)
+        xq, xd, _ = oracle.quantize_q8_0_act(self.case.x)
+        oracle.gemv_q4_0_a8(self.case.w, xq, xd, rows)
+        return self.alg_step * len(rows) / self.N
 
     def step(self, i):
         self.qg.qg_quantize_q8_0_act(self.x, self.m, self.K, self.xq, self.xd, self.xs)
@@ -303,6 +366,7 @@ class KQuantGemv(Workload):
         self.N, self.K = 17408, 5120
         self.code = {"q4_k": qg.QG_Q4_K, "q5_k": qg.QG_Q5_K, "q6_k": qg.QG_Q6_K, "iq4_xs": qg.QG_IQ4_XS}[self.fmt]
         case = synth.kquant_case(self.fmt, m=m)
+        self.case = case
         w = case.w
         buf = qg.qg_pack_kquant(self.code, w["codes"], w["d"], w["sub"], w.get("dmin"), w.get("mins"))
         self.R = _copies(buf.nbytes)
@@ -321,6 +385,16 @@ class KQuantGemv(Workload):
         self.flops_step = 2 * m * N * K
         self.name = f"{self.fmt} x q8_0 GEMV {N}x{K} (27B-class), batch {m}"
         self.dominant = f"{self.fmt} GEMV"
+
+    cpu_parts = 17
+
+    def cpu_sample(self, part, parts):
+        import oracle
+
+        rows = _slice(part, parts, self.N)
+        xq, xd, _ = oracle.quantize_q8_0_act(self.case.x)
+        oracle.gemv_a8(self.case.w, xq, xd, rows)
+        return self.alg_step * len(rows) / self.N
 
     def step(self, i):
         self.qg.qg_quantize_q8_0_act(self.x, self.m, self.K, self.xq, self.xd, self.xs)
@@ -378,6 +452,7 @@ class MoE(Workload):
         self.S = self.routing_samples
         g = synth.rng(synth.seed_for(4, 900))
         logits = synth.logits_f32(g, self.S * t, L.n_experts)
+        self.logits_np = logits.reshape(self.S, t, L.n_experts)
         self.logits = torch.from_numpy(logits).cuda().view(self.S, t, L.n_experts)
         self.x = torch.from_numpy(L.x.view(np.int16).copy()).cuda()
         self.ids = torch.empty((t, 8), dtype=torch.int32, device="cuda")
@@ -408,6 +483,28 @@ class MoE(Workload):
     def workspace_bytes(self, desc, t):
         return self.qg.moe_workspace_bytes(desc, t)
 
+    @property
+    def cpu_parts(self):
+        return self.S
+
+    def cpu_part_desc(self):
+        return "one whole step (the oracle's routing, grouping, gate/up, SwiGLU, down and combine) with its own routing"
+
+    def cpu_part_steps(self):
+        return 1.0
+
+    def _moe_bytes(self, ids, t):
+        H, I = self.L.hidden, self.L.inter
+        active = len(set(np.asarray(ids).ravel().tolist())) + 1
+        return active * (2 * I * H * 9 // 16 + H * I * 9 // 16) + t * (2 * H + 4 * H)
+
+    def cpu_sample(self, part, parts):
+        import oracle
+
+        ids, wts = oracle.route_topk(self.logits_np[part], 8)
+        oracle.moe_forward(self.L, self.L.x, ids, wts)
+        return self._moe_bytes(ids, self.t)
+
     def step(self, i):
         # routing + grouped expert GEMVs + combine: two launches
         self.qg.moe_forward(self.descs[i % self.R], self.x, self.logits[i % self.S], self.t, self.y, self.ws,
@@ -435,6 +532,27 @@ class MoEPrefill(MoE):
     def workspace_bytes(self, desc, t):
         return self.qg.moe_prefill_workspace_bytes(desc, t)
 
+    cpu_tokens = 8
+
+    @property
+    def cpu_parts(self):
+        return self.t // self.cpu_tokens
+
+    def cpu_part_desc(self):
+        return (f"the oracle's layer for {self.cpu_tokens} of the {self.t} tokens (bytes: the experts they select, "
+                f"each once, and their activations)")
+
+    def cpu_part_steps(self):
+        return self.cpu_tokens / self.t
+
+    def cpu_sample(self, part, parts):
+        import oracle
+
+        tok = _slice(part, parts, self.t)
+        ids, wts = oracle.route_topk(self.logits_np[0][tok], 8)
+        oracle.moe_forward(self.L, self.L.x[tok], ids, wts)
+        return self._moe_bytes(ids, len(tok))
+
     def step(self, i):
         self.qg.moe_prefill(self.descs[i % self.R], self.x, self.logits[i % self.S], self.t, self.y, self.ws,
                             self.ws_bytes)
@@ -454,6 +572,7 @@ class Prefill(Workload):
         self.qg, self.m = qg, m
         self.N, self.K = 12288, 4096
         case = synth.prefill_case(m=m)
+        self.case = case
         buf = qg.qg_pack_nvfp4(case.w["codes"], case.w["scales"])
         self.R = _copies(buf.nbytes)
         self.w = torch.from_numpy(buf).cuda().repeat(self.R, 1)
@@ -466,6 +585,15 @@ class Prefill(Workload):
         self.bound = "mfma" if m >= 96 else "hbm"
         self.name = f"prefill GEMM: X bf16 [{m}x{K}] x NVFP4 W [{N}x{K}], bf16 out"
         self.dominant = "prefill MFMA GEMM"
+
+    cpu_parts = 96
+
+    def cpu_sample(self, part, parts):
+        import oracle
+
+        cols = _slice(part, parts, self.N)
+        oracle.prefill(self.case.w, self.case.x, cols=cols)
+        return self.alg_step * len(cols) / self.N
 
     def step(self, i):
         self.qg.qgemm_prefill(self.w[i % self.R], 0.01, self.N, self.K, self.x, self.m, self.y)
@@ -489,6 +617,7 @@ class PrefillA8(Workload):
         self.qg, self.m = qg, m
         self.N, self.K = 17408, 5120
         case = synth.w4a8_case(m=m)
+        self.case = case
         buf = qg.qg_pack_q4_0(case.w["codes"], case.w["scales"])
         self.R = _copies(buf.nbytes)
         self.w = torch.from_numpy(buf).cuda().repeat(self.R, 1)
@@ -502,6 +631,16 @@ class PrefillA8(Workload):
         self.flops_step = 2 * m * N * K
         self.name = f"W4A8 prefill (int8 MFMA): q8_0 X [{m}x{K}] x q4_0 W [{N}x{K}] (27B-class), fp32 out"
         self.dominant = "W4A8 prefill int8 MFMA GEMM"
+
+    cpu_parts = 272
+
+    def cpu_sample(self, part, parts):
+        import oracle
+
+        rows = _slice(part, parts, self.N)
+        xq, xd, _ = oracle.quantize_q8_0_act(self.case.x)
+        oracle.gemv_q4_0_a8(self.case.w, xq, xd, rows)
+        return self.alg_step * len(rows) / self.N
 
     def step(self, i):
         self.qg.qg_quantize_q8_0_act(self.x, self.m, self.K, self.xq, self.xd, None)

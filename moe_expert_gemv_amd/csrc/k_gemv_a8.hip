@@ -104,7 +104,10 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restri
     if constexpr (C > 0) {
         // Every code chunk and scale of the R*C blocks is loaded first, at a
         // clamped (always valid) block index; lanes whose block c lies past
-        // the row end keep their sum unchanged.
+        // the row end keep their sum unchanged.  With one token the lane's C
+        // activation blocks are requested before the weights: loads complete
+        // in order, so activations requested behind the weight stream would
+        // wait for all of it, and then cost one more round trip per block.
         u32x4 cw[C][R];
         uint32_t sw[C][R];
         bool okc[C];
@@ -114,6 +117,14 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restri
             const int j = c * G + l;
             okc[c] = j < nb;
             jc[c] = okc[c] ? uint32_t(j) : 0u;
+        }
+        XBlock x1[MT == 1 ? C : 1];
+        if constexpr (MT == 1) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) x1[c] = load_xblock<XS>(xq, xd, xs, 0, k, nb, jc[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 cw[c][r] = ld_stream16(codes[r] + 16u * jc[c]);
@@ -129,7 +140,8 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restri
             for (int c = 0; c < C; ++c) {
                 XBlock b[TB];
 #pragma unroll
-                for (int t = 0; t < TB; ++t) b[t] = load_xblock<XS>(xq, xd, xs, tok[tb + t], k, nb, jc[c]);
+                for (int t = 0; t < TB; ++t)
+                    b[t] = MT == 1 ? x1[c] : load_xblock<XS>(xq, xd, xs, tok[tb + t], k, nb, jc[c]);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     uint32_t lo[4], hi[4];
