@@ -47,12 +47,16 @@ constexpr int kStreamUnitsDefault = 1;
 // cost occupancy and time.
 template <int G, int C, int U>
 constexpr bool kStreamLdsX = G == kWave && U == 1 && C >= 3;
+// Two to four tokens: activations staged in LDS for full rows of at most two
+// chunks per lane (32 KB of LDS at four tokens and k = 4096).
+template <int G, int C, int MT>
+constexpr bool kMultiLdsX = G == kWave && MT == 4 && C >= 1 && C <= 2;
 
 // SWIGLU: the matrix is packed with gate/up rows interleaved (packed row 2i =
 // gate i, 2i+1 = up i), so the R consecutive rows of a group are RA = R/2
 // (gate, up) pairs; the epilogue writes a = bf16(silu(g) * u) (and optionally
 // g, u into h).  nout is n (plain) or inter (SwiGLU).
-template <int R, int MT, int G, int C, bool SWIGLU>
+template <int R, int MT, int G, int C, bool SWIGLU, bool LDSX = false>
 __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4(const uint8_t* __restrict__ w, int64_t soff,
                                                        float s_t, int nout, int k,
                                                        const uint16_t* __restrict__ x, int m,
@@ -90,7 +94,64 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4(const uint8_t* __restrict
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[r][t] = 0.f;
 
-    nvfp4_partial<R, MT, G, C>(codes, scales, xp, m, k / 32, l, acc);
+    if constexpr (LDSX) {
+        // Two to four tokens over rows that fill every lane's chunk slots
+        // (k == 32 * C * G): the MT token slots' activations are staged in
+        // LDS once per workgroup instead of being read by every wave through
+        // L1 (4 tokens bring 64 bytes per lane per chunk, more than the
+        // weights).  Same loads and arithmetic per (row, token) as
+        // nvfp4_partial, so the sums are bitwise the same.
+        static_assert(G == kWave && MT <= 4 && C > 0, "one token block over full rows");
+        constexpr int kU = C * 256;  // 16-byte units of one token's activations
+        __shared__ u32x4 xs[MT * kU];
+        const int tid = int(threadIdx.x);
+        u32x4 xg[MT][C];
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int q = 0; q < C; ++q) xg[t][q] = ld16(xp[t] + 8u * (tid + kBlock * q));
+        u32x4 cw[C][R];
+        uint32_t sw[C][R];
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t j = uint32_t(c * G + l);
+                cw[c][r] = ld_stream16(codes[r] + 16u * j);
+                sw[c][r] = ld<uint16_t>(scales[r] + 2u * j);
+            }
+        // piece p of chunk j of token t at slot t*kU + 4j + ((p + j/2) & 3):
+        // conflict-free for the staging stores and the per-lane reads
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int q = 0; q < C; ++q) {
+                const uint32_t u = uint32_t(tid + kBlock * q);
+                xs[t * kU + 4 * (u >> 2) + (((u & 3u) + (u >> 3)) & 3u)] = xg[t][q];
+            }
+        lds_barrier();
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const uint32_t j = uint32_t(c * G + l);
+            u32x4 xv[MT][4];
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xv[t][i] = xs[t * kU + 4 * j + ((uint32_t(i) + (j >> 1)) & 3u)];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                bf16x2 d[16];
+                nvfp4_decode_chunk(cw[c][r], d);
+                const float s0 = e4m3_to_f32<0>(sw[c][r]), s1 = e4m3_to_f32<1>(sw[c][r]);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[r][t] = nvfp4_chunk_dot_decoded(d, s0, s1, xv[t], acc[r][t]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        nvfp4_partial<R, MT, G, C>(codes, scales, xp, m, k / 32, l, acc);
+    }
 
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -345,8 +406,12 @@ hipError_t go(const Args& A, hipStream_t s) {
         const int64_t units = (int64_t(A.nout) + per_unit - 1) / per_unit;
         const int64_t per_block = (kBlock / kWave) * (kWave / G);
         const dim3 grid(unsigned((units + per_block - 1) / per_block));
-        hipLaunchKernelGGL((k_gemv_nvfp4<R, MT, G, C, SW>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.s_t,
-                           A.nout, A.k, A.x, A.m, A.y, A.a, A.h);
+        if (kMultiLdsX<G, C, MT> && A.k == 32 * C * G)
+            hipLaunchKernelGGL((k_gemv_nvfp4<R, MT, G, C, SW, kMultiLdsX<G, C, MT>>), grid, dim3(kBlock), 0, s,
+                               A.w, A.soff, A.s_t, A.nout, A.k, A.x, A.m, A.y, A.a, A.h);
+        else
+            hipLaunchKernelGGL((k_gemv_nvfp4<R, MT, G, C, SW>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.s_t,
+                               A.nout, A.k, A.x, A.m, A.y, A.a, A.h);
         return hipGetLastError();
     }
 }
