@@ -12,6 +12,7 @@
 #include "qg_gemv_core.hpp"
 #include "qg_internal.hpp"
 #include "qg_layout.hpp"
+#include "qg_mfma.hpp"
 
 namespace qg {
 
@@ -66,7 +67,7 @@ __device__ __forceinline__ XBlock load_xblock(const int8_t* xq, const uint16_t* 
 
 // Chunk j of a row = Q4_0 block j: 16 code bytes and one fp16 scale.  XS:
 // the quantizer's int32 block sums are given (else formed from the codes).
-template <int R, int MT, int G, int C, bool XS>
+template <int R, int MT, int G, int C, bool XS, bool LDSX = false>
 __global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restrict__ w, int64_t soff,
                                                          int n, int k,
                                                          const int8_t* __restrict__ xq,
@@ -123,6 +124,35 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restri
 #pragma unroll
             for (int c = 0; c < C; ++c) x1[c] = load_xblock<XS>(xq, xd, xs, 0, k, nb, jc[c]);
         }
+        // LDSX (four token slots, k <= 6144): the slots' activation blocks
+        // are staged in LDS once per workgroup -- every wave would otherwise
+        // read about 2.5 times its weight bytes in activations through L1.
+        // Codes: 16-byte unit h of block j at slot 2j + (h ^ (j/4 & 1)), so
+        // the eight lanes of one 128-byte LDS cycle hit distinct banks.
+        // Staging loads are clamped (a clamped thread re-stores the last unit)
+        // and issued before the weights; the stores wait for them only.
+        constexpr int kXU = LDSX ? C * 128 : 1;  // code units per slot (nb <= 64 * C)
+        constexpr int kXB = LDSX ? C * 64 : 1;   // blocks per slot
+        __shared__ u32x4 s_q[LDSX ? MT * kXU : 1];
+        __shared__ uint16_t s_d[LDSX ? MT * kXB : 1];
+        __shared__ int32_t s_s[LDSX && XS ? MT * kXB : 1];
+        constexpr int kQPer = (kXU + kBlock - 1) / kBlock;
+        u32x4 gq[LDSX ? MT : 1][LDSX ? kQPer : 1];
+        uint16_t gd[LDSX ? MT : 1];
+        int32_t gs[LDSX ? MT : 1];
+        const int tid = int(threadIdx.x);
+        const int nu = 2 * nb;
+        if constexpr (LDSX) {
+            static_assert(G == kWave && MT == 4, "four token slots, one lane group per wave");
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+#pragma unroll
+                for (int q = 0; q < kQPer; ++q)
+                    gq[t][q] = ld16(xq + tok[t] * k + 16 * min(tid + kBlock * q, nu - 1));
+                gd[t] = (xd + tok[t] * nb)[min(tid, nb - 1)];
+                if constexpr (XS) gs[t] = (xs + tok[t] * nb)[min(tid, nb - 1)];
+            }
+        }
 #pragma unroll
         for (int c = 0; c < C; ++c) {
 #pragma unroll
@@ -131,6 +161,42 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restri
                 sw[c][r] = ld<uint16_t>(scales[r] + 2u * jc[c]);
             }
         }
+        if constexpr (LDSX) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+#pragma unroll
+                for (int q = 0; q < kQPer; ++q) {
+                    const uint32_t u = uint32_t(min(tid + kBlock * q, nu - 1));
+                    s_q[t * kXU + ((u & ~1u) | ((u & 1u) ^ ((u >> 3) & 1u)))] = gq[t][q];
+                }
+                const int jb = min(tid, nb - 1);
+                s_d[t * kXB + jb] = gd[t];
+                if constexpr (XS) s_s[t * kXB + jb] = gs[t];
+            }
+            lds_barrier();
+        }
+        // token slot t's block j from LDS, as load_xblock gives it
+        auto lds_xblock = [&](int t, uint32_t j) {
+            XBlock b;
+            const uint32_t f = (j >> 2) & 1u;
+            b.x0 = s_q[t * kXU + 2 * j + f];
+            b.x1 = s_q[t * kXU + 2 * j + (1u ^ f)];
+            b.dx = f16_to_f32(s_d[t * kXB + j]);
+            int sum;
+            if constexpr (XS) {
+                sum = s_s[t * kXB + j];
+            } else {
+                sum = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    sum = dot4_i8(0x01010101u, b.x0[q], sum);
+                    sum = dot4_i8(0x01010101u, b.x1[q], sum);
+                }
+            }
+            b.bsum8 = 8 * sum;
+            return b;
+        };
         // Tokens in blocks of up to four: per block and chunk, the tokens'
         // activation blocks are loaded and each row's codes unpacked once.
         constexpr int TB = MT < 4 ? MT : 4;
@@ -140,8 +206,12 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restri
             for (int c = 0; c < C; ++c) {
                 XBlock b[TB];
 #pragma unroll
-                for (int t = 0; t < TB; ++t)
-                    b[t] = MT == 1 ? x1[c] : load_xblock<XS>(xq, xd, xs, tok[tb + t], k, nb, jc[c]);
+                for (int t = 0; t < TB; ++t) {
+                    if constexpr (LDSX)
+                        b[t] = lds_xblock(tb + t, jc[c]);
+                    else
+                        b[t] = MT == 1 ? x1[c] : load_xblock<XS>(xq, xd, xs, tok[tb + t], k, nb, jc[c]);
+                }
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     uint32_t lo[4], hi[4];
@@ -268,12 +338,14 @@ hipError_t go(const Args& A, hipStream_t s) {
         const int64_t units = (int64_t(A.n) + R - 1) / R;
         const int64_t per_block = (kBlock / kWave) * (kWave / G);
         const dim3 grid(unsigned((units + per_block - 1) / per_block));
+        // four token slots: activations staged in LDS when they fit (k <= 6144)
+        constexpr bool L = G == kWave && MT == 4 && C > 0 && C <= 3;
         if (A.xs)
-            hipLaunchKernelGGL((k_gemv_q4_0_a8<R, MT, G, C, true>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.n,
+            hipLaunchKernelGGL((k_gemv_q4_0_a8<R, MT, G, C, true, L>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.n,
                                A.k, A.xq, A.xd, A.xs, A.m, A.y);
         else
-            hipLaunchKernelGGL((k_gemv_q4_0_a8<R, MT, G, C, false>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.n,
-                               A.k, A.xq, A.xd, A.xs, A.m, A.y);
+            hipLaunchKernelGGL((k_gemv_q4_0_a8<R, MT, G, C, false, L>), grid, dim3(kBlock), 0, s, A.w, A.soff,
+                               A.n, A.k, A.xq, A.xd, A.xs, A.m, A.y);
         return hipGetLastError();
     }
 }
