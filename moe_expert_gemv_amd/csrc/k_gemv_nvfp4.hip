@@ -47,10 +47,11 @@ constexpr int kStreamUnitsDefault = 1;
 // cost occupancy and time.
 template <int G, int C, int U>
 constexpr bool kStreamLdsX = G == kWave && U == 1 && C >= 3;
-// Two to four tokens: activations staged in LDS for full rows of at most two
-// chunks per lane (32 KB of LDS at four tokens and k = 4096).
+// Two to four tokens: activations staged in LDS for full rows of one or an
+// even number of chunks per lane, in passes of two chunks (32 KB of LDS at
+// four tokens).
 template <int G, int C, int MT>
-constexpr bool kMultiLdsX = G == kWave && MT == 4 && C >= 1 && C <= 2;
+constexpr bool kMultiLdsX = G == kWave && MT == 4 && (C == 1 || (C > 0 && C % 2 == 0));
 
 // SWIGLU: the matrix is packed with gate/up rows interleaved (packed row 2i =
 // gate i, 2i+1 = up i), so the R consecutive rows of a group are RA = R/2
@@ -99,17 +100,37 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4(const uint8_t* __restrict
         // (k == 32 * C * G): the MT token slots' activations are staged in
         // LDS once per workgroup instead of being read by every wave through
         // L1 (4 tokens bring 64 bytes per lane per chunk, more than the
-        // weights).  Same loads and arithmetic per (row, token) as
-        // nvfp4_partial, so the sums are bitwise the same.
+        // weights).  Long rows go in passes of PC chunks (32 KB of LDS at
+        // four tokens); the next pass's activations are loaded into
+        // registers while the current pass is computed.  Same loads and
+        // arithmetic per (row, token) as nvfp4_partial, so the sums are
+        // bitwise the same.
         static_assert(G == kWave && MT <= 4 && C > 0, "one token block over full rows");
-        constexpr int kU = C * 256;  // 16-byte units of one token's activations
+        constexpr int PC = C < 2 ? C : 2;  // chunks per pass
+        constexpr int NP = C / PC;
+        static_assert(NP * PC == C, "whole passes");
+        constexpr int kU = PC * 256;  // 16-byte units of one token's activations per pass
         __shared__ u32x4 xs[MT * kU];
         const int tid = int(threadIdx.x);
-        u32x4 xg[MT][C];
+        u32x4 xg[MT][PC];
+        auto xload = [&](int pass) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
+            for (int t = 0; t < MT; ++t)
 #pragma unroll
-            for (int q = 0; q < C; ++q) xg[t][q] = ld16(xp[t] + 8u * (tid + kBlock * q));
+                for (int q = 0; q < PC; ++q) xg[t][q] = ld16(xp[t] + 8u * (tid + kBlock * (pass * PC + q)));
+        };
+        // piece p of pass-chunk j of token t at slot t*kU + 4j + ((p + j/2) & 3):
+        // conflict-free for the staging stores and the per-lane reads
+        auto xstore = [&]() {
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int q = 0; q < PC; ++q) {
+                    const uint32_t u = uint32_t(tid + kBlock * q);
+                    xs[t * kU + 4 * (u >> 2) + (((u & 3u) + (u >> 3)) & 3u)] = xg[t][q];
+                }
+        };
+        xload(0);
         u32x4 cw[C][R];
         uint32_t sw[C][R];
 #pragma unroll
@@ -120,34 +141,36 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4(const uint8_t* __restrict
                 cw[c][r] = ld_stream16(codes[r] + 16u * j);
                 sw[c][r] = ld<uint16_t>(scales[r] + 2u * j);
             }
-        // piece p of chunk j of token t at slot t*kU + 4j + ((p + j/2) & 3):
-        // conflict-free for the staging stores and the per-lane reads
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int q = 0; q < C; ++q) {
-                const uint32_t u = uint32_t(tid + kBlock * q);
-                xs[t * kU + 4 * (u >> 2) + (((u & 3u) + (u >> 3)) & 3u)] = xg[t][q];
-            }
+        xstore();
         lds_barrier();
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const uint32_t j = uint32_t(c * G + l);
-            u32x4 xv[MT][4];
+        for (int pass = 0; pass < NP; ++pass) {
+            if (pass + 1 < NP) xload(pass + 1);
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
+            for (int cc = 0; cc < PC; ++cc) {
+                const int c = pass * PC + cc;
+                const uint32_t jl = uint32_t(cc * G + l);  // chunk within the pass
+                u32x4 xv[MT][4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) xv[t][i] = xs[t * kU + 4 * j + ((uint32_t(i) + (j >> 1)) & 3u)];
+                for (int t = 0; t < MT; ++t)
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                bf16x2 d[16];
-                nvfp4_decode_chunk(cw[c][r], d);
-                const float s0 = e4m3_to_f32<0>(sw[c][r]), s1 = e4m3_to_f32<1>(sw[c][r]);
+                    for (int i = 0; i < 4; ++i) xv[t][i] = xs[t * kU + 4 * jl + ((uint32_t(i) + (jl >> 1)) & 3u)];
 #pragma unroll
-                for (int t = 0; t < MT; ++t) acc[r][t] = nvfp4_chunk_dot_decoded(d, s0, s1, xv[t], acc[r][t]);
+                for (int r = 0; r < R; ++r) {
+                    bf16x2 d[16];
+                    nvfp4_decode_chunk(cw[c][r], d);
+                    const float s0 = e4m3_to_f32<0>(sw[c][r]), s1 = e4m3_to_f32<1>(sw[c][r]);
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) acc[r][t] = nvfp4_chunk_dot_decoded(d, s0, s1, xv[t], acc[r][t]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
+            if (pass + 1 < NP) {
+                lds_barrier();  // every wave is done with this pass's activations
+                xstore();
+                lds_barrier();
+            }
         }
     } else {
         nvfp4_partial<R, MT, G, C>(codes, scales, xp, m, k / 32, l, acc);
