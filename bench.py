@@ -303,7 +303,7 @@ class Fp8Gemv(Workload):
 
 
 class W4A8Gemv(Workload):
-    sources = ("k_gemv_a8.hip",)
+    sources = ("k_gemv_a8.hip", "qg_mfma.hpp")
     kernel_re = (r"k_gemv_q4_0_a8\b",)
 
     def __init__(self, m=1):
