@@ -489,6 +489,18 @@ __global__ __launch_bounds__(1024) void k_moe_down(MoeArgs A, const float* __res
 // flight.
 constexpr int kTileBlock = 512;
 constexpr int kTileWaves = kTileBlock / kWave;
+constexpr int kTileMaxPairs = 4 * (kMaxTopK + 1);  // pairs of a tile-path call (t <= 4)
+#ifndef QG_TILE_DEPTH
+#define QG_TILE_DEPTH 1
+#endif
+#ifndef QG_TILE_DEPTH_DN
+#define QG_TILE_DEPTH_DN 1
+#endif
+// Expert groups whose loads a wave keeps in flight ahead of the group it
+// computes (gate/up, down).  Measured at four tokens on MI355X: one ahead
+// 26.4 us, two 27.7 us, three 27.9 us, all groups at once 28.4 us.
+constexpr int kTileDepth = QG_TILE_DEPTH;
+constexpr int kTileDepthDn = QG_TILE_DEPTH_DN;
 constexpr int kStageBytes = 64 * 1024;  // LDS activation staging per workgroup
 constexpr int kStagePerThread = kStageBytes / 16 / kTileBlock;
 constexpr int kScalesPerThread = (kMaxScaleLds + kTileBlock - 1) / kTileBlock;
@@ -535,6 +547,18 @@ __device__ __forceinline__ void load_group_w(GroupW<C, R>& b, const uint8_t* con
             b.cw[c][r] = ld_stream16(codes[r] + 16u * jc[c]);
             b.sw[c][r] = ld<uint16_t>(scales[r] + 2u * jc[c]);
         }
+}
+
+// Calls f(std::integral_constant<int, n>) for the runtime count n in
+// [1, NMAX], so that f's body is straight-line code for that count.
+template <int NMAX, int N = 1, typename F>
+__device__ __forceinline__ void dispatch_count(int n, F&& f) {
+    if constexpr (N <= NMAX) {
+        if (n == N)
+            f(std::integral_constant<int, N>{});
+        else
+            dispatch_count<NMAX, N + 1>(n, f);
+    }
 }
 
 // Row sums of one token from a group's preloaded weights; the token's bf16
@@ -614,7 +638,13 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_gate_up_tile(MoeArgs A, cons
         for (int i = tid; i <= c.n_groups; i += kTileBlock) ws.offsets[i] = c.offsets[i];
     }
 
-    // 3. weight loads of all this wave's groups
+    // 3./4. weight loads and, per group, row sums, reduction and SwiGLU.  The
+    // group count is turned into straight-line code (dispatch_count), and a
+    // wave keeps kTileDepth groups' loads ahead of the group it computes, so
+    // the data of its groups arrives one after another and the decode of
+    // each overlaps the stream of the next (rather than all arriving at the
+    // end).  Results go to LDS and are stored after the last group: stores
+    // count on the same counter as loads.
     const int ng = c.n_groups;
     const int nv = min(GW, (ng - wave + kTileWaves - 1) / kTileWaves);  // groups of this wave (uniform)
     if (nv <= 0) return;
@@ -629,10 +659,12 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_gate_up_tile(MoeArgs A, cons
     }
     const int row0 = int(blockIdx.x) * R;
     const int64_t soff = scale_plane_offset(QG_NVFP4, 2 * int64_t(I), H);
-    GroupW<C, R> gw[GW];
-#pragma unroll
-    for (int j = 0; j < GW; ++j) {
-        if (j < nv) {
+    __shared__ uint16_t s_act[kTileMaxPairs][R / 2];
+    __shared__ float s_h[kTileMaxPairs][R];
+    auto run = [&](auto nv_c) {
+        constexpr int NV = decltype(nv_c)::value;
+        GroupW<C, R> gw[NV];
+        auto load = [&](int j) {
             const int e = c.experts[wave + kTileWaves * j];
             const uint8_t* w = A.gate_up + int64_t(e) * A.gu_stride;
             const uint8_t* codes[R];
@@ -644,42 +676,57 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_gate_up_tile(MoeArgs A, cons
                 scales[r] = w + soff + row * (H / 16);
             }
             load_group_w<C, R>(gw[j], codes, scales, jc);
-        }
-    }
-
-    // 4. per group: row sums, reduction, SwiGLU, store
+        };
 #pragma unroll
-    for (int j = 0; j < GW; ++j) {
-        if (j >= nv) break;
-        const int g = wave + kTileWaves * j;
-        const int e = c.experts[g];
-        const int p0 = c.offsets[g];
-        const int mg = c.offsets[g + 1] - p0;
-        const float s_t = s_scale[e];
-        for (int i = 0; i < mg; ++i) {  // the group's tokens, one at a time
-            const int p = p0 + i;
-            float acc[R];
+        for (int j = 0; j < NV && j < kTileDepth; ++j) load(j);
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = 0.f;
-            nvfp4_token_dot<R, C>(gw[j], okc, jc, s_x + c.tok[p] * H, acc);
+        for (int j = 0; j < NV; ++j) {
+            if (j + kTileDepth < NV) load(j + kTileDepth);
+            __builtin_amdgcn_sched_barrier(0);
+            const int g = wave + kTileWaves * j;
+            const int e = c.experts[g];
+            const int p0 = c.offsets[g];
+            const int mg = c.offsets[g + 1] - p0;
+            const float s_t = s_scale[e];
+            for (int i = 0; i < mg; ++i) {  // the group's tokens, one at a time
+                const int p = p0 + i;
+                float acc[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = group_sum<kWave>(acc[r]) * s_t;
-            if (lane == 0) {
+                for (int r = 0; r < R; ++r) acc[r] = 0.f;
+                nvfp4_token_dot<R, C>(gw[j], okc, jc, s_x + c.tok[p] * H, acc);
 #pragma unroll
-                for (int r = 0; r < R / 2; ++r) {
-                    const int row = row0 / 2 + r;
-                    if (row >= I) break;
-                    const float gv = acc[2 * r], uv = acc[2 * r + 1];
-                    const float act = gv / (1.0f + expf(-gv)) * uv;
-                    ws.a[int64_t(p) * I + row] = uint16_t(f32_to_bf16_rne(act));
-                    if (ws.h) {
-                        ws.h[int64_t(p) * 2 * I + row] = gv;
-                        ws.h[int64_t(p) * 2 * I + I + row] = uv;
+                for (int r = 0; r < R; ++r) acc[r] = group_sum<kWave>(acc[r]) * s_t;
+                if (lane == 0) {
+#pragma unroll
+                    for (int r = 0; r < R / 2; ++r) {
+                        const float gv = acc[2 * r], uv = acc[2 * r + 1];
+                        s_act[p][r] = uint16_t(f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv));
+                        s_h[p][2 * r] = gv;
+                        s_h[p][2 * r + 1] = uv;
                     }
                 }
             }
         }
-    }
+        // this wave's pairs (its groups' runs of the CSR) to the workspace
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int g = wave + kTileWaves * j;
+            const int p0 = c.offsets[g];
+            const int mg = c.offsets[g + 1] - p0;
+            for (int idx = lane; idx < mg * (R / 2); idx += kWave) {
+                const int p = p0 + idx / (R / 2), r = idx % (R / 2);
+                const int row = row0 / 2 + r;
+                if (row < I) {
+                    ws.a[int64_t(p) * I + row] = s_act[p][r];
+                    if (ws.h) {
+                        ws.h[int64_t(p) * 2 * I + row] = s_h[p][2 * r];
+                        ws.h[int64_t(p) * 2 * I + I + row] = s_h[p][2 * r + 1];
+                    }
+                }
+            }
+        }
+    };
+    dispatch_count<GW>(nv, run);
 }
 
 // Down + combine, tile path.  blockIdx.x = tile of (64 / G) * R output rows,
@@ -719,7 +766,11 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const f
     const int grp = lane / G, l = lane % G;
     const int tile0 = int(blockIdx.x) * kRows;
     const int nv = min(GW, (ng - wave + kTileWaves - 1) / kTileWaves);
-    if (nv > 0) {
+    // As in the gate/up tile kernel: straight-line code per group count,
+    // kTileDepthDn groups' loads in flight ahead of the computed one, and no
+    // global store until every weight load has been consumed.
+    auto run = [&](auto nv_c) {
+        constexpr int NV = decltype(nv_c)::value;
         const int nchunks = I / 32;
         bool okc[C];
         uint32_t jc[C];
@@ -730,26 +781,26 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const f
             jc[cc] = okc[cc] ? uint32_t(j) : 0u;
         }
         const int64_t soff = scale_plane_offset(QG_NVFP4, H, I);
-        GroupW<C, R> gw[GW];
+        GroupW<C, R> gw[NV];
+        auto load = [&](int j) {
+            const int e = s_exp[wave + kTileWaves * j];
+            const uint8_t* w = A.down + int64_t(e) * A.dn_stride;
+            const uint8_t* codes[R];
+            const uint8_t* scales[R];
 #pragma unroll
-        for (int j = 0; j < GW; ++j) {
-            if (j < nv) {
-                const int e = s_exp[wave + kTileWaves * j];
-                const uint8_t* w = A.down + int64_t(e) * A.dn_stride;
-                const uint8_t* codes[R];
-                const uint8_t* scales[R];
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int64_t row = min(tile0 + grp * R + r, H - 1);
-                    codes[r] = w + row * (I / 2);
-                    scales[r] = w + soff + row * (I / 16);
-                }
-                load_group_w<C, R>(gw[j], codes, scales, jc);
+            for (int r = 0; r < R; ++r) {
+                const int64_t row = min(tile0 + grp * R + r, H - 1);
+                codes[r] = w + row * (I / 2);
+                scales[r] = w + soff + row * (I / 16);
             }
-        }
+            load_group_w<C, R>(gw[j], codes, scales, jc);
+        };
 #pragma unroll
-        for (int j = 0; j < GW; ++j) {
-            if (j >= nv) break;
+        for (int j = 0; j < NV && j < kTileDepthDn; ++j) load(j);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            if (j + kTileDepthDn < NV) load(j + kTileDepthDn);
+            __builtin_amdgcn_sched_barrier(0);
             const int g = wave + kTileWaves * j;
             const int e = s_exp[g];
             const int p0 = s_off[g];
@@ -765,16 +816,19 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const f
                 for (int r = 0; r < R; ++r) acc[r] = group_sum<G>(acc[r]) * s_t;
                 if (l == 0) {
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const int row = tile0 + grp * R + r;
-                        s_o[p][grp * R + r] = acc[r];
-                        if (row < H) ws.o[int64_t(p) * H + row] = acc[r];
-                    }
+                    for (int r = 0; r < R; ++r) s_o[p][grp * R + r] = acc[r];
                 }
             }
         }
-    }
+    };
+    if (nv > 0) dispatch_count<GW>(nv, run);
     __syncthreads();
+    // per-pair down outputs to the workspace, then the combine
+    for (int idx = tid; idx < P * kRows; idx += kTileBlock) {
+        const int pp = idx / kRows, rr = idx % kRows;
+        const int row = tile0 + rr;
+        if (row < H) ws.o[int64_t(pp) * H + row] = s_o[pp][rr];
+    }
     for (int idx = tid; idx < t * kRows; idx += kTileBlock) {
         const int tt = idx / kRows, rr = idx % kRows;
         const int row = tile0 + rr;
