@@ -181,8 +181,8 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4(const uint8_t* __restrict
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[r][t] = group_sum<G>(acc[r][t]) * s_t;
 
-    if (l != 0) return;
     if constexpr (!SWIGLU) {
+        if (l != 0) return;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = unit * R + r;
@@ -192,22 +192,28 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4(const uint8_t* __restrict
                 if (t < m) y[int64_t(t) * nout + row] = acc[r][t];
         }
     } else {
+        // Every lane of the group holds every sum: lane l evaluates the
+        // SwiGLU of (a-row l / MT, token l % MT), so the RA * MT exponentials
+        // run side by side instead of one after another on lane 0.
         constexpr int RA = R / 2;
+        static_assert(RA * MT <= G, "one (a-row, token) per lane");
+        float g = 0.f, u = 0.f;
 #pragma unroll
-        for (int r = 0; r < RA; ++r) {
-            const int i = unit * RA + r;
-            if (i >= nout) break;
+        for (int r = 0; r < RA; ++r)
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                if (t < m) {
-                    const float g = acc[2 * r][t], u = acc[2 * r + 1][t];
-                    const float act = g / (1.0f + expf(-g)) * u;
-                    a[int64_t(t) * nout + i] = uint16_t(f32_to_bf16_rne(act));
-                    if (h) {
-                        h[int64_t(t) * 2 * nout + i] = g;
-                        h[int64_t(t) * 2 * nout + nout + i] = u;
-                    }
+            for (int t = 0; t < MT; ++t)
+                if (l == r * MT + t) {
+                    g = acc[2 * r][t];
+                    u = acc[2 * r + 1][t];
                 }
+        const int r = l / MT, t = l % MT;
+        const int i = unit * RA + r;
+        if (l < RA * MT && t < m && i < nout) {
+            const float act = g / (1.0f + expf(-g)) * u;
+            a[int64_t(t) * nout + i] = uint16_t(f32_to_bf16_rne(act));
+            if (h) {
+                h[int64_t(t) * 2 * nout + i] = g;
+                h[int64_t(t) * 2 * nout + nout + i] = u;
             }
         }
     }
@@ -313,21 +319,29 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4_stream(const uint8_t* __r
             }
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = group_sum<G>(acc[r]) * s_t;
-        if (store && l == 0) {
+        if constexpr (!SWIGLU) {
+            if (store && l == 0) {
 #pragma unroll
-            for (int r = 0; r < kPer; ++r) {
-                const int i = unit * kPer + r;
-                if (i < nout) {
-                    if constexpr (!SWIGLU) {
-                        y[i] = acc[r];
-                    } else {
-                        const float g = acc[2 * r], u = acc[2 * r + 1];
-                        a[i] = uint16_t(f32_to_bf16_rne(g / (1.0f + expf(-g)) * u));
-                        if (h) {
-                            h[i] = g;
-                            h[nout + i] = u;
-                        }
-                    }
+                for (int r = 0; r < kPer; ++r) {
+                    const int i = unit * kPer + r;
+                    if (i < nout) y[i] = acc[r];
+                }
+            }
+        } else {
+            // lane l of the group evaluates the SwiGLU of its a-row l
+            float g = 0.f, u = 0.f;
+#pragma unroll
+            for (int r = 0; r < kPer; ++r)
+                if (l == r) {
+                    g = acc[2 * r];
+                    u = acc[2 * r + 1];
+                }
+            const int i = unit * kPer + l;
+            if (store && l < kPer && i < nout) {
+                a[i] = uint16_t(f32_to_bf16_rne(g / (1.0f + expf(-g)) * u));
+                if (h) {
+                    h[i] = g;
+                    h[nout + i] = u;
                 }
             }
         }
