@@ -363,22 +363,30 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < MT; ++i) acc[r][i] = group_sum<G>(acc[r][i]) * s_t;
-    if (l != 0) return;
+    // every lane of the group holds every sum: lane l evaluates the SwiGLU
+    // of (a-row q / MT, token q % MT) for q = l, l + G, ..., side by side
+    // rather than all on lane 0
 #pragma unroll
-    for (int r = 0; r < RA; ++r) {
-        const int row = unit * RA + r;
-        if (row >= I) break;
+    for (int q0 = 0; q0 < RA * MT; q0 += G) {
+        const int q = q0 + l;
+        float gv = 0.f, uv = 0.f;
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            if (i < mg) {
-                const int p = p0 + i;
-                const float gv = acc[2 * r][i], uv = acc[2 * r + 1][i];
-                const float act = gv / (1.0f + expf(-gv)) * uv;
-                ws.a[int64_t(p) * I + row] = uint16_t(f32_to_bf16_rne(act));
-                if (ws.h) {
-                    ws.h[int64_t(p) * 2 * I + row] = gv;
-                    ws.h[int64_t(p) * 2 * I + I + row] = uv;
+        for (int r = 0; r < RA; ++r)
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+                if (q == r * MT + i) {
+                    gv = acc[2 * r][i];
+                    uv = acc[2 * r + 1][i];
                 }
+        const int ra = q / MT, ti = q % MT;
+        const int row = unit * RA + ra;
+        if (q < RA * MT && ti < mg && row < I) {
+            const int p = p0 + ti;
+            const float act = gv / (1.0f + expf(-gv)) * uv;
+            ws.a[int64_t(p) * I + row] = uint16_t(f32_to_bf16_rne(act));
+            if (ws.h) {
+                ws.h[int64_t(p) * 2 * I + row] = gv;
+                ws.h[int64_t(p) * 2 * I + I + row] = uv;
             }
         }
     }
@@ -696,14 +704,18 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_gate_up_tile(MoeArgs A, cons
                 nvfp4_token_dot<R, C>(gw[j], okc, jc, s_x + c.tok[p] * H, acc);
 #pragma unroll
                 for (int r = 0; r < R; ++r) acc[r] = group_sum<kWave>(acc[r]) * s_t;
-                if (lane == 0) {
+                // lane r evaluates the SwiGLU of a-row r
+                float gv = 0.f, uv = 0.f;
 #pragma unroll
-                    for (int r = 0; r < R / 2; ++r) {
-                        const float gv = acc[2 * r], uv = acc[2 * r + 1];
-                        s_act[p][r] = uint16_t(f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv));
-                        s_h[p][2 * r] = gv;
-                        s_h[p][2 * r + 1] = uv;
+                for (int r = 0; r < R / 2; ++r)
+                    if (lane == r) {
+                        gv = acc[2 * r];
+                        uv = acc[2 * r + 1];
                     }
+                if (lane < R / 2) {
+                    s_act[p][lane] = uint16_t(f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv));
+                    s_h[p][2 * lane] = gv;
+                    s_h[p][2 * lane + 1] = uv;
                 }
             }
         }
