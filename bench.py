@@ -146,7 +146,7 @@ def _copies(unit_bytes: int) -> int:
 class DenseLayer(Workload):
     """gate+up [2I x H] + SwiGLU, then down [H x I], batch m."""
 
-    sources = ("k_gemv_nvfp4.hip", "qg_gemv_core.hpp", "qg_mfma.hpp")
+    sources = ("k_gemv_nvfp4.hip", "qg_gemv_core.hpp", "qg_mfma.hpp", "qg_reduce.hpp")
     kernel_re = (r"k_gemv_nvfp4\w*<(?:\d+, ){4}true\b",)  # the SwiGLU instance (fifth argument)
 
     def __init__(self, m=1):
@@ -303,7 +303,7 @@ class Fp8Gemv(Workload):
 
 
 class W4A8Gemv(Workload):
-    sources = ("k_gemv_a8.hip", "qg_mfma.hpp")
+    sources = ("k_gemv_a8.hip", "qg_mfma.hpp", "qg_reduce.hpp")
     kernel_re = (r"k_gemv_q4_0_a8\b",)
 
     def __init__(self, m=1):

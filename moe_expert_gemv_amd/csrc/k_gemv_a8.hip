@@ -13,6 +13,7 @@
 #include "qg_internal.hpp"
 #include "qg_layout.hpp"
 #include "qg_mfma.hpp"
+#include "qg_reduce.hpp"
 
 namespace qg {
 
@@ -256,6 +257,22 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restri
                 }
             }
         }
+    }
+    if constexpr (MT > 1 && G == kWave && ((R * MT) & (R * MT - 1)) == 0 && R * MT <= 64) {
+        // several tokens: reduce-scatter, lane l ends with (row, token) index
+        // bitrev(l % N), index = row * MT + token -- bitwise the butterfly sums
+        constexpr int N = R * MT, L = log2i(N);
+        float flat[N];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) flat[r * MT + t] = acc[r][t];
+        const float v = reduce_scatter64<N>(flat);
+        const int idx = bitrev<L>(lane & (N - 1));
+        const int r = idx / MT, t = idx % MT;
+        const int row = unit * R + r;
+        if (lane < N && t < m && row < n) y[int64_t(t) * n + row] = v;
+        return;
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
