@@ -779,6 +779,67 @@ def time_dominant(wl: Workload, launches: int, reps: int = 3):
     return float(min(per)), float(np.mean(per))
 
 
+def parse_gpu_state(text: str):
+    """Clocks and temperatures from `amd-smi metric --clock --temperature
+    --json` output (one GPU): mean and max of the XCDs' current gfx clocks,
+    the memory clock, whether clocks are locked, hotspot and memory
+    temperature.  None if the text does not parse."""
+    try:
+        j = json.loads(text[text.index("["):text.rindex("]") + 1])
+        g = j[0]
+        clk, temp = g["clock"], g["temperature"]
+        gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_")]
+        val = lambda d: d["value"] if isinstance(d, dict) else None
+        return {"gfx_mhz_mean": float(np.mean(gfx)), "gfx_mhz_max": max(gfx),
+                "gfx_mhz_limit": clk["gfx_0"]["max_clk"]["value"], "mem_mhz": clk["mem_0"]["clk"]["value"],
+                "clocks_locked": clk["gfx_0"].get("clk_locked"), "hotspot_c": val(temp.get("hotspot")),
+                "mem_c": val(temp.get("mem"))}
+    except (ValueError, KeyError, IndexError, TypeError):
+        return None
+
+
+def gpu_state(device: int):
+    """The device's clocks and temperatures as amd-smi reports them (None
+    where amd-smi is missing or fails); clocks are not pinned."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", str(device), "--clock", "--temperature", "--json"],
+                           capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    return parse_gpu_state(r.stdout) if r.returncode == 0 else None
+
+
+def gpu_state_loaded(wl, device: int, backlog_s: float = 0.4):
+    """gpu_state sampled while the GPU runs the workload: a graph of steps is
+    replayed enough times to queue about backlog_s seconds of GPU work (one
+    launch per replay, so the queue runs ahead of the host), amd-smi is
+    queried while it drains, then the stream is synchronised.  Outside any
+    timed region."""
+    import torch
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        wl.step(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(50):
+            wl.step(i)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    per = max(time.perf_counter() - t0, 1e-5)
+    with torch.cuda.stream(stream):
+        for _ in range(int(min(backlog_s / per, 20000))):
+            g.replay()
+    st = gpu_state(device)
+    torch.cuda.synchronize()
+    return st
+
+
 def calibrate_copy():
     """A plain device copy of COPY_CAL_BYTES (fp32 negation: every byte read
     once, written once), run three times; the byte counters of a profiled run
@@ -924,8 +985,10 @@ def main():
         calibrate_copy()
     print(f"[bench] {wl.name}; {getattr(wl, 'R', 1)} weight copies; timing", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
+    state_before = gpu_state(torch.cuda.current_device())
     ms = time_steps(wl, args.steps, args.warmup, not args.no_graph)
     dom_best, dom_mean = time_dominant(wl, max(20, min(args.steps, 200)))
+    state_loaded = gpu_state_loaded(wl, torch.cuda.current_device())
     value = wl.alg_step / (ms * 1e-3) / 1e9
 
     if wl.bound == "mfma":
@@ -968,6 +1031,7 @@ def main():
                    "kernel_source_digest": source_digest(cls.sources)},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "gpu_state": {"idle_before": state_before, "under_load_after": state_loaded},
     }
     print(json.dumps(out), flush=True)
 
