@@ -935,10 +935,14 @@ hipError_t moe_go(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    constexpr int kRowsDown = kWave / GD;  // one row per lane group
+    // two rows per lane group: each wave's weight request is twice as large
+    // (measured at one token: 12.96 us with one row, 12.65 with two, 13.4
+    // with four)
+    constexpr int RDn = 2;
+    constexpr int kRowsDown = kWave / GD * RDn;
     const int waves = max_groups < 16 ? max_groups : 16;
     const dim3 g2((A.H + kRowsDown - 1) / kRowsDown);
-    hipLaunchKernelGGL((k_moe_down<MT, GD, CD, 1>), g2, dim3(kWave * waves), 0, s, A, w, t, y, ws);
+    hipLaunchKernelGGL((k_moe_down<MT, GD, CD, RDn>), g2, dim3(kWave * waves), 0, s, A, w, t, y, ws);
     return hipGetLastError();
 }
 
