@@ -798,25 +798,47 @@ def parse_gpu_state(text: str):
         return None
 
 
-def gpu_state(device: int):
-    """The device's clocks and temperatures as amd-smi reports them (None
-    where amd-smi is missing or fails); clocks are not pinned."""
+def _smi_start(device: int):
+    """Start amd-smi (a child process) on the device's clocks and
+    temperatures; None where it cannot be started."""
     import subprocess
 
     try:
-        r = subprocess.run(["amd-smi", "metric", "-g", str(device), "--clock", "--temperature", "--json"],
-                           capture_output=True, text=True, timeout=20)
-    except (OSError, subprocess.SubprocessError):
+        return subprocess.Popen(["amd-smi", "metric", "-g", str(device), "--clock", "--temperature", "--json"],
+                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except OSError:
         return None
-    return parse_gpu_state(r.stdout) if r.returncode == 0 else None
 
 
-def gpu_state_loaded(wl, device: int, backlog_s: float = 0.4):
-    """gpu_state sampled while the GPU runs the workload: a graph of steps is
-    replayed enough times to queue about backlog_s seconds of GPU work (one
-    launch per replay, so the queue runs ahead of the host), amd-smi is
-    queried while it drains, then the stream is synchronised.  Outside any
-    timed region."""
+def _smi_finish(proc):
+    import subprocess
+
+    if proc is None:
+        return None
+    try:
+        out, _ = proc.communicate(timeout=30)
+    except subprocess.TimeoutExpired:
+        proc.kill()
+        proc.communicate()
+        return None
+    return parse_gpu_state(out) if proc.returncode == 0 else None
+
+
+def gpu_state(device: int):
+    """The device's clocks and temperatures as amd-smi reports them (None
+    where amd-smi is missing or fails), and the seconds the query took;
+    clocks are not pinned."""
+    t0 = time.perf_counter()
+    st = _smi_finish(_smi_start(device))
+    return st, time.perf_counter() - t0
+
+
+def gpu_state_loaded(wl, device: int, smi_s: float):
+    """gpu_state sampled while the GPU runs the workload: amd-smi is started
+    first, then a graph of steps is replayed enough times to queue about
+    1.5 * smi_s + 0.5 seconds of GPU work (smi_s: how long an idle query
+    took; at most 8 s), so the whole query runs under load; then the stream
+    is synchronised.  Outside any timed region."""
     import torch
 
     stream = torch.cuda.Stream()
@@ -832,10 +854,12 @@ def gpu_state_loaded(wl, device: int, backlog_s: float = 0.4):
         g.replay()
     torch.cuda.synchronize()
     per = max(time.perf_counter() - t0, 1e-5)
+    backlog_s = min(1.5 * smi_s + 0.5, 8.0)
+    proc = _smi_start(device)
     with torch.cuda.stream(stream):
-        for _ in range(int(min(backlog_s / per, 20000))):
+        for _ in range(int(min(backlog_s / per, 50000))):
             g.replay()
-    st = gpu_state(device)
+    st = _smi_finish(proc)
     torch.cuda.synchronize()
     return st
 
@@ -948,6 +972,7 @@ def main():
     ap.add_argument("--config", default="dense", choices=sorted(CONFIGS))
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of a graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gpu-state", action="store_true", help="skip the amd-smi clock and temperature samples")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain copy of known size first (for byte-counter calibration)")
@@ -985,10 +1010,12 @@ def main():
         calibrate_copy()
     print(f"[bench] {wl.name}; {getattr(wl, 'R', 1)} weight copies; timing", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
-    state_before = gpu_state(torch.cuda.current_device())
+    state_before, smi_s = (None, 0.0) if args.no_gpu_state else gpu_state(torch.cuda.current_device())
     ms = time_steps(wl, args.steps, args.warmup, not args.no_graph)
     dom_best, dom_mean = time_dominant(wl, max(20, min(args.steps, 200)))
-    state_loaded = gpu_state_loaded(wl, torch.cuda.current_device())
+    state_loaded = None
+    if state_before is not None:
+        state_loaded = gpu_state_loaded(wl, torch.cuda.current_device(), smi_s)
     value = wl.alg_step / (ms * 1e-3) / 1e9
 
     if wl.bound == "mfma":
