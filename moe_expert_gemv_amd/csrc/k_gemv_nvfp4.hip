@@ -59,8 +59,8 @@ constexpr bool kMultiLdsX = G == kWave && MT == 4 && (C == 1 || (C > 0 && C % 2 
 // gate i, 2i+1 = up i), so the R consecutive rows of a group are RA = R/2
 // (gate, up) pairs; the epilogue writes a = bf16(silu(g) * u) (and optionally
 // g, u into h).  nout is n (plain) or inter (SwiGLU).
-template <int R, int MT, int G, int C, bool SWIGLU, bool LDSX = false>
-__global__ __launch_bounds__(kBlock) void k_gemv_nvfp4(const uint8_t* __restrict__ w, int64_t soff,
+template <int R, int MT, int G, int C, bool SWIGLU, bool LDSX = false, int NT = kBlock>
+__global__ __launch_bounds__(NT) void k_gemv_nvfp4(const uint8_t* __restrict__ w, int64_t soff,
                                                        float s_t, int nout, int k,
                                                        const uint16_t* __restrict__ x, int m,
                                                        float* __restrict__ y,
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4(const uint8_t* __restrict
     const int lane = lane_id();
     const int grp = G == kWave ? 0 : lane / G;  // one group per wave: rows are wave-uniform
     const int l = G == kWave ? lane : lane % G;
-    const int wave = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * (kBlock / kWave) + int(threadIdx.x) / kWave);
+    const int wave = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * (NT / kWave) + int(threadIdx.x) / kWave);
     const int unit = wave * kGroups + grp;
     const int64_t crow = k / 2, srow = k / 16;
 
@@ -112,14 +112,16 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4(const uint8_t* __restrict
         constexpr int NP = C / PC;
         static_assert(NP * PC == C, "whole passes");
         constexpr int kU = PC * 256;  // 16-byte units of one token's activations per pass
+        constexpr int PQ = kU / NT;   // of which each thread stages PQ
+        static_assert(PQ * NT == kU, "whole staging loads per thread");
         __shared__ u32x4 xs[MT * kU];
         const int tid = int(threadIdx.x);
-        u32x4 xg[MT][PC];
+        u32x4 xg[MT][PQ];
         auto xload = [&](int pass) {
 #pragma unroll
             for (int t = 0; t < MT; ++t)
 #pragma unroll
-                for (int q = 0; q < PC; ++q) xg[t][q] = ld16(xp[t] + 8u * (tid + kBlock * (pass * PC + q)));
+                for (int q = 0; q < PQ; ++q) xg[t][q] = ld16(xp[t] + 8u * (pass * kU + tid + NT * q));
         };
         // piece p of pass-chunk j of token t at slot t*kU + 4j + ((p + j/2) & 3):
         // conflict-free for the staging stores and the per-lane reads
@@ -127,8 +129,8 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4(const uint8_t* __restrict
 #pragma unroll
             for (int t = 0; t < MT; ++t)
 #pragma unroll
-                for (int q = 0; q < PC; ++q) {
-                    const uint32_t u = uint32_t(tid + kBlock * q);
+                for (int q = 0; q < PQ; ++q) {
+                    const uint32_t u = uint32_t(tid + NT * q);
                     xs[t * kU + 4 * (u >> 2) + (((u & 3u) + (u >> 3)) & 3u)] = xg[t][q];
                 }
         };
@@ -474,14 +476,25 @@ hipError_t go(const Args& A, hipStream_t s) {
         constexpr int R = SW ? (R0 < 2 ? 2 : R0) : R0;
         constexpr int per_unit = SW ? R / 2 : R;
         const int64_t units = (int64_t(A.nout) + per_unit - 1) / per_unit;
-        const int64_t per_block = (kBlock / kWave) * (kWave / G);
-        const dim3 grid(unsigned((units + per_block - 1) / per_block));
-        if (kMultiLdsX<G, C, MT> && A.k == 32 * C * G)
-            hipLaunchKernelGGL((k_gemv_nvfp4<R, MT, G, C, SW, kMultiLdsX<G, C, MT>>), grid, dim3(kBlock), 0, s,
+        if (kMultiLdsX<G, C, MT> && A.k == 32 * C * G) {
+            // Rows of six or more chunks per lane: eight waves share one
+            // staging of the activations (one 16-byte load per thread and
+            // token per pass), which halves the L2 -> LDS activation reads;
+            // these kernels hold two waves per SIMD either way.  Shorter
+            // rows keep four-wave workgroups: there the wider workgroup
+            // costs a resident wave per SIMD (batch-4 12288 x 4096 down
+            // 13.2 -> 12.6 us; the 24576 x 4096 gate+up would go 15.7 -> 19 us).
+            constexpr int NT = C % 2 == 0 && C >= 6 ? 2 * kBlock : kBlock;
+            const int64_t per_block = (NT / kWave) * (kWave / G);
+            const dim3 grid(unsigned((units + per_block - 1) / per_block));
+            hipLaunchKernelGGL((k_gemv_nvfp4<R, MT, G, C, SW, kMultiLdsX<G, C, MT>, NT>), grid, dim3(NT), 0, s,
                                A.w, A.soff, A.s_t, A.nout, A.k, A.x, A.m, A.y, A.a, A.h);
-        else
+        } else {
+            const int64_t per_block = (kBlock / kWave) * (kWave / G);
+            const dim3 grid(unsigned((units + per_block - 1) / per_block));
             hipLaunchKernelGGL((k_gemv_nvfp4<R, MT, G, C, SW>), grid, dim3(kBlock), 0, s, A.w, A.soff, A.s_t,
                                A.nout, A.k, A.x, A.m, A.y, A.a, A.h);
+        }
         return hipGetLastError();
     }
 }
