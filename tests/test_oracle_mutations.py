@@ -8,6 +8,7 @@ import synth
 from oracle import formats as F
 from oracle import ops as O
 from tests import test_oracle_a8 as A8
+from tests import test_oracle_abs as TA
 from tests import test_oracle_fp8 as TF8
 from tests import test_oracle_formats as TF
 from tests import test_oracle_gemv as TG
@@ -144,6 +145,60 @@ def _iq4_codebook_reversed(w, rows=None):
     return ORIG_IQ4(dict(w, codes=15 - w["codes"]), rows)
 
 
+
+# ---- tolerance scales (sum |w * x|) and the bf16 output allowance
+
+def _gemv_abs_signed_x(w, x, rows=None):
+    return O.act_values(x) @ np.abs(O.dequant(w, rows)).T
+
+
+def _gemv_abs_after_sum(w, x, rows=None):
+    return np.abs(O.act_values(x) @ O.dequant(w, rows).T)
+
+
+def _gemv_a8_abs_signed_w(w, xq, xd, rows=None):
+    return np.abs(O.act_q8_0_values(xq, xd)) @ O.dequant(w, rows).T
+
+
+def _q4_a8_abs_no_offset(w, xq, xd, rows=None):
+    return ORIG_Q4A8ABS(dict(w, codes=w["codes"].astype(np.int64) + 8), xq, xd, rows)
+
+
+def _moe_gate_up_abs_signed_w(layer, x, csr):
+    X = np.abs(O.act_values(x))
+    out = np.empty((len(csr["tok"]), 2 * layer.inter))
+    for u, e in enumerate(csr["experts"]):
+        lo, hi = csr["offsets"][u], csr["offsets"][u + 1]
+        out[lo:hi] = X[csr["tok"][lo:hi]] @ O.dequant_nvfp4(layer.gate_up[e]).T
+    return out
+
+
+def _moe_down_abs_signed_a(layer, a, csr, absolute=False):
+    if not absolute:
+        return ORIG_MOE_DOWN(layer, a, csr)
+    A = O.act_values(a)
+    out = np.empty((A.shape[0], layer.hidden))
+    for u, e in enumerate(csr["experts"]):
+        lo, hi = csr["offsets"][u], csr["offsets"][u + 1]
+        out[lo:hi] = A[lo:hi] @ np.abs(O.dequant_nvfp4(layer.down[e])).T
+    return out
+
+
+def _prefill_abs_after_sum(w, x, rows=None, cols=None):
+    Y, _ = ORIG_PREFILL(w, x, rows, cols)
+    return Y, np.abs(Y)
+
+
+def _bf16_ulp_binade_low(v):
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    _, e = np.frexp(v)
+    return np.where(v == 0, 2.0 ** -133, np.ldexp(1.0, np.maximum(e - 9, -133)))
+
+
+ORIG_Q4A8ABS = O.gemv_q4_0_a8_abs
+ORIG_MOE_DOWN = O.moe_down
+ORIG_PREFILL = O.prefill
+
 ORIG_Q4K = O.dequant_q4_k
 ORIG_IQ4 = O.dequant_iq4_xs
 
@@ -188,6 +243,28 @@ MUTATIONS = [
      [TK.test_iq4_xs_codebook_and_scale_offset]),
     ("IQ4_XS codebook reversed", [(O, "dequant_iq4_xs", _iq4_codebook_reversed)],
      [TK.test_iq4_xs_codebook_and_scale_offset]),
+    ("gemv_abs keeps the activation sign", [(O, "gemv_abs", _gemv_abs_signed_x),
+                                            (oracle, "gemv_abs", _gemv_abs_signed_x)],
+     [lambda: TA.test_gemv_abs_vs_exact("nvfp4", 3, 32, 2), lambda: TA.test_gemv_abs_vs_exact("q8_0", 4, 64, 2)]),
+    ("gemv_abs takes |.| after the sum", [(O, "gemv_abs", _gemv_abs_after_sum),
+                                          (oracle, "gemv_abs", _gemv_abs_after_sum)],
+     [TA.test_gemv_abs_is_larger_than_the_signed_sum]),
+    ("gemv_a8_abs keeps the weight sign", [(O, "gemv_a8_abs", _gemv_a8_abs_signed_w),
+                                           (oracle, "gemv_a8_abs", _gemv_a8_abs_signed_w)],
+     [lambda: TA.test_gemv_a8_abs_vs_exact(synth.Q4_K)]),
+    ("gemv_q4_0_a8_abs drops the offset of 8", [(O, "gemv_q4_0_a8_abs", _q4_a8_abs_no_offset),
+                                                (oracle, "gemv_q4_0_a8_abs", _q4_a8_abs_no_offset)],
+     [TA.test_gemv_q4_0_a8_abs_vs_exact]),
+    ("moe_gate_up_abs keeps the weight sign", [(O, "moe_gate_up_abs", _moe_gate_up_abs_signed_w)],
+     [TA.test_moe_gate_up_abs_vs_exact]),
+    ("moe_down(absolute) keeps the activation sign", [(O, "moe_down", _moe_down_abs_signed_a)],
+     [TA.test_moe_down_abs_vs_exact]),
+    ("prefill's abs output takes |.| after the sum", [(O, "prefill", _prefill_abs_after_sum),
+                                                      (oracle, "prefill", _prefill_abs_after_sum)],
+     [TA.test_prefill_abs_vs_exact]),
+    ("bf16_ulp one binade too fine", [(F, "bf16_ulp", _bf16_ulp_binade_low),
+                                      (oracle, "bf16_ulp", _bf16_ulp_binade_low)],
+     [TA.test_bf16_ulp_vs_torch_spacing]),
 ]
 
 
