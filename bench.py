@@ -75,6 +75,42 @@ def source_digest(files) -> str:
     return h.hexdigest()[:16]
 
 
+PROFILES = {  # config -> its rocprofv3 summary under profiles/
+    "dense": "nvfp4_gemv__dense_layer_h4096_i12288_m1", "dense-m4": "nvfp4_gemv__dense_layer_h4096_i12288_m4",
+    "q8": "q8_0_gemv__1024x1024_m1", "w4a8": "q4_0_a8_gemv__17408x5120_m1",
+    "w4a8-m4": "q4_0_a8_gemv__17408x5120_m4", "fp8": "fp8_gemv__24576x4096_block128_m1",
+    "q4k": "q4_k_a8_gemv__17408x5120_m1", "q5k": "q5_k_a8_gemv__17408x5120_m1",
+    "q6k": "q6_k_a8_gemv__17408x5120_m1", "iq4xs": "iq4_xs_a8_gemv__17408x5120_m1",
+    "moe": "moe_gate_up_down__e256_h2048_i512_top8_t1", "moe-t4": "moe_gate_up_down__e256_h2048_i512_top8_t4",
+    "moe-prefill": "moe_prefill_grouped_mfma__e256_h2048_i512_top8_t512",
+    "prefill64": "prefill_mfma__12288x4096_m64", "prefill128": "prefill_mfma__12288x4096_m128",
+    "prefill512": "prefill_mfma__12288x4096_m512",
+    "w4a8-prefill512": "q4_0_a8_prefill_int8_mfma__17408x5120_m512",
+    "probe-read": "probe_read__1GiB_streaming", "probe-mfma": "probe_mfma__bf16_16x16x32",
+}
+
+
+def kernel_trace_from_profile(config: str, cls) -> dict | None:
+    """The dominant launch's mean duration in the committed rocprofv3 kernel
+    trace of this config (sum over its kernels of their mean durations), or
+    None when there is no summary or it was taken on other kernel sources."""
+    name = PROFILES.get(config)
+    path = os.path.join(ROOT, "profiles", f"{name}.txt") if name else None
+    if not path or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel sources digest ([0-9a-f]+)", text)
+    if not m or m.group(1) != source_digest(cls.sources):
+        return None
+    total = 0.0
+    for pat in cls.kernel_re:
+        rows = [ln for ln in text.splitlines() if re.match(r"\s*\d+\s+[\d.]+", ln) and re.search(pat, ln)]
+        if not rows:
+            return None
+        total += sum(float(r.split()[1]) for r in rows)
+    return {"us_per_launch": total, "file": f"profiles/{name}.txt"}
+
+
 def traffic_from_profile(config: str, cls) -> int | None:
     """HBM bytes per dominant launch from profiles/traffic.json, or None when
     there is no entry or the kernel's sources changed since it was taken."""
@@ -120,19 +156,42 @@ class Workload:
     def cpu_sample(self, part: int, parts: int) -> float:
         raise NotImplementedError
 
-    def cpu_baseline(self, budget_s=12.0):
+    # also time the oracle on one thread (reported beside the all-core figure)
+    cpu_single_thread = False
+
+    def cpu_baseline(self, budget_s=12.0, threads=1):
         from threadpoolctl import threadpool_limits
 
         total, done, n = 0.0, 0.0, 0
-        with threadpool_limits(limits=1):
+        with threadpool_limits(limits=threads):
             while total < budget_s and n < 1_000_000:
                 t1 = time.perf_counter()
                 done += self.cpu_sample(n % self.cpu_parts, self.cpu_parts)
                 total += time.perf_counter() - t1
                 n += 1
-        return {"value": done / total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        return {"value": done / total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
                 "sample": f"{n} samples, each {self.cpu_part_desc()} ({n * self.cpu_part_steps():.3f} steps in "
-                          f"all) in {total:.1f} s, fp64 numpy, 1 thread"}
+                          f"all) in {total:.1f} s, fp64 numpy, BLAS on {threads} thread(s)"}
+
+
+def host_cores() -> int:
+    """CPU cores this process may run on (its affinity mask)."""
+    return len(os.sched_getaffinity(0))
+
+
+def blas_config() -> dict:
+    """What the CPU baseline's matmuls run on: numpy's BLAS build and the
+    thread pools threadpoolctl sees, plus OMP_NUM_THREADS."""
+    from threadpoolctl import threadpool_info
+
+    try:
+        build = np.show_config(mode="dicts").get("Build Dependencies", {}).get("blas", {})
+    except TypeError:  # older numpy: no dict mode
+        build = {}
+    pools = [{k: p.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer", "architecture")}
+             for p in threadpool_info()]
+    return {"numpy_blas": {k: build.get(k) for k in ("name", "version", "openblas configuration")},
+            "thread_pools": pools, "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
 
 
 def _slice(part: int, parts: int, n: int) -> np.ndarray:
@@ -147,7 +206,8 @@ class DenseLayer(Workload):
     """gate+up [2I x H] + SwiGLU, then down [H x I], batch m."""
 
     sources = ("k_gemv_nvfp4.hip", "qg_gemv_core.hpp", "qg_mfma.hpp", "qg_reduce.hpp")
-    kernel_re = (r"k_gemv_nvfp4\w*<(?:\d+, ){4}true\b",)  # the SwiGLU instance (fifth argument)
+    # the SwiGLU instance: fourth template argument of the batch-1 kernel, fifth of the batched one
+    kernel_re = (r"k_gemv_nvfp4_stream<(?:\d+, ){3}true\b|k_gemv_nvfp4<(?:\d+, ){4}true\b",)
 
     def __init__(self, m=1):
         import torch
@@ -189,10 +249,11 @@ class DenseLayer(Workload):
     def dominant_launch(self, i):
         self._gate_up(i)
 
-    def cpu_baseline(self, budget_s=12.0):
+    def cpu_baseline(self, budget_s=12.0, threads=1):
         """The oracle running whole decode steps of this layer (fp64 numpy
-        dequantize + dot, one thread), repeated until the time budget is used;
-        throughput over the same algorithmic bytes as the GPU step."""
+        dequantize + dot, the matmuls on `threads` BLAS threads), repeated
+        until the time budget is used; throughput over the same algorithmic
+        bytes as the GPU step."""
         import oracle
         from threadpoolctl import threadpool_limits
 
@@ -200,7 +261,7 @@ class DenseLayer(Workload):
         H, I = self.H, self.I
         chunk = 2048
         total, done_bytes, steps = 0.0, 0, 0
-        with threadpool_limits(limits=1):
+        with threadpool_limits(limits=threads):
             while total < budget_s:
                 t1 = time.perf_counter()
                 a = np.empty((self.m, I))
@@ -213,14 +274,15 @@ class DenseLayer(Workload):
                 total += time.perf_counter() - t1
                 done_bytes += self.alg_step
                 steps += 1
-        return {"value": done_bytes / total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        return {"value": done_bytes / total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
                 "sample": f"{steps} whole decode steps of the same layer (gate+up, SwiGLU, down) "
-                          f"in {total:.1f} s, fp64 numpy, 1 thread"}
+                          f"in {total:.1f} s, fp64 numpy, BLAS on {threads} thread(s)"}
 
 
 class Q8Gemv(Workload):
     sources = ("k_gemv_q8.hip",)
     kernel_re = (r"k_gemv_q8_0\b",)
+    cpu_single_thread = True
 
     def __init__(self, m=1):
         import torch
@@ -305,6 +367,7 @@ class Fp8Gemv(Workload):
 class W4A8Gemv(Workload):
     sources = ("k_gemv_a8.hip", "qg_mfma.hpp", "qg_reduce.hpp")
     kernel_re = (r"k_gemv_q4_0_a8\b",)
+    cpu_single_thread = True
 
     def __init__(self, m=1):
         import torch
@@ -673,6 +736,93 @@ class PrefillWs(Prefill):
     dominant_launch = step
 
 
+class ProbeRead(Workload):
+    """Achievable HBM read bandwidth: the library's streaming-read probe over
+    rotating 1 GiB buffers (16-byte non-temporal loads, 1 KB per wave-wide
+    load, eight in flight per lane), at the workgroups-per-CU count that reads
+    fastest here."""
+    sources = ("k_probe.hip", "qg_mfma.hpp")
+    kernel_re = (r"k_probe_read\b",)
+    cpu_parts = 1
+
+    def __init__(self, gib=1):
+        import torch
+        import moe_expert_gemv_amd as qg
+
+        self.qg = qg
+        self.bytes = gib << 30
+        self.bufs = [torch.full((self.bytes,), 7, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        self.sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+        self.wg = best_read_probe_shape(self.bufs[0], self.sink)
+        self.alg_step = self.dominant_bytes = self.bytes
+        self.flops_step = 0
+        self.name = f"streaming-read probe: {gib} GiB per launch, {self.wg} four-wave workgroup(s) per CU"
+        self.dominant = "streaming-read probe"
+
+    def step(self, i):
+        self.qg.qg_probe_read(self.bufs[i % 2], self.wg, self.sink)
+
+    dominant_launch = step
+
+
+class ProbeMfma(Workload):
+    """Achievable dense bf16 MFMA rate: v_mfma_f32_16x16x32_bf16 with sixteen
+    independent accumulators per wave, two waves per SIMD."""
+    sources = ("k_probe.hip", "qg_mfma.hpp")
+    kernel_re = (r"k_probe_mfma\b",)
+    bound = "mfma"
+    cpu_parts = 1
+
+    def __init__(self, iters=4000):
+        import torch
+        import moe_expert_gemv_amd as qg
+
+        self.qg, self.iters = qg, iters
+        self.sink = torch.zeros(64, dtype=torch.float32, device="cuda")
+        self.flops_step = qg.qg_probe_mfma_bf16(iters, self.sink)
+        torch.cuda.synchronize()
+        self.alg_step = self.dominant_bytes = 0
+        self.name = f"bf16 MFMA probe: {iters} rounds of 16 independent 16x16x32 MFMAs per wave, 8 waves per CU"
+        self.dominant = "bf16 MFMA probe"
+
+    def step(self, i):
+        self.qg.qg_probe_mfma_bf16(self.iters, self.sink)
+
+    dominant_launch = step
+
+
+def best_read_probe_shape(buf, sink, shapes=(1, 2, 4)) -> int:
+    """Workgroups per CU at which the read probe streams fastest (a short sweep)."""
+    import torch
+    import moe_expert_gemv_amd as qg
+
+    best, best_t = shapes[0], float("inf")
+    for wg in shapes:
+        qg.qg_probe_read(buf, wg, sink)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(5):
+            qg.qg_probe_read(buf, wg, sink)
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b)
+        if t < best_t:
+            best, best_t = wg, t
+    return best
+
+
+def achievable_peaks(bound: str) -> dict:
+    """What this GPU reaches with the probes: read GB/s for HBM-bound
+    configs, bf16 MFMA TFLOP/s for matrix-core-bound ones (graph replays of
+    the probe between two HIP events, best of three)."""
+    wl = ProbeRead() if bound == "hbm" else ProbeMfma()
+    _, mean = time_dominant(wl, 8)
+    if bound == "hbm":
+        return {"read_gbs": wl.bytes / (mean * 1e-3) / 1e9, "probe": wl.name}
+    return {"bf16_mfma_tflops": wl.flops_step / (mean * 1e-3) / 1e12, "probe": wl.name}
+
+
 CONFIGS = {  # name -> (workload class, its size argument)
     "dense": (DenseLayer, 1),
     "dense-m4": (DenseLayer, 4),
@@ -691,6 +841,8 @@ CONFIGS = {  # name -> (workload class, its size argument)
     "prefill128": (PrefillWs, 128),
     "prefill512": (Prefill, 512),
     "w4a8-prefill512": (PrefillA8, 512),
+    "probe-read": (ProbeRead, 1),
+    "probe-mfma": (ProbeMfma, 4000),
 }
 
 
@@ -777,91 +929,6 @@ def time_dominant(wl: Workload, launches: int, reps: int = 3):
         del keep
         per.append(a.elapsed_time(b) / launches)  # ms
     return float(min(per)), float(np.mean(per))
-
-
-def parse_gpu_state(text: str):
-    """Clocks and temperatures from `amd-smi metric --clock --temperature
-    --json` output (one GPU): mean and max of the XCDs' current gfx clocks,
-    the memory clock, whether clocks are locked, hotspot and memory
-    temperature.  None if the text does not parse."""
-    try:
-        j = json.loads(text[text.index("["):text.rindex("]") + 1])
-        g = j[0]
-        clk, temp = g["clock"], g["temperature"]
-        gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_")]
-        val = lambda d: d["value"] if isinstance(d, dict) else None
-        return {"gfx_mhz_mean": float(np.mean(gfx)), "gfx_mhz_max": max(gfx),
-                "gfx_mhz_limit": clk["gfx_0"]["max_clk"]["value"], "mem_mhz": clk["mem_0"]["clk"]["value"],
-                "clocks_locked": clk["gfx_0"].get("clk_locked"), "hotspot_c": val(temp.get("hotspot")),
-                "mem_c": val(temp.get("mem"))}
-    except (ValueError, KeyError, IndexError, TypeError):
-        return None
-
-
-def _smi_start(device: int):
-    """Start amd-smi (a child process) on the device's clocks and
-    temperatures; None where it cannot be started."""
-    import subprocess
-
-    try:
-        return subprocess.Popen(["amd-smi", "metric", "-g", str(device), "--clock", "--temperature", "--json"],
-                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
-    except OSError:
-        return None
-
-
-def _smi_finish(proc):
-    import subprocess
-
-    if proc is None:
-        return None
-    try:
-        out, _ = proc.communicate(timeout=30)
-    except subprocess.TimeoutExpired:
-        proc.kill()
-        proc.communicate()
-        return None
-    return parse_gpu_state(out) if proc.returncode == 0 else None
-
-
-def gpu_state(device: int):
-    """The device's clocks and temperatures as amd-smi reports them (None
-    where amd-smi is missing or fails), and the seconds the query took;
-    clocks are not pinned."""
-    t0 = time.perf_counter()
-    st = _smi_finish(_smi_start(device))
-    return st, time.perf_counter() - t0
-
-
-def gpu_state_loaded(wl, device: int, smi_s: float):
-    """gpu_state sampled while the GPU runs the workload: amd-smi is started
-    first, then a graph of steps is replayed enough times to queue about
-    1.5 * smi_s + 0.5 seconds of GPU work (smi_s: how long an idle query
-    took; at most 8 s), so the whole query runs under load; then the stream
-    is synchronised.  Outside any timed region."""
-    import torch
-
-    stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        wl.step(0)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(50):
-            wl.step(i)
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        g.replay()
-    torch.cuda.synchronize()
-    per = max(time.perf_counter() - t0, 1e-5)
-    backlog_s = min(1.5 * smi_s + 0.5, 8.0)
-    proc = _smi_start(device)
-    with torch.cuda.stream(stream):
-        for _ in range(int(min(backlog_s / per, 50000))):
-            g.replay()
-    st = _smi_finish(proc)
-    torch.cuda.synchronize()
-    return st
 
 
 def calibrate_copy():
@@ -972,7 +1039,7 @@ def main():
     ap.add_argument("--config", default="dense", choices=sorted(CONFIGS))
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of a graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-gpu-state", action="store_true", help="skip the amd-smi clock and temperature samples")
+    ap.add_argument("--no-probe", action="store_true", help="skip the achievable-peak probe")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain copy of known size first (for byte-counter calibration)")
@@ -1010,12 +1077,8 @@ def main():
         calibrate_copy()
     print(f"[bench] {wl.name}; {getattr(wl, 'R', 1)} weight copies; timing", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
-    state_before, smi_s = (None, 0.0) if args.no_gpu_state else gpu_state(torch.cuda.current_device())
     ms = time_steps(wl, args.steps, args.warmup, not args.no_graph)
     dom_best, dom_mean = time_dominant(wl, max(20, min(args.steps, 200)))
-    state_loaded = None
-    if state_before is not None:
-        state_loaded = gpu_state_loaded(wl, torch.cuda.current_device(), smi_s)
     value = wl.alg_step / (ms * 1e-3) / 1e9
 
     if wl.bound == "mfma":
@@ -1028,14 +1091,34 @@ def main():
                 "frac": achieved / PEAK_HBM_GBS}
     roof["traffic"] = traffic_from_profile(args.config, cls)
     roof["kernel"] = wl.dominant
+    # HIP events around a graph of back-to-back launches: the per-launch
+    # period, i.e. the kernel plus the gap between two dependent launches
     roof["us_per_launch"] = dom_mean * 1e3
     roof["us_per_launch_best_replay"] = dom_best * 1e3
     roof["alg_bytes_per_launch"] = wl.dominant_bytes
+    if not args.no_probe and not args.config.startswith("probe") and (
+            wl.bound == "hbm" or wl.mfma_peak[0] == PEAK_BF16_TFLOPS):
+        print("[bench] achievable peak (probe)", file=sys.stderr, flush=True)
+        roof["achievable"] = achievable_peaks("hbm" if wl.bound == "hbm" else "mfma")
+        ach = roof["achievable"].get("read_gbs") or roof["achievable"].get("bf16_mfma_tflops")
+        roof["achievable"]["frac_of_achievable"] = roof["achieved"] / ach
+    kt = kernel_trace_from_profile(args.config, cls)
+    if kt:  # the kernel alone, from the committed rocprofv3 trace of this command
+        t_k = kt["us_per_launch"] * 1e-6
+        roof["kernel_trace"] = dict(kt, frac=(wl.flops_step / t_k / 1e12 if wl.bound == "mfma"
+                                              else wl.dominant_bytes / t_k / 1e9) / roof["peak"])
 
     cpu = None
     if not args.no_cpu_baseline and hasattr(wl, "cpu_baseline"):
-        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        cpu = wl.cpu_baseline(args.cpu_budget)
+        cores = host_cores()
+        print(f"[bench] timing the CPU oracle baseline on {cores} cores", file=sys.stderr, flush=True)
+        cpu = wl.cpu_baseline(args.cpu_budget, cores)
+        if wl.cpu_single_thread:
+            print("[bench] timing the CPU oracle baseline on 1 thread", file=sys.stderr, flush=True)
+            one = wl.cpu_baseline(args.cpu_budget, 1)
+            cpu["single_thread"] = {"value": one["value"], "unit": one["unit"], "sample": one["sample"]}
+        cpu["host_cores"] = cores
+        cpu["blas"] = blas_config()
 
     out = {
         "metric": METRIC,
@@ -1058,7 +1141,6 @@ def main():
                    "kernel_source_digest": source_digest(cls.sources)},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "gpu_state": {"idle_before": state_before, "under_load_after": state_loaded},
     }
     print(json.dumps(out), flush=True)
 

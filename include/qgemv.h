@@ -74,6 +74,7 @@ extern "C" {
 #define QG_OK            0
 #define QG_EINVAL       (-1) /* null pointer, bad shape, misalignment, bad code */
 #define QG_EUNSUPPORTED (-2) /* shape outside what the kernels implement */
+#define QG_EVERSION     (-3) /* packed buffer or descriptor of another layout version */
 #define QG_ENOSPC       (-4) /* destination or workspace buffer too small */
 #define QG_EHIP         (-5) /* HIP runtime or launch error */
 
@@ -87,9 +88,10 @@ extern "C" {
 #define QG_Q5_K   7
 #define QG_Q6_K   8
 #define QG_IQ4_XS 9
+#define QG_NVFP4_GATE_UP 10 /* qg_packed_check only: a matrix from qg_pack_nvfp4_gate_up */
 
-#define QG_ABI_VERSION    1
-#define QG_LAYOUT_VERSION 1  /* packed device layout described below */
+#define QG_ABI_VERSION    2
+#define QG_LAYOUT_VERSION 2  /* packed device layout described below */
 #define QG_MAX_M          16 /* largest token count of the GEMV entry points */
 
 /* ABI and packed-layout versions this library implements. */
@@ -100,13 +102,26 @@ const char* qg_status_string(int status);
 /* hipError_t of the most recent QG_EHIP return on any thread (0 if none). */
 int qg_last_hip_error(void);
 
-/* ------------------------------------------------------ packed layout V1
+/* ------------------------------------------------------ packed layout V2
  * The "split-plane repack" of the pages (bw24 README and memra README, feature
  * lists): codes and scales live in separate planes so that each lane streams
  * 16 contiguous code bytes per load and the scales follow in a plane of their
  * own.  A packed matrix is one buffer:
  *
- *   [codes plane][pad to 256 B][scale plane][pad to 256 B]
+ *   [codes plane][pad to 256 B][scale plane][pad to 256 B][stamp, 256 B]
+ *
+ *   The stamp names the layout (the pages' container rejects files of a newer
+ *   format version rather than misread them: Lumen landing page, "06 Format"):
+ *   uint32 magic 0x4B504751 (the bytes "QGPK"), uint32 layout version
+ *   (QG_LAYOUT_VERSION), uint32 format code, uint32 row order (0 logical, 1
+ *   gate/up interleaved), int64 n, int64 k; the rest of the 256 bytes zero.
+ *   The unpackers and qg_packed_check verify it on the host (QG_EVERSION for
+ *   another layout version, QG_EINVAL for a missing stamp or another format,
+ *   row order or shape).  The device entry points cannot read device memory
+ *   from the host without a synchronisation, so they take a packed device
+ *   buffer as this version's layout: a buffer that crosses a version
+ *   boundary (a file, another process) is checked with qg_packed_check
+ *   before it is uploaded.  The kernels never read the stamp.
  *
  *   NVFP4  codes: n rows of k/2 bytes; byte j of a row holds element 2j in its
  *          low nibble and element 2j+1 in its high nibble.
@@ -140,6 +155,14 @@ int qg_last_hip_error(void);
 
 /* Bytes of a packed matrix (0 if fmt/n/k are invalid). */
 size_t qg_packed_bytes(int fmt, int64_t n, int64_t k);
+
+/* Check a packed host buffer (e.g. one read back from a file) against the
+ * format and shape the caller expects, before uploading it.  fmt: any format
+ * code, or QG_NVFP4_GATE_UP for a fused gate/up matrix of n = 2 * inter rows.
+ * QG_OK; QG_EVERSION if the stamp names another layout version; QG_EINVAL for
+ * a null buffer, invalid fmt/n/k, a missing stamp, or a stamp of another
+ * format, row order or shape; QG_ENOSPC if bytes < qg_packed_bytes. */
+int qg_packed_check(int fmt, const void* buf, size_t bytes, int64_t n, int64_t k);
 /* Byte offset of the scale plane inside a packed matrix (0 if invalid). */
 size_t qg_scale_plane_offset(int fmt, int64_t n, int64_t k);
 
@@ -164,7 +187,9 @@ int qg_pack_q8_0(const int8_t* codes, const uint16_t* scales_f16, int64_t n, int
 int qg_pack_nvfp4_gate_up(const uint8_t* codes, const uint8_t* scales_e4m3, int64_t inter, int64_t k,
                           void* dst, size_t dst_bytes);
 
-/* Unpackers: the exact inverse of the packers (host -> host). */
+/* Unpackers: the exact inverse of the packers (host -> host).  Each first
+ * verifies the buffer's stamp as qg_packed_check does (QG_EVERSION for a
+ * buffer of another layout version). */
 int qg_unpack_nvfp4(const void* src, size_t src_bytes, int64_t n, int64_t k,
                     uint8_t* codes, uint8_t* scales_e4m3);
 int qg_unpack_nvfp4_gate_up(const void* src, size_t src_bytes, int64_t inter, int64_t k,
@@ -312,7 +337,10 @@ int moe_route_topk(const float* logits, int64_t t, int64_t n_experts, int64_t to
  * qg_pack_nvfp4; expert e's packed matrices start at gate_up + e *
  * gate_up_stride and down + e * down_stride (device, strides in bytes,
  * multiples of 256, at least qg_packed_bytes of the matrix).  Tensor scales:
- * device fp32 arrays of n_experts + has_shared entries. */
+ * device fp32 arrays of n_experts + has_shared entries.  layout_version: the
+ * packed layout the caller built the experts with; every MoE entry point
+ * returns QG_EVERSION before any launch when it is not QG_LAYOUT_VERSION
+ * (moe_workspace_bytes and moe_prefill_workspace_bytes return 0). */
 typedef struct qg_moe_desc {
     int32_t n_experts;
     int32_t top_k;
@@ -326,6 +354,8 @@ typedef struct qg_moe_desc {
     int64_t down_stride;
     const float* gate_up_scale;
     const float* down_scale;
+    int32_t layout_version; /* QG_LAYOUT_VERSION of the packed experts, else QG_EVERSION */
+    int32_t reserved;       /* 0 */
 } qg_moe_desc;
 
 /* Workspace bytes moe_gemv_grouped needs for t tokens (0 if d is invalid). */
@@ -420,6 +450,28 @@ size_t qgemm_prefill_workspace_bytes(int64_t n, int64_t k, int64_t m);
  * agrees with qgemm_prefill to rounding (the summation order differs). */
 int qgemm_prefill_ws(const void* w, float tensor_scale, int64_t n, int64_t k, const uint16_t* x,
                      int64_t m, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------ achievable-peak probes
+ * Measurement tools, not part of the decode path: what this GPU reaches with
+ * the instructions the kernels use, printed beside the data-sheet peaks (the
+ * pages keep such microbenchmarks next to their kernels: bw24 README, crate
+ * table, the probe crate; memra README, research notes, microbenched peaks).
+ *
+ * qg_probe_read: stream `bytes` of the device buffer buf once (16-byte
+ * non-temporal loads, eight in flight per lane, 1 KB contiguous per wave-wide
+ * load) with wg_per_cu (1..8) four-wave workgroups per compute unit; time it
+ * on the stream for the achievable HBM read bandwidth.  buf: device, 16-byte
+ * aligned, bytes a positive multiple of 16; sink: device uint32, written only
+ * in the (practically impossible) case that the folded data equals a fixed
+ * key, so that the loads are not optimised away.
+ *
+ * qg_probe_mfma_bf16: iters rounds of sixteen independent
+ * v_mfma_f32_16x16x32_bf16 per wave, eight waves per compute unit, no memory
+ * traffic; *flops (host) receives the floating-point operations launched
+ * (2 * 16 * 16 * 32 per MFMA).  sink: device float, written only if the
+ * result equals a fixed key.  1 <= iters <= 2^32. */
+int qg_probe_read(const void* buf, size_t bytes, int wg_per_cu, uint32_t* sink, void* stream);
+int qg_probe_mfma_bf16(int64_t iters, float* sink, int64_t* flops, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,22 +22,25 @@ __all__ = [
     "QG_NVFP4", "QG_Q8_0", "QG_Q4_0", "QG_FP8_TENSOR", "QG_FP8_B128", "QG_MAX_M", "QG_MOE_KEEP_H",
     "QG_Q4_K", "QG_Q5_K", "QG_Q6_K", "QG_IQ4_XS", "KQUANT_FORMATS", "qg_pack_kquant", "qg_unpack_kquant",
     "qgemv_kquant_a8", "qgemm_prefill_a8",
-    "qg_abi_version", "qg_layout_version", "qg_status_string", "qg_packed_bytes",
+    "qg_abi_version", "qg_layout_version", "qg_status_string", "qg_packed_bytes", "qg_packed_check",
+    "QG_EVERSION", "QG_NVFP4_GATE_UP", "QG_LAYOUT_VERSION",
     "qg_scale_plane_offset", "qg_pack_nvfp4", "qg_pack_nvfp4_gate_up", "qg_pack_q4_0", "qg_pack_q8_0",
     "qg_unpack_nvfp4", "qg_unpack_nvfp4_gate_up", "qg_unpack_q4_0", "qg_unpack_q8_0", "qg_pack_fp8",
     "qg_unpack_fp8", "qgemv_fp8", "fp8_scale_shape", "qg_dequant",
     "qgemv_q8_0", "qgemv_nvfp4", "qgemv_nvfp4_swiglu", "qg_quantize_q8_0_act",
     "qgemv_q4_0_a8", "moe_route_topk", "QgMoeDesc", "moe_workspace_bytes",
     "moe_gemv_grouped", "moe_forward", "moe_prefill_workspace_bytes", "moe_prefill", "qgemm_prefill",
-    "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
+    "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws", "qg_probe_read", "qg_probe_mfma_bf16",
     "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
 
-QG_OK, QG_EINVAL, QG_EUNSUPPORTED, QG_ENOSPC, QG_EHIP = 0, -1, -2, -4, -5
+QG_OK, QG_EINVAL, QG_EUNSUPPORTED, QG_EVERSION, QG_ENOSPC, QG_EHIP = 0, -1, -2, -3, -4, -5
 QG_NVFP4, QG_Q8_0, QG_Q4_0, QG_FP8_TENSOR, QG_FP8_B128 = 1, 2, 3, 4, 5
 QG_Q4_K, QG_Q5_K, QG_Q6_K, QG_IQ4_XS = 6, 7, 8, 9
+QG_NVFP4_GATE_UP = 10  # qg_packed_check only
+QG_LAYOUT_VERSION = 2
 KQUANT_FORMATS = (QG_Q4_K, QG_Q5_K, QG_Q6_K, QG_IQ4_XS)
 QG_MAX_M = 16
 QG_MOE_KEEP_H = 1
@@ -71,7 +74,13 @@ class QgMoeDesc(ctypes.Structure):
         ("down_stride", ctypes.c_int64),
         ("gate_up_scale", ctypes.c_void_p),
         ("down_scale", ctypes.c_void_p),
+        ("layout_version", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
+
+    def __init__(self, **kw):
+        kw.setdefault("layout_version", QG_LAYOUT_VERSION)
+        super().__init__(**kw)
 
 
 _P, _I64, _I32, _F32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -83,6 +92,7 @@ _SIGNATURES = {
     "qg_status_string": (ctypes.c_char_p, [_I32]),
     "qg_last_hip_error": (_I32, []),
     "qg_packed_bytes": (_SZ, [_I32, _I64, _I64]),
+    "qg_packed_check": (_I32, [_I32, _P, _SZ, _I64, _I64]),
     "qg_scale_plane_offset": (_SZ, [_I32, _I64, _I64]),
     "qg_pack_nvfp4": (_I32, [_P, _P, _I64, _I64, _P, _SZ]),
     "qg_pack_nvfp4_gate_up": (_I32, [_P, _P, _I64, _I64, _P, _SZ]),
@@ -114,6 +124,8 @@ _SIGNATURES = {
     "qgemm_prefill": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P]),
     "qgemm_prefill_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "qgemm_prefill_ws": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]),
+    "qg_probe_read": (_I32, [_P, _SZ, _I32, _P, _P]),
+    "qg_probe_mfma_bf16": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_int64), _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -186,6 +198,13 @@ def qg_status_string(status: int) -> str:
 
 def qg_packed_bytes(fmt: int, n: int, k: int) -> int:
     return lib().qg_packed_bytes(fmt, n, k)
+
+
+def qg_packed_check(fmt: int, buf, n: int, k: int) -> int:
+    """Status of a packed host buffer's stamp against (fmt, n, k): QG_OK,
+    QG_EVERSION, QG_EINVAL or QG_ENOSPC (returned, not raised)."""
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    return int(lib().qg_packed_check(fmt, _hptr(buf), buf.nbytes, n, k))
 
 
 def qg_scale_plane_offset(fmt: int, n: int, k: int) -> int:
@@ -447,3 +466,16 @@ def qgemm_prefill_ws(w, tensor_scale, n, k, x, m, y, ws, ws_bytes=None, stream=N
     _check("qgemm_prefill_ws",
            lib().qgemm_prefill_ws(_dptr(w), tensor_scale, n, k, _dptr(x), m, _dptr(y), ptr, nbytes,
                                   _stream(stream)))
+
+
+def qg_probe_read(buf, wg_per_cu, sink, stream=None) -> None:
+    """Stream the device tensor buf once (achievable read bandwidth probe)."""
+    _check("qg_probe_read", lib().qg_probe_read(_dptr(buf), buf.numel() * buf.element_size(), wg_per_cu,
+                                                _dptr(sink), _stream(stream)))
+
+
+def qg_probe_mfma_bf16(iters, sink, stream=None) -> int:
+    """Launch the bf16 MFMA peak probe; returns the flops it performs."""
+    flops = ctypes.c_int64(0)
+    _check("qg_probe_mfma_bf16", lib().qg_probe_mfma_bf16(iters, _dptr(sink), ctypes.byref(flops), _stream(stream)))
+    return int(flops.value)

@@ -36,7 +36,7 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-
 
 HIP_SOURCES = ["qg_api.hip", "k_gemv_nvfp4.hip", "k_gemv_q8.hip", "k_gemv_a8.hip", "k_gemv_fp8.hip",
                "k_gemv_kquant.hip", "k_dequant.hip", "k_moe.hip", "k_moe_prefill.hip", "k_prefill.hip",
-               "k_prefill_a8.hip"]
+               "k_prefill_a8.hip", "k_probe.hip"]
 CXX_SOURCES = ["qg_host.cpp"]
 # Per-source compiler options.  The int8 prefill reads every MFMA result back
 # into VALU arithmetic; the VGPR form of the MFMA saves a v_accvgpr_read per

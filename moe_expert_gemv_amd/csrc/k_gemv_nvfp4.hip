@@ -18,7 +18,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <cstdlib>
 #include <type_traits>
 
 #include "qg_device.hpp"
@@ -35,20 +34,19 @@ namespace {
 constexpr int kBlock = 256;  // threads per workgroup (4 waves)
 
 // Streaming kernel shape, measured on MI355X over rows per unit R in
-// {1, 2, 4, 8} and units per wave U in {1, 2, 4, 8}: four rows per unit for
+// {1, 2, 4, 8} and units per wave in {1, 2, 4, 8}: four rows per unit for
 // short rows (8 KB of codes per wave at k = 4096), two for long rows (12 KB
 // at k = 12288), one unit per wave.
 template <int C>
 constexpr int kStreamRows = C <= 2 ? 4 : 2;
-constexpr int kStreamUnitsDefault = 1;
 // Activations staged in LDS once per workgroup (rather than loaded by every
 // lane from L1/L2) for rows of three or more chunks per lane that fill every
 // lane's chunk slots (k == 2048 * C; other rows keep the per-lane loads): measured on
 // MI355X, the 4096 x 12288 down projection went from 7.35 to 6.9 us, while
 // at two chunks per lane (4096-element rows) the staging's extra registers
 // cost occupancy and time.
-template <int G, int C, int U>
-constexpr bool kStreamLdsX = G == kWave && U == 1 && C >= 3;
+template <int G, int C>
+constexpr bool kStreamLdsX = G == kWave && C >= 3;
 // Two to four tokens: activations staged in LDS for full rows of one or an
 // even number of chunks per lane, in passes of two chunks (32 KB of LDS at
 // four tokens).
@@ -254,23 +252,14 @@ __global__ __launch_bounds__(NT) void k_gemv_nvfp4(const uint8_t* __restrict__ w
     }
 }
 
-// One-token streaming variant.  A wave handles U units (U compile-time):
-// units w, w + W, w + 2W, ... of the W waves in the grid, so at any moment the
-// GPU's waves read neighbouring rows.  The U units run as a straight-line
-// two-deep register pipeline -- the loads of unit i+1 are issued before unit
-// i is decoded and reduced -- and the lane's activation chunks are loaded once
-// (a lane always covers the same k range).  Being straight-line code (no loop
-// back-edge), the compiler counts outstanding loads exactly and keeps the
-// prefetch in flight; sched_barrier stops it from sinking a prefetch below
-// the arithmetic.  Same per-row arithmetic and reduction order as
-// k_gemv_nvfp4.
-template <int R, int G, int C>
-struct StreamBuf {
-    u32x4 cw[C][R];
-    uint32_t sw[C][R];
-};
-
-template <int R, int G, int C, int U, bool SWIGLU, bool LDSX>
+// One-token streaming variant: one unit (R rows per lane group) per wave,
+// every code and scale load of the unit issued before any arithmetic, and the
+// lane's activation chunks loaded once (a lane always covers the same k
+// range).  Same per-row arithmetic and reduction order as k_gemv_nvfp4.
+// (Two to eight units per wave in a straight-line register pipeline were
+// measured on MI355X and were slower: 13.2-15.4 us against 11.6 us for the
+// 24576 x 4096 gate+up.)
+template <int R, int G, int C, bool SWIGLU, bool LDSX>
 __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4_stream(const uint8_t* __restrict__ w, int64_t soff,
                                                               float s_t, int nout, int k,
                                                               const uint16_t* __restrict__ x,
@@ -282,7 +271,6 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4_stream(const uint8_t* __r
     const int lane = lane_id();
     const int grp = G == kWave ? 0 : lane / G;  // one group per wave: rows are wave-uniform
     const int l = G == kWave ? lane : lane % G;
-    const int nwaves = int(gridDim.x) * (kBlock / kWave);
     // wave-uniform, kept in a scalar register
     const int wave = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * (kBlock / kWave) + int(threadIdx.x) / kWave);
     const int64_t crow = k / 2, srow = k / 16;
@@ -319,16 +307,16 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4_stream(const uint8_t* __r
     }
 
     const int nrows = SWIGLU ? 2 * nout : nout;  // packed rows (gate/up interleaved)
-    auto row_of = [&](int unit, int r) -> int { return min(unit * R + r, nrows - 1); };
-    // unit index of step i, clamped to a valid unit (a clamped step stores nothing)
-    auto wunit_of = [&](int i) -> int { return min(wave + i * nwaves, n_wunits - 1); };
-    auto load = [&](StreamBuf<R, G, C>& b, int wunit) {
-        const int unit = wunit * kGroups + grp;
+    const int wunit = min(wave, n_wunits - 1);    // a clamped wave stores nothing
+    const int unit = wunit * kGroups + grp;
+    u32x4 cw[C][R];
+    uint32_t sw[C][R];
+    {
         const uint8_t* cp[R];
         const uint8_t* sp[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int64_t row = row_of(unit, r);
+            const int64_t row = min(unit * R + r, nrows - 1);
             cp[r] = w + row * crow;
             sp[r] = w + soff + row * srow;
         }
@@ -336,54 +324,10 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4_stream(const uint8_t* __r
 #pragma unroll
         for (int q = 0; q < R * C; ++q) {
             const int r = LDSX ? q % R : q / C, c = LDSX ? q / R : q % C;
-            b.cw[c][r] = ld_stream16(cp[r] + 16u * jc[c]);
-            b.sw[c][r] = ld<uint16_t>(sp[r] + 2u * jc[c]);
+            cw[c][r] = ld_stream16(cp[r] + 16u * jc[c]);
+            sw[c][r] = ld<uint16_t>(sp[r] + 2u * jc[c]);
         }
-    };
-    auto process = [&](const StreamBuf<R, G, C>& b, int wunit, bool store) {
-        const int unit = wunit * kGroups + grp;
-        float acc[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = 0.f;
-#pragma unroll
-        for (int c = 0; c < C; ++c)
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float v = nvfp4_chunk_dot(b.cw[c][r], b.sw[c][r], xv[c], acc[r]);
-                acc[r] = okc[c] ? v : acc[r];
-            }
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = group_sum<G>(acc[r]) * s_t;
-        if constexpr (!SWIGLU) {
-            if (store && l == 0) {
-#pragma unroll
-                for (int r = 0; r < kPer; ++r) {
-                    const int i = unit * kPer + r;
-                    if (i < nout) y[i] = acc[r];
-                }
-            }
-        } else {
-            // lane l of the group evaluates the SwiGLU of its a-row l
-            float g = 0.f, u = 0.f;
-#pragma unroll
-            for (int r = 0; r < kPer; ++r)
-                if (l == r) {
-                    g = acc[2 * r];
-                    u = acc[2 * r + 1];
-                }
-            const int i = unit * kPer + l;
-            if (store && l < kPer && i < nout) {
-                a[i] = uint16_t(f32_to_bf16_rne(g / (1.0f + expf(-g)) * u));
-                if (h) {
-                    h[i] = g;
-                    h[nout + i] = u;
-                }
-            }
-        }
-    };
-
-    StreamBuf<R, G, C> buf[2];
-    load(buf[0], wunit_of(0));
+    }
     if constexpr (LDSX) {
         // The x loads were issued before the weights, so the stores wait for
         // them only; the scheduling barrier keeps any decode of the weights
@@ -401,11 +345,45 @@ __global__ __launch_bounds__(kBlock) void k_gemv_nvfp4_stream(const uint8_t* __r
 #pragma unroll
             for (int i = 0; i < 4; ++i) xv[c][i] = xs[4 * jc[c] + ((uint32_t(i) + (jc[c] >> 1)) & 3u)];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    const bool store = wave < n_wunits;
+    float acc[R];
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-        if (i + 1 < U) load(buf[(i + 1) & 1], wunit_of(i + 1));
-        __builtin_amdgcn_sched_barrier(0);
-        process(buf[i & 1], wunit_of(i), wave + i * nwaves < n_wunits);
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float v = nvfp4_chunk_dot(cw[c][r], sw[c][r], xv[c], acc[r]);
+            acc[r] = okc[c] ? v : acc[r];
+        }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = group_sum<G>(acc[r]) * s_t;
+    if constexpr (!SWIGLU) {
+        if (store && l == 0) {
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) {
+                const int i = unit * kPer + r;
+                if (i < nout) y[i] = acc[r];
+            }
+        }
+    } else {
+        // lane l of the group evaluates the SwiGLU of its a-row l
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int r = 0; r < kPer; ++r)
+            if (l == r) {
+                g = acc[2 * r];
+                u = acc[2 * r + 1];
+            }
+        const int i = unit * kPer + l;
+        if (store && l < kPer && i < nout) {
+            a[i] = uint16_t(f32_to_bf16_rne(g / (1.0f + expf(-g)) * u));
+            if (h) {
+                h[i] = g;
+                h[nout + i] = u;
+            }
+        }
     }
 }
 
@@ -421,33 +399,6 @@ struct Args {
     float* h;
 };
 
-// Units per wave of the streaming kernel (tunable for a machine through
-// QG_STREAM_UNITS; results do not depend on it): the grid gets units / U
-// waves.
-int stream_units_per_wave() {
-    static const int v = [] {
-        const char* e = std::getenv("QG_STREAM_UNITS");
-        const int x = e ? std::atoi(e) : 0;
-        return x == 1 || x == 2 || x == 4 || x == 8 ? x : kStreamUnitsDefault;
-    }();
-    return v;
-}
-
-template <int G, int C, int U, bool SW>
-hipError_t go_stream_u(const Args& A, int64_t wunits, hipStream_t s) {
-    constexpr int R0 = kStreamRows<C>;
-    constexpr int R = SW ? (R0 < 2 ? 2 : R0) : R0;
-    const int64_t waves = (wunits + U - 1) / U;
-    const dim3 grid(unsigned((waves + kBlock / kWave - 1) / (kBlock / kWave)));
-    if (kStreamLdsX<G, C, U> && A.k == 32 * C * G)
-        hipLaunchKernelGGL((k_gemv_nvfp4_stream<R, G, C, U, SW, true>), grid, dim3(kBlock), 0, s, A.w, A.soff,
-                           A.s_t, A.nout, A.k, A.x, A.y, A.a, A.h, int(wunits));
-    else
-        hipLaunchKernelGGL((k_gemv_nvfp4_stream<R, G, C, U, SW, false>), grid, dim3(kBlock), 0, s, A.w, A.soff,
-                           A.s_t, A.nout, A.k, A.x, A.y, A.a, A.h, int(wunits));
-    return hipGetLastError();
-}
-
 template <int G, int C, bool SW>
 hipError_t go_stream(const Args& A, hipStream_t s) {
     constexpr int R0 = kStreamRows<C>;
@@ -455,12 +406,14 @@ hipError_t go_stream(const Args& A, hipStream_t s) {
     constexpr int per_unit = SW ? R / 2 : R;
     const int64_t units = (int64_t(A.nout) + per_unit - 1) / per_unit;
     const int64_t wunits = (units + (kWave / G) - 1) / (kWave / G);
-    switch (stream_units_per_wave()) {
-        case 1: return go_stream_u<G, C, 1, SW>(A, wunits, s);
-        case 2: return go_stream_u<G, C, 2, SW>(A, wunits, s);
-        case 4: return go_stream_u<G, C, 4, SW>(A, wunits, s);
-        default: return go_stream_u<G, C, 8, SW>(A, wunits, s);
-    }
+    const dim3 grid(unsigned((wunits + kBlock / kWave - 1) / (kBlock / kWave)));
+    if (kStreamLdsX<G, C> && A.k == 32 * C * G)
+        hipLaunchKernelGGL((k_gemv_nvfp4_stream<R, G, C, SW, true>), grid, dim3(kBlock), 0, s, A.w, A.soff,
+                           A.s_t, A.nout, A.k, A.x, A.y, A.a, A.h, int(wunits));
+    else
+        hipLaunchKernelGGL((k_gemv_nvfp4_stream<R, G, C, SW, false>), grid, dim3(kBlock), 0, s, A.w, A.soff,
+                           A.s_t, A.nout, A.k, A.x, A.y, A.a, A.h, int(wunits));
+    return hipGetLastError();
 }
 
 template <int G, int C, int MT, bool SW>

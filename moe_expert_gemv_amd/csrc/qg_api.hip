@@ -155,7 +155,9 @@ int moe_route_topk(const float* logits, int64_t t, int64_t n_experts, int64_t to
 }
 
 static int check_moe_desc(const qg_moe_desc* d) {
-    if (!d || !d->gate_up || !d->down || !d->gate_up_scale || !d->down_scale) return QG_EINVAL;
+    if (!d) return QG_EINVAL;
+    if (d->layout_version != QG_LAYOUT_VERSION) return QG_EVERSION;
+    if (!d->gate_up || !d->down || !d->gate_up_scale || !d->down_scale || d->reserved != 0) return QG_EINVAL;
     if (d->n_experts < 1 || d->top_k < 1 || d->top_k > d->n_experts) return QG_EINVAL;
     if (d->has_shared != 0 && d->has_shared != 1) return QG_EINVAL;
     if (d->flags & ~QG_MOE_KEEP_H) return QG_EINVAL;
@@ -248,6 +250,17 @@ int qgemm_prefill_ws(const void* w, float tensor_scale, int64_t n, int64_t k, co
     }
     return finish(launch_prefill_ws(static_cast<const uint8_t*>(w), tensor_scale, n, k, x, m, y,
                                     static_cast<float*>(ws), as_stream(stream)));
+}
+
+int qg_probe_read(const void* buf, size_t bytes, int wg_per_cu, uint32_t* sink, void* stream) {
+    if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4)) return QG_EINVAL;
+    if (bytes < 16 || bytes % 16 || bytes > (size_t(1) << 40) || wg_per_cu < 1 || wg_per_cu > 8) return QG_EINVAL;
+    return finish(launch_probe_read(buf, int64_t(bytes), sink, wg_per_cu, as_stream(stream)));
+}
+
+int qg_probe_mfma_bf16(int64_t iters, float* sink, int64_t* flops, void* stream) {
+    if (!sink || !flops || !aligned(sink, 4) || iters < 1 || iters > (int64_t(1) << 32)) return QG_EINVAL;
+    return finish(launch_probe_mfma(iters, sink, as_stream(stream), flops));
 }
 
 }  // extern "C"

@@ -48,7 +48,7 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_f
 __device__ __forceinline__ float bf16x2_lo(bf16x2 v) { return float(v.x); }
 __device__ __forceinline__ float bf16x2_hi(bf16x2 v) { return float(v.y); }
 
-// One dword of a Q4_0 block (layout V1): lo = elements 4q..4q+3 (low
+// One dword of a Q4_0 block (packed layout): lo = elements 4q..4q+3 (low
 // nibbles), hi = elements 16+4q..16+4q+3 (high nibbles), one unsigned code
 // per byte.
 __device__ __forceinline__ void q4_unpack(uint32_t c, uint32_t& lo, uint32_t& hi) {

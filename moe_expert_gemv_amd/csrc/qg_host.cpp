@@ -25,6 +25,7 @@ const char* qg_status_string(int status) {
         case QG_OK: return "ok";
         case QG_EINVAL: return "invalid argument (null pointer, bad shape, misalignment or bad code)";
         case QG_EUNSUPPORTED: return "shape outside what the kernels implement";
+        case QG_EVERSION: return "packed buffer or descriptor of another layout version";
         case QG_ENOSPC: return "destination or workspace buffer too small";
         case QG_EHIP: return "HIP runtime or launch error";
         default: return "unknown status";
@@ -39,6 +40,38 @@ size_t qg_packed_bytes(int fmt, int64_t n, int64_t k) {
 size_t qg_scale_plane_offset(int fmt, int64_t n, int64_t k) {
     if (!qg::valid_fmt(fmt) || !qg::valid_fmt_shape(fmt, n, k)) return 0;
     return size_t(qg::scale_plane_offset(fmt, n, k));
+}
+
+// ---------------------------------------------------------------- layout stamp
+
+namespace {
+
+void write_stamp(void* buf, int fmt, uint32_t kind, int64_t n, int64_t k) {
+    qg::Stamp st{qg::kStampMagic, uint32_t(QG_LAYOUT_VERSION), uint32_t(fmt), kind, n, k};
+    std::memcpy(static_cast<uint8_t*>(buf) + qg::stamp_offset(fmt, n, k), &st, sizeof st);
+}
+
+// The stamp of a packed host buffer of at least packed_bytes(fmt, n, k).
+int check_stamp(const void* buf, int fmt, uint32_t kind, int64_t n, int64_t k) {
+    qg::Stamp st;
+    std::memcpy(&st, static_cast<const uint8_t*>(buf) + qg::stamp_offset(fmt, n, k), sizeof st);
+    if (st.magic != qg::kStampMagic) return QG_EINVAL;
+    if (st.version != uint32_t(QG_LAYOUT_VERSION)) return QG_EVERSION;
+    if (st.fmt != uint32_t(fmt) || st.kind != kind || st.n != n || st.k != k) return QG_EINVAL;
+    return QG_OK;
+}
+
+}  // namespace
+
+int qg_packed_check(int fmt, const void* buf, size_t bytes, int64_t n, int64_t k) {
+    const uint32_t kind = fmt == QG_NVFP4_GATE_UP ? qg::kKindGateUp : qg::kKindPlain;
+    if (fmt == QG_NVFP4_GATE_UP) {
+        fmt = QG_NVFP4;
+        if (n % 2) return QG_EINVAL;
+    }
+    if (!buf || !qg::valid_fmt(fmt) || !qg::valid_fmt_shape(fmt, n, k)) return QG_EINVAL;
+    if (bytes < size_t(qg::packed_bytes(fmt, n, k))) return QG_ENOSPC;
+    return check_stamp(buf, fmt, kind, n, k);
 }
 
 // ---------------------------------------------------------------- packers
@@ -66,6 +99,7 @@ int qg_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_
         for (int64_t j = 0; j < crow; ++j) o[j] = uint8_t(c[2 * j] | (c[2 * j + 1] << 4));
     }
     std::memcpy(out + qg::scale_plane_offset(QG_NVFP4, n, k), scales, size_t(n * (k / 16)));
+    write_stamp(out, QG_NVFP4, qg::kKindPlain, n, k);
     return QG_OK;
 }
 
@@ -86,6 +120,7 @@ int qg_pack_q4_0(const uint8_t* codes, const uint16_t* scales, int64_t n, int64_
                 o[16 * b + i] = uint8_t(c[32 * b + i] | (c[32 * b + 16 + i] << 4));
     }
     std::memcpy(out + qg::scale_plane_offset(QG_Q4_0, n, k), scales, size_t(n * (k / 32)) * 2);
+    write_stamp(out, QG_Q4_0, qg::kKindPlain, n, k);
     return QG_OK;
 }
 
@@ -97,6 +132,7 @@ int qg_pack_q8_0(const int8_t* codes, const uint16_t* scales, int64_t n, int64_t
     std::memset(out, 0, size_t(qg::packed_bytes(QG_Q8_0, n, k)));
     std::memcpy(out, codes, size_t(n * k));
     std::memcpy(out + qg::scale_plane_offset(QG_Q8_0, n, k), scales, size_t(n * (k / 32)) * 2);
+    write_stamp(out, QG_Q8_0, qg::kKindPlain, n, k);
     return QG_OK;
 }
 
@@ -120,6 +156,7 @@ int qg_pack_nvfp4_gate_up(const uint8_t* codes, const uint8_t* scales, int64_t i
         for (int64_t j = 0; j < crow; ++j) o[j] = uint8_t(c[2 * j] | (c[2 * j + 1] << 4));
         std::memcpy(splane + pr * srow, scales + r * srow, size_t(srow));
     }
+    write_stamp(out, QG_NVFP4, qg::kKindGateUp, n, k);
     return QG_OK;
 }
 
@@ -129,6 +166,7 @@ int qg_unpack_nvfp4(const void* src, size_t src_bytes, int64_t n, int64_t k, uin
                     uint8_t* scales) {
     int st = check_pack_args(QG_NVFP4, codes, scales, n, k, src, src_bytes);
     if (st) return st;
+    if ((st = check_stamp(src, QG_NVFP4, qg::kKindPlain, n, k))) return st;
     const uint8_t* in = static_cast<const uint8_t*>(src);
     const int64_t crow = k / 2;
     for (int64_t r = 0; r < n; ++r)
@@ -146,6 +184,7 @@ int qg_unpack_nvfp4_gate_up(const void* src, size_t src_bytes, int64_t inter, in
     const int64_t n = 2 * inter;
     int st = check_pack_args(QG_NVFP4, codes, scales, n, k, src, src_bytes);
     if (st) return st;
+    if ((st = check_stamp(src, QG_NVFP4, qg::kKindGateUp, n, k))) return st;
     const uint8_t* in = static_cast<const uint8_t*>(src);
     const int64_t crow = k / 2, srow = k / 16;
     const uint8_t* splane = in + qg::scale_plane_offset(QG_NVFP4, n, k);
@@ -165,6 +204,7 @@ int qg_unpack_q4_0(const void* src, size_t src_bytes, int64_t n, int64_t k, uint
                    uint16_t* scales) {
     int st = check_pack_args(QG_Q4_0, codes, scales, n, k, src, src_bytes);
     if (st) return st;
+    if ((st = check_stamp(src, QG_Q4_0, qg::kKindPlain, n, k))) return st;
     const uint8_t* in = static_cast<const uint8_t*>(src);
     const int64_t crow = k / 2;
     for (int64_t r = 0; r < n; ++r)
@@ -182,6 +222,7 @@ int qg_unpack_q8_0(const void* src, size_t src_bytes, int64_t n, int64_t k, int8
                    uint16_t* scales) {
     int st = check_pack_args(QG_Q8_0, codes, scales, n, k, src, src_bytes);
     if (st) return st;
+    if ((st = check_stamp(src, QG_Q8_0, qg::kKindPlain, n, k))) return st;
     const uint8_t* in = static_cast<const uint8_t*>(src);
     std::memcpy(codes, in, size_t(n * k));
     std::memcpy(scales, in + qg::scale_plane_offset(QG_Q8_0, n, k), size_t(n * (k / 32)) * 2);
@@ -197,6 +238,7 @@ int qg_pack_fp8(int fmt, const uint8_t* codes, const float* scales, int64_t n, i
     std::memset(out, 0, size_t(qg::packed_bytes(fmt, n, k)));
     std::memcpy(out, codes, size_t(n * k));
     std::memcpy(out + qg::scale_plane_offset(fmt, n, k), scales, size_t(qg::scale_plane_bytes(fmt, n, k)));
+    write_stamp(out, fmt, qg::kKindPlain, n, k);
     return QG_OK;
 }
 
@@ -205,6 +247,7 @@ int qg_unpack_fp8(int fmt, const void* src, size_t src_bytes, int64_t n, int64_t
     if (!qg::is_fp8(fmt)) return QG_EINVAL;
     int st = check_pack_args(fmt, codes, scales, n, k, src, src_bytes);
     if (st) return st;
+    if ((st = check_stamp(src, fmt, qg::kKindPlain, n, k))) return st;
     const uint8_t* in = static_cast<const uint8_t*>(src);
     std::memcpy(codes, in, size_t(n * k));
     std::memcpy(scales, in + qg::scale_plane_offset(fmt, n, k), size_t(qg::scale_plane_bytes(fmt, n, k)));
@@ -280,6 +323,7 @@ int qg_pack_kquant(int fmt, const uint8_t* codes, const uint16_t* d, const uint1
             std::memcpy(so + sup, sub + r * qg::kq_sub_bytes(fmt, k), size_t(qg::kq_sub_bytes(fmt, k)));
         }
     }
+    write_stamp(out, fmt, qg::kKindPlain, n, k);
     return QG_OK;
 }
 
@@ -287,6 +331,7 @@ int qg_unpack_kquant(int fmt, const void* src, size_t src_bytes, int64_t n, int6
                      uint16_t* d, uint16_t* dmin, uint8_t* sub, uint8_t* mins) {
     int st = check_kquant_args(fmt, codes, d, dmin, sub, mins, n, k, src, src_bytes);
     if (st) return st;
+    if ((st = check_stamp(src, fmt, qg::kKindPlain, n, k))) return st;
     const uint8_t* in = static_cast<const uint8_t*>(src);
     const int64_t crow = qg::code_row_bytes(fmt, k), srow = qg::scale_row_bytes(fmt, k);
     const int64_t S = k / qg::kKqSuper, B = k / 32, sup = qg::kq_super_bytes(fmt, k);

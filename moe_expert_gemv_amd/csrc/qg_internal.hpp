@@ -77,4 +77,8 @@ size_t prefill_workspace_bytes(int64_t n, int64_t k, int64_t m);
 hipError_t launch_prefill_ws(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x, int64_t m,
                              uint16_t* y, float* ws, hipStream_t s);
 
+// Achievable-peak probes (k_probe.hip).
+hipError_t launch_probe_read(const void* buf, int64_t bytes, uint32_t* sink, int wg_per_cu, hipStream_t s);
+hipError_t launch_probe_mfma(int64_t iters, float* sink, hipStream_t s, int64_t* flops);
+
 }  // namespace qg

@@ -1,6 +1,7 @@
-// Packed layout V1: plane sizes and offsets (host and device code).
+// Packed layout (version QG_LAYOUT_VERSION): plane sizes and offsets (host and
+// device code).
 //
-// A packed matrix is [codes plane][pad][scale plane][pad], every plane
+// A packed matrix is [codes plane][pad][scale plane][pad][stamp], every plane
 // 256-byte aligned.  Rows of both planes are stored back to back; with
 // k % 32 == 0 every row starts on a 16-byte boundary.
 #pragma once
@@ -75,8 +76,26 @@ inline constexpr int64_t scale_plane_bytes(int fmt, int64_t n, int64_t k) {
     return is_fp8(fmt) ? 4 * fp8_scale_count(fmt, n, k) : n * scale_row_bytes(fmt, k);
 }
 
-inline constexpr int64_t packed_bytes(int fmt, int64_t n, int64_t k) {
+// Layout stamp: the last kStampBytes of every packed matrix name its layout
+// version, format, row order and shape, so that a buffer written by another
+// layout version is rejected rather than misread.  The kernels never read it.
+constexpr int64_t kStampBytes = 256;
+constexpr uint32_t kStampMagic = 0x4B504751u;  // the bytes "QGPK"
+constexpr uint32_t kKindPlain = 0;             // rows in logical order
+constexpr uint32_t kKindGateUp = 1;            // fused gate/up, rows interleaved
+struct Stamp {
+    uint32_t magic;
+    uint32_t version;
+    uint32_t fmt;
+    uint32_t kind;
+    int64_t n;
+    int64_t k;
+};
+
+inline constexpr int64_t stamp_offset(int fmt, int64_t n, int64_t k) {
     return scale_plane_offset(fmt, n, k) + align_up(scale_plane_bytes(fmt, n, k), kPlaneAlign);
 }
+
+inline constexpr int64_t packed_bytes(int fmt, int64_t n, int64_t k) { return stamp_offset(fmt, n, k) + kStampBytes; }
 
 }  // namespace qg

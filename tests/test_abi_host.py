@@ -49,9 +49,9 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_versions_and_status_strings(L):
-    assert qg.qg_abi_version() == 1
-    assert qg.qg_layout_version() == 1
-    for s in (0, -1, -2, -4, -5):
+    assert qg.qg_abi_version() == 2
+    assert qg.qg_layout_version() == qg.QG_LAYOUT_VERSION == 2
+    for s in (0, -1, -2, -3, -4, -5):
         assert qg.qg_status_string(s) and qg.qg_status_string(s) != "unknown status"
     assert qg.qg_status_string(12345) == "unknown status"
 
@@ -63,7 +63,7 @@ def test_versions_and_status_strings(L):
 def test_packed_sizes(L, fmt, n, k, codes, scales):
     off = qg.qg_scale_plane_offset(fmt, n, k)
     assert off % 256 == 0 and off >= codes and off - codes < 256
-    total = qg.qg_packed_bytes(fmt, n, k)
+    total = qg.qg_packed_bytes(fmt, n, k) - 256  # the layout stamp closes the buffer
     assert total % 256 == 0 and total - off >= scales and total - off - scales < 256
 
 
@@ -120,7 +120,8 @@ def test_gate_up_pack_interleaves_rows(L):
     # the same bytes as the plain packer applied to the interleaved row order
     order = np.ravel(np.column_stack([np.arange(5), 5 + np.arange(5)]))
     plain = qg.qg_pack_nvfp4(w["codes"][order], w["scales"][order])
-    assert np.array_equal(buf, plain)
+    assert np.array_equal(buf[:-256], plain[:-256])  # all but the stamp, which names the row order
+    assert buf[-256 + 12] == 1 and plain[-256 + 12] == 0
 
 
 @settings(max_examples=40, deadline=None)
@@ -255,7 +256,7 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 def test_fp8_packed_sizes(L, fmt, n, k, scales):
     off = qg.qg_scale_plane_offset(fmt, n, k)
     assert off % 256 == 0 and off >= n * k and off - n * k < 256
-    total = qg.qg_packed_bytes(fmt, n, k)
+    total = qg.qg_packed_bytes(fmt, n, k) - 256  # the layout stamp closes the buffer
     assert total % 256 == 0 and total - off >= scales and total - off - scales < 256
 
 
@@ -303,7 +304,7 @@ def test_kquant_pack_roundtrip_and_sizes(L, fmt, n, k):
     high = {synth.Q5_K: k // 8, synth.Q6_K: k // 4}.get(fmt, 0)
     scale_row = {synth.Q4_K: 20, synth.Q5_K: 20, synth.Q6_K: 18, synth.IQ4_XS: 10}[fmt] * (k // 256)
     align = lambda v: (v + 255) // 256 * 256  # noqa: E731
-    assert buf.nbytes == align(n * (k // 2 + high)) + align(n * scale_row)
+    assert buf.nbytes == align(n * (k // 2 + high)) + align(n * scale_row) + 256
     assert qg.qg_scale_plane_offset(KQ[fmt], n, k) == align(n * (k // 2 + high))
     u = qg.qg_unpack_kquant(KQ[fmt], buf, n, k)
     for key, v in u.items():
@@ -377,3 +378,84 @@ def test_new_entry_points_reject_empty_and_null(L):
     assert L.qgemm_prefill_a8(256, 4, 64, 256, 256, 4, None, None) == qg.QG_EINVAL  # y
     for fmt in qg.KQUANT_FORMATS:
         assert qg.qg_packed_bytes(fmt, 1, 128) == 0 and qg.qg_packed_bytes(fmt, 1, 256) > 0
+
+
+# ---------------------------------------------------------------- layout stamp and version
+
+
+def _packed_examples():
+    """(format code for qg_packed_check, n, k, packed buffer, unpack call) of every packer."""
+    g = synth.rng(77)
+    nv, q4, q8 = synth.nvfp4_weights(g, 3, 64), synth.q4_0_weights(g, 3, 64), synth.q8_0_weights(g, 3, 64)
+    f8 = synth.fp8_weights(g, 3, 64, tiled=True)
+    kq = synth.kquant_weights(g, synth.Q5_K, 2, 256)
+    return [
+        (qg.QG_NVFP4, 3, 64, qg.qg_pack_nvfp4(nv["codes"], nv["scales"]), lambda b: qg.qg_unpack_nvfp4(b, 3, 64)),
+        (qg.QG_NVFP4_GATE_UP, 4, 64, qg.qg_pack_nvfp4_gate_up(nv["codes"][:2].repeat(2, 0), nv["scales"][:2].repeat(2, 0)),
+         lambda b: qg.qg_unpack_nvfp4_gate_up(b, 2, 64)),
+        (qg.QG_Q4_0, 3, 64, qg.qg_pack_q4_0(q4["codes"], q4["scales"]), lambda b: qg.qg_unpack_q4_0(b, 3, 64)),
+        (qg.QG_Q8_0, 3, 64, qg.qg_pack_q8_0(q8["codes"], q8["scales"]), lambda b: qg.qg_unpack_q8_0(b, 3, 64)),
+        (qg.QG_FP8_B128, 3, 64, qg.qg_pack_fp8(qg.QG_FP8_B128, f8["codes"], f8["scales"]),
+         lambda b: qg.qg_unpack_fp8(qg.QG_FP8_B128, b, 3, 64)),
+        (qg.QG_Q5_K, 2, 256, _kq_pack(kq), lambda b: qg.qg_unpack_kquant(qg.QG_Q5_K, b, 2, 256)),
+    ]
+
+
+def test_stamp_is_as_documented(L):
+    for fmt, n, k, buf, _ in _packed_examples():
+        st_ = buf[-256:]
+        assert st_[:4].tobytes() == b"QGPK"
+        v, f, kind = (int(x) for x in st_[4:16].view(np.uint32))
+        assert v == qg.QG_LAYOUT_VERSION
+        assert (f, kind) == ((qg.QG_NVFP4, 1) if fmt == qg.QG_NVFP4_GATE_UP else (fmt, 0))
+        assert st_[16:32].view(np.int64).tolist() == [n, k] and not st_[32:].any()
+        assert qg.qg_packed_check(fmt, buf, n, k) == qg.QG_OK
+
+
+def test_other_layout_versions_are_rejected(L):
+    """A buffer stamped by another layout version: QG_EVERSION from every
+    unpacker and from qg_packed_check, before anything is read."""
+    for fmt, n, k, buf, unpack in _packed_examples():
+        for version in (1, qg.QG_LAYOUT_VERSION + 1):
+            old = buf.copy()
+            old[-256 + 4:-256 + 8] = np.array([version], np.uint32).view(np.uint8)
+            assert qg.qg_packed_check(fmt, old, n, k) == qg.QG_EVERSION
+            with pytest.raises(qg.QGError) as e:
+                unpack(old)
+            assert e.value.status == qg.QG_EVERSION
+
+
+def test_unstamped_or_mismatched_buffers_are_rejected(L):
+    for fmt, n, k, buf, unpack in _packed_examples():
+        bare = buf.copy()
+        bare[-256:] = 0  # no stamp (e.g. the previous layout, which had none)
+        assert qg.qg_packed_check(fmt, bare, n, k) == qg.QG_EINVAL
+        with pytest.raises(qg.QGError) as e:
+            unpack(bare)
+        assert e.value.status == qg.QG_EINVAL
+        assert qg.qg_packed_check(fmt, buf[:-256], n, k) == qg.QG_ENOSPC
+    nv = _packed_examples()[0][3]
+    gu = _packed_examples()[1][3]
+    assert qg.qg_packed_check(qg.QG_Q8_0, nv, 3, 64) != qg.QG_OK       # another format
+    assert qg.qg_packed_check(qg.QG_NVFP4, gu, 4, 64) == qg.QG_EINVAL  # gate/up row order
+    assert qg.qg_packed_check(qg.QG_NVFP4_GATE_UP, nv, 4, 64) == qg.QG_EINVAL
+    with pytest.raises(qg.QGError):
+        qg.qg_unpack_nvfp4(gu, 4, 64)                                     # plain unpack of gate/up
+    big = np.concatenate([nv, np.zeros(4096, np.uint8)])
+    assert qg.qg_packed_check(qg.QG_NVFP4, big, 3, 64) == qg.QG_OK       # larger buffers are fine
+    assert qg.qg_packed_check(qg.QG_NVFP4, nv, 2, 64) != qg.QG_OK        # another shape
+
+
+def test_moe_entry_points_reject_other_layout_versions(L):
+    """Every MoE entry point takes packed experts through qg_moe_desc; a
+    descriptor of another layout version is refused before any launch."""
+    for version in (0, 1, qg.QG_LAYOUT_VERSION + 1):
+        d = _desc(layout_version=version)
+        assert qg.moe_workspace_bytes(d, 1) == 0
+        assert qg.moe_prefill_workspace_bytes(d, 64) == 0
+        r = ctypes.byref(d)
+        assert L.moe_gemv_grouped(r, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1 << 30, None) == qg.QG_EVERSION
+        assert L.moe_forward(r, FAKE, FAKE, 1, FAKE, FAKE, 1 << 30, None) == qg.QG_EVERSION
+        assert L.moe_prefill(r, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == qg.QG_EVERSION
+    assert qg.moe_workspace_bytes(_desc(), 1) > 0
+    assert qg.moe_workspace_bytes(_desc(reserved=1), 1) == 0

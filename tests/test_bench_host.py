@@ -44,21 +44,3 @@ def test_every_config_has_a_profile_summary(config):
     names = os.listdir(os.path.join(ROOT, "profiles"))
     assert any(f"config name in bench.py: {config}\n" in open(os.path.join(ROOT, "profiles", n)).read()
                for n in names if n.endswith(".txt"))
-
-
-def test_gpu_state_parser():
-    """The clocks/temperature record bench.py prints beside its timings: a
-    trimmed amd-smi reply parses, anything else gives None."""
-    import bench
-
-    gfx = {"clk": {"value": 2100, "unit": "MHz"}, "max_clk": {"value": 2400, "unit": "MHz"},
-           "clk_locked": "DISABLED"}
-    reply = json.dumps([{"gpu": 0, "clock": {"gfx_0": gfx, "gfx_1": dict(gfx, clk={"value": 2300}),
-                                              "mem_0": {"clk": {"value": 2000, "unit": "MHz"}}},
-                         "temperature": {"edge": "N/A", "hotspot": {"value": 61, "unit": "C"},
-                                         "mem": {"value": 48, "unit": "C"}}}])
-    st = bench.parse_gpu_state("some banner\n" + reply)
-    assert st == {"gfx_mhz_mean": 2200.0, "gfx_mhz_max": 2300, "gfx_mhz_limit": 2400, "mem_mhz": 2000,
-                  "clocks_locked": "DISABLED", "hotspot_c": 61, "mem_c": 48}
-    assert bench.parse_gpu_state("") is None
-    assert bench.parse_gpu_state("[{\"gpu\": 0}]") is None

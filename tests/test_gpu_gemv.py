@@ -184,21 +184,6 @@ def test_q8_0_full_size_layer():
     assert_within(got, oracle.gemv(case.w, case.x), oracle.gemv_abs(case.w, case.x), "q8_0 1024x1024")
 
 
-@pytest.mark.parametrize("which", ["gate_up", "down"])
-def test_nvfp4_full_size_layer_sampled(which):
-    """9B-class dense layer matrices at full size, checked on sampled rows."""
-    require_gpu()
-    print(f"[nvfp4 full {which}]", flush=True)
-    L = synth.nvfp4_layer_case()
-    w = L.gate_up if which == "gate_up" else L.down
-    n, k = w["codes"].shape
-    x = L.x if which == "gate_up" else synth.x_bf16(synth.rng(99), 1, k)
-    got = run_nvfp4(w, x)
-    rows = np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n), synth.rng(1).integers(0, n, 240)]))
-    assert_within(got[:, rows], oracle.gemv(w, x, rows), oracle.gemv_abs(w, x, rows), f"nvfp4 {which}")
-    assert np.all(np.isfinite(got))
-
-
 @pytest.mark.parametrize("k", [6144, 8192, 12288, 16384, 5120, 7168, 10240])
 def test_nvfp4_batch1_long_rows(k):
     """Batch-1 rows of three or more chunks per lane: the full ones (k a
@@ -215,3 +200,23 @@ def test_nvfp4_batch1_long_rows(k):
     assert_within(y1, oracle.gemv(w, x[:1]), oracle.gemv_abs(w, x[:1]), f"nvfp4 {n}x{k} m=1")
     y2 = run_nvfp4(w, x)
     assert np.array_equal(y1.view(np.uint32), y2[:1].view(np.uint32)), k
+
+
+@pytest.mark.parametrize("k", [4096, 8192, 12288, 16384])
+def test_nvfp4_two_to_four_tokens_every_token(k):
+    """2-4 tokens over full rows: the four-slot kernels that stage the
+    activations in LDS (four-wave workgroups at 2 and 4 chunks per lane,
+    eight-wave ones at 6 and 8).  Every token of m = 2, 3, 4 against the
+    oracle, and bitwise against the batch-1 call on that token."""
+    require_gpu()
+    print(f"[nvfp4 m=2..4 k={k}]", flush=True)
+    g = synth.rng(k + 77)
+    n = 333
+    w = synth.nvfp4_weights(g, n, k)
+    x = synth.x_bf16(g, 4, k)
+    singles = [run_nvfp4(w, x[t:t + 1]) for t in range(4)]
+    for m in (2, 3, 4):
+        ym = run_nvfp4(w, x[:m])
+        assert_within(ym, oracle.gemv(w, x[:m]), oracle.gemv_abs(w, x[:m]), f"nvfp4 {n}x{k} m={m}")
+        for t in range(m):
+            assert np.array_equal(ym[t:t + 1].view(np.uint32), singles[t].view(np.uint32)), (k, m, t)

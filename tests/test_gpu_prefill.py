@@ -136,13 +136,3 @@ def test_rows_are_independent():
     assert np.array_equal(run_prefill(w, x[100:260]), large[100:260])
 
 
-@pytest.mark.parametrize("m,ws", [(64, False), (128, False), (512, False), (64, True), (128, True)])
-def test_full_size_sampled(m, ws):
-    """X [m x 4096] times the 9B-class [12288 x 4096] NVFP4 matrix."""
-    require_gpu()
-    print(f"[prefill full m={m} ws={ws}]", flush=True)
-    case = synth.prefill_case(m=m)
-    n = case.w["codes"].shape[0]
-    rows = np.unique(np.concatenate([[0, m - 1], synth.rng(4).integers(0, m, 14)]))
-    cols = np.unique(np.concatenate([np.arange(4), np.arange(n - 4, n), synth.rng(5).integers(0, n, 120)]))
-    check(case.w, case.x, rows, cols, f"prefill full m={m}", run=run_prefill_ws if ws else run_prefill)

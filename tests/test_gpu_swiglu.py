@@ -60,37 +60,6 @@ def test_swiglu_batch_invariance():
         assert np.array_equal(a1, a8[t:t + 1]) and np.array_equal(h1.view(np.uint32), h8[t:t + 1].view(np.uint32))
 
 
-def test_dense_layer_full_size_stagewise():
-    """The 9B-class dense MLP step at full size (the benchmarked workload),
-    batch 1, launched exactly as the benchmark launches it."""
-    import torch
-
-    require_gpu()
-    print("[dense layer full]", flush=True)
-    L = synth.nvfp4_layer_case()
-    inter, hidden = 12288, 4096
-    wgu, wdn = pack_dev_gate_up(L.gate_up), pack_dev(L.down)
-    x = dev(L.x)
-    a = empty((1, inter), torch.int16)
-    h = empty((1, 2 * inter), torch.float32)
-    y = empty((1, hidden), torch.float32)
-    qg.qgemv_nvfp4_swiglu(wgu, 0.01, inter, hidden, x, 1, a, h)
-    qg.qgemv_nvfp4(wdn, 0.01, hidden, inter, a, 1, y)
-    a_bits, hh, yy = host(a).view(np.uint16), host(h), host(y)
-    rows = np.unique(np.concatenate([np.arange(8), np.arange(inter - 8, inter), synth.rng(3).integers(0, inter, 200)]))
-    both = np.concatenate([rows, rows + inter])
-    assert_within(hh[:, both], oracle.gemv(L.gate_up, L.x, both), oracle.gemv_abs(L.gate_up, L.x, both), "h")
-    exact = oracle.swiglu(hh.astype(np.float64))
-    assert np.all(np.abs(oracle.decode_bf16(a_bits) - exact) <= oracle.bf16_ulp(exact))
-    # the down projection from the GPU's own a, every output row
-    assert_within(yy, oracle.gemv(L.down, a_bits), oracle.gemv_abs(L.down, a_bits), "y")
-    # end to end from the original x (informational: printed, not asserted)
-    a_ref = oracle.swiglu(oracle.gemv(L.gate_up, L.x))
-    y_ref = oracle.ops.act_values(a_ref) @ oracle.ops.dequant(L.down).T
-    rel = np.linalg.norm(yy - y_ref) / np.linalg.norm(y_ref)
-    print(f"dense layer end-to-end relative L2 error vs fp64 chain: {rel:.3e}")
-
-
 @pytest.mark.parametrize("k", [6144, 12288])
 def test_swiglu_batch1_long_rows(k):
     """The SwiGLU epilogue on the LDS-staged batch-1 kernel (full rows)."""
@@ -103,3 +72,23 @@ def test_swiglu_batch1_long_rows(k):
     a1, h1 = check_swiglu_stage(w, x[:1], inter)
     a2, h2 = run_swiglu(w, x, inter)
     assert np.array_equal(a1, a2[:1]) and np.array_equal(h1.view(np.uint32), h2[:1].view(np.uint32))
+
+
+@pytest.mark.parametrize("k", [4096, 8192, 12288, 16384])
+def test_swiglu_two_to_four_tokens_every_token(k):
+    """The SwiGLU epilogue of the LDS-staged four-slot kernels (four- and
+    eight-wave workgroups): every token of m = 2, 3, 4 against the oracle, and
+    bitwise against the batch-1 call on that token."""
+    require_gpu()
+    print(f"[swiglu m=2..4 k={k}]", flush=True)
+    g = synth.rng(k + 78)
+    inter = 96
+    w = synth.nvfp4_weights(g, 2 * inter, k)
+    x = synth.x_bf16(g, 4, k)
+    singles = [run_swiglu(w, x[t:t + 1], inter) for t in range(4)]
+    for m in (2, 3, 4):
+        am, hm = check_swiglu_stage(w, x[:m], inter)
+        for t in range(m):
+            a1, h1 = singles[t]
+            assert np.array_equal(am[t:t + 1], a1), (k, m, t)
+            assert np.array_equal(hm[t:t + 1].view(np.uint32), h1.view(np.uint32)), (k, m, t)
