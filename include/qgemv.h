@@ -42,6 +42,8 @@
  *  - Ownership: the caller allocates and frees every buffer.  The library
  *    allocates nothing and keeps no state between calls (besides an immutable
  *    device-property cache), so calls are thread-safe and stream-ordered.
+ *    The one exception is moe_forward_noalloc, whose workspace is a
+ *    library-owned device array per GPU (see there).
  *  - Pointers named "device" must point to device memory of the current HIP
  *    device; "host" pointers to host memory.  Device pointers must be 16-byte
  *    aligned, packed weight buffers 256-byte aligned.  Inputs never alias
@@ -398,6 +400,24 @@ int moe_gemv_grouped(const qg_moe_desc* d, const uint16_t* x, const int32_t* ids
  * for moe_gemv_grouped. */
 int moe_forward(const qg_moe_desc* d, const uint16_t* x, const float* logits, int64_t t, float* y,
                 void* ws, size_t ws_bytes, void* stream);
+
+/* moe_forward without a caller workspace.  For callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  The workspace lives in a library-owned
+ * device array of QG_MOE_NOALLOC_SCRATCH_BYTES per GPU (allocated with the
+ * library's code object on each device it runs on, held until the process
+ * ends); the call itself allocates nothing.  Same result as moe_forward,
+ * bitwise (the same kernels on the same workspace layout).  QG_ENOSPC when
+ * moe_workspace_bytes(d, t) exceeds QG_MOE_NOALLOC_SCRATCH_BYTES (the 257-
+ * expert, hidden 2048, inter 512 layer needs 1.4 MB at t = 16, 2.0 MB with
+ * QG_MOE_KEEP_H).  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  The array keeps the last call's workspace; no
+ * region needs clearing between calls.  Other arguments as for moe_forward;
+ * QG_EHIP if the array's device address cannot be obtained. */
+#define QG_MOE_NOALLOC_SCRATCH_BYTES (4 << 20)
+int moe_forward_noalloc(const qg_moe_desc* d, const uint16_t* x, const float* logits, int64_t t, float* y,
+                        void* stream);
 
 /* ------------------------------------------------------ MoE prefill
  * The same MoE layer as moe_forward (same routing, grouping, SwiGLU and

@@ -29,7 +29,7 @@ __all__ = [
     "qg_unpack_fp8", "qgemv_fp8", "fp8_scale_shape", "qg_dequant",
     "qgemv_q8_0", "qgemv_nvfp4", "qgemv_nvfp4_swiglu", "qg_quantize_q8_0_act",
     "qgemv_q4_0_a8", "moe_route_topk", "QgMoeDesc", "moe_workspace_bytes",
-    "moe_gemv_grouped", "moe_forward", "moe_prefill_workspace_bytes", "moe_prefill", "qgemm_prefill",
+    "moe_gemv_grouped", "moe_forward", "moe_forward_noalloc", "QG_MOE_NOALLOC_SCRATCH_BYTES", "moe_prefill_workspace_bytes", "moe_prefill", "qgemm_prefill",
     "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws", "qg_probe_read", "qg_probe_mfma_bf16",
     "EXPORTED_SYMBOLS",
 ]
@@ -44,6 +44,7 @@ QG_LAYOUT_VERSION = 2
 KQUANT_FORMATS = (QG_Q4_K, QG_Q5_K, QG_Q6_K, QG_IQ4_XS)
 QG_MAX_M = 16
 QG_MOE_KEEP_H = 1
+QG_MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 class QGLibraryMissing(RuntimeError):
@@ -119,6 +120,7 @@ _SIGNATURES = {
     "moe_workspace_bytes": (_SZ, [ctypes.POINTER(QgMoeDesc), _I64]),
     "moe_gemv_grouped": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "moe_forward": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _I64, _P, _P, _SZ, _P]),
+    "moe_forward_noalloc": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _I64, _P, _P]),
     "moe_prefill_workspace_bytes": (_SZ, [ctypes.POINTER(QgMoeDesc), _I64]),
     "moe_prefill": (_I32, [ctypes.POINTER(QgMoeDesc), _P, _P, _I64, _P, _P, _SZ, _P]),
     "qgemm_prefill": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P]),
@@ -435,6 +437,11 @@ def moe_forward(desc: QgMoeDesc, x, logits, t, y, ws, ws_bytes=None, stream=None
     _check("moe_forward",
            lib().moe_forward(ctypes.byref(desc), _dptr(x), _dptr(logits), t, _dptr(y), _dptr(ws), nbytes,
                              _stream(stream)))
+
+
+def moe_forward_noalloc(desc: QgMoeDesc, x, logits, t, y, stream=None) -> None:
+    _check("moe_forward_noalloc",
+           lib().moe_forward_noalloc(ctypes.byref(desc), _dptr(x), _dptr(logits), t, _dptr(y), _stream(stream)))
 
 
 def moe_prefill_workspace_bytes(desc: QgMoeDesc, t: int) -> int:

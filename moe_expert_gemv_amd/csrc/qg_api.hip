@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "qg_internal.hpp"
 #include "qg_layout.hpp"
@@ -190,6 +191,66 @@ int moe_gemv_grouped(const qg_moe_desc* d, const uint16_t* x, const int32_t* ids
     const size_t need = moe_workspace_layout(d, t, &lay, ws);
     if (ws_bytes < need) return QG_ENOSPC;
     return finish(launch_moe(d, x, ids, weights, nullptr, int(t), y, lay, as_stream(stream)));
+}
+
+}  // extern "C"
+
+// Workspace of moe_forward_noalloc: a library-owned device array, one copy per
+// GPU (each device holds its own instance at its own address), kept until the
+// process ends.  In host code the name `scratch` is only a host-side stand-in
+// for the symbol: every use goes through the device address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch).
+static __device__ __align__(256) unsigned char scratch[QG_MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace qg {
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device: looked up once per
+// device (with that device current) and cached.
+hipError_t noalloc_scratch(void** out) {
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    if (void* p = g_scratch_ptr[dev].load(std::memory_order_acquire)) {
+        *out = p;
+        return hipSuccess;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+}  // namespace
+}  // namespace qg
+
+extern "C" {
+
+int moe_forward_noalloc(const qg_moe_desc* d, const uint16_t* x, const float* logits, int64_t t, float* y,
+                        void* stream) {
+    if (int st = check_moe_desc(d)) return st;
+    if (!x || !logits || !y) return QG_EINVAL;
+    if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(y, 16)) return QG_EINVAL;
+    if (t < 1) return QG_EINVAL;
+    if (t > QG_MAX_M || d->n_experts > 1024) return QG_EUNSUPPORTED;
+    const size_t need = moe_workspace_layout(d, t, nullptr, nullptr);
+    if (need > size_t(QG_MOE_NOALLOC_SCRATCH_BYTES)) return QG_ENOSPC;
+    void* base = nullptr;
+    if (hipError_t e = noalloc_scratch(&base); e != hipSuccess) return finish(e);
+    MoeWorkspace lay;
+    moe_workspace_layout(d, t, &lay, base);
+    // Every workspace region is written before it is read within the call,
+    // so nothing left over from an earlier call needs clearing.
+    return finish(launch_moe(d, x, nullptr, nullptr, logits, int(t), y, lay, as_stream(stream)));
 }
 
 int moe_forward(const qg_moe_desc* d, const uint16_t* x, const float* logits, int64_t t, float* y, void* ws,

@@ -456,6 +456,19 @@ def test_moe_entry_points_reject_other_layout_versions(L):
         r = ctypes.byref(d)
         assert L.moe_gemv_grouped(r, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1 << 30, None) == qg.QG_EVERSION
         assert L.moe_forward(r, FAKE, FAKE, 1, FAKE, FAKE, 1 << 30, None) == qg.QG_EVERSION
+        assert L.moe_forward_noalloc(r, FAKE, FAKE, 1, FAKE, None) == qg.QG_EVERSION
         assert L.moe_prefill(r, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == qg.QG_EVERSION
     assert qg.moe_workspace_bytes(_desc(), 1) > 0
     assert qg.moe_workspace_bytes(_desc(reserved=1), 1) == 0
+
+
+def test_noalloc_size_limit_on_host(L):
+    """moe_forward_noalloc refuses a layer whose workspace exceeds its array
+    (QG_ENOSPC) before touching the GPU."""
+    d = _desc(hidden=8192, inter=4096, flags=qg.QG_MOE_KEEP_H,
+              gate_up_stride=qg.qg_packed_bytes(qg.QG_NVFP4, 8192, 8192),
+              down_stride=qg.qg_packed_bytes(qg.QG_NVFP4, 8192, 4096))
+    assert qg.moe_workspace_bytes(d, 16) > qg.QG_MOE_NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(ctypes.byref(d), FAKE, FAKE, 16, FAKE, None) == qg.QG_ENOSPC
+    assert L.moe_forward_noalloc(ctypes.byref(_desc()), FAKE, FAKE, 0, FAKE, None) == qg.QG_EINVAL
+    assert L.moe_forward_noalloc(ctypes.byref(_desc()), FAKE, FAKE, 17, FAKE, None) == qg.QG_EUNSUPPORTED
