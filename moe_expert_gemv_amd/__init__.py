@@ -34,7 +34,9 @@ __all__ = [
     "EXPORTED_SYMBOLS",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
+# QG_LIBRARY: another build of the same library to load instead (machine
+# configuration, e.g. the host-sanitizer build of ``build.py --sanitize``).
+LIB_PATH = os.environ.get("QG_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
 
 QG_OK, QG_EINVAL, QG_EUNSUPPORTED, QG_EVERSION, QG_ENOSPC, QG_EHIP = 0, -1, -2, -3, -4, -5
 QG_NVFP4, QG_Q8_0, QG_Q4_0, QG_FP8_TENSOR, QG_FP8_B128 = 1, 2, 3, 4, 5

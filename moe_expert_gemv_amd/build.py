@@ -3,6 +3,14 @@
 ``python -m moe_expert_gemv_amd.build`` compiles every source under ``csrc/``
 and links ``moe_expert_gemv_amd/libqgemv.so``.  Object files go to
 ``_build/`` at the repository root.  The library is built for gfx950 only.
+
+``python -m moe_expert_gemv_amd.build --sanitize`` builds a second copy,
+``moe_expert_gemv_amd/libqgemv_sanitize.so``, whose host code (the packers,
+the argument checks and dispatch of every entry point, the launch stubs) is
+compiled with AddressSanitizer and UndefinedBehaviorSanitizer; device code is
+built as usual.  It is for CPU-side checks: load it with the clang ASan
+runtime preloaded (``sanitizer_runtime()``) and point the binding at it with
+``QG_LIBRARY``.
 """
 from __future__ import annotations
 
@@ -33,6 +41,12 @@ HIP_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
+# Sanitizer build: host code only (each flag behind -Xarch_host on hipcc lines;
+# the device passes are untouched), no recovery so the first report aborts.
+SANITIZE_LIB_PATH = os.path.join(HERE, "libqgemv_sanitize.so")
+SAN_HOST = ["-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+SAN_HIP_FLAGS = [f for flag in SAN_HOST for f in ("-Xarch_host", flag)] + ["-g"]
+CLANGXX = os.path.join(ROCM, "llvm", "bin", "clang++")
 
 HIP_SOURCES = ["qg_api.hip", "k_gemv_nvfp4.hip", "k_gemv_q8.hip", "k_gemv_a8.hip", "k_gemv_fp8.hip",
                "k_gemv_kquant.hip", "k_dequant.hip", "k_moe.hip", "k_moe_prefill.hip", "k_prefill.hip",
@@ -54,30 +68,49 @@ def _run(cmd: list[str]) -> None:
         sys.stderr.write(err + "\n")
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+def build(verbose: bool = False, jobs: int = 8, sanitize: bool = False) -> str:
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    build_dir = os.path.join(BUILD_DIR, "sanitize") if sanitize else BUILD_DIR
+    lib_path = SANITIZE_LIB_PATH if sanitize else LIB_PATH
+    os.makedirs(build_dir, exist_ok=True)
     cmds, objs = [], []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        cmds.append([HIPCC, *HIP_FLAGS, *HIP_FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+        san = SAN_HIP_FLAGS if sanitize else []
+        cmds.append([HIPCC, *HIP_FLAGS, *san, *HIP_FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".cpp", ".host.o"))
-        cmds.append([shutil.which("g++") or "g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, src.replace(".cpp", ".host.o"))
+        if sanitize:  # clang, so that host objects share one sanitizer runtime
+            cmds.append([CLANGXX, *CXX_FLAGS, *SAN_HOST, "-g", "-c", os.path.join(CSRC, src), "-o", obj])
+        else:
+            cmds.append([shutil.which("g++") or "g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         futs = [ex.submit(_run, c) for c in cmds]
         for f in futs:
             f.result()
-    tmp = LIB_PATH + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB_PATH)
+    tmp = lib_path + ".tmp"
+    link_san = SAN_HIP_FLAGS if sanitize else []
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_san, "-o", tmp, *objs])
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {lib_path}")
+    return lib_path
+
+
+def sanitizer_runtime() -> str:
+    """The clang ASan runtime that a process loading the sanitizer build must
+    preload (LD_PRELOAD)."""
+    import glob
+
+    found = sorted(glob.glob(os.path.join(ROCM, "llvm", "lib", "clang", "*", "lib", "linux",
+                                          "libclang_rt.asan-x86_64.so")))
+    if not found:
+        raise RuntimeError("clang ASan runtime not found under " + ROCM)
+    return found[-1]
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, sanitize="--sanitize" in sys.argv[1:])

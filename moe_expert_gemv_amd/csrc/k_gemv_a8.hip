@@ -291,46 +291,33 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4_0_a8(const uint8_t* __restri
 
 // ------------------------------------------------------------------ quantizer
 
-// One thread per 32-element block.
-__global__ __launch_bounds__(kBlock) void k_quantize_q8_0(const float* __restrict__ x, int64_t nblocks,
+// One lane per element, one half-wave (32 lanes) per 32-element block: the
+// block's amax and code sum are half-wave butterflies (exact in any order), so
+// every element's division runs on its own lane instead of 32 in sequence on
+// one thread.  Each lane's arithmetic is the oracle's reading step by step:
+// d32 = amax / 127 and x / d32 as correctly rounded fp32 divisions (this
+// library is built without fast-math), v_rndne_f32, clamp to +-127.
+__global__ __launch_bounds__(kBlock) void k_quantize_q8_0(const float* __restrict__ x, int64_t nelem,
                                                           int8_t* __restrict__ xq,
                                                           uint16_t* __restrict__ xd,
                                                           int32_t* __restrict__ xs) {
-    const int64_t b = int64_t(blockIdx.x) * kBlock + threadIdx.x;
-    if (b >= nblocks) return;
-    const float* p = x + 32 * b;
-    float v[32];
+    const int64_t e = int64_t(blockIdx.x) * kBlock + threadIdx.x;  // nelem % 32 == 0: whole half-waves
+    if (e >= nelem) return;                                         // uniform per half-wave
+    const float v = x[e];
+    float amax = fabsf(v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float4 f = ld<float4>(p + 4 * i);
-        v[4 * i] = f.x;
-        v[4 * i + 1] = f.y;
-        v[4 * i + 2] = f.z;
-        v[4 * i + 3] = f.w;
+    for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+    const float d32 = amax / 127.0f;
+    const int q = d32 != 0.f ? int(fminf(fmaxf(rintf(v / d32), -127.f), 127.f)) : 0;
+    int sum = q;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) sum += __shfl_xor(sum, o, 32);
+    xq[e] = int8_t(q);
+    if ((threadIdx.x & 31) == 0) {
+        const int64_t b = e / 32;
+        xd[b] = __builtin_bit_cast(uint16_t, _Float16(d32));
+        if (xs) xs[b] = sum;
     }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    const float d32 = amax / 127.0f;  // correctly rounded (no fast-math in this library)
-    const _Float16 d16 = _Float16(d32);
-    uint32_t packed[8];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) packed[i] = 0;
-    if (d32 != 0.f) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const float r = fminf(fmaxf(rintf(v[i] / d32), -127.f), 127.f);
-            const int q = int(r);
-            sum += q;
-            packed[i / 4] |= uint32_t(q & 0xff) << (8 * (i % 4));
-        }
-    }
-    u32x4* o = reinterpret_cast<u32x4*>(xq + 32 * b);
-    o[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
-    o[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
-    xd[b] = __builtin_bit_cast(uint16_t, d16);
-    if (xs) xs[b] = sum;
 }
 
 struct Args {
@@ -406,9 +393,9 @@ hipError_t launch_gemv_q4_0_a8(const uint8_t* w, int64_t n, int64_t k, const int
 
 hipError_t launch_quantize_q8_0(const float* x, int64_t m, int64_t k, int8_t* xq, uint16_t* xd,
                                 int32_t* xs, hipStream_t s) {
-    const int64_t nblocks = m * (k / 32);
-    hipLaunchKernelGGL(k_quantize_q8_0, dim3(unsigned((nblocks + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, x,
-                       nblocks, xq, xd, xs);
+    const int64_t nelem = m * k;
+    hipLaunchKernelGGL(k_quantize_q8_0, dim3(unsigned((nelem + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, x,
+                       nelem, xq, xd, xs);
     return hipGetLastError();
 }
 
