@@ -533,195 +533,278 @@ __global__ __launch_bounds__(kBlock) void k_prefill_ks(const uint8_t* __restrict
 
 // M <= 128 with a workspace: the k range is split over several workgroups
 // (kSkRange each), so a workgroup reads only its slice of X -- 64 tokens x
-// 1024 k, 128 KB, staged into LDS once -- instead of all of X.  Eight waves,
-// two per SIMD: waves w and w + 4 take the same 48 weight rows, w the even
-// 128-k slabs of the range and w + 4 the odd ones, so one wave's weight
-// decode (VALU) runs while the other's MFMAs do.  The X loads are requested
-// first and return first (a wave's vector-memory operations complete in
-// order); kSkEarly weight slabs follow them before X is published and the
-// rest right after, so the weight stream starts early without queueing the
-// X data behind it.  The two halves are added through LDS at the end, the
-// fp32 partial sums go to the workspace, and k_prefill_reduce adds them in
-// range order.
-constexpr int kSkRange = 1024;                   // k per workgroup
-constexpr int kSkBlock = 512;                    // threads per workgroup
-constexpr int kSkHalves = 2;                     // waves sharing a row set
+// 1024 k, 128 KB, staged into LDS -- instead of all of X.  A workgroup owns
+// 192 weight rows of one k range for every token block (one for m <= 64, two
+// for m <= 128: the weights stay in registers and the second X block replaces
+// the first in LDS), so the grid is one round of workgroups and each weight
+// byte is read once.  Eight waves, two per SIMD: waves w and w + 4 take the
+// same 48 weight rows, w the even 128-k slabs of the range and w + 4 the odd
+// ones, so one wave's weight decode (VALU) runs while the other's MFMAs do.
+//
+// Memory order.  Every wave first requests its part of the X block and of the
+// block scales of the workgroup's rows (16-byte loads, contiguous across the
+// wave); the weight slabs are requested once that X block is in LDS.  Issued
+// together with the X loads, the whole grid's 28 MB of weight requests share
+// the memory queues with X and the first MFMA waits for X for several
+// microseconds more (measured: X staged 3 us after a workgroup starts with
+// the weights behind it, 12 us with them beside it).  The scales go through
+// LDS because a lane needs only two of a row's bytes per slab: 2-byte loads
+// scattered over 16 rows per instruction cost more than the codes
+// themselves.  The two halves' sums and the result tile go through LDS too,
+// so each token's fp32 partials leave as one contiguous 768-byte row
+// segment; k_prefill_reduce adds the ranges' partials in range order.
+constexpr int kSkRange = 1024;                       // k per workgroup
+constexpr int kSkBlock = 512;                        // threads per workgroup
+constexpr int kSkHalves = 2;                         // waves sharing a row set
 constexpr int kSkSlabs = kSkRange / KW / kSkHalves;  // slabs per wave: 4
-constexpr int kSkRows = 64;                      // tokens per workgroup
-constexpr int kSkEarly = 1;                      // slabs requested before X is published
+constexpr int kSkRows = 64;                          // tokens per block
+constexpr int kSkNB = 3;                             // 16-row blocks per wave
+constexpr int kSkCols = 16 * kSkNB * (kSkBlock / kWave / kSkHalves);  // weight rows per workgroup: 192
+constexpr int kSkScaleStride = 80;  // LDS bytes per weight row of scales (64 used; 80 keeps 16 rows on distinct banks)
+constexpr int kSkTileStride = kSkCols + 4;  // floats per token of the LDS result tile (padding: no bank conflicts)
 
-template <int NB, bool TAIL, int EARLY>
+template <bool TAIL, int TB>
 __global__ __launch_bounds__(kSkBlock) void k_prefill_sk(const uint8_t* __restrict__ w, int64_t soff, int n, int k,
                                                          const uint16_t* __restrict__ x, int m,
                                                          float* __restrict__ part) {
+    constexpr int NB = kSkNB;
     constexpr int MB = kSkRows / 16;
     constexpr int RW = kSkBlock / kWave / kSkHalves;  // row sets per workgroup: 4
-    constexpr int BN = 16 * NB * RW;
-    constexpr int CPR = kSkRange / 8;  // 16-byte chunks per X row
-    constexpr int kAccFloats = MB * NB * 4;
-    static_assert(RW * kAccFloats * kWave * 4 <= kSkRows * kSkRange * 2, "halves combine in the X buffer");
+    constexpr int CPR = kSkRange / 8;                  // 16-byte chunks per X row
+    constexpr int kCopies = kSkRows * CPR / kSkBlock;  // X chunks per lane: 16
+    constexpr int SPR = kSkRange / 32;                 // scale pairs (2 bytes, 32 k) per row of the range
+    constexpr int kScale16 = kSkCols * (SPR * 2 / 16);  // 16-byte scale chunks per workgroup: 768
+    constexpr int kScale16PerLane = (kScale16 + kSkBlock - 1) / kSkBlock;
+    constexpr int kScale2PerLane = kSkCols * SPR / kSkBlock;  // 2-byte scale pairs per lane: 12
+    static_assert(kSkCols * SPR % kSkBlock == 0, "scale pairs split evenly");
+    static_assert(2 * kSkRows * kSkTileStride * 4 <= kSkRows * kSkRange * 2, "result tile fits in the X buffer");
     __shared__ __attribute__((aligned(16))) uint16_t xs[kSkRows * kSkRange];
+    __shared__ __attribute__((aligned(16))) uint8_t ss[kSkCols * kSkScaleStride];
 
     const int tid = int(threadIdx.x);
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rs = wave % RW, half = wave / RW;
     const int lr = lane & 15, lg = lane >> 4;
-    const int m0 = int(blockIdx.y) * kSkRows;
-    const int n0 = int(blockIdx.x) * BN + rs * 16 * NB;
+    const int nw = int(blockIdx.x) * kSkCols;  // the workgroup's first weight row
+    const int n0 = nw + rs * 16 * NB;          // this wave's
     const int kz = int(blockIdx.z) * kSkRange;
 
-    // 1. X slice, requested first: this lane's kCopies chunks go to registers
-    // now and to LDS once they arrive.  Chunk slot p of the LDS tile holds
-    // X[row][kz + 8c], row = p / CPR, c = (p % CPR) ^ (row & 15) (fragment
-    // reads then hit 16 distinct slots per 16 lanes); lane i of copy step cp
-    // fills slot cp * 64 + i.  Rows past m repeat row m-1; chunks past k are
-    // zeroed below.
-    constexpr int kCopies = kSkRows * CPR / kSkBlock;  // per lane
-    u32x4 xr[kCopies];
+    // X block loads: chunk slot p of the LDS tile holds X[row][kz + 8c],
+    // row = p / CPR, c = (p % CPR) ^ (row & 15) (fragment reads then hit 16
+    // distinct slots per 16 lanes); lane i of copy step cp fills slot
+    // cp * 64 + i.  Tokens past m repeat token m-1 (their results are not
+    // stored); chunks past k are zero.
+    auto x_load = [&](u32x4(&xr)[kCopies], int m0) {
 #pragma unroll
-    for (int i = 0; i < kCopies; ++i) {
-        const int cp = wave + (kSkBlock / kWave) * i;
-        const int p = cp * kWave + lane;
-        const int row = p / CPR, c = (p % CPR) ^ (row & 15);
-        const int kk = kz + 8 * c;
-        xr[i] = ld16(x + int64_t(min(m0 + row, m - 1)) * k + (kk < k ? kk : 0));
-    }
-    // 2. this wave's weight slabs (past k: the row's own first block); slab j
-    // covers k = kz + 128 (2 j + half) + [0, 128).  The first EARLY slabs are
-    // requested right behind the X loads -- after a bare barrier (it waits for
-    // no memory), so every wave's X loads are ahead of them -- and the rest
-    // once X is in LDS.
-    WStage<NB> wr[kSkSlabs];
-    const uint8_t* wc[NB];
-    const uint8_t* ws[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int64_t row = min(n0 + 16 * nb + lr, n - 1);
-        wc[nb] = w + row * (k / 2);
-        ws[nb] = w + soff + row * (k / 16);
-    }
-    auto w_load = [&](int j) {
-        const int kb = kz + KW * (kSkHalves * j + half) + 32 * lg;
-        const int kc = kb < k ? kb : 0;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const u32x4 v = ld16(wc[nb] + kc / 2);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) wr[j].c[nb][q] = v[q];
-            wr[j].s[nb] = ld<uint16_t>(ws[nb] + kc / 16);
+        for (int i = 0; i < kCopies; ++i) {
+            const int p = (wave + (kSkBlock / kWave) * i) * kWave + lane;
+            const int row = p / CPR, c = (p % CPR) ^ (row & 15);
+            const int kk = kz + 8 * c;
+            xr[i] = ld16(x + int64_t(min(m0 + row, m - 1)) * k + (kk < k ? kk : 0));
         }
     };
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (EARLY > 0) {
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+    // (the chunks past k are zeroed here, not at the load: a select there
+    // would wait for the data before the weight loads are issued)
+    auto x_store = [&](const u32x4(&xr)[kCopies]) {
 #pragma unroll
-        for (int j = 0; j < EARLY; ++j) w_load(j);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+        for (int i = 0; i < kCopies; ++i) {
+            const int p = (wave + (kSkBlock / kWave) * i) * kWave + lane;
+            const int row = p / CPR, c = (p % CPR) ^ (row & 15);
+            *reinterpret_cast<u32x4*>(&xs[8 * p]) = TAIL ? zero_unless(kz + 8 * c < k, xr[i]) : xr[i];
+        }
+    };
 
-    // Publish the X slice: the X loads complete before the weight loads
-    // issued after them (the compiler's wait for xr leaves those in flight),
-    // and an LDS-only release/acquire around the barrier waits for the LDS
-    // writes alone.
+    // 1. X block 0 and the scales of rows nw.. (rows past n repeat row n-1).
+    // Scale pair e of a row covers k = kz + 32 e .. +32; pairs past k take
+    // the row's first pair, as the codes past k take the row's first codes
+    // (they meet zero X).  Without a k tail every row's range of scales is 64
+    // aligned bytes: four 16-byte loads; with one, 2-byte loads.
+    u32x4 xr[kCopies];
+    x_load(xr, 0);
+    u32x4 sr16[kScale16PerLane];
+    uint32_t sr2[kScale2PerLane];
+    if constexpr (!TAIL) {
 #pragma unroll
-    for (int i = 0; i < kCopies; ++i) {
-        const int cp = wave + (kSkBlock / kWave) * i;
-        *reinterpret_cast<u32x4*>(&xs[8 * (cp * kWave + lane)]) = xr[i];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    __builtin_amdgcn_sched_barrier(0);  // no decode is hoisted above the barrier
+        for (int i = 0; i < kScale16PerLane; ++i) {
+            const int c = min(tid + kSkBlock * i, kScale16 - 1);
+            const int64_t row = min(nw + c / 4, n - 1);
+            sr16[i] = ld16(w + soff + row * (k / 16) + kz / 16 + 16 * (c % 4));
+        }
+    } else {
 #pragma unroll
-    for (int j = EARLY; j < kSkSlabs; ++j) w_load(j);
-    __builtin_amdgcn_sched_barrier(0);
-    // TAIL (k not a multiple of kSkRange): the last range zeroes its X chunks
-    // past k.  Without it the kernel is one basic block, which keeps each
-    // weight load's zero-extension next to the load (across a branch the
-    // compiler moves them all to the join, where they would wait for every
-    // slab at once).
-    if constexpr (TAIL) {
-        if (kz + kSkRange > k) {
-            for (int p = tid; p < kSkRows * CPR; p += kSkBlock) {
-                const int row = p / CPR, c = (p % CPR) ^ (row & 15);
-                if (kz + 8 * c >= k) *reinterpret_cast<u32x4*>(&xs[8 * p]) = u32x4{0u, 0u, 0u, 0u};
-            }
-            __syncthreads();
+        for (int i = 0; i < kScale2PerLane; ++i) {
+            const int e = tid + kSkBlock * i;
+            const int64_t row = min(nw + e / SPR, n - 1);
+            const int kk = kz + 32 * (e % SPR);
+            sr2[i] = ld<uint16_t>(w + soff + row * (k / 16) + (kk < k ? kk / 16 : 0));
         }
     }
 
-    // 3. MFMAs, slab by slab, without a runtime branch (slabs past the range
-    // meet zeroed X and add nothing)
-    floatx4 acc[MB][NB];
+    // 2. this wave's weight slabs, all of them (issued after step 3); slab j
+    // covers k = kz + 128 (2 j + half) + [0, 128), lane group lg its 32 k from
+    // kz + 128 (2 j + half) + 32 lg (past k: the row's first 32)
+    WStage<NB> wr[kSkSlabs];
+    auto w_load = [&]() {
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < kSkSlabs; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            u32x4 bfr[NB];
+        for (int j = 0; j < kSkSlabs; ++j) {
+            const int kb = kz + KW * (kSkHalves * j + half) + 32 * lg;
+            const int kc = kb < k ? kb : 0;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const float sc = (q < 2) ? e4m3_to_f32<0>(wr[j].s[nb]) : e4m3_to_f32<1>(wr[j].s[nb]);
-                bfr[nb] = decode8_scaled(wr[j].c[nb][q], sc);
-            }
-            const int c = 16 * (kSkHalves * j + half) + 4 * lg + q;  // k = 128 slab + 32 lg + 8 q
+                const int64_t row = min(n0 + 16 * nb + lr, n - 1);
+                const u32x4 v = ld16(w + row * (k / 2) + kc / 2);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int row = 16 * mb + lr;
-                const u32x4 a = *reinterpret_cast<const u32x4*>(&xs[8 * (row * CPR + (c ^ (row & 15)))]);
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32_bf16(a, bfr[nb], acc[mb][nb]);
+                for (int q = 0; q < 4; ++q) wr[j].c[nb][q] = v[q];
             }
         }
-    }
+    };
 
-    // 4. odd half + even half (in that fixed order) through the X buffer, then
-    // the partial sums of this range: part[z][row][col]
-    float* red = reinterpret_cast<float*>(xs) + rs * kAccFloats * kWave;
-    __syncthreads();  // every wave is done with X
-    if (half == 1) {
+    // 3. publish X block 0 and the scales, then request the weights
+    x_store(xr);
+    if constexpr (!TAIL) {
+        // lanes past the last chunk store the last chunk again (the same
+        // bytes): no branch, which would let the compiler sink the load
+        // behind the weight loads and wait for all of them
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int i = 0; i < kScale16PerLane; ++i) {
+            const int c = min(tid + kSkBlock * i, kScale16 - 1);
+            *reinterpret_cast<u32x4*>(&ss[(c / 4) * kSkScaleStride + 16 * (c % 4)]) = sr16[i];
+        }
+    } else {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) red[((mb * NB + nb) * 4 + v) * kWave + lane] = acc[mb][nb][v];
+        for (int i = 0; i < kScale2PerLane; ++i) {
+            const int e = tid + kSkBlock * i;
+            *reinterpret_cast<uint16_t*>(&ss[(e / SPR) * kSkScaleStride + 2 * (e % SPR)]) = uint16_t(sr2[i]);
+        }
     }
-    __syncthreads();
-    if (half == 0) {
-        float* pz = part + int64_t(blockIdx.z) * m * n;
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);  // no decode is hoisted above the barrier
+    w_load();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (TB > 1) x_load(xr, kSkRows);  // block 1, queued behind the weights
+
+    // this wave's scale pairs: slab j, row block nb
+    uint32_t sc2[kSkSlabs][NB];
+#pragma unroll
+    for (int j = 0; j < kSkSlabs; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            sc2[j][nb] = *reinterpret_cast<const uint16_t*>(
+                &ss[(rs * 16 * NB + 16 * nb + lr) * kSkScaleStride + 2 * (4 * (kSkHalves * j + half) + lg)]);
+
+    float* tile = reinterpret_cast<float*>(xs);  // [half][token][column], after the MFMAs
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        if (tb > 0) {
+            // a later block decodes the weights again: kept decoded they would
+            // take 192 registers, so the registers are marked as rewritten here
+            // (an empty asm), which stops the compiler from reusing block 0's
+            // decode.  Every weight load has completed by now.
+#pragma unroll
+            for (int j = 0; j < kSkSlabs; ++j)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(wr[j].c[nb][q]));
+                    asm volatile("" : "+v"(sc2[j][nb]));
+                }
+        }
+        // 4. MFMAs, slab by slab, without a runtime branch (slabs past k meet
+        // zero X and add nothing)
+        floatx4 acc[MB][NB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kSkSlabs; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u32x4 bfr[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float sc = (q < 2) ? e4m3_to_f32<0>(sc2[j][nb]) : e4m3_to_f32<1>(sc2[j][nb]);
+                    bfr[nb] = decode8_scaled(wr[j].c[nb][q], sc);
+                }
+                const int c = 16 * (kSkHalves * j + half) + 4 * lg + q;  // k = 128 slab + 32 lg + 8 q
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int row = 16 * mb + lr;
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(&xs[8 * (row * CPR + (c ^ (row & 15)))]);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32_bf16(a, bfr[nb], acc[mb][nb]);
+                }
+            }
+        }
+
+        // 5. both halves' sums into the tile (the X block is no longer read),
+        // then even half + odd half per output, stored as contiguous row
+        // segments of part[z][token][column]
+        lds_barrier();
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float sum = red[((mb * NB + nb) * 4 + v) * kWave + lane] + acc[mb][nb][v];
-                    const int row = m0 + 16 * mb + 4 * lg + v, col = n0 + 16 * nb + lr;
-                    if (row < m && col < n) pz[int64_t(row) * n + col] = sum;
+                for (int v = 0; v < 4; ++v)
+                    tile[(half * kSkRows + 16 * mb + 4 * lg + v) * kSkTileStride + rs * 16 * NB + 16 * nb + lr] =
+                        acc[mb][nb][v];
+        lds_barrier();
+        float* pz = part + int64_t(blockIdx.z) * m * n;
+        constexpr int C4 = kSkCols / 4;
+#pragma unroll
+        for (int i = 0; i < kSkRows * C4 / kSkBlock; ++i) {
+            const int c = tid + kSkBlock * i;
+            const int r = c / C4, col = 4 * (c % C4);
+            const floatx4 a = *reinterpret_cast<const floatx4*>(&tile[r * kSkTileStride + col]);
+            const floatx4 b = *reinterpret_cast<const floatx4*>(&tile[(kSkRows + r) * kSkTileStride + col]);
+            const floatx4 sum = {a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
+            const int tok = tb * kSkRows + r, gc = nw + col;
+            if (tok < m && gc < n) {
+                float* dst = pz + int64_t(tok) * n + gc;
+                if (n % 4 == 0) {
+                    *reinterpret_cast<floatx4*>(dst) = sum;
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (gc + v < n) dst[v] = sum[v];
                 }
+            }
+        }
+        if constexpr (TB > 1) {
+            if (tb + 1 < TB) {
+                lds_barrier();  // the tile is read
+                x_store(xr);
+                lds_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     }
 }
 
-// y = bf16_rne(s_t * sum over the nz ranges of part[z]), ranges in order.
-// Four outputs per thread when count % 4 == 0 (every slice then starts
-// 16-byte aligned), else one.
+// y = bf16_rne(s_t * sum over the nz ranges of part[z]), ranges in order
+// (the first range's value is the start, so a lone -0 stays -0).  Four
+// outputs per thread when count % 4 == 0 (every slice then starts 16-byte
+// aligned), else one; the ranges' loads are issued four at a time.
 __global__ __launch_bounds__(kBlock) void k_prefill_reduce(const float* __restrict__ part, int nz, int64_t count,
                                                            float s_t, uint16_t* __restrict__ y) {
     const int64_t n4 = count % 4 == 0 ? count / 4 : 0;
     for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < n4; i += int64_t(gridDim.x) * kBlock) {
         floatx4 sum = *reinterpret_cast<const floatx4*>(part + 4 * i);
-        for (int z = 1; z < nz; ++z) {
-            const floatx4 v = *reinterpret_cast<const floatx4*>(part + z * count + 4 * i);
-            sum[0] += v[0];
-            sum[1] += v[1];
-            sum[2] += v[2];
-            sum[3] += v[3];
+        for (int z0 = 1; z0 < nz; z0 += 4) {
+            floatx4 v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (z0 + j < nz) v[j] = *reinterpret_cast<const floatx4*>(part + (z0 + j) * count + 4 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (z0 + j < nz) {
+                    sum[0] += v[j][0];
+                    sum[1] += v[j][1];
+                    sum[2] += v[j][2];
+                    sum[3] += v[j][3];
+                }
         }
         const uint32_t lo = f32_to_bf16_rne(sum[0] * s_t) | (f32_to_bf16_rne(sum[1] * s_t) << 16);
         const uint32_t hi = f32_to_bf16_rne(sum[2] * s_t) | (f32_to_bf16_rne(sum[3] * s_t) << 16);
@@ -755,18 +838,14 @@ size_t prefill_workspace_bytes(int64_t n, int64_t k, int64_t m) {
 
 hipError_t launch_prefill_ws(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x, int64_t m,
                              uint16_t* y, float* ws, hipStream_t s) {
-    if (m > 128) return launch_prefill(w, s_t, n, k, x, m, y, s);
+    if (m > 2 * kSkRows) return launch_prefill(w, s_t, n, k, x, m, y, s);
     const int64_t soff = scale_plane_offset(QG_NVFP4, n, k);
-    constexpr int NB = 3;
     const int nz = int((k + kSkRange - 1) / kSkRange);
-    constexpr int BN = 16 * NB * (kSkBlock / kWave / kSkHalves);
-    const dim3 grid(unsigned((n + BN - 1) / BN), unsigned((m + kSkRows - 1) / kSkRows), unsigned(nz));
-    if (k % kSkRange == 0)
-        hipLaunchKernelGGL((k_prefill_sk<NB, false, kSkEarly>), grid, dim3(kSkBlock), 0, s, w, soff, int(n), int(k),
-                           x, int(m), ws);
-    else
-        hipLaunchKernelGGL((k_prefill_sk<NB, true, kSkEarly>), grid, dim3(kSkBlock), 0, s, w, soff, int(n), int(k),
-                           x, int(m), ws);
+    const dim3 grid(unsigned((n + kSkCols - 1) / kSkCols), 1u, unsigned(nz));
+    const bool tail = k % kSkRange != 0;
+    auto kern = m > kSkRows ? (tail ? k_prefill_sk<true, 2> : k_prefill_sk<false, 2>)
+                            : (tail ? k_prefill_sk<true, 1> : k_prefill_sk<false, 1>);
+    hipLaunchKernelGGL(kern, grid, dim3(kSkBlock), 0, s, w, soff, int(n), int(k), x, int(m), ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t count = m * n;
