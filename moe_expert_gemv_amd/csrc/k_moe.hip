@@ -63,29 +63,25 @@ __device__ __forceinline__ float route_key_value(uint64_t key) {
 
 __device__ __forceinline__ int route_key_index(uint64_t key) { return int(~uint32_t(key)); }
 
-// One DPP exchange of the wave-wide key maximum; rows outside ROW_MASK keep
-// their own key.
+// One DPP exchange of a wave-wide unsigned maximum.  Lanes of rows outside
+// ROW_MASK (and lanes without a source) see 0, the identity of the maximum,
+// so the exchange folds into one v_max_u32 with a DPP operand.
 template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ uint64_t route_max_step(uint64_t k) {
-    const uint32_t lo = uint32_t(k), hi = uint32_t(k >> 32);
-    const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false);
-    const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false);
-    const uint64_t o = (uint64_t(ohi) << 32) | olo;
-    return o > k ? o : k;
+__device__ __forceinline__ uint32_t route_max_step(uint32_t v) {
+    const uint32_t o = __builtin_amdgcn_update_dpp(0u, v, CTRL, ROW_MASK, 0xf, false);
+    return o > v ? o : v;
 }
 
-// Largest key of the wave, returned to every lane: butterflies inside rows of
-// 16 lanes, then row broadcasts that leave the total in lane 63.
-__device__ __forceinline__ uint64_t route_wave_max(uint64_t k) {
-    k = route_max_step<0xB1>(k);        // quad_perm [1,0,3,2]
-    k = route_max_step<0x4E>(k);        // quad_perm [2,3,0,1]
-    k = route_max_step<0x141>(k);       // row_half_mirror
-    k = route_max_step<0x140>(k);       // row_mirror: every lane holds its row's maximum
-    k = route_max_step<0x142, 0xA>(k);  // row_bcast:15 into rows 1 and 3
-    k = route_max_step<0x143, 0xC>(k);  // row_bcast:31 into rows 2 and 3
-    const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(k), 63);
-    const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(k >> 32), 63);
-    return (uint64_t(hi) << 32) | lo;
+// Largest value of the wave, returned to every lane: butterflies inside rows
+// of 16 lanes, then row broadcasts that leave the total in lane 63.
+__device__ __forceinline__ uint32_t route_wave_max(uint32_t v) {
+    v = route_max_step<0xB1>(v);        // quad_perm [1,0,3,2]
+    v = route_max_step<0x4E>(v);        // quad_perm [2,3,0,1]
+    v = route_max_step<0x141>(v);       // row_half_mirror
+    v = route_max_step<0x140>(v);       // row_mirror: every lane holds its row's maximum
+    v = route_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = route_max_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Loads of one token's e logits for route_select (e <= 64 * PER): lane l
@@ -123,9 +119,20 @@ __device__ __forceinline__ void route_select(const float (&v)[PER], int e, int t
             key[j - 1] = a > b ? a : b;
             key[j] = a > b ? b : a;
         }
+    // A round's maximum is taken over the keys' high words (the logit order)
+    // alone; the low word (~expert) decides only among lanes whose leading
+    // logits are equal, in a second reduction that is skipped when one lane
+    // holds the maximum (the usual case).  The result is the 64-bit key
+    // maximum either way.
     uint64_t mine = 0;
     for (int s = 0; s < top_k; ++s) {
-        const uint64_t best = route_wave_max(key[0]);
+        const uint32_t hi = uint32_t(key[0] >> 32);
+        const uint32_t m = route_wave_max(hi);
+        const uint64_t tie = __ballot(hi == m);
+        const uint32_t lo = __popcll(tie) == 1
+                                ? __builtin_amdgcn_readlane(uint32_t(key[0]), __builtin_ctzll(tie))
+                                : route_wave_max(hi == m ? uint32_t(key[0]) : 0u);
+        const uint64_t best = (uint64_t(m) << 32) | lo;
         if (lane == s) mine = best;
         if (key[0] == best) {  // the winner (keys are distinct) moves to its next key
 #pragma unroll
