@@ -471,6 +471,32 @@ size_t qgemm_prefill_workspace_bytes(int64_t n, int64_t k, int64_t m);
 int qgemm_prefill_ws(const void* w, float tensor_scale, int64_t n, int64_t k, const uint16_t* x,
                      int64_t m, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------ kernel policy
+ * The one rollback seam (the pages keep configuration flags only for runtime
+ * parameters, machine configuration and rollback seams: memra README, quick
+ * start, flag catalog).  QG_KERNEL_TUNED, the default, runs the
+ * shape-specialised kernels.  QG_KERNEL_GENERIC sends the calls that have
+ * one to a simpler kernel of the same family:
+ *   qgemv_nvfp4 / qgemv_nvfp4_swiglu at m = 1: the chunk-loop kernel of
+ *     m = 2..16 rather than the streaming kernel (bitwise the same result);
+ *   moe_gemv_grouped / moe_forward / moe_forward_noalloc at 2..4 tokens: the
+ *     per-(expert group, row tile) kernels of one token rather than the
+ *     row-tile kernels (bitwise the same result);
+ *   qgemm_prefill_ws at m <= 128: the single-pass kernel of qgemm_prefill
+ *     (the workspace is left untouched; the result is qgemm_prefill's, which
+ *     agrees with the split-k result to rounding).
+ * Every other call is unaffected.  The initial policy comes from the
+ * environment variable QG_FORCE_KERNEL ("generic" or "tuned"; anything else,
+ * or unset, is tuned), read once, when the library is first used.
+ * qg_set_kernel_policy changes it for the whole process from the next call
+ * on (work already enqueued keeps its kernels); it returns QG_OK, or
+ * QG_EINVAL for an unknown policy.  qg_kernel_policy returns the current
+ * one. */
+#define QG_KERNEL_TUNED   0
+#define QG_KERNEL_GENERIC 1
+int qg_set_kernel_policy(int policy);
+int qg_kernel_policy(void);
+
 /* ------------------------------------------------------ achievable-peak probes
  * Measurement tools, not part of the decode path: what this GPU reaches with
  * the instructions the kernels use, printed beside the data-sheet peaks (the

@@ -31,6 +31,7 @@ __all__ = [
     "qgemv_q4_0_a8", "moe_route_topk", "QgMoeDesc", "moe_workspace_bytes",
     "moe_gemv_grouped", "moe_forward", "moe_forward_noalloc", "QG_MOE_NOALLOC_SCRATCH_BYTES", "moe_prefill_workspace_bytes", "moe_prefill", "qgemm_prefill",
     "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws", "qg_probe_read", "qg_probe_mfma_bf16",
+    "QG_KERNEL_TUNED", "QG_KERNEL_GENERIC", "qg_set_kernel_policy", "qg_kernel_policy",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -47,6 +48,7 @@ KQUANT_FORMATS = (QG_Q4_K, QG_Q5_K, QG_Q6_K, QG_IQ4_XS)
 QG_MAX_M = 16
 QG_MOE_KEEP_H = 1
 QG_MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
+QG_KERNEL_TUNED, QG_KERNEL_GENERIC = 0, 1
 
 
 class QGLibraryMissing(RuntimeError):
@@ -130,6 +132,8 @@ _SIGNATURES = {
     "qgemm_prefill_ws": (_I32, [_P, _F32, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]),
     "qg_probe_read": (_I32, [_P, _SZ, _I32, _P, _P]),
     "qg_probe_mfma_bf16": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_int64), _P]),
+    "qg_set_kernel_policy": (_I32, [_I32]),
+    "qg_kernel_policy": (_I32, []),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -488,3 +492,13 @@ def qg_probe_mfma_bf16(iters, sink, stream=None) -> int:
     flops = ctypes.c_int64(0)
     _check("qg_probe_mfma_bf16", lib().qg_probe_mfma_bf16(iters, _dptr(sink), ctypes.byref(flops), _stream(stream)))
     return int(flops.value)
+
+
+def qg_set_kernel_policy(policy: int) -> None:
+    """Select the tuned (default) or the generic kernels for the calls that
+    have both (the library's rollback seam; QG_FORCE_KERNEL sets the start)."""
+    _check("qg_set_kernel_policy", lib().qg_set_kernel_policy(policy))
+
+
+def qg_kernel_policy() -> int:
+    return int(lib().qg_kernel_policy())

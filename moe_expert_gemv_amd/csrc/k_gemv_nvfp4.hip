@@ -419,8 +419,9 @@ hipError_t go_stream(const Args& A, hipStream_t s) {
 template <int G, int C, int MT, bool SW>
 hipError_t go(const Args& A, hipStream_t s) {
     if constexpr (MT == 1 && C > 0 && C <= 6) {
-        return go_stream<G, C, SW>(A, s);
-    } else if constexpr (MT >= 16 && C > 4) {
+        if (kernel_policy() != QG_KERNEL_GENERIC) return go_stream<G, C, SW>(A, s);
+    }
+    if constexpr (MT >= 16 && C > 4) {
         // 16 tokens over long rows: the all-loads-first form does not fit in
         // registers; use the chunk loop.
         return go<G, 0, MT, SW>(A, s);

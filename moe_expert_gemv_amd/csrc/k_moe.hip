@@ -1048,7 +1048,8 @@ hipError_t launch_moe(const qg_moe_desc* d, const uint16_t* x, const int32_t* id
             if (moe_tile_go(A, x, ids, w, logits, t, y, ws, s, err)) return err;
             return moe_mt<1>(A, x, ids, w, logits, t, y, ws, s);
         case 4:
-            if (moe_tile_go(A, x, ids, w, logits, t, y, ws, s, err)) return err;
+            if (kernel_policy() != QG_KERNEL_GENERIC && moe_tile_go(A, x, ids, w, logits, t, y, ws, s, err))
+                return err;
             return moe_mt<4>(A, x, ids, w, logits, t, y, ws, s);
         default: return moe_mt<16>(A, x, ids, w, logits, t, y, ws, s);
     }

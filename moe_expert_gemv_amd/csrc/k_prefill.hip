@@ -838,7 +838,7 @@ size_t prefill_workspace_bytes(int64_t n, int64_t k, int64_t m) {
 
 hipError_t launch_prefill_ws(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x, int64_t m,
                              uint16_t* y, float* ws, hipStream_t s) {
-    if (m > 2 * kSkRows) return launch_prefill(w, s_t, n, k, x, m, y, s);
+    if (m > 2 * kSkRows || kernel_policy() == QG_KERNEL_GENERIC) return launch_prefill(w, s_t, n, k, x, m, y, s);
     const int64_t soff = scale_plane_offset(QG_NVFP4, n, k);
     const int nz = int((k + kSkRange - 1) / kSkRange);
     const dim3 grid(unsigned((n + kSkCols - 1) / kSkCols), 1u, unsigned(nz));

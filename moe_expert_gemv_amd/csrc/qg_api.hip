@@ -1,10 +1,13 @@
 // The C entry points: argument validation on the host, then one launch (or a
 // short fixed sequence of launches) on the caller's stream.  Nothing here
-// allocates, synchronises or keeps per-call state.
+// allocates, synchronises or keeps per-call state; the only process-wide
+// setting is the kernel policy (the rollback seam).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 #include "qg_internal.hpp"
@@ -39,6 +42,24 @@ hipError_t device_cu_count(int* cus) {
 
 namespace {
 
+std::atomic<int> g_policy{QG_KERNEL_TUNED};
+std::once_flag g_policy_env;
+
+// QG_FORCE_KERNEL, read once: "generic" selects the generic kernels.
+void read_policy_env() {
+    const char* v = std::getenv("QG_FORCE_KERNEL");
+    if (v && std::strcmp(v, "generic") == 0) g_policy.store(QG_KERNEL_GENERIC);
+}
+
+}  // namespace
+
+int kernel_policy() {
+    std::call_once(g_policy_env, read_policy_env);
+    return g_policy.load(std::memory_order_relaxed);
+}
+
+namespace {
+
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
@@ -66,6 +87,15 @@ inline int check_gemv(const void* w, int64_t n, int64_t k, const void* x, int64_
 using namespace qg;
 
 extern "C" {
+
+int qg_set_kernel_policy(int policy) {
+    if (policy != QG_KERNEL_TUNED && policy != QG_KERNEL_GENERIC) return QG_EINVAL;
+    std::call_once(g_policy_env, read_policy_env);
+    g_policy.store(policy);
+    return QG_OK;
+}
+
+int qg_kernel_policy(void) { return kernel_policy(); }
 
 int qg_dequant(int fmt, const void* w, float tensor_scale, int64_t n, int64_t k, float* out,
                void* stream) {

@@ -14,6 +14,8 @@ void record_hip_error(hipError_t e);
 
 // Compute units of the current device (cached per device after the first call).
 hipError_t device_cu_count(int* cus);
+// The kernel policy (QG_KERNEL_TUNED or QG_KERNEL_GENERIC) in force for a new call.
+int kernel_policy();
 
 // Returns hipSuccess or the launch error.
 hipError_t launch_dequant(int fmt, const uint8_t* w, float s_t, int64_t n, int64_t k, float* out,

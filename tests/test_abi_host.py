@@ -472,3 +472,28 @@ def test_noalloc_size_limit_on_host(L):
     assert L.moe_forward_noalloc(ctypes.byref(d), FAKE, FAKE, 16, FAKE, None) == qg.QG_ENOSPC
     assert L.moe_forward_noalloc(ctypes.byref(_desc()), FAKE, FAKE, 0, FAKE, None) == qg.QG_EINVAL
     assert L.moe_forward_noalloc(ctypes.byref(_desc()), FAKE, FAKE, 17, FAKE, None) == qg.QG_EUNSUPPORTED
+
+
+def test_kernel_policy_seam():
+    """qg_set_kernel_policy / qg_kernel_policy: the two documented values,
+    QG_EINVAL for anything else (the policy unchanged), and QG_FORCE_KERNEL
+    read once at first use (in a fresh process)."""
+    import subprocess
+    import sys
+
+    try:
+        assert qg.qg_kernel_policy() == qg.QG_KERNEL_TUNED
+        qg.qg_set_kernel_policy(qg.QG_KERNEL_GENERIC)
+        assert qg.qg_kernel_policy() == qg.QG_KERNEL_GENERIC
+        for bad in (-1, 2, 99):
+            assert qg.lib().qg_set_kernel_policy(bad) == qg.QG_EINVAL
+            assert qg.qg_kernel_policy() == qg.QG_KERNEL_GENERIC
+        qg.qg_set_kernel_policy(qg.QG_KERNEL_TUNED)
+        assert qg.qg_kernel_policy() == qg.QG_KERNEL_TUNED
+    finally:
+        qg.qg_set_kernel_policy(qg.QG_KERNEL_TUNED)
+    code = "import moe_expert_gemv_amd as qg; print(qg.qg_kernel_policy())"
+    for env, want in (("generic", 1), ("tuned", 0), ("GENERIC", 0), ("", 0)):
+        out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True,
+                             env={**os.environ, "QG_FORCE_KERNEL": env}, cwd=ROOT)
+        assert int(out.stdout.strip()) == want, env
