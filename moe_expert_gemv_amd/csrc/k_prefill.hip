@@ -24,7 +24,7 @@
 //    workspace (k_prefill_sk + k_prefill_reduce): k is also split over
 //    workgroups, 1024 per workgroup, whose fp32 partials are added in range
 //    order by a second kernel.  M > 128: workgroups of 128 tokens x 192
-//    weight rows; with k a multiple of 256 eight waves (k_prefill8, two
+//    weight rows; with k a multiple of 128 eight waves (k_prefill8, two
 //    chains per output, added in a fixed order), otherwise four
 //    (k_prefill, each wave 48 rows over all k in one ascending MFMA chain).
 //    Within a shape the summation order of an output does not depend on M or
@@ -253,30 +253,55 @@ __global__ __launch_bounds__(kBlock) void k_prefill(const uint8_t* __restrict__ 
     }
 }
 
-// M > 128 with k a multiple of 256, eight waves (two per SIMD, so one wave's
-// weight decode and LDS reads overlap the other's MFMAs): waves w and w + 4
-// take the same 48 weight rows, w the first 128-k slab of each 256-k stage and
-// w + 4 the second.  The X tile of a stage (BM tokens x 256 k) is
-// double-buffered in LDS and filled by gfx950's direct global-to-LDS loads,
-// which hold no registers; each wave's weight slab for the next stage is
-// loaded into registers at the start of the current one.  Everything a stage
-// requests is needed at the start of the next, so one full wait before the
-// stage's closing barrier covers both.  At the end the second half's sums go
-// through LDS and are added to the first half's in that fixed order.
+// An LDS address, as the direct global -> LDS copies take it.
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// M > 128, k a multiple of 128 (k_prefill8): 128 tokens x 192 weight rows
+// per workgroup, eight waves (two per SIMD): waves w and w + 4 share 48 rows
+// and take the two 64-k halves of every 128-k stage.  Everything a stage
+// needs -- the X tile (128 x 128 bf16, 32 KB), the weight codes (192 rows x 64
+// bytes) and their block scales (192 x 8 bytes) -- is copied global -> LDS by
+// DMA (global_load_lds), into a ring of three stage slots, two stages ahead.
+// With every load of the loop being such a copy, the wait for a stage is an
+// exact vmcnt (the copies of the two later stages stay in flight), and one
+// LDS barrier per stage both publishes the stage and frees the slot the next
+// copy overwrites.  Fragments are then read from LDS: a lane group's 8 code
+// bytes (16 k, one E4M3 block: both MFMA steps of the stage half), one scale
+// byte, and the X chunks of the same 16 k (MFMA step s of lane group g takes
+// k = stage + 64 half + 16 g + 8 s .. +8 on both operands).  Rows of codes
+// sit 80 bytes apart in LDS (64 used), which puts the 16 rows of one
+// fragment read on distinct banks.  Per output the two halves' chains (each
+// over the stages in order) are added in a fixed order at the end.
+constexpr int kP8Threads = 512;
+constexpr int kP8BK = 128;                   // k per stage
+constexpr int kP8Slots = 3;                  // stage slots in LDS
+constexpr int kP8RowBytes = 80;              // LDS bytes per weight row of a stage (64 used)
+constexpr int kP8WSlots = 1024;              // 16-byte LDS slots per stage for the codes (960 used)
+constexpr int kP8Ops = 7;                    // copies per thread per stage: X 4, codes 2, scales 1
+
 template <int MB, int NB>
-__global__ __launch_bounds__(512) void k_prefill8(const uint8_t* __restrict__ w, int64_t soff, float s_t, int n,
-                                                  int k, const uint16_t* __restrict__ x, int m,
-                                                  uint16_t* __restrict__ y) {
-    constexpr int NT = 512, WN = 4;
-    constexpr int BM = 16 * MB, BN = 16 * NB * WN, BK = 2 * KW;
-    constexpr int CPR = BK / 8;                 // 16-byte X chunks per LDS row
-    constexpr int NCP = BM * CPR / NT;          // copy instructions per wave per stage
-    constexpr int SPS = KW / 32;                // MFMA steps per slab
-    static_assert((BM * CPR) % NT == 0, "X tile split evenly over the threads");
-    static_assert(sizeof(float) * BM * BN <= 2 * BM * BK * 2, "second-half sums fit in the X buffers");
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * BK];
+__global__ __launch_bounds__(kP8Threads) void k_prefill8(const uint8_t* __restrict__ w, int64_t soff, float s_t,
+                                                         int n, int k, const uint16_t* __restrict__ x, int m,
+                                                         uint16_t* __restrict__ y) {
+    constexpr int NT = kP8Threads, WN = 4, BK = kP8BK;
+    constexpr int BM = 16 * MB, BN = 16 * NB * WN;
+    constexpr int CPR = BK / 8;                 // 16-byte X chunks per token row
+    constexpr int NCP = BM * CPR / NT;          // X copies per thread per stage
+    constexpr int XW = BM * BK;                 // bf16 per X stage
+    constexpr int WB = kP8WSlots * 16;          // code bytes per stage slot
+    constexpr int SB = (NT / kWave) * kWave * 4;  // scale bytes per stage slot (512 dwords, 384 used)
+    static_assert(NCP == 4 && BN == 192, "the copy counts below assume this tile");
+    static_assert(BN * 5 <= kP8WSlots && BN * 2 <= NT, "code and scale slots");
+    static_assert(sizeof(float) * 2 * NB * 4 * kWave * WN <= XW * 2, "two token blocks' second-half sums fit in an X slot");
+    // The kP8Slots = 3 slots are separate objects, and the stage loop below is
+    // unrolled by three so that every read and every copy names its slot at
+    // compile time: the compiler then sees that the copies in flight into one
+    // slot cannot alias the reads of another and leaves them outstanding (with
+    // one array indexed by a run-time slot it waits for every copy before any
+    // LDS read).
+    __shared__ __attribute__((aligned(16))) uint16_t x0[XW], x1[XW], x2[XW];
+    __shared__ __attribute__((aligned(16))) uint8_t w0[WB], w1[WB], w2[WB];
+    __shared__ __attribute__((aligned(16))) uint8_t s0[SB], s1[SB], s2[SB];
 
     const int tid = int(threadIdx.x);
     const int lane = tid & 63;
@@ -284,43 +309,45 @@ __global__ __launch_bounds__(512) void k_prefill8(const uint8_t* __restrict__ w,
     const int wn = wave % WN, wk = wave / WN;
     const int lr = lane & 15, lg = lane >> 4;
     const int m0 = int(blockIdx.y) * BM;
-    const int n0 = int(blockIdx.x) * BN + wn * 16 * NB;
+    const int nw = int(blockIdx.x) * BN;  // the workgroup's first weight row
     const int nst = k / BK;
     const int64_t crow = k / 2, srow = k / 16;
 
-    // X tile of stage st into buffer buf: slot p holds X[row][st BK + 8c],
-    // row = p / CPR, c = (p % CPR) ^ (row & 15) (fragment reads hit 16
-    // distinct slots per 16 lanes); copy instruction i of this wave fills the
-    // 64 consecutive slots from (wave + 8 i) * 64, lane j the j-th.  Rows past
-    // m repeat row m - 1.
-    auto x_copy = [&](int buf, int st) {
+    // Copies of stage st (clamped to the last: the two issued past the end
+    // reload it into slots not read any more) into one slot.  Every thread
+    // issues kP8Ops copies per stage, so a wave's wait count is exact.
+    //  * X: slot p of the tile holds X[row][st BK + 8c], row = p / CPR, c =
+    //    (p % CPR) ^ (row & 15); copy i of this wave fills slots (wave + 8 i) *
+    //    64 ..; rows past m repeat row m - 1.
+    //  * codes: 16-byte slot q = 5 r + part holds bytes 16 part .. of weight
+    //    row r's 64 code bytes of the stage (part 4 and slots past 5 BN:
+    //    padding, filled from the matrix start).
+    //  * scales: dword slot q = 2 r + h holds bytes 4 h .. 4 h + 3 of row r's 8
+    //    scale bytes of the stage (slots past 2 BN: padding).
+    auto issue = [&](int st, uint16_t* xd, uint8_t* wd, uint8_t* sd) {
+        const int sc = min(st, nst - 1);
 #pragma unroll
         for (int i = 0; i < NCP; ++i) {
             const int cp = wave + (NT / kWave) * i;
             const int p = cp * kWave + lane;
             const int row = p / CPR, c = (p % CPR) ^ (row & 15);
-            const uint16_t* src = x + int64_t(min(m0 + row, m - 1)) * k + st * BK + 8 * c;
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(xs[buf] + 8 * cp * kWave), 16, 0, 0);
+            const uint16_t* src = x + int64_t(min(m0 + row, m - 1)) * k + sc * BK + 8 * c;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(xd + 8 * cp * kWave), 16, 0, 0);
         }
-    };
-
-    const uint8_t* wc[NB];
-    const uint8_t* ws[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int64_t row = min(n0 + 16 * nb + lr, n - 1);
-        wc[nb] = w + row * crow;
-        ws[nb] = w + soff + row * srow;
-    }
-    // stages past the end reread stage 0 (a valid address; never used)
-    auto w_load = [&](WStage<NB>& b, int st) {
-        const int kl = (st < nst ? st : 0) * BK + wk * KW + lg * (KW / 4);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const u32x4 v = ld16(wc[nb] + kl / 2);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
-            b.s[nb] = ld<uint16_t>(ws[nb] + kl / 16);
+        for (int i = 0; i < 2; ++i) {
+            const int cp = wave + (NT / kWave) * i;
+            const int q = cp * kWave + lane;
+            const int r = q / 5, part = q % 5;
+            const bool real = r < BN && part < 4;
+            const uint8_t* src = w + (real ? int64_t(min(nw + r, n - 1)) * crow + sc * (BK / 2) + 16 * part : 0);
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(wd + 16 * cp * kWave), 16, 0, 0);
+        }
+        {
+            const int q = wave * kWave + lane;
+            const int r = q / 2, h = q % 2;
+            const uint8_t* src = w + soff + (r < BN ? int64_t(min(nw + r, n - 1)) * srow + sc * (BK / 16) + 4 * h : 0);
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(sd + 4 * wave * kWave), 4, 0, 0);
         }
     };
 
@@ -330,31 +357,35 @@ __global__ __launch_bounds__(512) void k_prefill8(const uint8_t* __restrict__ w,
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    WStage<NB> wr;
-    w_load(wr, 0);
-    x_copy(0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stage's copies and weights have landed
-    lds_barrier();
-
-    for (int st = 0; st < nst; ++st) {
-        const int buf = st & 1;
-        const uint16_t* xb = xs[buf];
-        const WStage<NB> cur = wr;
-        w_load(wr, st + 1);
-        // the last stage recopies its own tile into the idle buffer: no branch
-        // (a join after the copies would make the compiler wait for them at
-        // the first use of any loaded register)
-        x_copy(buf ^ 1, st + 1 < nst ? st + 1 : st);
-        __builtin_amdgcn_sched_barrier(0);  // the next stage's loads are issued before this stage's work
+    // stage st from slot (xb, wb, sb), after its copies have landed; the
+    // copies of stage st + 2 go to slot (xn, wnx, sn), freed by the barrier
+    auto stage = [&](int st, const uint16_t* xb, const uint8_t* wb, const uint8_t* sb, uint16_t* xn, uint8_t* wnx,
+                     uint8_t* sn) {
+        // vmcnt(kP8Ops): this wave's copies of stage st have landed, the next
+        // stage's stay in flight.  Then a bare barrier: every wave's copies of
+        // stage st have landed and every wave is done reading the slot of
+        // stage st - 1.  No release fence: the loop writes LDS only by copies,
+        // which such a fence would wait for in full; the acquire keeps the
+        // reads below the barrier.
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kP8Ops);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        issue(st + 2, xn, wnx, sn);
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t sv[NB];
+        u32x2 cv[NB];
 #pragma unroll
-        for (int s = 0; s < SPS; ++s) {
+        for (int nb = 0; nb < NB; ++nb) {
+            const int r = wn * 16 * NB + 16 * nb + lr;
+            cv[nb] = *reinterpret_cast<const u32x2*>(&wb[r * kP8RowBytes + wk * 32 + 8 * lg]);
+            sv[nb] = sb[r * 8 + wk * 4 + lg];
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
             u32x4 bfr[NB];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const float sc = (s < 2) ? e4m3_to_f32<0>(cur.s[nb]) : e4m3_to_f32<1>(cur.s[nb]);
-                bfr[nb] = decode8_scaled(cur.c[nb][s], sc);
-            }
-            const int c = (wk * KW + lg * (KW / 4) + 8 * s) / 8;
+            for (int nb = 0; nb < NB; ++nb) bfr[nb] = decode8_scaled(cv[nb][s2], e4m3_to_f32<0>(sv[nb]));
+            const int c = wk * 8 + 2 * lg + s2;  // k = stage + 64 wk + 16 lg + 8 s2
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = 16 * mb + lr;
@@ -363,34 +394,55 @@ __global__ __launch_bounds__(512) void k_prefill8(const uint8_t* __restrict__ w,
                 for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32_bf16(a, bfr[nb], acc[mb][nb]);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next stage's copies and weights
-        lds_barrier();
-    }
+    };
 
-    // second half's sums through LDS (the X buffers are free after the last
-    // barrier), added to the first half's in that order
-    float* red = reinterpret_cast<float*>(&xs[0][0]) + wn * (MB * NB * 4 * kWave);
-    if (wk == 1) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) red[((mb * NB + nb) * 4 + v) * kWave + lane] = acc[mb][nb][v];
+    issue(0, x0, w0, s0);
+    issue(1, x1, w1, s1);
+    // slot of stage st: st % 3.  Whole triples in the loop, the one or two
+    // stages left after it: with no conditional stage inside the loop every
+    // path into a stage has the same copies outstanding, which the compiler
+    // needs in order to keep the exact wait.
+    int st = 0;
+    for (; st + 3 <= nst; st += 3) {
+        stage(st, x0, w0, s0, x2, w2, s2);
+        stage(st + 1, x1, w1, s1, x0, w0, s0);
+        stage(st + 2, x2, w2, s2, x1, w1, s1);
     }
+    if (st < nst) stage(st, x0, w0, s0, x2, w2, s2);
+    if (st + 1 < nst) stage(st + 1, x1, w1, s1, x0, w0, s0);
+
+    // second half's sums through LDS, two 16-token blocks at a time in X slot
+    // 0 (every copy has landed and every wave is done with the slots), added
+    // to the first half's in that order
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the trailing copies past the end
     __syncthreads();
-    if (wk == 0) {
+    float* red = reinterpret_cast<float*>(x0) + wn * (2 * NB * 4 * kWave);
+    const int n0 = nw + wn * 16 * NB;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+    for (int mp = 0; mp < MB; mp += 2) {
+        if (wk == 1) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float sum = acc[mb][nb][v] + red[((mb * NB + nb) * 4 + v) * kWave + lane];
-                    const int row = m0 + 16 * mb + 4 * lg + v;
-                    const int col = n0 + 16 * nb + lr;
-                    if (row < m && col < n) y[int64_t(row) * n + col] = uint16_t(f32_to_bf16_rne(sum * s_t));
-                }
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) red[((h * NB + nb) * 4 + v) * kWave + lane] = acc[mp + h][nb][v];
+        }
+        __syncthreads();
+        if (wk == 0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float sum = acc[mp + h][nb][v] + red[((h * NB + nb) * 4 + v) * kWave + lane];
+                        const int row = m0 + 16 * (mp + h) + 4 * lg + v;
+                        const int col = n0 + 16 * nb + lr;
+                        if (row < m && col < n) y[int64_t(row) * n + col] = uint16_t(f32_to_bf16_rne(sum * s_t));
+                    }
+        }
+        __syncthreads();
     }
 }
 
@@ -864,7 +916,7 @@ hipError_t launch_prefill(const uint8_t* w, float s_t, int64_t n, int64_t k, con
                            int(m), y);
         return hipGetLastError();
     }
-    if (k % (2 * KW) == 0) {
+    if (k % kP8BK == 0) {
         constexpr int MB = 8, NB = 3, BN = 16 * NB * 4, BM = 16 * MB;
         const dim3 grid(unsigned((n + BN - 1) / BN), unsigned((m + BM - 1) / BM));
         hipLaunchKernelGGL((k_prefill8<MB, NB>), grid, dim3(512), 0, s, w, soff, s_t, int(n), int(k), x, int(m), y);
