@@ -315,40 +315,54 @@ __global__ __launch_bounds__(kP8Threads) void k_prefill8(const uint8_t* __restri
 
     // Copies of stage st (clamped to the last: the two issued past the end
     // reload it into slots not read any more) into one slot.  Every thread
-    // issues kP8Ops copies per stage, so a wave's wait count is exact.
+    // issues kP8Ops copies per stage, so a wave's wait count is exact.  Each
+    // source is a workgroup-uniform base for the stage plus a 32-bit offset
+    // fixed for the whole loop (computed once here, so the loop spends no
+    // arithmetic on addresses):
     //  * X: slot p of the tile holds X[row][st BK + 8c], row = p / CPR, c =
     //    (p % CPR) ^ (row & 15); copy i of this wave fills slots (wave + 8 i) *
-    //    64 ..; rows past m repeat row m - 1.
+    //    64 ..; rows past m repeat row m - 1.  Offsets in elements from X[m0]:
+    //    row < 128 and k <= 2^24 keep them below 2^31.
     //  * codes: 16-byte slot q = 5 r + part holds bytes 16 part .. of weight
     //    row r's 64 code bytes of the stage (part 4 and slots past 5 BN:
-    //    padding, filled from the matrix start).
+    //    padding, filled from the workgroup's first row).
     //  * scales: dword slot q = 2 r + h holds bytes 4 h .. 4 h + 3 of row r's 8
-    //    scale bytes of the stage (slots past 2 BN: padding).
+    //    scale bytes of the stage (slots past 2 BN: padding, as above).
+    const uint16_t* xt = x + int64_t(m0) * k;
+    const uint8_t* wt = w + int64_t(nw) * crow;
+    const uint8_t* stt = w + soff + int64_t(nw) * srow;
+    uint32_t xo[NCP], wo[2], so;
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+        const int p = (wave + (NT / kWave) * i) * kWave + lane;
+        const int row = p / CPR, c = (p % CPR) ^ (row & 15);
+        xo[i] = uint32_t(min(row, m - 1 - m0)) * uint32_t(k) + uint32_t(8 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = (wave + (NT / kWave) * i) * kWave + lane;
+        const int r = q / 5, part = q % 5;
+        wo[i] = (r < BN && part < 4) ? uint32_t(min(r, n - 1 - nw)) * uint32_t(crow) + uint32_t(16 * part) : 0u;
+    }
+    {
+        const int q = wave * kWave + lane;
+        const int r = q / 2, h = q % 2;
+        so = r < BN ? uint32_t(min(r, n - 1 - nw)) * uint32_t(srow) + uint32_t(4 * h) : 0u;
+    }
+    // (the sources are passed as const void *: without the cast the host pass
+    // of this file silently drops the kernel's launch stub)
     auto issue = [&](int st, uint16_t* xd, uint8_t* wd, uint8_t* sd) {
         const int sc = min(st, nst - 1);
+        const uint16_t* xs_ = xt + sc * BK;
+        const uint8_t* ws_ = wt + sc * (BK / 2);
+        const uint8_t* ss_ = stt + sc * (BK / 16);
 #pragma unroll
-        for (int i = 0; i < NCP; ++i) {
-            const int cp = wave + (NT / kWave) * i;
-            const int p = cp * kWave + lane;
-            const int row = p / CPR, c = (p % CPR) ^ (row & 15);
-            const uint16_t* src = x + int64_t(min(m0 + row, m - 1)) * k + sc * BK + 8 * c;
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(xd + 8 * cp * kWave), 16, 0, 0);
-        }
+        for (int i = 0; i < NCP; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(xs_ + xo[i]), (lds_ptr)(xd + 8 * (wave + (NT / kWave) * i) * kWave), 16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int cp = wave + (NT / kWave) * i;
-            const int q = cp * kWave + lane;
-            const int r = q / 5, part = q % 5;
-            const bool real = r < BN && part < 4;
-            const uint8_t* src = w + (real ? int64_t(min(nw + r, n - 1)) * crow + sc * (BK / 2) + 16 * part : 0);
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(wd + 16 * cp * kWave), 16, 0, 0);
-        }
-        {
-            const int q = wave * kWave + lane;
-            const int r = q / 2, h = q % 2;
-            const uint8_t* src = w + soff + (r < BN ? int64_t(min(nw + r, n - 1)) * srow + sc * (BK / 16) + 4 * h : 0);
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(sd + 4 * wave * kWave), 4, 0, 0);
-        }
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(ws_ + wo[i]), (lds_ptr)(wd + 16 * (wave + (NT / kWave) * i) * kWave), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(ss_ + so), (lds_ptr)(sd + 4 * wave * kWave), 4, 0, 0);
     };
 
     floatx4 acc[MB][NB];
