@@ -625,7 +625,7 @@ class MoEPrefill(MoE):
 
 class Prefill(Workload):
     sources = ("k_prefill.hip", "qg_mfma.hpp")
-    kernel_re = (r"k_prefill8?\b",)
+    kernel_re = (r"k_prefill(8|_sm)?\b",)
 
     def __init__(self, m=512):
         import torch
@@ -711,29 +711,6 @@ class PrefillA8(Workload):
 
     def dominant_launch(self, i):
         self.qg.qgemm_prefill_a8(self.w[i % self.R], self.N, self.K, self.xq, self.xd, self.m, self.y)
-
-
-class PrefillWs(Prefill):
-    """m <= 128: the workspace variant (k split into slices of 1024 over
-    workgroups, then a fixed-order sum of the slices' partials)."""
-
-    kernel_re = (r"k_prefill_sk\b", r"k_prefill_reduce\b")
-
-    def __init__(self, m=64):
-        import torch
-
-        super().__init__(m)
-        self.ws_bytes = self.qg.qgemm_prefill_workspace_bytes(self.N, self.K, m)
-        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device="cuda")
-        # the partial sums make a round trip through memory
-        self.name += f"; k split in {self.K // 1024} slices, fp32 partials {self.ws_bytes} B"
-        self.dominant = "prefill MFMA GEMM (k-split kernel + slice sum)"
-
-    def step(self, i):
-        self.qg.qgemm_prefill_ws(self.w[i % self.R], 0.01, self.N, self.K, self.x, self.m, self.y, self.ws,
-                                 self.ws_bytes)
-
-    dominant_launch = step
 
 
 class ProbeRead(Workload):
@@ -837,8 +814,8 @@ CONFIGS = {  # name -> (workload class, its size argument)
     "moe": (MoE, 1),
     "moe-t4": (MoE, 4),
     "moe-prefill": (MoEPrefill, 512),
-    "prefill64": (PrefillWs, 64),
-    "prefill128": (PrefillWs, 128),
+    "prefill64": (Prefill, 64),
+    "prefill128": (Prefill, 128),
     "prefill512": (Prefill, 512),
     "w4a8-prefill512": (PrefillA8, 512),
     "probe-read": (ProbeRead, 1),

@@ -448,26 +448,32 @@ int moe_prefill(const qg_moe_desc* d, const uint16_t* x, const float* logits, in
  * (LumenLLM README, feature list: NVFP4 prefill GEMMs; memra README, known
  * gaps: prefill keeps bf16 activations rather than W4A4 numerics).
  * w: device packed NVFP4 [n][k]; x: device bf16 [m][k]; y: device bf16
- * [m][n].  Any m >= 1. */
+ * [m][n].  Any m >= 1.  For m <= 128 with k a multiple of 256 one launch
+ * reads every weight byte once (48 weight rows and all tokens a workgroup);
+ * there a row's result does not depend on the other rows or on m. */
 int qgemm_prefill(const void* w, float tensor_scale, int64_t n, int64_t k, const uint16_t* x,
                   int64_t m, uint16_t* y, void* stream);
 
 /* Device workspace bytes that qgemm_prefill_ws needs for this shape: nonzero
- * for m <= 128 (ceil(k / 1024) * m * n fp32 partial sums), 0 when the shape
- * runs without one (m > 128), and 0 for invalid arguments. */
+ * for m <= 128 with k not a multiple of 256 (ceil(k / 1024) * m * n fp32
+ * partial sums), 0 when the shape runs without one (m > 128, or k a multiple
+ * of 256), and 0 for invalid arguments. */
 size_t qgemm_prefill_workspace_bytes(int64_t n, int64_t k, int64_t m);
 
 /* The same product as qgemm_prefill, with a caller-owned device workspace.
- * For m <= 128 the k range is split into slices of 1024 handled by separate
- * workgroups (each reads only its slice of x, the dominant memory traffic of
- * a small-m product); their fp32 partial sums go to ws and a second launch
- * adds them in slice order and rounds once.  ws: device, 256-byte aligned,
+ * For m <= 128 with k not a multiple of 256 the k range is split into slices
+ * of 1024 handled by separate workgroups (each reads only its slice of x, the
+ * dominant memory traffic of a small-m product); their fp32 partial sums go
+ * to ws and a second launch adds them in slice order and rounds once.  Every
+ * other shape runs qgemm_prefill's kernels (bitwise its result) and leaves ws
+ * untouched.  ws: device, 256-byte aligned,
  * ws_bytes >= qgemm_prefill_workspace_bytes(n, k, m) (else QG_EINVAL for a
  * null or misaligned ws, QG_ENOSPC for too few bytes); ignored (may be null)
  * when that size is 0.  The library reads and writes ws only during the call
  * (stream-ordered); calls that share a workspace must not overlap.  A row's
- * result does not depend on the other rows or on m within m <= 128; it
- * agrees with qgemm_prefill to rounding (the summation order differs). */
+ * result does not depend on the other rows or on m within m <= 128; with the
+ * split k it agrees with qgemm_prefill to rounding (the summation order
+ * differs). */
 int qgemm_prefill_ws(const void* w, float tensor_scale, int64_t n, int64_t k, const uint16_t* x,
                      int64_t m, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
@@ -482,9 +488,9 @@ int qgemm_prefill_ws(const void* w, float tensor_scale, int64_t n, int64_t k, co
  *   moe_gemv_grouped / moe_forward / moe_forward_noalloc at 2..4 tokens: the
  *     per-(expert group, row tile) kernels of one token rather than the
  *     row-tile kernels (bitwise the same result);
- *   qgemm_prefill_ws at m <= 128: the single-pass kernel of qgemm_prefill
- *     (the workspace is left untouched; the result is qgemm_prefill's, which
- *     agrees with the split-k result to rounding).
+ *   qgemm_prefill_ws at m <= 128 with k not a multiple of 256: the kernel
+ *     of qgemm_prefill (the workspace is left untouched; the result is
+ *     qgemm_prefill's, which agrees with the split-k result to rounding).
  * Every other call is unaffected.  The initial policy comes from the
  * environment variable QG_FORCE_KERNEL ("generic" or "tuned"; anything else,
  * or unset, is tuned), read once, when the library is first used.

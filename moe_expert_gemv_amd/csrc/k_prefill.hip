@@ -17,13 +17,16 @@
 //    step s of the MFMA sums, for lane group g, the k range
 //    slab + 32g + 8s .. +8 on both operands (A and B use the same permutation
 //    of k, so the contraction is unchanged).
-//  * Three shapes.  M <= 128 without a workspace (k_prefill_ks): workgroups
-//    of 64 tokens x 48 weight rows; slab j of k goes to wave j mod 4, each
-//    wave chains its slabs through the MFMAs in ascending order, and the four
-//    partial sums are added in wave order through LDS.  M <= 128 with a
-//    workspace (k_prefill_sk + k_prefill_reduce): k is also split over
-//    workgroups, 1024 per workgroup, whose fp32 partials are added in range
-//    order by a second kernel.  M > 128: workgroups of 128 tokens x 192
+//  * Four shapes.  M <= 128 with k a multiple of 256, either entry point
+//    (k_prefill_sm): one workgroup per 48 weight rows over all of k and
+//    every token, X and the weights staged by LDS DMA, eight k chains added
+//    in wave order.  M <= 128, other k, without a workspace (k_prefill_ks):
+//    workgroups of 64 tokens x 48 weight rows; slab j of k goes to wave j
+//    mod 4, each wave chains its slabs through the MFMAs in ascending order,
+//    and the four partial sums are added in wave order through LDS.  M <= 128,
+//    other k, with a workspace (k_prefill_sk + k_prefill_reduce): k is also
+//    split over workgroups, 1024 per workgroup, whose fp32 partials are added
+//    in range order by a second kernel.  M > 128: workgroups of 128 tokens x 192
 //    weight rows; with k a multiple of 128 eight waves (k_prefill8, two
 //    chains per output, added in a fixed order), otherwise four
 //    (k_prefill, each wave 48 rows over all k in one ascending MFMA chain).
@@ -33,6 +36,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "qg_device.hpp"
 #include "qg_mfma.hpp"
@@ -376,12 +380,14 @@ __global__ __launch_bounds__(kP8Threads) void k_prefill8(const uint8_t* __restri
     auto stage = [&](int st, const uint16_t* xb, const uint8_t* wb, const uint8_t* sb, uint16_t* xn, uint8_t* wnx,
                      uint8_t* sn) {
         // vmcnt(kP8Ops): this wave's copies of stage st have landed, the next
-        // stage's stay in flight.  Then a bare barrier: every wave's copies of
-        // stage st have landed and every wave is done reading the slot of
-        // stage st - 1.  No release fence: the loop writes LDS only by copies,
+        // stage's stay in flight; lgkmcnt(0): its reads of the slot of stage
+        // st - 1 are done.  Then a bare barrier: every wave's copies of stage
+        // st have landed and no wave still reads the slot the copies below
+        // overwrite.  No release fence: the loop writes LDS only by copies,
         // which such a fence would wait for in full; the acquire keeps the
         // reads below the barrier.
-        __builtin_amdgcn_s_waitcnt(0x0F70 | kP8Ops);
+        static_assert(kP8Ops < 16, "vmcnt in the low field");
+        __builtin_amdgcn_s_waitcnt(0x0070 | kP8Ops);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         issue(st + 2, xn, wnx, sn);
@@ -594,6 +600,201 @@ __global__ __launch_bounds__(kBlock) void k_prefill_ks(const uint8_t* __restrict
         for (int q = 1; q < 4; ++q) sum += red[(q * BM + r) * BN + c];
         const int row = m0 + r, col = n0 + c;
         if (row < m && col < n) y[int64_t(row) * n + col] = uint16_t(f32_to_bf16_rne(sum * s_t));
+    }
+}
+
+// M <= 128 in one pass (k_prefill_sm): a workgroup owns 48 weight rows over
+// all of k and every token (TB blocks of 64), so each weight byte is read
+// once, nothing leaves the workgroup but its outputs, and the grid (n / 48
+// workgroups) fills the machine.  X, the codes and the scales come through
+// an LDS DMA ring of 256-k stages as in k_prefill8 (four slots for one token
+// block -- 160 KB, three stages in flight -- two for two); wave s (of eight)
+// takes k = stage + 32 s .. +32, one MFMA step per stage, so each wave runs
+// one chain per output over the stages in order, and the eight chains are
+// added in wave order at the end.  The per-token arithmetic is the same for
+// TB = 1 and 2, so a token's result does not depend on m within m <= 128.
+constexpr int kSmThreads = 512;
+constexpr int kSmBK = 256;         // k per stage
+constexpr int kSmRows = 48;        // weight rows per workgroup
+constexpr int kSmRowBytes = 144;   // LDS bytes per weight row of a stage (128 used; 144 keeps 16 rows on distinct banks)
+constexpr int kSmScaleOff = kSmRows * kSmRowBytes;  // the stage's 16 scale bytes a row follow the codes: 6912
+constexpr int kSmTileStride = 36;  // floats a column in the epilogue's [column][32 tokens] tiles
+
+template <int TB>
+__global__ __launch_bounds__(kSmThreads) void k_prefill_sm(const uint8_t* __restrict__ w, int64_t soff, float s_t,
+                                                           int n, int k, const uint16_t* __restrict__ x, int m,
+                                                           uint16_t* __restrict__ y) {
+    constexpr int NT = kSmThreads, BK = kSmBK, NB = kSmRows / 16, MB = 4 * TB;
+    constexpr int BM = 16 * MB;                 // tokens
+    constexpr int CPR = BK / 8;                 // 16-byte X chunks per token row: 32
+    constexpr int NCP = BM * CPR / NT;          // X copies per thread per stage: 4 or 8
+    constexpr int XW = BM * BK;                 // bf16 per X slot
+    constexpr int WB = NT * 16;                 // code and scale bytes per slot (one 16-byte copy per thread)
+    constexpr int OPS = NCP + 1;                // copies per thread per stage
+    constexpr int SLOTS = TB == 1 ? 4 : 2;
+    constexpr int TILE = kSmRows * kSmTileStride;  // epilogue floats a wave
+    static_assert(kSmRows * 9 + kSmRows <= NT && kSmScaleOff + 16 * kSmRows <= WB, "code and scale copies");
+    static_assert(4 * TILE * 4 <= XW * 2, "four waves' epilogue tiles fit one X slot");
+    // separate slot objects, the loop unrolled by the slot count (see k_prefill8)
+    __shared__ __attribute__((aligned(16))) uint16_t xa[XW], xb_[XW], xc[SLOTS > 2 ? XW : 8], xd_[SLOTS > 3 ? XW : 8];
+    __shared__ __attribute__((aligned(16))) uint8_t wa[WB], wb_[WB], wc[SLOTS > 2 ? WB : 16], wd[SLOTS > 3 ? WB : 16];
+
+    const int tid = int(threadIdx.x);
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // the 32-k slice of every stage
+    const int lr = lane & 15, lg = lane >> 4;
+    const int nw = int(blockIdx.x) * kSmRows;
+    const int nst = k / BK;
+    const int64_t crow = k / 2, srow = k / 16;
+
+    // Copy sources: a workgroup-uniform base per stage plus a 32-bit offset
+    // fixed for the loop.
+    //  * X: slot p holds X[tok][st BK + 8c], tok = p / CPR, c = (p % CPR) ^
+    //    (tok & 15); copy i of this wave fills slots (wave + 8 i) * 64 ..;
+    //    tokens past m repeat token m - 1.
+    //  * codes and scales, one 16-byte copy a thread: thread q < 432 = 9 r +
+    //    part, part < 8, copies bytes 16 part .. of row r's 128 code bytes of
+    //    the stage to r * 144 + 16 part (part 8: padding, from the workgroup's
+    //    first row); thread 432 + r copies row r's 16 scale bytes of the stage
+    //    to 6912 + 16 r; the rest copy row 0's scales into the padding after.
+    uint32_t xo[NCP];
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+        const int p = (wave + (NT / kWave) * i) * kWave + lane;
+        const int tok = p / CPR, c = (p % CPR) ^ (tok & 15);
+        xo[i] = uint32_t(min(tok, m - 1)) * uint32_t(k) + uint32_t(8 * c);
+    }
+    uint32_t wo;
+    bool wsc;  // this thread copies scales
+    {
+        const int q = tid, r = q / 9, part = q % 9;
+        if (q < 9 * kSmRows) {
+            wsc = false;
+            wo = part < 8 ? uint32_t(min(r, n - 1 - nw)) * uint32_t(crow) + uint32_t(16 * part) : 0u;
+        } else {
+            wsc = true;
+            const int rs = q - 9 * kSmRows;
+            wo = rs < kSmRows ? uint32_t(min(rs, n - 1 - nw)) * uint32_t(srow) : 0u;
+        }
+    }
+    const uint8_t* wt = w + int64_t(nw) * crow;
+    const uint8_t* stt = w + soff + int64_t(nw) * srow;
+    // (sources passed as const void *: see k_prefill8)
+    auto issue = [&](int st, uint16_t* xd, uint8_t* wd) {
+        const int sc = min(st, nst - 1);
+        const uint16_t* xs_ = x + sc * BK;
+#pragma unroll
+        for (int i = 0; i < NCP; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(xs_ + xo[i]),
+                                             (lds_ptr)(xd + 8 * (wave + (NT / kWave) * i) * kWave), 16, 0, 0);
+        const uint8_t* src = wsc ? stt + sc * (BK / 16) + wo : wt + sc * (BK / 2) + wo;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(wd + 16 * wave * kWave), 16, 0, 0);
+    };
+
+    floatx4 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // step weights of this wave's 32 k of a stage, decoded from slot ws_
+    auto decode_w = [&](const uint8_t* ws_, u32x4* bfr) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int r = 16 * nb + lr;
+            const uint32_t cw = *reinterpret_cast<const uint32_t*>(&ws_[r * kSmRowBytes + 16 * wave + 4 * lg]);
+            const uint32_t sv = ws_[kSmScaleOff + r * 16 + 2 * wave + (lg >> 1)];  // block (32 wave + 8 lg) / 16
+            bfr[nb] = decode8_scaled(cw, e4m3_to_f32<0>(sv));
+        }
+    };
+    auto mfma_x = [&](const uint16_t* xs_, const u32x4* bfr) {
+        const int c = 4 * wave + lg;  // k = stage + 32 wave + 8 lg
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int tok = 16 * mb + lr;
+            const u32x4 a = *reinterpret_cast<const u32x4*>(&xs_[8 * (tok * CPR + (c ^ (tok & 15)))]);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32_bf16(a, bfr[nb], acc[mb][nb]);
+        }
+    };
+    // this wave's copies of stage st have landed (the later ones stay in
+    // flight) and its LDS reads are done (a slot read in the previous stage
+    // is the next copy's target), then a bare barrier and an acquire (see
+    // k_prefill8)
+    auto sync = [&](auto ahead) {
+        constexpr int vm = OPS * (SLOTS - 2 - decltype(ahead)::value);
+        static_assert(vm < 16, "vmcnt in the low field");
+        __builtin_amdgcn_s_waitcnt(0x0070 | vm);  // lgkmcnt(0) vmcnt(vm)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    using ahead0 = std::integral_constant<int, 0>;
+
+    auto stage = [&](int st, const uint16_t* xs_, const uint8_t* ws_, uint16_t* xn, uint8_t* wn_) {
+        sync(ahead0{});
+        issue(st + SLOTS - 1, xn, wn_);
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 bfr[NB];
+        decode_w(ws_, bfr);
+        mfma_x(xs_, bfr);
+    };
+    if constexpr (SLOTS == 4) {
+        issue(0, xa, wa);
+        issue(1, xb_, wb_);
+        issue(2, xc, wc);
+        int st = 0;
+        for (; st + 4 <= nst; st += 4) {
+            stage(st, xa, wa, xd_, wd);
+            stage(st + 1, xb_, wb_, xa, wa);
+            stage(st + 2, xc, wc, xb_, wb_);
+            stage(st + 3, xd_, wd, xc, wc);
+        }
+        if (st < nst) stage(st, xa, wa, xd_, wd);
+        if (st + 1 < nst) stage(st + 1, xb_, wb_, xa, wa);
+        if (st + 2 < nst) stage(st + 2, xc, wc, xb_, wb_);
+    } else {
+        issue(0, xa, wa);
+        int st = 0;
+        for (; st + 2 <= nst; st += 2) {
+            stage(st, xa, wa, xb_, wb_);
+            stage(st + 1, xb_, wb_, xa, wa);
+        }
+        if (st < nst) stage(st, xa, wa, xb_, wb_);
+    }
+
+    // the eight chains of each output through LDS, 32 tokens at a time,
+    // added in wave order: wave v's [column][token] tile sits in xa (v < 4)
+    // or xb_
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the trailing copies
+    __syncthreads();
+    float* const tile = reinterpret_cast<float*>(wave < 4 ? xa : xb_) + (wave & 3) * TILE;
+#pragma unroll
+    for (int h = 0; h < 2 * TB; ++h) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                *reinterpret_cast<floatx4*>(&tile[(16 * nb + lr) * kSmTileStride + 16 * mb + 4 * lg]) =
+                    acc[2 * h + mb][nb];
+        __syncthreads();
+        if (tid < kSmRows * 8) {  // column tid % 48, tokens 4 (tid / 48) .. + 4
+            const int col = tid % kSmRows, t4 = tid / kSmRows;
+            const int off = col * kSmTileStride + 4 * t4;
+            floatx4 sum = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(xa) + off);
+#pragma unroll
+            for (int v = 1; v < 8; ++v)
+                sum += *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(v < 4 ? xa : xb_) +
+                                                         (v & 3) * TILE + off);
+            const int gc = nw + col;
+            if (gc < n) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tok = 32 * h + 4 * t4 + e;
+                    if (tok < m) y[int64_t(tok) * n + gc] = uint16_t(f32_to_bf16_rne(sum[e] * s_t));
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -896,15 +1097,19 @@ hipError_t go(const uint8_t* w, int64_t soff, float s_t, int64_t n, int64_t k, c
 
 }  // namespace
 
+// The k-split kernel only where the one-pass kernel (k_prefill_sm) does not
+// run: m <= 128 with k not a multiple of 256.
+static bool prefill_splits_k(int64_t k, int64_t m) { return m <= 2 * kSkRows && k % kSmBK != 0; }
+
 size_t prefill_workspace_bytes(int64_t n, int64_t k, int64_t m) {
-    if (m > 128) return 0;
+    if (!prefill_splits_k(k, m)) return 0;
     const int64_t nz = (k + kSkRange - 1) / kSkRange;
     return size_t(nz * m * n * 4);
 }
 
 hipError_t launch_prefill_ws(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x, int64_t m,
                              uint16_t* y, float* ws, hipStream_t s) {
-    if (m > 2 * kSkRows || kernel_policy() == QG_KERNEL_GENERIC) return launch_prefill(w, s_t, n, k, x, m, y, s);
+    if (!prefill_splits_k(k, m) || kernel_policy() == QG_KERNEL_GENERIC) return launch_prefill(w, s_t, n, k, x, m, y, s);
     const int64_t soff = scale_plane_offset(QG_NVFP4, n, k);
     const int nz = int((k + kSkRange - 1) / kSkRange);
     const dim3 grid(unsigned((n + kSkCols - 1) / kSkCols), 1u, unsigned(nz));
@@ -923,6 +1128,14 @@ hipError_t launch_prefill_ws(const uint8_t* w, float s_t, int64_t n, int64_t k, 
 hipError_t launch_prefill(const uint8_t* w, float s_t, int64_t n, int64_t k, const uint16_t* x,
                           int64_t m, uint16_t* y, hipStream_t s) {
     const int64_t soff = scale_plane_offset(QG_NVFP4, n, k);
+    if (m <= 128 && k % kSmBK == 0) {
+        const dim3 grid(unsigned((n + kSmRows - 1) / kSmRows));
+        if (m > 64)
+            hipLaunchKernelGGL(k_prefill_sm<2>, grid, dim3(kSmThreads), 0, s, w, soff, s_t, int(n), int(k), x, int(m), y);
+        else
+            hipLaunchKernelGGL(k_prefill_sm<1>, grid, dim3(kSmThreads), 0, s, w, soff, s_t, int(n), int(k), x, int(m), y);
+        return hipGetLastError();
+    }
     if (m <= 128) {
         constexpr int MB = 4, NB = 3;
         const dim3 grid(unsigned((n + 16 * NB - 1) / (16 * NB)), unsigned((m + 16 * MB - 1) / (16 * MB)));

@@ -184,15 +184,17 @@ def test_prefill_workspace_size_and_checks(L):
     """qgemm_prefill_ws: workspace size rule and argument errors (checked on
     the host before any launch)."""
     f = L.qgemm_prefill_ws
-    need = qg.qgemm_prefill_workspace_bytes(12288, 4096, 64)
-    assert need == 4 * 64 * 12288 * 4                      # ceil(k/1024) slices of fp32 [m][n]
+    need = qg.qgemm_prefill_workspace_bytes(12288, 4160, 64)
+    assert need == 5 * 64 * 12288 * 4                      # ceil(k/1024) slices of fp32 [m][n]
     assert qg.qgemm_prefill_workspace_bytes(100, 1056, 7) == 2 * 7 * 100 * 4
+    assert qg.qgemm_prefill_workspace_bytes(12288, 4096, 64) == 0   # k a multiple of 256: one pass
+    assert qg.qgemm_prefill_workspace_bytes(300, 768, 128) == 0
     assert qg.qgemm_prefill_workspace_bytes(12288, 4096, 512) == 0  # m > 128: no workspace
     assert qg.qgemm_prefill_workspace_bytes(8, 48, 1) == 0          # invalid k
     assert qg.qgemm_prefill_workspace_bytes(8, 64, 0) == 0          # invalid m
-    assert f(FAKE, 1.0, 12288, 4096, FAKE, 64, FAKE, None, need, None) == qg.QG_EINVAL       # null ws
-    assert f(FAKE, 1.0, 12288, 4096, FAKE, 64, FAKE, FAKE + 16, need, None) == qg.QG_EINVAL  # misaligned ws
-    assert f(FAKE, 1.0, 12288, 4096, FAKE, 64, FAKE, FAKE, need - 4, None) == qg.QG_ENOSPC   # too small
+    assert f(FAKE, 1.0, 12288, 4160, FAKE, 64, FAKE, None, need, None) == qg.QG_EINVAL       # null ws
+    assert f(FAKE, 1.0, 12288, 4160, FAKE, 64, FAKE, FAKE + 16, need, None) == qg.QG_EINVAL  # misaligned ws
+    assert f(FAKE, 1.0, 12288, 4160, FAKE, 64, FAKE, FAKE, need - 4, None) == qg.QG_ENOSPC   # too small
     assert f(FAKE, 1.0, 8, 64, FAKE, 0, FAKE, FAKE, 1 << 20, None) == qg.QG_EINVAL           # m = 0
     assert f(None, 1.0, 8, 64, FAKE, 1, FAKE, FAKE, 1 << 20, None) == qg.QG_EINVAL           # null w
 

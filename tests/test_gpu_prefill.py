@@ -23,7 +23,8 @@ def run_prefill(w, x_bits):
 
 
 def run_prefill_ws(w, x_bits):
-    """The workspace variant (k split over workgroups for m <= 128)."""
+    """The workspace variant (k split over workgroups for m <= 128 with k not
+    a multiple of 256)."""
     import torch
 
     n, k = w["codes"].shape
@@ -64,6 +65,10 @@ def test_worked_example():
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 32), (3, 17, 64), (64, 64, 64), (65, 130, 96), (100, 300, 512),
                                    (128, 64, 4096), (7, 1000, 2080), (513, 129, 160),
+                                   # M <= 128, k a multiple of 256 (one-pass kernel): 1 to 14 stages of
+                                   # 256 (whole rounds of four and the tails), ragged n, one and two
+                                   # token blocks
+                                   (1, 47, 256), (64, 97, 768), (65, 48, 1280), (128, 145, 2304), (33, 50, 3584),
                                    # M > 128, k a multiple of 256 (eight-wave kernel), ragged m and n
                                    (129, 193, 256), (300, 200, 768), (257, 385, 2048),
                                    # M > 128, other k (four-wave kernel)
@@ -89,6 +94,19 @@ def test_random_workspace(m, n, k):
     w = synth.nvfp4_weights(g, n, k)
     x = synth.x_bf16(g, m, k)
     check(w, x, what=f"prefill ws {m}x{n}x{k}", run=run_prefill_ws)
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 100, 1024), (128, 49, 768)])
+def test_workspace_path_is_one_pass_for_whole_stages(m, n, k):
+    """With k a multiple of 256 the workspace variant is qgemm_prefill itself
+    (no workspace; bitwise the same result)."""
+    require_gpu()
+    print(f"[prefill ws one-pass m={m} n={n} k={k}]", flush=True)
+    assert qg.qgemm_prefill_workspace_bytes(n, k, m) == 0
+    g = synth.rng(m + n + k)
+    w = synth.nvfp4_weights(g, n, k)
+    x = synth.x_bf16(g, m, k)
+    assert np.array_equal(run_prefill_ws(w, x), run_prefill(w, x))
 
 
 def test_workspace_rows_are_independent():
