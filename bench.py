@@ -714,30 +714,35 @@ class PrefillA8(Workload):
 
 
 class ProbeRead(Workload):
-    """Achievable HBM read bandwidth: the library's streaming-read probe over
-    rotating 1 GiB buffers (16-byte non-temporal loads, 1 KB per wave-wide
-    load, eight in flight per lane), at the workgroups-per-CU count that reads
-    fastest here."""
+    """Achievable HBM read bandwidth: the library's streaming-read probe
+    (16-byte non-temporal loads, 1 KB per wave-wide load, eight in flight per
+    lane) over copies of `nbytes` that rotate through at least 1 GiB (four
+    times the 256 MB Infinity Cache), at the workgroups-per-CU count that
+    reads fastest here.  At 1 GiB the launch ramp is negligible; at a
+    kernel's own byte count it is what a plain read of those bytes costs."""
     sources = ("k_probe.hip", "qg_mfma.hpp")
     kernel_re = (r"k_probe_read\b",)
     cpu_parts = 1
 
-    def __init__(self, gib=1):
+    def __init__(self, nbytes=1 << 30):
         import torch
         import moe_expert_gemv_amd as qg
 
         self.qg = qg
-        self.bytes = gib << 30
-        self.bufs = [torch.full((self.bytes,), 7, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        self.bytes = max(16, nbytes // 16 * 16)
+        self.R = max(2, -(-(1 << 30) // self.bytes))
+        self.bufs = torch.full((self.R, self.bytes), 7, dtype=torch.uint8, device="cuda")
         self.sink = torch.zeros(64, dtype=torch.int32, device="cuda")
         self.wg = best_read_probe_shape(self.bufs[0], self.sink)
         self.alg_step = self.dominant_bytes = self.bytes
         self.flops_step = 0
-        self.name = f"streaming-read probe: {gib} GiB per launch, {self.wg} four-wave workgroup(s) per CU"
+        size = f"{self.bytes >> 30} GiB" if self.bytes % (1 << 30) == 0 else f"{self.bytes / 1e6:.1f} MB"
+        self.name = (f"streaming-read probe: {size} per launch over {self.R} rotating copies, "
+                     f"{self.wg} four-wave workgroup(s) per CU")
         self.dominant = "streaming-read probe"
 
     def step(self, i):
-        self.qg.qg_probe_read(self.bufs[i % 2], self.wg, self.sink)
+        self.qg.qg_probe_read(self.bufs[i % self.R], self.wg, self.sink)
 
     dominant_launch = step
 
@@ -789,15 +794,25 @@ def best_read_probe_shape(buf, sink, shapes=(1, 2, 4)) -> int:
     return best
 
 
-def achievable_peaks(bound: str) -> dict:
+def achievable_peaks(bound: str, launch_bytes: int = 0) -> dict:
     """What this GPU reaches with the probes: read GB/s for HBM-bound
     configs, bf16 MFMA TFLOP/s for matrix-core-bound ones (graph replays of
-    the probe between two HIP events, best of three)."""
-    wl = ProbeRead() if bound == "hbm" else ProbeMfma()
+    the probe between two HIP events, best of three).  For HBM-bound configs
+    also the read probe at the dominant launch's own byte count, whose ramp
+    and drain a one-shot GEMV pays as well."""
+    if bound != "hbm":
+        wl = ProbeMfma()
+        _, mean = time_dominant(wl, 8)
+        return {"bf16_mfma_tflops": wl.flops_step / (mean * 1e-3) / 1e12, "probe": wl.name}
+    wl = ProbeRead()
     _, mean = time_dominant(wl, 8)
-    if bound == "hbm":
-        return {"read_gbs": wl.bytes / (mean * 1e-3) / 1e9, "probe": wl.name}
-    return {"bf16_mfma_tflops": wl.flops_step / (mean * 1e-3) / 1e12, "probe": wl.name}
+    out = {"read_gbs": wl.bytes / (mean * 1e-3) / 1e9, "probe": wl.name}
+    del wl
+    if launch_bytes:
+        wl = ProbeRead(launch_bytes)
+        _, mean = time_dominant(wl, min(wl.R, 32))
+        out["at_launch_bytes"] = {"us": mean * 1e3, "read_gbs": wl.bytes / (mean * 1e-3) / 1e9, "probe": wl.name}
+    return out
 
 
 CONFIGS = {  # name -> (workload class, its size argument)
@@ -818,7 +833,7 @@ CONFIGS = {  # name -> (workload class, its size argument)
     "prefill128": (Prefill, 128),
     "prefill512": (Prefill, 512),
     "w4a8-prefill512": (PrefillA8, 512),
-    "probe-read": (ProbeRead, 1),
+    "probe-read": (ProbeRead, 1 << 30),
     "probe-mfma": (ProbeMfma, 4000),
 }
 
@@ -1076,9 +1091,13 @@ def main():
     if not args.no_probe and not args.config.startswith("probe") and (
             wl.bound == "hbm" or wl.mfma_peak[0] == PEAK_BF16_TFLOPS):
         print("[bench] achievable peak (probe)", file=sys.stderr, flush=True)
-        roof["achievable"] = achievable_peaks("hbm" if wl.bound == "hbm" else "mfma")
+        roof["achievable"] = achievable_peaks("hbm" if wl.bound == "hbm" else "mfma",
+                                              wl.dominant_bytes if wl.bound == "hbm" else 0)
         ach = roof["achievable"].get("read_gbs") or roof["achievable"].get("bf16_mfma_tflops")
         roof["achievable"]["frac_of_achievable"] = roof["achieved"] / ach
+        at = roof["achievable"].get("at_launch_bytes")
+        if at:  # the same bytes by a plain read, against this launch
+            at["frac_of_plain_read"] = roof["achieved"] / at["read_gbs"]
     kt = kernel_trace_from_profile(args.config, cls)
     if kt:  # the kernel alone, from the committed rocprofv3 trace of this command
         t_k = kt["us_per_launch"] * 1e-6
