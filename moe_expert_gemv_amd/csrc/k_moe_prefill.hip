@@ -213,7 +213,11 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
     constexpr int SPP = KP / KW;            // slabs per pass
     constexpr int CPR = KP / 8;             // 16-byte chunks per LDS row
     constexpr int NCP = kPfPairs * CPR / kPfBlock;  // activation chunks per thread per pass
-    constexpr int WD = KS >= 8 ? 3 : 4;     // weight slabs in flight per wave (within 128 VGPRs)
+    // weight slabs in flight per wave: with several activation passes one
+    // (each pass's activation loads return behind the weight requests
+    // already out; at 512 tokens three slabs were 2.6 % slower for the whole
+    // layer, two 0.5 %), with one pass four
+    constexpr int WD = NP > 1 ? 1 : 4;
     static_assert(CPR >= 16 && (CPR & (CPR - 1)) == 0, "rows of a power-of-two count of 16 chunks");
     static_assert(K % KP == 0 && NCP * kPfBlock == kPfPairs * CPR && NS >= WD, "pass and slab shapes");
     __shared__ __attribute__((aligned(16))) uint16_t xs[kPfPairs * KP];
