@@ -303,6 +303,7 @@ __global__ __launch_bounds__(kP8Threads) void k_prefill8(const uint8_t* __restri
     // slot cannot alias the reads of another and leaves them outstanding (with
     // one array indexed by a run-time slot it waits for every copy before any
     // LDS read).
+    static_assert(kP8Slots == 3, "the slot objects below and the loop's unroll");
     __shared__ __attribute__((aligned(16))) uint16_t x0[XW], x1[XW], x2[XW];
     __shared__ __attribute__((aligned(16))) uint8_t w0[WB], w1[WB], w2[WB];
     __shared__ __attribute__((aligned(16))) uint8_t s0[SB], s1[SB], s2[SB];
