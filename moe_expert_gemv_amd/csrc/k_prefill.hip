@@ -401,19 +401,27 @@ __global__ __launch_bounds__(kP8Threads) void k_prefill8(const uint8_t* __restri
             cv[nb] = *reinterpret_cast<const u32x2*>(&wb[r * kP8RowBytes + wk * 32 + 8 * lg]);
             sv[nb] = sb[r * 8 + wk * 4 + lg];
         }
+        u32x4 aa[2][MB];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            u32x4 bfr[NB];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) bfr[nb] = decode8_scaled(cv[nb][s2], e4m3_to_f32<0>(sv[nb]));
             const int c = wk * 8 + 2 * lg + s2;  // k = stage + 64 wk + 16 lg + 8 s2
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = 16 * mb + lr;
-                const u32x4 a = *reinterpret_cast<const u32x4*>(&xb[8 * (row * CPR + (c ^ (row & 15)))]);
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32_bf16(a, bfr[nb], acc[mb][nb]);
+                aa[s2][mb] = *reinterpret_cast<const u32x4*>(&xb[8 * (row * CPR + (c ^ (row & 15)))]);
             }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const u32x4* a = aa[s2];
+            u32x4 bfr[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) bfr[nb] = decode8_scaled(cv[nb][s2], e4m3_to_f32<0>(sv[nb]));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32_bf16(a[mb], bfr[nb], acc[mb][nb]);
         }
     };
 
