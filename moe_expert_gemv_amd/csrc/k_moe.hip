@@ -7,9 +7,10 @@
 // (bw24 README, CUDA-graph decode: a few bytes of host traffic per token).
 // A layer is two launches on one stream:
 //   1. gate/up: the routing (moe_forward: one wave per token, from the logits;
-//      moe_gemv_grouped: ids given) and the expert-major CSR are built inside
-//      every workgroup, in LDS, then the grouped gate/up GEMV + SwiGLU; the
-//      first workgroup publishes routing and CSR in the workspace;
+//      moe_gemv_grouped: ids given) and the expert-major grouping are done
+//      inside every workgroup (a CSR in LDS, or for two to four tokens
+//      ballots over the routed ids), then the grouped gate/up GEMV + SwiGLU;
+//      the first workgroup publishes routing and CSR in the workspace;
 //   2. down: the grouped down GEMV, then the weighted sum of the routed
 //      outputs in slot order plus the shared expert, inside the workgroup
 //      through LDS (no synchronisation between workgroups).
@@ -25,6 +26,7 @@
 #include "qg_gemv_core.hpp"
 #include "qg_internal.hpp"
 #include "qg_layout.hpp"
+#include "qg_mfma.hpp"
 
 namespace qg {
 
@@ -198,7 +200,7 @@ __device__ void build_csr(const int32_t* __restrict__ ids, int t, int k, int E, 
     const int p = int(threadIdx.x);
     const int e = p < P ? min(max(ids[p], 0), E - 1) : 0x7fffffff;  // padding sorts after every expert
     if (p < P4) s_e[p] = e;
-    __syncthreads();
+    lds_barrier();
     int less = 0, before = 0;  // pairs of a smaller expert; earlier pairs of the same expert
     if (p < P) {
 #pragma unroll 4
@@ -214,7 +216,7 @@ __device__ void build_csr(const int32_t* __restrict__ ids, int t, int k, int E, 
     }
     const bool first = p < P && before == 0;  // the expert's first pair
     if (p < P4) s_first[p] = first ? 1 : 0;
-    const int U = __syncthreads_count(first);  // active experts
+    lds_barrier();
     if (first) {
         int g = 0;  // active experts below e
 #pragma unroll 4
@@ -227,6 +229,12 @@ __device__ void build_csr(const int32_t* __restrict__ ids, int t, int k, int E, 
         c.offsets[g] = less;
     }
     if (p == 0) {
+        int U = 0;  // active experts
+#pragma unroll 4
+        for (int q = 0; q < P4; q += 4) {
+            const int4 f = *reinterpret_cast<const int4*>(s_first + q);
+            U += f.x + f.y + f.z + f.w;
+        }
         c.offsets[U] = P;
         if (has_shared) {
             c.experts[U] = E;
@@ -238,7 +246,7 @@ __device__ void build_csr(const int32_t* __restrict__ ids, int t, int k, int E, 
         c.tok[P + p] = p;
         c.slot[P + p] = k;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 struct MoeArgs {
@@ -565,7 +573,7 @@ __device__ __forceinline__ void load_group_w(GroupW<C, R>& b, const uint8_t* con
 }
 
 // Calls f(std::integral_constant<int, n>) for the runtime count n in
-// [1, NMAX], so that f's body is straight-line code for that count.
+// [N, NMAX], so that f's body is straight-line code for that count.
 template <int NMAX, int N = 1, typename F>
 __device__ __forceinline__ void dispatch_count(int n, F&& f) {
     if constexpr (N <= NMAX) {
@@ -597,34 +605,163 @@ __device__ __forceinline__ void nvfp4_token_dot(const GroupW<C, R>& b, const boo
     }
 }
 
+// Routing and CSR of a tile-path call for the down kernel (workspace header),
+// by one wave: lane q < P = t*k (P <= 32) holds pair q's expert in idv, and
+// s_ids[0, P) the same ids unclamped (padding is ignored).  The same CSR as
+// build_csr: active experts ascending, pairs of an expert in (token, slot)
+// order, then the shared expert with every token.  Per lane, bit q of lt / eq
+// marks pairs of a smaller / the same expert.
+__device__ __forceinline__ void publish_csr(int idv, const int* s_ids, int P, int t, int k, int E, int has_shared,
+                                            const MoeWorkspace& ws) {
+    const int lane = lane_id();
+    uint32_t lt = 0, eq = 0;
+#pragma unroll
+    for (int q = 0; q < 32; q += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(s_ids + q);
+        const int e4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = min(max(e4[i], 0), E - 1);
+            const bool ok = q + i < P;
+            lt |= (ok && e < idv) ? 1u << (q + i) : 0u;
+            eq |= (ok && e == idv) ? 1u << (q + i) : 0u;
+        }
+    }
+    const uint32_t earlier = eq & (lane < 32 ? (1u << lane) - 1u : ~0u);  // lanes >= 32 hold no pair
+    const bool first = lane < P && earlier == 0;       // the expert's first pair
+    const uint32_t fmask = uint32_t(__ballot(first));
+    const int less = __popc(lt), rank = less + __popc(earlier), g = __popc(lt & fmask);
+    if (lane < P) {
+        ws.pair_tok[rank] = lane / k;
+        ws.pair_slot[rank] = lane % k;
+        if (first) {
+            ws.experts[g] = idv;
+            ws.offsets[g] = less;
+        }
+    }
+    const int U = __popc(fmask);
+    if (lane == 0) {
+        ws.offsets[U] = P;
+        if (has_shared) {
+            ws.experts[U] = E;
+            ws.offsets[U + 1] = P + t;
+        }
+        *ws.n_groups = U + has_shared;
+    }
+    if (has_shared && lane < t) {
+        ws.pair_tok[P + lane] = lane;
+        ws.pair_slot[P + lane] = k;
+    }
+}
+
 // Gate/up + SwiGLU, tile path.  blockIdx.x = tile of R consecutive packed
 // rows (R/2 a-rows; gate/up rows interleaved), every group; a row of H/32
 // chunks spread over the whole wave (G = 64).  ROUTE as in k_moe_gate_up.
+// No CSR is built here: every wave holds the t*k routed experts one per lane
+// and takes the pairs q = wave, wave + 8, ... that are their expert's first
+// pair (so each active expert has one owner), finding the expert's other
+// pairs and its place in the expert-major order with ballots.  The shared
+// expert needs no routing: its token i goes to wave 7 - i, which requests the
+// shared rows before anything else and computes them while its first routed
+// group is in flight (the barrier before publishes LDS only, so those loads
+// stay outstanding).  GW bounds the routed groups of one wave.
 template <int C, int R, bool ROUTE, int PER, int GW>
 __global__ __launch_bounds__(kTileBlock) void k_moe_gate_up_tile(MoeArgs A, const uint16_t* __restrict__ x,
                                                                  const int32_t* __restrict__ ids_in,
                                                                  const float* __restrict__ logits, int t,
                                                                  MoeWorkspace ws) {
     static_assert(R % 2 == 0, "gate and up rows come in pairs");
-    __shared__ Csr c;
-    __shared__ __align__(16) int s_e[kMaxPairs];
-    __shared__ __align__(16) int s_first[kMaxPairs];
-    __shared__ int s_ids[kMaxTokens * kMaxTopK];
+    __shared__ __align__(16) int s_ids[kMaxTokens * kMaxTopK];
     __shared__ float s_scale[kMaxScaleLds];
     __shared__ __align__(16) uint16_t s_x[kStageBytes / 2];
+    __shared__ uint16_t s_act[kTileMaxPairs][R / 2];
+    __shared__ float s_h[kTileMaxPairs][R];
     const int tid = int(threadIdx.x);
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int H = A.H, I = A.I, E = A.E;
+    const int P = t * A.k;  // routed pairs (<= 32 on this path)
+    const int nchunks = H / 32;
+    bool okc[C];
+    uint32_t jc[C];
+#pragma unroll
+    for (int cc = 0; cc < C; ++cc) {
+        const int j = cc * kWave + lane;
+        okc[cc] = j < nchunks;
+        jc[cc] = okc[cc] ? uint32_t(j) : 0u;
+    }
+    const int row0 = int(blockIdx.x) * R;
+    const int64_t soff = scale_plane_offset(QG_NVFP4, 2 * int64_t(I), H);
+    auto load_rows = [&](GroupW<C, R>& b, int e) {  // this tile's rows of expert e
+        const uint8_t* w = A.gate_up + int64_t(e) * A.gu_stride;
+        const uint8_t* codes[R];
+        const uint8_t* scales[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t row = min(row0 + r, 2 * I - 1);
+            codes[r] = w + row * (H / 2);
+            scales[r] = w + soff + row * (H / 16);
+        }
+        load_group_w<C, R>(b, codes, scales, jc);
+    };
+    // A group's row sums, reduction and SwiGLU, one pair at a time: the
+    // pairs are the set bits of m (bit n: token n / div), at CSR positions
+    // p0, p0 + 1, ...  Results to LDS, stored after the last group (stores
+    // count on the same counter as loads).
+    auto compute = [&](const GroupW<C, R>& b, int e, int p0, uint64_t m, int div) {
+        const float s_t = s_scale[e];
+        for (int p = p0; m; ++p, m &= m - 1) {
+            const int tok = int(__builtin_ctzll(m)) / div;
+            float acc[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = 0.f;
+            nvfp4_token_dot<R, C>(b, okc, jc, s_x + tok * H, acc);
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = group_sum<kWave>(acc[r]) * s_t;
+            // lane r evaluates the SwiGLU of a-row r
+            float gv = 0.f, uv = 0.f;
+#pragma unroll
+            for (int r = 0; r < R / 2; ++r)
+                if (lane == r) {
+                    gv = acc[2 * r];
+                    uv = acc[2 * r + 1];
+                }
+            if (lane < R / 2) {
+                s_act[p][lane] = uint16_t(f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv));
+                s_h[p][2 * lane] = gv;
+                s_h[p][2 * lane + 1] = uv;
+            }
+        }
+    };
+    auto store = [&](int p0, int mg) {  // a group's pairs (its run of the CSR) to the workspace
+        for (int idx = lane; idx < mg * (R / 2); idx += kWave) {
+            const int p = p0 + idx / (R / 2), r = idx % (R / 2);
+            const int row = row0 / 2 + r;
+            if (row < I) {
+                ws.a[int64_t(p) * I + row] = s_act[p][r];
+                if (ws.h) {
+                    ws.h[int64_t(p) * 2 * I + row] = s_h[p][2 * r];
+                    ws.h[int64_t(p) * 2 * I + I + row] = s_h[p][2 * r + 1];
+                }
+            }
+        }
+    };
 
-    // 1. loads: this wave's token logits first, then scales and x into LDS
+    // 0. the shared expert's rows (the waves of its tokens); with two chunks
+    // per lane they are requested after the routing instead, as holding them
+    // through it runs out of registers
+    const int sh_tok = kTileWaves - 1 - wave;
+    const bool own_shared = A.has_shared && sh_tok < t;
+    constexpr bool kEarly = C == 1;
+    GroupW<C, R> gs;
+    if (kEarly && own_shared) load_rows(gs, E);
+    // 1. loads: this wave's token logits, then scales and x into LDS
     float lv[PER];
     if constexpr (ROUTE)
         if (wave < t) route_load<PER>(logits + int64_t(wave) * E, E, lv);
     stage_scales(s_scale, A.gu_scale, E + A.has_shared);
     stage16(reinterpret_cast<u32x4*>(s_x), x, t * H / 8);  // x [t][H]
-    // 2. routing (one wave per token), then the CSR
-    const int32_t* ids = ids_in;
+    // 2. routing (one wave per token)
     if constexpr (ROUTE) {
         if (wave < t) {
             float sv, sw;
@@ -638,118 +775,66 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_gate_up_tile(MoeArgs A, cons
                 }
             }
         }
-        __syncthreads();
-        ids = s_ids;
+    } else {
+        if (tid < P) s_ids[tid] = ids_in[tid];
     }
-    build_csr(ids, t, A.k, E, A.has_shared, c, s_e, s_first);
-    if (blockIdx.x == 0) {
-        const int P = t * (A.k + A.has_shared);
-        if (tid == 0) *ws.n_groups = c.n_groups;
-        for (int i = tid; i < P; i += kTileBlock) {
-            ws.pair_tok[i] = c.tok[i];
-            ws.pair_slot[i] = c.slot[i];
+    lds_barrier();  // x, scales and the routed ids
+    // 3. every wave: pair q's expert in lane q; this wave's groups
+    int idv = -1;
+    if (lane < P) idv = min(max(s_ids[lane], 0), E - 1);
+    uint32_t own = 0;  // bit j: pair wave + 8j is its expert's first pair
+#pragma unroll
+    for (int j = 0; j < GW; ++j) {
+        const int q = wave + kTileWaves * j;
+        if (q < P) {
+            const int e = __builtin_amdgcn_readlane(idv, q);
+            if (__builtin_ctzll(__ballot(idv == e)) == q) own |= 1u << j;
         }
-        for (int i = tid; i < c.n_groups; i += kTileBlock) ws.experts[i] = c.experts[i];
-        for (int i = tid; i <= c.n_groups; i += kTileBlock) ws.offsets[i] = c.offsets[i];
     }
+    if (blockIdx.x == 0 && wave == 0) publish_csr(idv, s_ids, P, t, A.k, E, A.has_shared, ws);
 
-    // 3./4. weight loads and, per group, row sums, reduction and SwiGLU.  The
+    // 4. weight loads and, per group, row sums, reduction and SwiGLU.  The
     // group count is turned into straight-line code (dispatch_count), and a
     // wave keeps kTileDepth groups' loads ahead of the group it computes, so
     // the data of its groups arrives one after another and the decode of
-    // each overlaps the stream of the next (rather than all arriving at the
-    // end).  Results go to LDS and are stored after the last group: stores
-    // count on the same counter as loads.
-    const int ng = c.n_groups;
-    const int nv = min(GW, (ng - wave + kTileWaves - 1) / kTileWaves);  // groups of this wave (uniform)
-    if (nv <= 0) return;
-    const int nchunks = H / 32;
-    bool okc[C];
-    uint32_t jc[C];
-#pragma unroll
-    for (int cc = 0; cc < C; ++cc) {
-        const int j = cc * kWave + lane;
-        okc[cc] = j < nchunks;
-        jc[cc] = okc[cc] ? uint32_t(j) : 0u;
-    }
-    const int row0 = int(blockIdx.x) * R;
-    const int64_t soff = scale_plane_offset(QG_NVFP4, 2 * int64_t(I), H);
-    __shared__ uint16_t s_act[kTileMaxPairs][R / 2];
-    __shared__ float s_h[kTileMaxPairs][R];
+    // each overlaps the stream of the next.
+    const int nv = __popc(own);
     auto run = [&](auto nv_c) {
         constexpr int NV = decltype(nv_c)::value;
-        GroupW<C, R> gw[NV];
-        auto load = [&](int j) {
-            const int e = c.experts[wave + kTileWaves * j];
-            const uint8_t* w = A.gate_up + int64_t(e) * A.gu_stride;
-            const uint8_t* codes[R];
-            const uint8_t* scales[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int64_t row = min(row0 + r, 2 * I - 1);
-                codes[r] = w + row * (H / 2);
-                scales[r] = w + soff + row * (H / 16);
-            }
-            load_group_w<C, R>(gw[j], codes, scales, jc);
-        };
-#pragma unroll
-        for (int j = 0; j < NV && j < kTileDepth; ++j) load(j);
+        constexpr int NA = NV > 0 ? NV : 1;
+        GroupW<C, R> gw[NA];
+        int ge[NA];
+        uint32_t rem = own;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            if (j + kTileDepth < NV) load(j + kTileDepth);
+            ge[j] = __builtin_amdgcn_readlane(idv, wave + kTileWaves * int(__builtin_ctz(rem)));
+            rem &= rem - 1;
+        }
+#pragma unroll
+        for (int j = 0; j < NV && j < kTileDepth; ++j) load_rows(gw[j], ge[j]);
+        if (!kEarly && own_shared) load_rows(gs, E);
+        if (own_shared) compute(gs, E, P + sh_tok, 1ull << sh_tok, 1);
+        int gp[NA], gm[NA];  // each group's first CSR position and pair count
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            if (j + kTileDepth < NV) load_rows(gw[j + kTileDepth], ge[j + kTileDepth]);
             __builtin_amdgcn_sched_barrier(0);
-            const int g = wave + kTileWaves * j;
-            const int e = c.experts[g];
-            const int p0 = c.offsets[g];
-            const int mg = c.offsets[g + 1] - p0;
-            const float s_t = s_scale[e];
-            for (int i = 0; i < mg; ++i) {  // the group's tokens, one at a time
-                const int p = p0 + i;
-                float acc[R];
-#pragma unroll
-                for (int r = 0; r < R; ++r) acc[r] = 0.f;
-                nvfp4_token_dot<R, C>(gw[j], okc, jc, s_x + c.tok[p] * H, acc);
-#pragma unroll
-                for (int r = 0; r < R; ++r) acc[r] = group_sum<kWave>(acc[r]) * s_t;
-                // lane r evaluates the SwiGLU of a-row r
-                float gv = 0.f, uv = 0.f;
-#pragma unroll
-                for (int r = 0; r < R / 2; ++r)
-                    if (lane == r) {
-                        gv = acc[2 * r];
-                        uv = acc[2 * r + 1];
-                    }
-                if (lane < R / 2) {
-                    s_act[p][lane] = uint16_t(f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv));
-                    s_h[p][2 * lane] = gv;
-                    s_h[p][2 * lane + 1] = uv;
-                }
-            }
+            const uint64_t m = __ballot(idv == ge[j]);
+            gp[j] = __popcll(__ballot(lane < P && idv < ge[j]));
+            gm[j] = __popcll(m);
+            compute(gw[j], ge[j], gp[j], m, A.k);
         }
-        // this wave's pairs (its groups' runs of the CSR) to the workspace
+        if (own_shared) store(P + sh_tok, 1);
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int g = wave + kTileWaves * j;
-            const int p0 = c.offsets[g];
-            const int mg = c.offsets[g + 1] - p0;
-            for (int idx = lane; idx < mg * (R / 2); idx += kWave) {
-                const int p = p0 + idx / (R / 2), r = idx % (R / 2);
-                const int row = row0 / 2 + r;
-                if (row < I) {
-                    ws.a[int64_t(p) * I + row] = s_act[p][r];
-                    if (ws.h) {
-                        ws.h[int64_t(p) * 2 * I + row] = s_h[p][2 * r];
-                        ws.h[int64_t(p) * 2 * I + I + row] = s_h[p][2 * r + 1];
-                    }
-                }
-            }
-        }
+        for (int j = 0; j < NV; ++j) store(gp[j], gm[j]);
     };
-    dispatch_count<GW>(nv, run);
+    dispatch_count<GW, 0>(nv, run);
 }
 
 // Down + combine, tile path.  blockIdx.x = tile of (64 / G) * R output rows,
-// every group; the SwiGLU outputs of all pairs are staged in LDS.  The
+// every group; the SwiGLU outputs of all pairs are staged in LDS.  Routed
+// group g goes to wave g % 8, the shared expert's pair of token i to wave
+// 7 - i, which requests the shared rows before the header is read.  The
 // combine is the same fixed-order sum as in k_moe_down.
 template <int G, int C, int R, int GW>
 __global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const float* __restrict__ wts, int t,
@@ -766,6 +851,51 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const f
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int I = A.I, H = A.H;
+    const int grp = lane / G, l = lane % G;
+    const int tile0 = int(blockIdx.x) * kRows;
+    const int nchunks = I / 32;
+    bool okc[C];
+    uint32_t jc[C];
+#pragma unroll
+    for (int cc = 0; cc < C; ++cc) {
+        const int j = cc * G + l;
+        okc[cc] = j < nchunks;
+        jc[cc] = okc[cc] ? uint32_t(j) : 0u;
+    }
+    const int64_t soff = scale_plane_offset(QG_NVFP4, H, I);
+    auto load_rows = [&](GroupW<C, R>& b, int e) {  // this lane group's rows of expert e
+        const uint8_t* w = A.down + int64_t(e) * A.dn_stride;
+        const uint8_t* codes[R];
+        const uint8_t* scales[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t row = min(tile0 + grp * R + r, H - 1);
+            codes[r] = w + row * (I / 2);
+            scales[r] = w + soff + row * (I / 16);
+        }
+        load_group_w<C, R>(b, codes, scales, jc);
+    };
+    auto compute = [&](const GroupW<C, R>& b, int e, int p0, int mg) {  // the group's pairs, one at a time
+        const float s_t = s_scale[e];
+        for (int i = 0; i < mg; ++i) {
+            const int p = p0 + i;
+            float acc[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = 0.f;
+            nvfp4_token_dot<R, C>(b, okc, jc, s_a + p * I, acc);
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = group_sum<G>(acc[r]) * s_t;
+            if (l == 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) s_o[p][grp * R + r] = acc[r];
+            }
+        }
+    };
+
+    const int sh_tok = kTileWaves - 1 - wave;
+    const bool own_shared = A.has_shared && sh_tok < t;
+    GroupW<C, R> gs;
+    if (own_shared) load_rows(gs, A.E);
     // header up to the worst-case group count, scales and a: one round of loads
     const int ng = *ws.n_groups;
     const int P = t * (A.k + A.has_shared);
@@ -780,67 +910,29 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const f
         if (tid < gmax) s_exp[tid] = ee;
         if (tid < P) s_pair[pt][ps] = tid;
     }
-    __syncthreads();
+    lds_barrier();
 
-    const int grp = lane / G, l = lane % G;
-    const int tile0 = int(blockIdx.x) * kRows;
-    const int nv = min(GW, (ng - wave + kTileWaves - 1) / kTileWaves);
+    const int nr = ng - A.has_shared;                                   // routed groups
+    const int nv = min(GW, (nr - wave + kTileWaves - 1) / kTileWaves);  // of this wave (uniform, >= 0)
     // As in the gate/up tile kernel: straight-line code per group count,
     // kTileDepthDn groups' loads in flight ahead of the computed one, and no
     // global store until every weight load has been consumed.
     auto run = [&](auto nv_c) {
         constexpr int NV = decltype(nv_c)::value;
-        const int nchunks = I / 32;
-        bool okc[C];
-        uint32_t jc[C];
+        GroupW<C, R> gw[NV > 0 ? NV : 1];
 #pragma unroll
-        for (int cc = 0; cc < C; ++cc) {
-            const int j = cc * G + l;
-            okc[cc] = j < nchunks;
-            jc[cc] = okc[cc] ? uint32_t(j) : 0u;
-        }
-        const int64_t soff = scale_plane_offset(QG_NVFP4, H, I);
-        GroupW<C, R> gw[NV];
-        auto load = [&](int j) {
-            const int e = s_exp[wave + kTileWaves * j];
-            const uint8_t* w = A.down + int64_t(e) * A.dn_stride;
-            const uint8_t* codes[R];
-            const uint8_t* scales[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int64_t row = min(tile0 + grp * R + r, H - 1);
-                codes[r] = w + row * (I / 2);
-                scales[r] = w + soff + row * (I / 16);
-            }
-            load_group_w<C, R>(gw[j], codes, scales, jc);
-        };
-#pragma unroll
-        for (int j = 0; j < NV && j < kTileDepthDn; ++j) load(j);
+        for (int j = 0; j < NV && j < kTileDepthDn; ++j) load_rows(gw[j], s_exp[wave + kTileWaves * j]);
+        if (own_shared) compute(gs, A.E, s_off[nr] + sh_tok, 1);
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            if (j + kTileDepthDn < NV) load(j + kTileDepthDn);
+            if (j + kTileDepthDn < NV)
+                load_rows(gw[j + kTileDepthDn], s_exp[wave + kTileWaves * (j + kTileDepthDn)]);
             __builtin_amdgcn_sched_barrier(0);
             const int g = wave + kTileWaves * j;
-            const int e = s_exp[g];
-            const int p0 = s_off[g];
-            const int mg = s_off[g + 1] - p0;
-            const float s_t = s_scale[e];
-            for (int i = 0; i < mg; ++i) {  // the group's pairs, one at a time
-                const int p = p0 + i;
-                float acc[R];
-#pragma unroll
-                for (int r = 0; r < R; ++r) acc[r] = 0.f;
-                nvfp4_token_dot<R, C>(gw[j], okc, jc, s_a + p * I, acc);
-#pragma unroll
-                for (int r = 0; r < R; ++r) acc[r] = group_sum<G>(acc[r]) * s_t;
-                if (l == 0) {
-#pragma unroll
-                    for (int r = 0; r < R; ++r) s_o[p][grp * R + r] = acc[r];
-                }
-            }
+            compute(gw[j], s_exp[g], s_off[g], s_off[g + 1] - s_off[g]);
         }
     };
-    if (nv > 0) dispatch_count<GW>(nv, run);
+    dispatch_count<GW, 0>(nv, run);
     __syncthreads();
     // per-pair down outputs to the workspace, then the combine
     for (int idx = tid; idx < P * kRows; idx += kTileBlock) {
@@ -865,18 +957,18 @@ bool moe_tile_go(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const 
     constexpr int RU = 4;  // packed gate/up rows per tile
     constexpr int RD = 2;  // down rows per lane group
     const int ju = A.H / 32, jd = A.I / 32;
-    const int gmax = t * A.k + A.has_shared;
+    const int nrmax = t * A.k;  // routed groups at most
     const int P = t * (A.k + A.has_shared);
     const int cu = chunks_per_lane(ju, 64);
     const bool down16 = lanes_per_row(jd) == 16;
     const int cd = chunks_per_lane(jd, down16 ? 16 : 64);
     // one token: the per-(group, tile) kernels are as fast and need no staging
-    if (t < 2 || t > 4 || gmax > 5 * kTileWaves) return false;
+    if (t < 2 || t > 4 || nrmax > 4 * kTileWaves) return false;
     if (lanes_per_row(ju) != 64 || (cu != 1 && cu != 2) || (cd != 1 && cd != 2)) return false;
     if (int64_t(t) * A.H * 2 > kStageBytes || int64_t(P) * A.I * 2 > kStageBytes) return false;
     if (A.E + A.has_shared > kMaxScaleLds) return false;
-    const bool gw1 = gmax <= 2 * kTileWaves;  // else up to 5 groups per wave
-    if (cu == 2 && !gw1) return false;         // too many registers: the general path
+    const bool gw1 = nrmax <= 2 * kTileWaves;  // else up to 4 routed groups per wave
+    if (cu == 2 && !gw1) return false;          // too many registers: the general path
     const dim3 g1((2 * A.I + RU - 1) / RU);
     auto up = [&](auto cu_c, auto gw_c) {
         constexpr int CU = decltype(cu_c)::value, GWc = decltype(gw_c)::value;
@@ -894,9 +986,9 @@ bool moe_tile_go(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const 
     };
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    using I5 = std::integral_constant<int, 5>;
-    if (cu == 1) gw1 ? up(I1{}, I2{}) : up(I1{}, I5{});
-    else gw1 ? up(I2{}, I2{}) : up(I2{}, I5{});
+    using I4 = std::integral_constant<int, 4>;
+    if (cu == 1) gw1 ? up(I1{}, I2{}) : up(I1{}, I4{});
+    else up(I2{}, I2{});
     err = hipGetLastError();
     if (err != hipSuccess) return true;
     if (logits) w = ws.wts;
@@ -909,11 +1001,11 @@ bool moe_tile_go(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const 
     using I16 = std::integral_constant<int, 16>;
     using I64 = std::integral_constant<int, 64>;
     if (down16) {
-        if (cd == 1) gw1 ? down(I16{}, I1{}, I2{}) : down(I16{}, I1{}, I5{});
-        else gw1 ? down(I16{}, I2{}, I2{}) : down(I16{}, I2{}, I5{});
+        if (cd == 1) gw1 ? down(I16{}, I1{}, I2{}) : down(I16{}, I1{}, I4{});
+        else gw1 ? down(I16{}, I2{}, I2{}) : down(I16{}, I2{}, I4{});
     } else {
-        if (cd == 1) gw1 ? down(I64{}, I1{}, I2{}) : down(I64{}, I1{}, I5{});
-        else gw1 ? down(I64{}, I2{}, I2{}) : down(I64{}, I2{}, I5{});
+        if (cd == 1) gw1 ? down(I64{}, I1{}, I2{}) : down(I64{}, I1{}, I4{});
+        else gw1 ? down(I64{}, I2{}, I2{}) : down(I64{}, I2{}, I4{});
     }
     err = hipGetLastError();
     return true;
