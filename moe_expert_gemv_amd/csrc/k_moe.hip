@@ -521,7 +521,9 @@ constexpr int kTileMaxPairs = 4 * (kMaxTopK + 1);  // pairs of a tile-path call 
 #endif
 // Expert groups whose loads a wave keeps in flight ahead of the group it
 // computes (gate/up, down).  Measured at four tokens on MI355X: one ahead
-// 26.4 us, two 27.7 us, three 27.9 us, all groups at once 28.4 us.
+// 26.4 us, two 27.7 us, three 27.9 us, all groups at once 28.4 us; with the
+// groups taken from ballots, one ahead 22.3 us against gate/up two ahead
+// 23.2 us, down two ahead 22.5 us and four ahead 22.8 us.
 constexpr int kTileDepth = QG_TILE_DEPTH;
 constexpr int kTileDepthDn = QG_TILE_DEPTH_DN;
 constexpr int kStageBytes = 64 * 1024;  // LDS activation staging per workgroup

@@ -164,8 +164,11 @@ def test_moe_small(t, E, k, H, I, shared):
 @pytest.mark.parametrize("t,E,k,H,I,shared", [(2, 16, 4, 4096, 256, True),   # gate/up 2 chunks per lane
                                               (3, 8, 2, 2048, 2048, True),   # down rows over 64 lanes
                                               (2, 8, 2, 2048, 4096, False),  # down 2 chunks per lane
-                                              (4, 64, 8, 2048, 512, True),   # up to 5 groups per wave
-                                              (2, 40, 8, 2048, 512, True)])  # 17 groups
+                                              (4, 64, 8, 2048, 512, True),   # up to 4 routed groups per wave
+                                              (2, 40, 8, 2048, 512, True),   # 17 groups
+                                              (4, 8, 8, 2048, 512, True),    # 8 groups of 4 tokens, one per wave
+                                              (3, 4, 4, 2048, 512, True),    # waves 4-7 own no routed group
+                                              (2, 3, 2, 1024, 256, False)])  # repeated experts, no shared one
 def test_moe_tile_path(t, E, k, H, I, shared):
     """Two to four tokens run the row-tile kernels: every launch shape they
     take, against the oracle."""
@@ -226,7 +229,8 @@ def test_moe_batch_invariance_and_determinism():
 @pytest.mark.parametrize("t,E,k,shared,H,I", [(1, 256, 8, True, 256, 64), (4, 64, 8, True, 256, 64),
                                               (16, 300, 8, False, 256, 64), (3, 8, 2, True, 256, 64),
                                               (4, 128, 8, True, 2048, 512), (2, 300, 8, False, 2048, 256),
-                                              (1, 300, 8, False, 256, 64), (1, 8, 2, True, 256, 64)])
+                                              (1, 300, 8, False, 256, 64), (1, 8, 2, True, 256, 64),
+                                              (4, 8, 8, True, 2048, 512), (3, 4, 4, True, 2048, 512)])
 def test_moe_forward_matches_route_then_grouped(t, E, k, shared, H, I):
     """The fused path (routing inside the gate/up kernel) gives bitwise the
     same ids, weights and outputs as moe_route_topk + moe_gemv_grouped, and
