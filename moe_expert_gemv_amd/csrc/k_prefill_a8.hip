@@ -17,12 +17,18 @@
 // Each 32-element block needs its own scale step per output (both operands
 // have per-block fp16 scales), so the VALU work -- a convert, a multiply and
 // an FMA per output per block -- bounds the kernel well before the matrix
-// cores do.  Tiles: a wave computes 64 tokens x 32 rows (4 x 2 MFMA tiles, so
-// each decoded weight fragment serves four token tiles); a workgroup is four
-// waves on 128 rows sharing the 64 tokens, whose fp32 activation scales are
-// staged in LDS per chunk of 128 blocks, block-major, so that one 16-byte LDS
-// read gives the four tokens of a lane's outputs.
+// cores do.  Tiles: a wave computes 64 tokens x 16 NB rows (4 x NB MFMA
+// tiles, so each decoded weight fragment serves four token tiles); a
+// workgroup is four waves on 64 NB rows sharing the 64 tokens, whose fp32
+// activation scales are staged in LDS block-major, so that one 16-byte LDS
+// read gives the four tokens of a lane's outputs.  NB = 2, or 3 where the
+// NB = 2 grid would not fit in one round of resident workgroups (three per CU
+// either way): at 17408 x 5120 x 512 tokens, 1088 workgroups of 128 rows fill
+// the 768 slots 1.42 times (233.8 us), 728 of 192 rows fit in one round
+// (210.2 us).  The tile does not change any output's arithmetic.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "qg_device.hpp"
 #include "qg_internal.hpp"
@@ -39,15 +45,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMB = 4;                    // 16-token tiles per wave
-constexpr int kNB = 2;                    // 16-row tiles per wave
 constexpr int kTM = 16 * kMB;             // tokens per workgroup
-constexpr int kTN = 16 * kNB * kWaves;    // rows per workgroup
 constexpr int kS = 4;                     // 32-element blocks per stage
 constexpr int kAL = kTM * 2 * kS / kThreads;  // 16-byte activation loads per thread per stage
-constexpr int kBL = kTN * kS / kThreads;      // 16-byte weight loads per thread per stage
 constexpr int kXcds = 8;
-static_assert(kAL * kThreads == kTM * 2 * kS && kBL * kThreads == kTN * kS, "whole loads per thread");
-static_assert(kS == 4 && kTN + kTM <= kThreads, "scale loads: one thread per row or token, two dwords of 2 blocks");
+constexpr int kSlotsPerCu = 3;            // resident workgroups per CU (LDS and VGPRs) for NB = 2 and 3
+template <int NB>
+constexpr int kTN = 16 * NB * kWaves;     // rows per workgroup
+template <int NB>
+constexpr int kBL = kTN<NB> * kS / kThreads;  // 16-byte weight loads per thread per stage
+static_assert(kAL * kThreads == kTM * 2 * kS, "whole activation loads per thread");
 
 // Four Q4_0 codes (bytes 0..15) -> the int8 values q - 8.
 __device__ __forceinline__ uint32_t q4_to_s8(uint32_t q) {
@@ -56,26 +63,34 @@ __device__ __forceinline__ uint32_t q4_to_s8(uint32_t q) {
 }
 
 // One stage of the workgroup's operands in LDS, block-major.
+template <int TN>
 struct Tile {
     uint8_t a[kS][kTM][32];   // activation codes: block, token, 32 bytes
-    uint8_t b[kS][kTN][16];   // weight codes: block, row, the block's 16 bytes
+    uint8_t b[kS][TN][16];    // weight codes: block, row, the block's 16 bytes
     float dx[kS][kTM];        // activation scales (fp32)
-    uint16_t dw[kS][kTN];     // weight scales (fp16 bits; 0 for blocks past k)
+    uint16_t dw[kS][TN];      // weight scales (fp16 bits; 0 for blocks past k)
 };
 
 // The global loads of one stage, held in registers between the load and
 // the LDS store (all 16-byte loads are whole-line reads of contiguous runs).
+template <int BL>
 struct Regs {
     u32x4 a[kAL];
-    u32x4 b[kBL];
+    u32x4 b[BL];
     uint16_t dx[kS];
     uint32_t dw[2];
 };
 
+template <int NB>
 __global__ __launch_bounds__(kThreads) void k_prefill_a8(const uint8_t* __restrict__ w, int64_t soff, int n,
                                                          int k, const int8_t* __restrict__ xq,
                                                          const uint16_t* __restrict__ xd, int m,
                                                          float* __restrict__ y, int m_blocks, int items) {
+    constexpr int kNB = NB, kTN = qg::kTN<NB>, kBL = qg::kBL<NB>;
+    static_assert(kBL * kThreads == kTN * kS, "whole weight loads per thread");
+    static_assert(kS == 4 && kTN + kTM <= kThreads, "scale loads: one thread per row or token, two dwords of 2 blocks");
+    using Tile = qg::Tile<kTN>;
+    using Regs = qg::Regs<kBL>;
     __shared__ Tile tile[2];
 
     // work item -> (row block, token block): each XCD takes a contiguous run
@@ -228,17 +243,28 @@ __global__ __launch_bounds__(kThreads) void k_prefill_a8(const uint8_t* __restri
 
 bool prefill_a8_shape_ok(int64_t n, int64_t k, int64_t m) {
     if (m < 1 || m > (int64_t(1) << 24)) return false;
-    const int64_t items = (m + kTM - 1) / kTM * ((n + kTN - 1) / kTN);
+    const int64_t items = (m + kTM - 1) / kTM * ((n + kTN<2> - 1) / kTN<2>);  // the larger grid of the two tiles
     return items <= (int64_t(1) << 30) && m * k < (int64_t(1) << 40);
 }
 
 hipError_t launch_prefill_a8(const uint8_t* w, int64_t n, int64_t k, const int8_t* xq, const uint16_t* xd,
                              int64_t m, float* y, hipStream_t s) {
     const int m_blocks = int((m + kTM - 1) / kTM);
-    const int items = m_blocks * int((n + kTN - 1) / kTN);
-    const int per_xcd = (items + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL(k_prefill_a8, dim3(unsigned(per_xcd * kXcds)), dim3(kThreads), 0, s, w,
-                       scale_plane_offset(QG_Q4_0, n, k), int(n), int(k), xq, xd, int(m), y, m_blocks, items);
+    int cus = 0;
+    if (hipError_t e = device_cu_count(&cus); e != hipSuccess) return e;
+    const int64_t soff = scale_plane_offset(QG_Q4_0, n, k);
+    auto go = [&](auto nb_c) {
+        constexpr int NB = decltype(nb_c)::value;
+        const int items = m_blocks * int((n + kTN<NB> - 1) / kTN<NB>);
+        const int per_xcd = (items + kXcds - 1) / kXcds;
+        hipLaunchKernelGGL(k_prefill_a8<NB>, dim3(unsigned(per_xcd * kXcds)), dim3(kThreads), 0, s, w, soff, int(n),
+                           int(k), xq, xd, int(m), y, m_blocks, items);
+    };
+    // 128-row tiles, or 192-row ones where the former need a second round
+    if (int64_t(m_blocks) * ((n + kTN<2> - 1) / kTN<2>) > int64_t(kSlotsPerCu) * cus)
+        go(std::integral_constant<int, 3>{});
+    else
+        go(std::integral_constant<int, 2>{});
     return hipGetLastError();
 }
 

@@ -69,6 +69,25 @@ def test_tokens_are_independent():
         assert np.array_equal(run_pa8(w, q1, d1).view(np.uint32), y[lo:hi].view(np.uint32))
 
 
+def test_192_row_tile_matches_oracle_and_128_row_tile():
+    """A grid of 128-row tiles that would need more than one round of
+    resident workgroups (here 97 token blocks x 8 row blocks) runs on 192-row
+    tiles: every output against the oracle (ragged rows, tokens and k stage),
+    and token slices (128-row tiles) bitwise equal."""
+    require_gpu()
+    g = synth.rng(53)
+    n, k, m = 1000, 160, 6200
+    w = synth.q4_0_weights(g, n, k)
+    x = synth.x_f32(g, m, k)
+    xq, xd, _ = quantize_gpu(x)
+    y = run_pa8(w, xq, xd)
+    rq, rd, _ = oracle.quantize_q8_0_act(x)
+    assert_within(y, oracle.gemv_q4_0_a8(w, rq, rd), oracle.gemv_q4_0_a8_abs(w, rq, rd), "prefill_a8 192-row tile")
+    for lo, hi in ((0, 64), (3001, 3130), (6150, 6200)):
+        q1, d1, _ = quantize_gpu(x[lo:hi])
+        assert np.array_equal(run_pa8(w, q1, d1).view(np.uint32), y[lo:hi].view(np.uint32)), (lo, hi)
+
+
 def test_full_size_512_tokens_sampled():
     """27B-class projection [17408 x 5120] over 512 tokens, sampled rows."""
     require_gpu()
