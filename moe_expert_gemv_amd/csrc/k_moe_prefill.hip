@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <type_traits>
 
 #include "qg_device.hpp"
 #include "qg_internal.hpp"
@@ -195,16 +197,23 @@ struct GemmArgs {
     float* o_out;            // plain output [P][n] fp32
 };
 
+// Instances that may run half row blocks: the gate/up GEMMs over K >= 1024.
+// (The down GEMM's many short items leave no thin last round to shorten, and
+// at K = 512 the second code path would cost the gate/up GEMM a third
+// resident workgroup per CU.)
+template <int KS, bool SWIGLU>
+constexpr bool kPfHalf = SWIGLU && KS >= 4;
+
 // One tile of up to kPfPairs pairs of one expert x kPfBN weight rows, over
 // K = 256 * KS.  SWIGLU: activations gathered by token, output a (and h);
 // else activations are the pairs' own rows of a, output o.
 template <int KS, bool SWIGLU>
 __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspace ws,
                                                           const int32_t* __restrict__ tile_off, int n_blocks,
-                                                          int items) {
+                                                          int max_tiles, int xcd_slots) {
     constexpr int K = 2 * KW * KS;          // reduction length
     constexpr int NS = K / KW;              // 128-k weight slabs
-    constexpr int MB = kPfPairs / 16, NB = kPfNB;
+    constexpr int MB = kPfPairs / 16;
     // The tile's activations are gathered in passes of 512 k through the same
     // 32 KB of LDS, so two workgroups share a CU and one's gathers overlap
     // the other's weight stream.
@@ -227,17 +236,31 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
 
-    // work item (XCD-contiguous over the real items, so every XCD gets an
-    // equal share) -> (tile ty, row block); tile -> expert group (largest g
-    // with tile_off[g] <= ty).  The grid is sized for the worst case; the
-    // surplus workgroups come last in launch order and exit.
+    // workgroup -> (tile ty, row block): workgroup b runs on XCD b % 8 as
+    // that XCD's (b / 8)-th; tiles are dealt to the XCDs in turn, last tile
+    // first (the shared expert's full tiles end the CSR, and the longest items
+    // should start first), and an XCD takes every row block of a tile in a
+    // row, so they share its L2.  Where an XCD's items would leave a last
+    // round at most half as full as its xcd_slots resident workgroups (0: never),
+    // its last tiles run as half row blocks (16 rows a wave), so that round
+    // takes about half as long.  tile -> expert group (largest g with
+    // tile_off[g] <= ty).  The grid is sized for the worst case; the surplus
+    // workgroups come last in launch order and exit.
     const int ng = *ws.n_groups;
-    const int real_items = min(tile_off[ng] * n_blocks, items);
-    const int per_xcd = (real_items + kXcds - 1) / kXcds;
-    if (int(blockIdx.x) / kXcds >= per_xcd) return;
-    const int item = int(blockIdx.x) % kXcds * per_xcd + int(blockIdx.x) / kXcds;
-    if (item >= real_items) return;
-    const int ty = item / n_blocks, nblk = item % n_blocks;
+    const int n_tiles = min(tile_off[ng], max_tiles);
+    const int xcd = int(blockIdx.x) % kXcds, xj = int(blockIdx.x) / kXcds;
+    const int tx = n_tiles > xcd ? (n_tiles - xcd + kXcds - 1) / kXcds : 0;  // this XCD's tiles
+    int qh = 0;                                                              // its tiles run as halves
+    if (xcd_slots > 0 && tx * n_blocks > xcd_slots) {
+        const int rem = tx * n_blocks % xcd_slots;
+        if (rem > 0 && 2 * rem <= xcd_slots) qh = min(tx, (rem + n_blocks - 1) / n_blocks);
+    }
+    const int qf = tx - qh;
+    const bool half = xj >= qf * n_blocks;
+    const int q = half ? qf + (xj - qf * n_blocks) / (2 * n_blocks) : xj / n_blocks;
+    const int blk = half ? (xj - qf * n_blocks) % (2 * n_blocks) : xj % n_blocks;
+    if (q >= tx) return;
+    const int ty = n_tiles - 1 - (xcd + kXcds * q);
     int lo = 0, hi = ng - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) / 2;
@@ -248,7 +271,6 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
     const int e = ws.experts[g];
     const int p0 = ws.offsets[g] + (ty - tile_off[g]) * kPfPairs;
     const int np = min(kPfPairs, ws.offsets[g + 1] - p0);  // >= 1
-    const int n0 = nblk * kPfBN + wave * 16 * NB;           // this wave's first weight row
     const uint8_t* w = A.w + int64_t(e) * A.stride;
     const float s_t = A.scale[e];
 
@@ -272,108 +294,120 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
     x_load(0);
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. weight slabs: slab s covers k = 128 s + [0, 128) of this wave's rows
-    const uint8_t* wc[NB];
-    const uint8_t* wsc[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int64_t row = min(n0 + 16 * nb + lr, A.n - 1);
-        wc[nb] = w + row * (K / 2);
-        wsc[nb] = w + A.soff + row * (K / 16);
-    }
-    auto w_load = [&](WStage<NB>& b, int sl) {
-        const int kb = KW * sl + 32 * lg;
-#pragma unroll
+    // 2.-5. with NB 16-row blocks a wave: kPfNB, or 1 for half row blocks
+    auto rows = [&](auto nb_c) {
+        constexpr int NB = decltype(nb_c)::value;
+        const int n0 = blk * (16 * NB * (kPfBlock / 64)) + wave * 16 * NB;  // this wave's first weight row
+        // 2. weight slabs: slab s covers k = 128 s + [0, 128) of this wave's rows
+        const uint8_t* wc[NB];
+        const uint8_t* wsc[NB];
+    #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const u32x4 v = ld16(wc[nb] + kb / 2);  // fragment-shaped: ordinary loads (see k_prefill.hip)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
-            b.s[nb] = ld<uint16_t>(wsc[nb] + kb / 16);
+            const int64_t row = min(n0 + 16 * nb + lr, A.n - 1);
+            wc[nb] = w + row * (K / 2);
+            wsc[nb] = w + A.soff + row * (K / 16);
         }
-    };
-    // one slab right behind the activation loads, the rest once the tile is
-    // published (requested all up front, the weight stream delays the
-    // activation data, which returns in order behind it)
-    WStage<NB> wr[WD];
-    w_load(wr[0], 0);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // 3. publish the activation tile (the loads complete in order, ahead of
-    // the weight loads; the LDS-only barrier leaves those in flight)
-    x_store();
-    lds_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 1; j < WD; ++j) w_load(wr[j], j);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // 4. one MFMA chain per output over the slabs in order
-    floatx4 acc[MB][NB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int sl = 0; sl < NS; ++sl) {
-        if (NP > 1 && sl > 0 && sl % SPP == 0) {
-            // next pass: every wave is done with the previous part of the
-            // tile; gather the next part into the same space
-            __builtin_amdgcn_sched_barrier(0);
-            x_load(sl / SPP);
-            lds_barrier();
-            x_store();
-            lds_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const WStage<NB> cur = wr[sl % WD];
-        if (sl + WD < NS) w_load(wr[sl % WD], sl + WD);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            u32x4 bfr[NB];
-#pragma unroll
+        auto w_load = [&](WStage<NB>& b, int sl) {
+            const int kb = KW * sl + 32 * lg;
+    #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const float sc = (q < 2) ? e4m3_to_f32<0>(cur.s[nb]) : e4m3_to_f32<1>(cur.s[nb]);
-                bfr[nb] = decode8_scaled(cur.c[nb][q], sc);
+                const u32x4 v = ld16(wc[nb] + kb / 2);  // fragment-shaped: ordinary loads (see k_prefill.hip)
+    #pragma unroll
+                for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
+                b.s[nb] = ld<uint16_t>(wsc[nb] + kb / 16);
             }
-            const int c = 16 * (sl % SPP) + 4 * lg + q;  // chunk within the pass
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int row = 16 * mb + lr;
-                const u32x4 a = *reinterpret_cast<const u32x4*>(&xs[8 * (row * CPR + (c ^ (row & 15)))]);
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32_bf16(a, bfr[nb], acc[mb][nb]);
-            }
-        }
-    }
+        };
+        // one slab right behind the activation loads, the rest once the tile is
+        // published (requested all up front, the weight stream delays the
+        // activation data, which returns in order behind it)
+        WStage<NB> wr[WD];
+        w_load(wr[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
 
-    // 5. epilogue, per wave: tensor scale, then SwiGLU or the plain output
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float sum = acc[mb][nb][v] * s_t;
-                const int row = 16 * mb + 4 * lg + v;  // pair of the tile
-                const int col = n0 + 16 * nb + lr;     // weight row
-                if constexpr (SWIGLU) {
-                    // packed rows 2i (gate) and 2i+1 (up) sit in neighbouring lanes
-                    const float other = __shfl_xor(sum, 1);
-                    if ((lr & 1) == 0 && row < np && col < A.n) {
-                        const int64_t pos = p0 + row;
-                        const int I = A.n / 2, i = col / 2;
-                        const float gv = sum, uv = other;
-                        A.a_out[pos * I + i] = uint16_t(f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv));
-                        if (A.h_out) {
-                            A.h_out[pos * 2 * I + i] = gv;
-                            A.h_out[pos * 2 * I + I + i] = uv;
-                        }
-                    }
-                } else {
-                    if (row < np && col < A.n) A.o_out[int64_t(p0 + row) * A.n + col] = sum;
+        // 3. publish the activation tile (the loads complete in order, ahead of
+        // the weight loads; the LDS-only barrier leaves those in flight)
+        x_store();
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+        for (int j = 1; j < WD; ++j) w_load(wr[j], j);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // 4. one MFMA chain per output over the slabs in order
+        floatx4 acc[MB][NB];
+    #pragma unroll
+        for (int i = 0; i < MB; ++i)
+    #pragma unroll
+            for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+            if (NP > 1 && sl > 0 && sl % SPP == 0) {
+                // next pass: every wave is done with the previous part of the
+                // tile; gather the next part into the same space
+                __builtin_amdgcn_sched_barrier(0);
+                x_load(sl / SPP);
+                lds_barrier();
+                x_store();
+                lds_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const WStage<NB> cur = wr[sl % WD];
+            if (sl + WD < NS) w_load(wr[sl % WD], sl + WD);
+            __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u32x4 bfr[NB];
+    #pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float sc = (q < 2) ? e4m3_to_f32<0>(cur.s[nb]) : e4m3_to_f32<1>(cur.s[nb]);
+                    bfr[nb] = decode8_scaled(cur.c[nb][q], sc);
+                }
+                const int c = 16 * (sl % SPP) + 4 * lg + q;  // chunk within the pass
+    #pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int row = 16 * mb + lr;
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(&xs[8 * (row * CPR + (c ^ (row & 15)))]);
+    #pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32_bf16(a, bfr[nb], acc[mb][nb]);
                 }
             }
+        }
+
+        // 5. epilogue, per wave: tensor scale, then SwiGLU or the plain output
+    #pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+    #pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+    #pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float sum = acc[mb][nb][v] * s_t;
+                    const int row = 16 * mb + 4 * lg + v;  // pair of the tile
+                    const int col = n0 + 16 * nb + lr;     // weight row
+                    if constexpr (SWIGLU) {
+                        // packed rows 2i (gate) and 2i+1 (up) sit in neighbouring lanes
+                        const float other = __shfl_xor(sum, 1);
+                        if ((lr & 1) == 0 && row < np && col < A.n) {
+                            const int64_t pos = p0 + row;
+                            const int I = A.n / 2, i = col / 2;
+                            const float gv = sum, uv = other;
+                            A.a_out[pos * I + i] = uint16_t(f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv));
+                            if (A.h_out) {
+                                A.h_out[pos * 2 * I + i] = gv;
+                                A.h_out[pos * 2 * I + I + i] = uv;
+                            }
+                        }
+                    } else {
+                        if (row < np && col < A.n) A.o_out[int64_t(p0 + row) * A.n + col] = sum;
+                    }
+                }
+    };
+    if constexpr (kPfHalf<KS, SWIGLU>) {
+        if (half) {
+            rows(std::integral_constant<int, 1>{});
+            return;
+        }
+    }
+    rows(std::integral_constant<int, kPfNB>{});
 }
 
 // y[t][h] = sum_s w[t][s] * o[pair (t, s)][h] (slots ascending), + o[pair
@@ -395,10 +429,30 @@ template <int KS, bool SW>
 hipError_t gemm(const GemmArgs& A, const MoeWorkspace& ws, const int32_t* tile_off, int max_tiles,
                 hipStream_t s) {
     const int n_blocks = (A.n + kPfBN - 1) / kPfBN;
-    const int64_t items = int64_t(n_blocks) * max_tiles;
-    const int64_t per_xcd = (items + kXcds - 1) / kXcds;
+    // resident workgroups per XCD of this instance, for the half row blocks
+    // (queried once per device)
+    int xcd_slots = 0;
+    if constexpr (kPfHalf<KS, SW>) {
+        constexpr int kMaxDevices = 64;
+        static std::atomic<int> cache[kMaxDevices];  // 0 = not yet queried
+        int dev = 0;
+        if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+        xcd_slots = dev >= 0 && dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
+        if (xcd_slots == 0) {
+            int cus = 0, per_cu = 0;
+            if (hipError_t e = device_cu_count(&cus); e != hipSuccess) return e;
+            if (hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_mpf_gemm<KS, SW>, kPfBlock, 0);
+                e != hipSuccess)
+                return e;
+            xcd_slots = std::max(1, per_cu * cus / kXcds);
+            if (dev >= 0 && dev < kMaxDevices) cache[dev].store(xcd_slots, std::memory_order_relaxed);
+        }
+    }
+    // whole tiles per XCD, plus room for the half row blocks
+    const int64_t per_xcd = int64_t(n_blocks) * ((max_tiles + kXcds - 1) / kXcds) +
+                            int64_t(n_blocks) * ((xcd_slots / 2 + n_blocks - 1) / n_blocks);
     hipLaunchKernelGGL((k_mpf_gemm<KS, SW>), dim3(unsigned(per_xcd * kXcds)), dim3(kPfBlock), 0, s, A, ws, tile_off,
-                       n_blocks, int(items));
+                       n_blocks, max_tiles, xcd_slots);
     return hipGetLastError();
 }
 

@@ -90,6 +90,21 @@ def test_moe_prefill_tokens_are_independent_and_deterministic():
         assert np.array_equal(ys.view(np.uint32), y[lo:hi].view(np.uint32))
 
 
+def test_moe_prefill_half_row_blocks():
+    """384 tokens over 128 experts (H=1024, K = 1024 for gate/up): on a
+    256-CU part each XCD's gate/up items leave a last round under half full,
+    which runs as half row blocks.  Every output against the oracle, and
+    token slices (other tilings, no half blocks) bitwise equal."""
+    require_gpu()
+    print("[moe prefill half row blocks t=384]", flush=True)
+    L = synth.moe_case(t=384, n_experts=128, top_k=8, hidden=1024, inter=512, has_shared=True, seed=384)
+    layer = Layer(L)
+    y = check_prefill(L, layer)
+    for lo, hi in ((0, 64), (300, 384)):
+        ys, _ = run_prefill(layer, L.x[lo:hi], L.logits[lo:hi])
+        assert np.array_equal(ys.view(np.uint32), y[lo:hi].view(np.uint32)), (lo, hi)
+
+
 def test_moe_prefill_unsupported_shapes():
     require_gpu()
     L = synth.moe_case(t=2, n_experts=4, top_k=2, hidden=256, inter=64, has_shared=False, seed=1)
