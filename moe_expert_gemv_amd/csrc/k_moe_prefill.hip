@@ -118,12 +118,16 @@ __global__ __launch_bounds__(kGroupThreads) void k_mpf_count(const int32_t* __re
     if (threadIdx.x == 0) counts[e] = c;
 }
 
-// Workgroup e < E places expert e's pairs in pair-index order; workgroup E
-// places the shared expert's (if any) and writes the end entries.
+// Workgroup e < E places expert e's pairs in pair-index order and describes
+// its tiles; workgroup E places the shared expert's (if any) and writes the
+// end entries and the tile count.  tile_info[0].x is the tile count, entry
+// 1 + i (expert, first pair, pair count, 0) describes tile i, so that a GEMM
+// workgroup finds its tile with two loads.
 __global__ __launch_bounds__(kGroupThreads) void k_mpf_place(const int32_t* __restrict__ ids, int t, int k, int E,
                                                              int has_shared, const int32_t* __restrict__ counts,
                                                              MoeWorkspace ws, int32_t* __restrict__ tile_off,
-                                                             int32_t* __restrict__ pair_pos) {
+                                                             int32_t* __restrict__ pair_pos,
+                                                             int4* __restrict__ tile_info) {
     __shared__ int s_tmp[kGroupThreads / kWave];
     const int e = int(blockIdx.x), tid = int(threadIdx.x);
     const int pr = t * k;
@@ -138,12 +142,15 @@ __global__ __launch_bounds__(kGroupThreads) void k_mpf_place(const int32_t* __re
     grp = block_sum_i(grp, s_tmp);
     tiles = block_sum_i(tiles, s_tmp);
     if (e < E) {
-        if (counts[e] == 0) return;  // uniform
+        const int c = counts[e];
+        if (c == 0) return;  // uniform
         if (tid == 0) {
             ws.experts[grp] = e;
             ws.offsets[grp] = off;
             tile_off[grp] = tiles;
         }
+        for (int j = tid; j * kPfPairs < c; j += kGroupThreads)
+            tile_info[1 + tiles + j] = int4{e, off + j * kPfPairs, min(kPfPairs, c - j * kPfPairs), 0};
         int base = off;
         for (int i0 = 0; i0 < pr; i0 += kIdsPerPass) {  // uniform trip count
             const int i = i0 + 4 * tid;
@@ -170,6 +177,8 @@ __global__ __launch_bounds__(kGroupThreads) void k_mpf_place(const int32_t* __re
                 ws.offsets[g] = pr;
                 tile_off[g] = tiles;
             }
+            for (int j = tid; j * kPfPairs < t; j += kGroupThreads)
+                tile_info[1 + tiles + j] = int4{E, pr + j * kPfPairs, min(kPfPairs, t - j * kPfPairs), 0};
             for (int tok = tid; tok < t; tok += kGroupThreads) {
                 ws.pair_tok[pr + tok] = tok;
                 ws.pair_slot[pr + tok] = k;
@@ -182,6 +191,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_mpf_place(const int32_t* __re
             ws.offsets[g] = pr + (has_shared ? t : 0);
             tile_off[g] = tiles;
             *ws.n_groups = g;
+            tile_info[0] = int4{tiles, 0, 0, 0};
         }
     }
 }
@@ -209,7 +219,7 @@ constexpr bool kPfHalf = SWIGLU && KS >= 4;
 // else activations are the pairs' own rows of a, output o.
 template <int KS, bool SWIGLU>
 __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspace ws,
-                                                          const int32_t* __restrict__ tile_off, int n_blocks,
+                                                          const int4* __restrict__ tile_info, int n_blocks,
                                                           int max_tiles, int xcd_slots) {
     constexpr int K = 2 * KW * KS;          // reduction length
     constexpr int NS = K / KW;              // 128-k weight slabs
@@ -243,11 +253,10 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
     // row, so they share its L2.  Where an XCD's items would leave a last
     // round at most half as full as its xcd_slots resident workgroups (0: never),
     // its last tiles run as half row blocks (16 rows a wave), so that round
-    // takes about half as long.  tile -> expert group (largest g with
-    // tile_off[g] <= ty).  The grid is sized for the worst case; the surplus
+    // takes about half as long.  The tile's expert and pairs come from the
+    // tile table.  The grid is sized for the worst case; the surplus
     // workgroups come last in launch order and exit.
-    const int ng = *ws.n_groups;
-    const int n_tiles = min(tile_off[ng], max_tiles);
+    const int n_tiles = min(tile_info[0].x, max_tiles);
     const int xcd = int(blockIdx.x) % kXcds, xj = int(blockIdx.x) / kXcds;
     const int tx = n_tiles > xcd ? (n_tiles - xcd + kXcds - 1) / kXcds : 0;  // this XCD's tiles
     int qh = 0;                                                              // its tiles run as halves
@@ -261,16 +270,8 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
     const int blk = half ? (xj - qf * n_blocks) % (2 * n_blocks) : xj % n_blocks;
     if (q >= tx) return;
     const int ty = n_tiles - 1 - (xcd + kXcds * q);
-    int lo = 0, hi = ng - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) / 2;
-        if (tile_off[mid] <= ty) lo = mid;
-        else hi = mid - 1;
-    }
-    const int g = lo;
-    const int e = ws.experts[g];
-    const int p0 = ws.offsets[g] + (ty - tile_off[g]) * kPfPairs;
-    const int np = min(kPfPairs, ws.offsets[g + 1] - p0);  // >= 1
+    const int4 tinfo = tile_info[1 + ty];
+    const int e = tinfo.x, p0 = tinfo.y, np = tinfo.z;  // np >= 1
     const uint8_t* w = A.w + int64_t(e) * A.stride;
     const float s_t = A.scale[e];
 
@@ -426,7 +427,7 @@ __global__ __launch_bounds__(256) void k_mpf_combine(const float* __restrict__ o
 }
 
 template <int KS, bool SW>
-hipError_t gemm(const GemmArgs& A, const MoeWorkspace& ws, const int32_t* tile_off, int max_tiles,
+hipError_t gemm(const GemmArgs& A, const MoeWorkspace& ws, const int4* tile_info, int max_tiles,
                 hipStream_t s) {
     const int n_blocks = (A.n + kPfBN - 1) / kPfBN;
     // resident workgroups per XCD of this instance, for the half row blocks
@@ -451,18 +452,18 @@ hipError_t gemm(const GemmArgs& A, const MoeWorkspace& ws, const int32_t* tile_o
     // whole tiles per XCD, plus room for the half row blocks
     const int64_t per_xcd = int64_t(n_blocks) * ((max_tiles + kXcds - 1) / kXcds) +
                             int64_t(n_blocks) * ((xcd_slots / 2 + n_blocks - 1) / n_blocks);
-    hipLaunchKernelGGL((k_mpf_gemm<KS, SW>), dim3(unsigned(per_xcd * kXcds)), dim3(kPfBlock), 0, s, A, ws, tile_off,
+    hipLaunchKernelGGL((k_mpf_gemm<KS, SW>), dim3(unsigned(per_xcd * kXcds)), dim3(kPfBlock), 0, s, A, ws, tile_info,
                        n_blocks, max_tiles, xcd_slots);
     return hipGetLastError();
 }
 
 template <bool SW>
-hipError_t gemm_k(int64_t K, const GemmArgs& A, const MoeWorkspace& ws, const int32_t* tile_off, int max_tiles,
+hipError_t gemm_k(int64_t K, const GemmArgs& A, const MoeWorkspace& ws, const int4* tile_info, int max_tiles,
                   hipStream_t s) {
     switch (K) {
-        case 512: return gemm<2, SW>(A, ws, tile_off, max_tiles, s);
-        case 1024: return gemm<4, SW>(A, ws, tile_off, max_tiles, s);
-        default: return gemm<8, SW>(A, ws, tile_off, max_tiles, s);
+        case 512: return gemm<2, SW>(A, ws, tile_info, max_tiles, s);
+        case 1024: return gemm<4, SW>(A, ws, tile_info, max_tiles, s);
+        default: return gemm<8, SW>(A, ws, tile_info, max_tiles, s);
     }
 }
 
@@ -471,6 +472,14 @@ hipError_t gemm_k(int64_t K, const GemmArgs& A, const MoeWorkspace& ws, const in
 bool moe_prefill_shape_ok(int64_t hidden, int64_t inter) {
     auto ok = [](int64_t v) { return v == 512 || v == 1024 || v == 2048; };
     return ok(hidden) && ok(inter);
+}
+
+// GEMM tiles of a call, at most: full tiles of all routed pairs, one partial
+// tile per active expert, and the shared expert's.
+static int max_gemm_tiles(int64_t t, int k, int E, int has_shared) {
+    const int64_t pr = t * k;
+    return int((pr + kPfPairs - 1) / kPfPairs + std::min<int64_t>(E, pr) +
+               (has_shared ? (t + kPfPairs - 1) / kPfPairs : 0));
 }
 
 size_t moe_prefill_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, MoePrefillExtra* ex, void* base) {
@@ -485,11 +494,13 @@ size_t moe_prefill_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, Moe
     const size_t o_tiles = take(4 * (P + 2));
     const size_t o_cnt = take(4 * int64_t(d->n_experts));
     const size_t o_pos = take(4 * t * (d->top_k + 1));
+    const size_t o_info = take(16 * (max_gemm_tiles(t, d->top_k, d->n_experts, d->has_shared) + 1));
     if (ex && base) {
         char* b = static_cast<char*>(base);
         ex->tile_off = reinterpret_cast<int32_t*>(b + o_tiles);
         ex->counts = reinterpret_cast<int32_t*>(b + o_cnt);
         ex->pair_pos = reinterpret_cast<int32_t*>(b + o_pos);
+        ex->tile_info = reinterpret_cast<int4*>(b + o_info);
     }
     return off;
 }
@@ -504,16 +515,15 @@ hipError_t launch_moe_prefill(const qg_moe_desc* d, const uint16_t* x, const flo
     hipLaunchKernelGGL(k_mpf_count, dim3(unsigned(E)), dim3(kGroupThreads), 0, s, ws.ids, pr, ex.counts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(k_mpf_place, dim3(unsigned(E + 1)), dim3(kGroupThreads), 0, s, ws.ids, t, k, E, hs,
-                       ex.counts, ws, ex.tile_off, ex.pair_pos);
+                       ex.counts, ws, ex.tile_off, ex.pair_pos, ex.tile_info);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    // tiles: at most one partial tile per active expert (and the shared one)
-    const int max_tiles = (pr + kPfPairs - 1) / kPfPairs + std::min(E, pr) + (hs ? (t + kPfPairs - 1) / kPfPairs : 0);
+    const int max_tiles = max_gemm_tiles(t, k, E, hs);
     GemmArgs gu{static_cast<const uint8_t*>(d->gate_up), d->gate_up_stride,
                 scale_plane_offset(QG_NVFP4, 2 * int64_t(I), H), d->gate_up_scale, 2 * I, x, ws.a, ws.h, nullptr};
-    if ((err = gemm_k<true>(H, gu, ws, ex.tile_off, max_tiles, s)) != hipSuccess) return err;
+    if ((err = gemm_k<true>(H, gu, ws, ex.tile_info, max_tiles, s)) != hipSuccess) return err;
     GemmArgs dn{static_cast<const uint8_t*>(d->down), d->down_stride, scale_plane_offset(QG_NVFP4, int64_t(H), I),
                 d->down_scale, H, ws.a, nullptr, nullptr, ws.o};
-    if ((err = gemm_k<false>(I, dn, ws, ex.tile_off, max_tiles, s)) != hipSuccess) return err;
+    if ((err = gemm_k<false>(I, dn, ws, ex.tile_info, max_tiles, s)) != hipSuccess) return err;
     hipLaunchKernelGGL(k_mpf_combine, dim3(unsigned(t), unsigned((H + 255) / 256)), dim3(256), 0, s, ws.o, ws.wts,
                        ex.pair_pos, k, hs, H, y);
     return hipGetLastError();

@@ -66,6 +66,7 @@ struct MoePrefillExtra {
     int32_t* tile_off;  // [P + 2] first GEMM tile of each group
     int32_t* counts;    // [n_experts] routed pairs per expert
     int32_t* pair_pos;  // [t * (top_k + 1)] CSR position of pair (token, slot)
+    int4* tile_info;    // [1 + max tiles]: the tile count, then (expert, first pair, pairs, 0) per GEMM tile
 };
 bool moe_prefill_shape_ok(int64_t hidden, int64_t inter);
 size_t moe_prefill_layout(const qg_moe_desc* d, int64_t t, MoeWorkspace* ws, MoePrefillExtra* ex, void* base);
