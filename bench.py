@@ -582,7 +582,7 @@ class MoEPrefill(MoE):
     257 experts' weights once."""
 
     sources = ("k_moe_prefill.hip", "k_moe.hip", "qg_mfma.hpp")
-    kernel_re = (r"k_route_topk\b", r"k_mpf_count\b", r"k_mpf_place\b", r"k_mpf_gemm\w*<[^>]*\btrue>",
+    kernel_re = (r"k_route_topk\b", r"k_mpf_place\b", r"k_mpf_gemm\w*<[^>]*\btrue>",
                  r"k_mpf_gemm\w*<[^>]*\bfalse>", r"k_mpf_combine\b")
     routing_samples = 8
 
@@ -590,7 +590,7 @@ class MoEPrefill(MoE):
         super().__init__(t)
         self.name = (f"moe prefill (35B-A3B-like): 256 routed + 1 shared experts, hidden {self.L.hidden}, "
                      f"inter {self.L.inter}, top-8, {t} tokens, routing drawn per step")
-        self.dominant = "moe_prefill: routing, grouping, grouped gate/up + SwiGLU and down GEMMs, combine (6 kernels)"
+        self.dominant = "moe_prefill: routing, grouping, grouped gate/up + SwiGLU and down GEMMs, combine (5 kernels)"
 
     def workspace_bytes(self, desc, t):
         return self.qg.moe_prefill_workspace_bytes(desc, t)

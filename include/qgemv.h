@@ -437,8 +437,8 @@ int moe_forward_noalloc(const qg_moe_desc* d, const uint16_t* x, const float* lo
  * pair_pos[t][top_k + 1] and int32 tiles[T + 1][4] with T = ceil(t * top_k /
  * 32) + min(n_experts, t * top_k) + (has_shared ? ceil(t / 32) : 0): the
  * tile count in tiles[0][0], then per 32-pair GEMM tile its expert, first
- * pair and pair count (each region 256-byte aligned).  Six launches on the
- * stream: routing, pair counts, pair placement, gate/up + SwiGLU, down,
+ * pair and pair count (each region 256-byte aligned).  Five launches on the
+ * stream: routing, pair counting and placement, gate/up + SwiGLU, down,
  * combine. */
 size_t moe_prefill_workspace_bytes(const qg_moe_desc* d, int64_t t);
 int moe_prefill(const qg_moe_desc* d, const uint16_t* x, const float* logits, int64_t t, float* y,

@@ -8,11 +8,11 @@
 // its tokens (MoE feature entry).  Same layer and same results definition as
 // the decode path (k_moe.hip), for any token count:
 //   1. routing: k_route_topk, one wave per token;
-//   2. grouping: k_mpf_count counts each expert's pairs, k_mpf_place writes
-//      the expert-major CSR (active experts ascending, then the shared
-//      expert; inside an expert, pairs in (token, slot) order -- a stable
-//      placement, so the CSR is exactly the decode path's) and the tile table
-//      of the GEMMs (kPfPairs pairs per tile);
+//   2. grouping: k_mpf_place counts each expert's pairs and writes the
+//      expert-major CSR (active experts ascending, then the shared expert;
+//      inside an expert, pairs in (token, slot) order -- a stable placement,
+//      so the CSR is exactly the decode path's) and the tile table of the
+//      GEMMs (kPfPairs pairs per tile);
 //   3. k_mpf_gemm<SWIGLU>: one workgroup per (tile, block of 256 weight
 //      rows): the tile's activation rows are gathered into LDS (in passes of
 //      512 k), the expert's NVFP4 rows decoded straight into MFMA fragments
@@ -46,7 +46,8 @@ constexpr int kPfBN = 16 * kPfNB * (kPfBlock / 64);  // weight rows per GEMM wor
 // run one after another on the same XCD.  Results do not depend on it.
 constexpr int kXcds = 8;
 
-constexpr int kGroupThreads = 256;  // count / place workgroups
+constexpr int kGroupThreads = 256;  // placement workgroups
+constexpr int kPfMaxExperts = 1024;  // routed experts of a prefill call, at most
 constexpr int kIdsPerPass = 4 * kGroupThreads;  // ids a workgroup reads per pass (four per thread)
 
 __device__ __forceinline__ int wave_sum_i(int v) {
@@ -102,38 +103,36 @@ __device__ __forceinline__ int4 ids4(const int32_t* __restrict__ ids, int i, int
     return v;
 }
 
-// counts[e] = number of routed pairs of expert e.  One workgroup per expert;
-// every thread reads four ids per 16-byte load, all loads of a pass at once.
-__global__ __launch_bounds__(kGroupThreads) void k_mpf_count(const int32_t* __restrict__ ids, int pr,
-                                                             int32_t* __restrict__ counts) {
-    __shared__ int s_tmp[kGroupThreads / kWave];
-    const int e = int(blockIdx.x);
-    int c = 0;
-#pragma unroll 4
-    for (int i = 4 * int(threadIdx.x); i < pr; i += kIdsPerPass) {
-        const int4 v = ids4(ids, i, pr);
-        c += int(v.x == e) + int(v.y == e) + int(v.z == e) + int(v.w == e);
-    }
-    c = block_sum_i(c, s_tmp);
-    if (threadIdx.x == 0) counts[e] = c;
-}
-
-// Workgroup e < E places expert e's pairs in pair-index order and describes
-// its tiles; workgroup E places the shared expert's (if any) and writes the
-// end entries and the tile count.  tile_info[0].x is the tile count, entry
-// 1 + i (expert, first pair, pair count, 0) describes tile i, so that a GEMM
-// workgroup finds its tile with two loads.
+// Every workgroup first counts the routed pairs of every expert (an LDS
+// histogram of the t*k ids, four per thread per pass); workgroup e < E then
+// writes counts[e], places expert e's pairs in pair-index order and
+// describes its tiles; workgroup E places the shared expert's (if any) and
+// writes the end entries and the tile count.  tile_info[0].x is the tile
+// count, entry 1 + i (expert, first pair, pair count, 0) describes tile i,
+// so that a GEMM workgroup finds its tile with two loads.
 __global__ __launch_bounds__(kGroupThreads) void k_mpf_place(const int32_t* __restrict__ ids, int t, int k, int E,
-                                                             int has_shared, const int32_t* __restrict__ counts,
+                                                             int has_shared, int32_t* __restrict__ counts,
                                                              MoeWorkspace ws, int32_t* __restrict__ tile_off,
                                                              int32_t* __restrict__ pair_pos,
                                                              int4* __restrict__ tile_info) {
     __shared__ int s_tmp[kGroupThreads / kWave];
+    __shared__ int s_hist[kPfMaxExperts];
     const int e = int(blockIdx.x), tid = int(threadIdx.x);
     const int pr = t * k;
+    for (int j = tid; j < E; j += kGroupThreads) s_hist[j] = 0;
+    __syncthreads();
+#pragma unroll 4
+    for (int i = 4 * tid; i < pr; i += kIdsPerPass) {
+        const int4 v = ids4(ids, i, pr);
+        const int id4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (id4[q] >= 0 && id4[q] < E) atomicAdd(&s_hist[id4[q]], 1);  // padding and stray ids skipped
+    }
+    __syncthreads();
     int off = 0, grp = 0, tiles = 0;  // over the experts before e
     for (int j = tid; j < e; j += kGroupThreads) {
-        const int c = counts[j];
+        const int c = s_hist[j];
         off += c;
         grp += int(c > 0);
         tiles += (c + kPfPairs - 1) / kPfPairs;
@@ -142,7 +141,8 @@ __global__ __launch_bounds__(kGroupThreads) void k_mpf_place(const int32_t* __re
     grp = block_sum_i(grp, s_tmp);
     tiles = block_sum_i(tiles, s_tmp);
     if (e < E) {
-        const int c = counts[e];
+        const int c = s_hist[e];
+        if (tid == 0) counts[e] = c;
         if (c == 0) return;  // uniform
         if (tid == 0) {
             ws.experts[grp] = e;
@@ -412,18 +412,44 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
 }
 
 // y[t][h] = sum_s w[t][s] * o[pair (t, s)][h] (slots ascending), + o[pair
-// (t, shared)][h].
-__global__ __launch_bounds__(256) void k_mpf_combine(const float* __restrict__ o, const float* __restrict__ wts,
-                                                     const int32_t* __restrict__ pair_pos, int k, int has_shared,
-                                                     int H, float* __restrict__ y) {
+// (t, shared)][h].  Four outputs a thread (H is a multiple of 512), each
+// pair row read with 16-byte loads, so a wave reads 1 KB runs; the sum of
+// each output is the same chain as one output a thread.
+constexpr int kCombineThreads = 256;
+constexpr int kPfMaxTopK = 8;  // top_k of a MoE layer, at most
+__global__ __launch_bounds__(kCombineThreads) void k_mpf_combine(const float* __restrict__ o,
+                                                                 const float* __restrict__ wts,
+                                                                 const int32_t* __restrict__ pair_pos, int k,
+                                                                 int has_shared, int H, float* __restrict__ y) {
     const int tok = int(blockIdx.x);
-    const int h = int(blockIdx.y) * 256 + int(threadIdx.x);
+    const int h = 4 * (int(blockIdx.y) * kCombineThreads + int(threadIdx.x));
     if (h >= H) return;
-    float sum = 0.f;
-    for (int s = 0; s < k; ++s)
-        sum = fmaf(wts[int64_t(tok) * k + s], o[int64_t(pair_pos[tok * (k + 1) + s]) * H + h], sum);
-    if (has_shared) sum += o[int64_t(pair_pos[tok * (k + 1) + k]) * H + h];
-    y[int64_t(tok) * H + h] = sum;
+    // every row's load first (slots past k re-read slot k - 1; without a
+    // shared expert its row is slot k - 1 too), then the sums in order
+    const int32_t* pp = pair_pos + int64_t(tok) * (k + 1);
+    floatx4 v[kPfMaxTopK + 1];
+    float w[kPfMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kPfMaxTopK; ++s) {
+        const int sc = min(s, k - 1);
+        v[s] = *reinterpret_cast<const floatx4*>(o + int64_t(pp[sc]) * H + h);
+        w[s] = wts[int64_t(tok) * k + sc];
+    }
+    v[kPfMaxTopK] = *reinterpret_cast<const floatx4*>(o + int64_t(pp[has_shared ? k : k - 1]) * H + h);
+    floatx4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kPfMaxTopK; ++s)
+        if (s < k) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sum[j] = fmaf(w[s], v[s][j], sum[j]);
+        }
+    if (has_shared) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sum[j] += v[kPfMaxTopK][j];
+    }
+    float* yo = y + int64_t(tok) * H + h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) yo[j] = sum[j];
 }
 
 template <int KS, bool SW>
@@ -509,11 +535,8 @@ hipError_t launch_moe_prefill(const qg_moe_desc* d, const uint16_t* x, const flo
                               const MoeWorkspace& ws, const MoePrefillExtra& ex, hipStream_t s) {
     const int E = d->n_experts, k = d->top_k, hs = d->has_shared ? 1 : 0;
     const int H = int(d->hidden), I = int(d->inter);
-    const int pr = t * k;
     hipError_t err = launch_route_topk(logits, t, E, k, ws.ids, ws.wts, s);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_mpf_count, dim3(unsigned(E)), dim3(kGroupThreads), 0, s, ws.ids, pr, ex.counts);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(k_mpf_place, dim3(unsigned(E + 1)), dim3(kGroupThreads), 0, s, ws.ids, t, k, E, hs,
                        ex.counts, ws, ex.tile_off, ex.pair_pos, ex.tile_info);
     if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -524,8 +547,8 @@ hipError_t launch_moe_prefill(const qg_moe_desc* d, const uint16_t* x, const flo
     GemmArgs dn{static_cast<const uint8_t*>(d->down), d->down_stride, scale_plane_offset(QG_NVFP4, int64_t(H), I),
                 d->down_scale, H, ws.a, nullptr, nullptr, ws.o};
     if ((err = gemm_k<false>(I, dn, ws, ex.tile_info, max_tiles, s)) != hipSuccess) return err;
-    hipLaunchKernelGGL(k_mpf_combine, dim3(unsigned(t), unsigned((H + 255) / 256)), dim3(256), 0, s, ws.o, ws.wts,
-                       ex.pair_pos, k, hs, H, y);
+    hipLaunchKernelGGL(k_mpf_combine, dim3(unsigned(t), unsigned((H + 4 * kCombineThreads - 1) / (4 * kCombineThreads))),
+                       dim3(kCombineThreads), 0, s, ws.o, ws.wts, ex.pair_pos, k, hs, H, y);
     return hipGetLastError();
 }
 
