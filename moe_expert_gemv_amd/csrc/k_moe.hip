@@ -281,8 +281,12 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
     const int32_t* ids = ids_in;
     const int n_scales = A.E + A.has_shared;
     const bool scales_in_lds = n_scales <= kMaxScaleLds;
-    if (scales_in_lds)
-        for (int i = tid; i < n_scales; i += kBlock) s_scale[i] = A.gu_scale[i];  // visible after the CSR barrier
+    // The scales go to LDS (visible after the CSR barrier) through the waves
+    // that do not route when there are such, so that a routing wave's first
+    // request is its logits.
+    const int w0 = ROUTE && t < kBlock / kWave ? t : 0;  // first staging wave
+    if (scales_in_lds && tid >= w0 * kWave)
+        for (int i = tid - w0 * kWave; i < n_scales; i += kBlock - w0 * kWave) s_scale[i] = A.gu_scale[i];
     bool csr_done = false;
     if constexpr (ROUTE) {
         const int lane = lane_id();
@@ -757,12 +761,27 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_gate_up_tile(MoeArgs A, cons
     constexpr bool kEarly = C == 1;
     GroupW<C, R> gs;
     if (kEarly && own_shared) load_rows(gs, E);
-    // 1. loads: this wave's token logits, then scales and x into LDS
+    // 1. loads: the routing waves (one per token) their token's logits; the
+    // other waves the scales and x into LDS, so that the routing waits for
+    // its logits only
     float lv[PER];
-    if constexpr (ROUTE)
+    if constexpr (ROUTE) {
         if (wave < t) route_load<PER>(logits + int64_t(wave) * E, E, lv);
-    stage_scales(s_scale, A.gu_scale, E + A.has_shared);
-    stage16(reinterpret_cast<u32x4*>(s_x), x, t * H / 8);  // x [t][H]
+    }
+    const int w0 = ROUTE ? t : 0;  // first staging wave
+    if (wave >= w0) {
+        const int st = tid - w0 * kWave, nst = kTileBlock - w0 * kWave;
+        const int ns = E + A.has_shared, n16 = t * H / 8;  // x [t][H] in 16-byte units
+        for (int i = st; i < ns; i += nst) s_scale[i] = A.gu_scale[i];
+        for (int b = 0; b < n16; b += 4 * nst) {
+            u32x4 v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = ld16(x + 8 * int64_t(min(b + st + q * nst, n16 - 1)));
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (b + st + q * nst < n16) reinterpret_cast<u32x4*>(s_x)[b + st + q * nst] = v[q];
+        }
+    }
     // 2. routing (one wave per token)
     if constexpr (ROUTE) {
         if (wave < t) {
