@@ -535,30 +535,6 @@ constexpr int kStagePerThread = kStageBytes / 16 / kTileBlock;
 constexpr int kScalesPerThread = (kMaxScaleLds + kTileBlock - 1) / kTileBlock;
 static_assert(kMaxTokens * kMaxTopK <= kTileBlock, "build_csr gives each routed pair its own thread");
 
-// Copy n16 16-byte units (n16 >= 1, at most kStagePerThread * kTileBlock)
-// from global memory to LDS: every load is issued (at a clamped, valid index)
-// before the first LDS write, so they are all in flight together.
-__device__ __forceinline__ void stage16(u32x4* __restrict__ dst, const uint16_t* __restrict__ src, int n16) {
-    const int tid = int(threadIdx.x);
-    u32x4 v[kStagePerThread];
-#pragma unroll
-    for (int k = 0; k < kStagePerThread; ++k) v[k] = ld16(src + 8 * int64_t(min(tid + k * kTileBlock, n16 - 1)));
-#pragma unroll
-    for (int k = 0; k < kStagePerThread; ++k)
-        if (tid + k * kTileBlock < n16) dst[tid + k * kTileBlock] = v[k];
-}
-
-// Same for n fp32 scales (1 <= n <= kMaxScaleLds).
-__device__ __forceinline__ void stage_scales(float* __restrict__ dst, const float* __restrict__ src, int n) {
-    const int tid = int(threadIdx.x);
-    float v[kScalesPerThread];
-#pragma unroll
-    for (int k = 0; k < kScalesPerThread; ++k) v[k] = src[min(tid + k * kTileBlock, n - 1)];
-#pragma unroll
-    for (int k = 0; k < kScalesPerThread; ++k)
-        if (tid + k * kTileBlock < n) dst[tid + k * kTileBlock] = v[k];
-}
-
 // One expert group's weights for one wave: R rows x C chunks per lane.
 template <int C, int R>
 struct GroupW {
@@ -917,21 +893,38 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const f
     const bool own_shared = A.has_shared && sh_tok < t;
     GroupW<C, R> gs;
     if (own_shared) load_rows(gs, A.E);
-    // header up to the worst-case group count, scales and a: one round of loads
+    // header up to the worst-case group count, scales and a: one round of
+    // loads.  The header goes to LDS first, so that the waves request their
+    // first groups' rows before the staged scales and a are stored (those
+    // loads were issued earlier and complete before the weights).
     const int ng = *ws.n_groups;
     const int P = t * (A.k + A.has_shared);
     const int gmax = t * A.k + A.has_shared;
+    const int n_sc = A.E + A.has_shared, n16 = P * I / 8;  // scales; a [P][I] in 16-byte units
+    float scv[kScalesPerThread];
+    u32x4 av[kStagePerThread];
     {  // gmax < P < kTileBlock: one entry per thread, loads first
         const int oo = ws.offsets[min(tid, gmax)];
         const int ee = ws.experts[min(tid, gmax - 1)];
         const int pt = ws.pair_tok[min(tid, P - 1)], ps = ws.pair_slot[min(tid, P - 1)];
-        stage_scales(s_scale, A.dn_scale, A.E + A.has_shared);
-        stage16(reinterpret_cast<u32x4*>(s_a), ws.a, P * I / 8);  // a [P][I]
+#pragma unroll
+        for (int q = 0; q < kScalesPerThread; ++q) scv[q] = A.dn_scale[min(tid + q * kTileBlock, n_sc - 1)];
+#pragma unroll
+        for (int q = 0; q < kStagePerThread; ++q) av[q] = ld16(ws.a + 8 * int64_t(min(tid + q * kTileBlock, n16 - 1)));
         if (tid <= gmax) s_off[tid] = oo;
         if (tid < gmax) s_exp[tid] = ee;
         if (tid < P) s_pair[pt][ps] = tid;
     }
     lds_barrier();
+    auto store_staged = [&]() {
+#pragma unroll
+        for (int q = 0; q < kScalesPerThread; ++q)
+            if (tid + q * kTileBlock < n_sc) s_scale[tid + q * kTileBlock] = scv[q];
+#pragma unroll
+        for (int q = 0; q < kStagePerThread; ++q)
+            if (tid + q * kTileBlock < n16) reinterpret_cast<u32x4*>(s_a)[tid + q * kTileBlock] = av[q];
+        lds_barrier();
+    };
 
     const int nr = ng - A.has_shared;                                   // routed groups
     const int nv = min(GW, (nr - wave + kTileWaves - 1) / kTileWaves);  // of this wave (uniform, >= 0)
@@ -943,6 +936,8 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const f
         GroupW<C, R> gw[NV > 0 ? NV : 1];
 #pragma unroll
         for (int j = 0; j < NV && j < kTileDepthDn; ++j) load_rows(gw[j], s_exp[wave + kTileWaves * j]);
+        __builtin_amdgcn_sched_barrier(0);
+        store_staged();
         if (own_shared) compute(gs, A.E, s_off[nr] + sh_tok, 1);
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
