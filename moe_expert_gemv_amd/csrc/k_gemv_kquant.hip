@@ -33,15 +33,18 @@ constexpr uint32_t kIq4T1 = 0xF6EADDCFu;  //  -49,  -35,  -22,  -10
 constexpr uint32_t kIq4T2 = 0x26190D01u;  //    1,   13,   25,   38
 constexpr uint32_t kIq4T3 = 0x71594535u;  //   53,   69,   89,  113
 
-// Four 4-bit indices (one per byte) -> their four codebook bytes.  Byte
-// permutes take selectors 0..7 as byte indices (and other values as
-// constants), so the first permute is right for indices 0..7, the second
-// (index ^ 8) for 8..15, and a third takes byte i from the first or the
-// second by bit 3 of index i (selector i or i + 4).
-__device__ __forceinline__ uint32_t iq4_lookup(uint32_t idx) {
-    const uint32_t lo = __builtin_amdgcn_perm(kIq4T1, kIq4T0, idx);                // entries 0..7
-    const uint32_t hi = __builtin_amdgcn_perm(kIq4T3, kIq4T2, idx ^ 0x08080808u);  // entries 8..15
-    const uint32_t pick = ((idx >> 1) & 0x04040404u) | 0x03020100u;
+// Four 4-bit indices, the low nibbles of the bytes of c -> their four
+// codebook bytes.  Byte permutes take selectors 0..7 as byte indices, so
+// one permute looks bits 0..2 of every index up in entries 0..7 and another
+// in entries 8..15, and a third takes byte i from the first or the second by
+// bit 3 of index i (selector i or i + 4).  The high nibbles: c >> 4.
+__device__ __forceinline__ uint32_t iq4_lookup(uint32_t c) {
+    const uint32_t sel = c & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(kIq4T1, kIq4T0, sel);  // entries 0..7
+    const uint32_t hi = __builtin_amdgcn_perm(kIq4T3, kIq4T2, sel);  // entries 8..15
+    // ((c >> 1) & 0x04040404) | 0x03020100 as one three-input bit operation
+    // (truth table 0xEA: a & b | c)
+    const uint32_t pick = __builtin_amdgcn_bitop3_b32(c >> 1, 0x04040404u, 0x03020100u, 0xEA);
     return __builtin_amdgcn_perm(hi, lo, pick);
 }
 
@@ -86,6 +89,11 @@ template <int FMT>
 __device__ __forceinline__ void kq_codes(const KqRaw& o, uint32_t (&lo)[4], uint32_t (&hi)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+        if constexpr (FMT == QG_IQ4_XS) {
+            lo[q] = iq4_lookup(o.c[q]);
+            hi[q] = iq4_lookup(o.c[q] >> 4);
+            continue;
+        }
         q4_unpack(o.c[q], lo[q], hi[q]);
         if constexpr (FMT == QG_Q5_K) {
             lo[q] |= ((o.h0 >> q) & 0x01010101u) << 4;
@@ -93,9 +101,6 @@ __device__ __forceinline__ void kq_codes(const KqRaw& o, uint32_t (&lo)[4], uint
         } else if constexpr (FMT == QG_Q6_K) {
             lo[q] |= ((o.h0 >> (2 * q)) & 0x03030303u) << 4;
             hi[q] |= ((o.h1 >> (2 * q)) & 0x03030303u) << 4;
-        } else if constexpr (FMT == QG_IQ4_XS) {
-            lo[q] = iq4_lookup(lo[q]);
-            hi[q] = iq4_lookup(hi[q]);
         }
     }
 }
