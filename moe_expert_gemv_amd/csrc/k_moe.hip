@@ -280,57 +280,63 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
     const int tid = int(threadIdx.x);
     const int32_t* ids = ids_in;
     const int n_scales = A.E + A.has_shared;
-    const bool scales_in_lds = n_scales <= kMaxScaleLds;
+    // One routed token: its k experts are distinct, so group k is the shared
+    // expert, with pair k.  Its workgroups need neither the routing nor the
+    // CSR and request their rows at once.
+    const bool shared_only = ROUTE && t == 1 && A.has_shared && int(blockIdx.y) == A.k;
+    const bool scales_in_lds = n_scales <= kMaxScaleLds && !shared_only;
     // The scales go to LDS (visible after the CSR barrier) through the waves
     // that do not route when there are such, so that a routing wave's first
     // request is its logits.
     const int w0 = ROUTE && t < kBlock / kWave ? t : 0;  // first staging wave
     if (scales_in_lds && tid >= w0 * kWave)
         for (int i = tid - w0 * kWave; i < n_scales; i += kBlock - w0 * kWave) s_scale[i] = A.gu_scale[i];
-    bool csr_done = false;
+    bool csr_done = shared_only;
     if constexpr (ROUTE) {
-        const int lane = lane_id();
-        for (int tok = tid / kWave; tok < t; tok += kBlock / kWave) {  // uniform per wave
-            float sv, sw;
-            int si;
-            route_one_token<PER>(logits + int64_t(tok) * A.E, A.E, A.k, sv, si, sw);
-            if (lane < A.k) {
-                s_ids[tok * A.k + lane] = si;
-                if (blockIdx.x == 0 && blockIdx.y == 0) {
-                    ws.ids[tok * A.k + lane] = si;
-                    ws.wts[tok * A.k + lane] = sw;
-                }
-            }
-            if (t == 1) {
-                // One token: its k experts are distinct, so the CSR is their
-                // ascending order, one pair each (what build_csr produces),
-                // written by this wave -- one barrier instead of four.
-                int rank = 0;
-                for (int j = 0; j < A.k; ++j) rank += int(__builtin_amdgcn_readlane(si, j) < si);
+        if (!shared_only) {
+            const int lane = lane_id();
+            for (int tok = tid / kWave; tok < t; tok += kBlock / kWave) {  // uniform per wave
+                float sv, sw;
+                int si;
+                route_one_token<PER>(logits + int64_t(tok) * A.E, A.E, A.k, sv, si, sw);
                 if (lane < A.k) {
-                    c.experts[rank] = si;
-                    c.offsets[rank] = rank;
-                    c.tok[rank] = 0;
-                    c.slot[rank] = lane;
-                }
-                if (lane == 0) {
-                    c.offsets[A.k] = A.k;
-                    if (A.has_shared) {
-                        c.experts[A.k] = A.E;
-                        c.offsets[A.k + 1] = A.k + 1;
-                        c.tok[A.k] = 0;
-                        c.slot[A.k] = A.k;
+                    s_ids[tok * A.k + lane] = si;
+                    if (blockIdx.x == 0 && blockIdx.y == 0) {
+                        ws.ids[tok * A.k + lane] = si;
+                        ws.wts[tok * A.k + lane] = sw;
                     }
-                    c.n_groups = A.k + A.has_shared;
+                }
+                if (t == 1) {
+                    // One token: its k experts are distinct, so the CSR is their
+                    // ascending order, one pair each (what build_csr produces),
+                    // written by this wave -- one barrier instead of four.
+                    int rank = 0;
+                    for (int j = 0; j < A.k; ++j) rank += int(__builtin_amdgcn_readlane(si, j) < si);
+                    if (lane < A.k) {
+                        c.experts[rank] = si;
+                        c.offsets[rank] = rank;
+                        c.tok[rank] = 0;
+                        c.slot[rank] = lane;
+                    }
+                    if (lane == 0) {
+                        c.offsets[A.k] = A.k;
+                        if (A.has_shared) {
+                            c.experts[A.k] = A.E;
+                            c.offsets[A.k + 1] = A.k + 1;
+                            c.tok[A.k] = 0;
+                            c.slot[A.k] = A.k;
+                        }
+                        c.n_groups = A.k + A.has_shared;
+                    }
                 }
             }
+            __syncthreads();
+            ids = s_ids;
+            csr_done = t == 1;
         }
-        __syncthreads();
-        ids = s_ids;
-        csr_done = t == 1;
     }
     if (!csr_done) build_csr(ids, t, A.k, A.E, A.has_shared, c, s_e, s_first);
-    if (blockIdx.x == 0 && blockIdx.y == 0) {
+    if (blockIdx.x == 0 && blockIdx.y == 0) {  // never a shared_only workgroup (k >= 1)
         const int P = t * (A.k + A.has_shared);
         if (tid == 0) *ws.n_groups = c.n_groups;
         for (int i = tid; i < P; i += kBlock) {
@@ -341,10 +347,10 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
         for (int i = tid; i <= c.n_groups; i += kBlock) ws.offsets[i] = c.offsets[i];
     }
     const int g = int(blockIdx.y);
-    if (g >= c.n_groups) return;
-    const int e = c.experts[g];
-    const int p0 = c.offsets[g];
-    const int mg = c.offsets[g + 1] - p0;
+    if (!shared_only && g >= c.n_groups) return;
+    const int e = shared_only ? A.E : c.experts[g];
+    const int p0 = shared_only ? A.k : c.offsets[g];
+    const int mg = shared_only ? 1 : c.offsets[g + 1] - p0;
 
     constexpr int R = 2 * RA;
     constexpr int kGroups = kWave / G;
@@ -370,7 +376,7 @@ __global__ __launch_bounds__(kBlock) void k_moe_gate_up(MoeArgs A, const uint16_
     }
     const uint16_t* xp[MT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) xp[i] = x + int64_t(c.tok[p0 + (i < mg ? i : 0)]) * H;
+    for (int i = 0; i < MT; ++i) xp[i] = x + int64_t(shared_only ? 0 : c.tok[p0 + (i < mg ? i : 0)]) * H;
 
     float acc[R][MT];
 #pragma unroll
