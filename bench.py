@@ -146,6 +146,7 @@ class Workload:
     # at a time until the time budget is used; each slice reports the
     # algorithmic bytes of the step it accounts for.
     cpu_parts = 1
+    has_oracle = True  # False for the chip probes, which have no oracle to time
 
     def cpu_part_desc(self) -> str:
         return f"the oracle on 1/{self.cpu_parts} of the weight rows"
@@ -720,6 +721,7 @@ class ProbeRead(Workload):
     times the 256 MB Infinity Cache), at the workgroups-per-CU count that
     reads fastest here.  At 1 GiB the launch ramp is negligible; at a
     kernel's own byte count it is what a plain read of those bytes costs."""
+    has_oracle = False
     sources = ("k_probe.hip", "qg_mfma.hpp")
     kernel_re = (r"k_probe_read\b",)
     cpu_parts = 1
@@ -750,6 +752,7 @@ class ProbeRead(Workload):
 class ProbeMfma(Workload):
     """Achievable dense bf16 MFMA rate: v_mfma_f32_16x16x32_bf16 with sixteen
     independent accumulators per wave, two waves per SIMD."""
+    has_oracle = False
     sources = ("k_probe.hip", "qg_mfma.hpp")
     kernel_re = (r"k_probe_mfma\b",)
     bound = "mfma"
@@ -1105,7 +1108,7 @@ def main():
                                               else wl.dominant_bytes / t_k / 1e9) / roof["peak"])
 
     cpu = None
-    if not args.no_cpu_baseline and hasattr(wl, "cpu_baseline"):
+    if not args.no_cpu_baseline and wl.has_oracle:
         cores = host_cores()
         print(f"[bench] timing the CPU oracle baseline on {cores} cores", file=sys.stderr, flush=True)
         cpu = wl.cpu_baseline(args.cpu_budget, cores)
