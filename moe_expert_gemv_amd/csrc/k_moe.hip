@@ -519,7 +519,10 @@ __global__ __launch_bounds__(1024) void k_moe_down(MoeArgs A, const float* __res
 // CSR are thus built once per workgroup rather than once per (group, tile),
 // and with one workgroup per CU the grid is resident at once.  Eight waves
 // per workgroup leave each wave up to 256 registers for the weights in
-// flight.
+// flight; the down kernel with one chunk per lane fits in 128 and runs
+// sixteen waves, so that each takes at most two routed groups (t = 4:
+// 20.75 -> 20.45 us per layer; the gate/up kernel spills at sixteen waves
+// and was 3.5 us slower).
 constexpr int kTileBlock = 512;
 constexpr int kTileWaves = kTileBlock / kWave;
 constexpr int kTileMaxPairs = 4 * (kMaxTopK + 1);  // pairs of a tile-path call (t <= 4)
@@ -835,15 +838,18 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_gate_up_tile(MoeArgs A, cons
 }
 
 // Down + combine, tile path.  blockIdx.x = tile of (64 / G) * R output rows,
-// every group; the SwiGLU outputs of all pairs are staged in LDS.  Routed
-// group g goes to wave g % 8, the shared expert's pair of token i to wave
-// 7 - i, which requests the shared rows before the header is read.  The
-// combine is the same fixed-order sum as in k_moe_down.
-template <int G, int C, int R, int GW>
-__global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const float* __restrict__ wts, int t,
+// every group; the SwiGLU outputs of all pairs are staged in LDS.  NW waves:
+// routed group g goes to wave g % NW, the shared expert's pair of token i to
+// wave NW - 1 - i, which requests the shared rows before the header is read.
+// The combine is the same fixed-order sum as in k_moe_down.
+template <int G, int C, int R, int GW, int NW = kTileWaves>
+__global__ __launch_bounds__(NW * kWave) void k_moe_down_tile(MoeArgs A, const float* __restrict__ wts, int t,
                                                               float* __restrict__ y, MoeWorkspace ws) {
     constexpr int kGroups = kWave / G;
     constexpr int kRows = kGroups * R;  // rows per tile
+    constexpr int kNT = NW * kWave;     // threads
+    constexpr int kStPT = kStageBytes / 16 / kNT;
+    constexpr int kScPT = (kMaxScaleLds + kNT - 1) / kNT;
     __shared__ int s_off[kMaxPairs + 1];
     __shared__ int s_exp[kMaxPairs];
     __shared__ int s_pair[kMaxTokens][kMaxTopK + 1];
@@ -895,7 +901,7 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const f
         }
     };
 
-    const int sh_tok = kTileWaves - 1 - wave;
+    const int sh_tok = NW - 1 - wave;
     const bool own_shared = A.has_shared && sh_tok < t;
     GroupW<C, R> gs;
     if (own_shared) load_rows(gs, A.E);
@@ -907,16 +913,16 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const f
     const int P = t * (A.k + A.has_shared);
     const int gmax = t * A.k + A.has_shared;
     const int n_sc = A.E + A.has_shared, n16 = P * I / 8;  // scales; a [P][I] in 16-byte units
-    float scv[kScalesPerThread];
-    u32x4 av[kStagePerThread];
-    {  // gmax < P < kTileBlock: one entry per thread, loads first
+    float scv[kScPT];
+    u32x4 av[kStPT];
+    {  // gmax < P < kNT: one entry per thread, loads first
         const int oo = ws.offsets[min(tid, gmax)];
         const int ee = ws.experts[min(tid, gmax - 1)];
         const int pt = ws.pair_tok[min(tid, P - 1)], ps = ws.pair_slot[min(tid, P - 1)];
 #pragma unroll
-        for (int q = 0; q < kScalesPerThread; ++q) scv[q] = A.dn_scale[min(tid + q * kTileBlock, n_sc - 1)];
+        for (int q = 0; q < kScPT; ++q) scv[q] = A.dn_scale[min(tid + q * kNT, n_sc - 1)];
 #pragma unroll
-        for (int q = 0; q < kStagePerThread; ++q) av[q] = ld16(ws.a + 8 * int64_t(min(tid + q * kTileBlock, n16 - 1)));
+        for (int q = 0; q < kStPT; ++q) av[q] = ld16(ws.a + 8 * int64_t(min(tid + q * kNT, n16 - 1)));
         if (tid <= gmax) s_off[tid] = oo;
         if (tid < gmax) s_exp[tid] = ee;
         if (tid < P) s_pair[pt][ps] = tid;
@@ -924,16 +930,16 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const f
     lds_barrier();
     auto store_staged = [&]() {
 #pragma unroll
-        for (int q = 0; q < kScalesPerThread; ++q)
-            if (tid + q * kTileBlock < n_sc) s_scale[tid + q * kTileBlock] = scv[q];
+        for (int q = 0; q < kScPT; ++q)
+            if (tid + q * kNT < n_sc) s_scale[tid + q * kNT] = scv[q];
 #pragma unroll
-        for (int q = 0; q < kStagePerThread; ++q)
-            if (tid + q * kTileBlock < n16) reinterpret_cast<u32x4*>(s_a)[tid + q * kTileBlock] = av[q];
+        for (int q = 0; q < kStPT; ++q)
+            if (tid + q * kNT < n16) reinterpret_cast<u32x4*>(s_a)[tid + q * kNT] = av[q];
         lds_barrier();
     };
 
     const int nr = ng - A.has_shared;                                   // routed groups
-    const int nv = min(GW, (nr - wave + kTileWaves - 1) / kTileWaves);  // of this wave (uniform, >= 0)
+    const int nv = min(GW, (nr - wave + NW - 1) / NW);  // of this wave (uniform, >= 0)
     // As in the gate/up tile kernel: straight-line code per group count,
     // kTileDepthDn groups' loads in flight ahead of the computed one, and no
     // global store until every weight load has been consumed.
@@ -941,28 +947,28 @@ __global__ __launch_bounds__(kTileBlock) void k_moe_down_tile(MoeArgs A, const f
         constexpr int NV = decltype(nv_c)::value;
         GroupW<C, R> gw[NV > 0 ? NV : 1];
 #pragma unroll
-        for (int j = 0; j < NV && j < kTileDepthDn; ++j) load_rows(gw[j], s_exp[wave + kTileWaves * j]);
+        for (int j = 0; j < NV && j < kTileDepthDn; ++j) load_rows(gw[j], s_exp[wave + NW * j]);
         __builtin_amdgcn_sched_barrier(0);
         store_staged();
         if (own_shared) compute(gs, A.E, s_off[nr] + sh_tok, 1);
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             if (j + kTileDepthDn < NV)
-                load_rows(gw[j + kTileDepthDn], s_exp[wave + kTileWaves * (j + kTileDepthDn)]);
+                load_rows(gw[j + kTileDepthDn], s_exp[wave + NW * (j + kTileDepthDn)]);
             __builtin_amdgcn_sched_barrier(0);
-            const int g = wave + kTileWaves * j;
+            const int g = wave + NW * j;
             compute(gw[j], s_exp[g], s_off[g], s_off[g + 1] - s_off[g]);
         }
     };
     dispatch_count<GW, 0>(nv, run);
     __syncthreads();
     // per-pair down outputs to the workspace, then the combine
-    for (int idx = tid; idx < P * kRows; idx += kTileBlock) {
+    for (int idx = tid; idx < P * kRows; idx += kNT) {
         const int pp = idx / kRows, rr = idx % kRows;
         const int row = tile0 + rr;
         if (row < H) ws.o[int64_t(pp) * H + row] = s_o[pp][rr];
     }
-    for (int idx = tid; idx < t * kRows; idx += kTileBlock) {
+    for (int idx = tid; idx < t * kRows; idx += kNT) {
         const int tt = idx / kRows, rr = idx % kRows;
         const int row = tile0 + rr;
         if (row >= H) continue;
@@ -1018,7 +1024,11 @@ bool moe_tile_go(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const 
         constexpr int GD = decltype(g_c)::value, CD = decltype(cd_c)::value, GWc = decltype(gw_c)::value;
         constexpr int kRowsDown = (kWave / GD) * RD;
         const dim3 g2((A.H + kRowsDown - 1) / kRowsDown);
-        hipLaunchKernelGGL((k_moe_down_tile<GD, CD, RD, GWc>), g2, dim3(kTileBlock), 0, s, A, w, t, y, ws);
+        if constexpr (CD == 1)  // sixteen waves: at most two routed groups each
+            hipLaunchKernelGGL((k_moe_down_tile<GD, CD, RD, 2, 2 * kTileWaves>), g2, dim3(2 * kTileBlock), 0, s, A, w,
+                               t, y, ws);
+        else
+            hipLaunchKernelGGL((k_moe_down_tile<GD, CD, RD, GWc>), g2, dim3(kTileBlock), 0, s, A, w, t, y, ws);
     };
     using I16 = std::integral_constant<int, 16>;
     using I64 = std::integral_constant<int, 64>;
@@ -1064,7 +1074,8 @@ hipError_t moe_go(const MoeArgs& A, const uint16_t* x, const int32_t* ids, const
         if (t == 1 && A.k <= kMaxTopK && A.E + A.has_shared <= kMaxScaleLds) {
             constexpr int kRowsTile = (kWave / 16) * 2;
             const dim3 gt((A.H + kRowsTile - 1) / kRowsTile);
-            hipLaunchKernelGGL((k_moe_down_tile<16, 1, 2, 2>), gt, dim3(kTileBlock), 0, s, A, w, t, y, ws);
+            hipLaunchKernelGGL((k_moe_down_tile<16, 1, 2, 2, 2 * kTileWaves>), gt, dim3(2 * kTileBlock), 0, s, A, w, t,
+                               y, ws);
             return hipGetLastError();
         }
     }
