@@ -153,7 +153,8 @@ def check_moe(L: synth.MoELayer, layer: Layer, t: int):
 
 @pytest.mark.parametrize("t,E,k,H,I,shared", [(1, 4, 2, 64, 32, True), (3, 8, 3, 96, 64, False),
                                               (4, 16, 8, 512, 128, True), (16, 32, 8, 256, 64, True),
-                                              (2, 6, 6, 2048, 512, True), (5, 64, 4, 2080, 96, False)])
+                                              (2, 6, 6, 2048, 512, True), (5, 64, 4, 2080, 96, False),
+                                              (1, 16, 4, 2080, 96, True)])
 def test_moe_small(t, E, k, H, I, shared):
     require_gpu()
     print(f"[moe t={t} E={E} k={k} H={H} I={I} shared={shared}]", flush=True)
@@ -230,7 +231,8 @@ def test_moe_batch_invariance_and_determinism():
                                               (16, 300, 8, False, 256, 64), (3, 8, 2, True, 256, 64),
                                               (4, 128, 8, True, 2048, 512), (2, 300, 8, False, 2048, 256),
                                               (1, 300, 8, False, 256, 64), (1, 8, 2, True, 256, 64),
-                                              (4, 8, 8, True, 2048, 512), (3, 4, 4, True, 2048, 512)])
+                                              (4, 8, 8, True, 2048, 512), (3, 4, 4, True, 2048, 512),
+                                              (1, 64, 1, True, 2080, 96), (1, 16, 4, True, 2080, 96)])
 def test_moe_forward_matches_route_then_grouped(t, E, k, shared, H, I):
     """The fused path (routing inside the gate/up kernel) gives bitwise the
     same ids, weights and outputs as moe_route_topk + moe_gemv_grouped, and
