@@ -240,6 +240,14 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
     static_assert(CPR >= 16 && (CPR & (CPR - 1)) == 0, "rows of a power-of-two count of 16 chunks");
     static_assert(K % KP == 0 && NCP * kPfBlock == kPfPairs * CPR && NS >= WD, "pass and slab shapes");
     __shared__ __attribute__((aligned(16))) uint16_t xs[kPfPairs * KP];
+    // The item's weight scales: its rows are consecutive, so their scales are
+    // one contiguous run of the scale plane, staged in LDS with the first
+    // activation pass (rows padded by 16 bytes, so that the 16 rows of an MFMA
+    // step spread over the banks) instead of one 2-byte load per slab.
+    constexpr int SR = K / 16 + 16;                 // LDS bytes per row of scales
+    constexpr int NSC = kPfBN * (K / 16) / 16 / kPfBlock;  // 16-byte pieces per thread
+    static_assert(NSC >= 1 && NSC * 16 * kPfBlock == kPfBN * (K / 16), "scale run shape");
+    __shared__ __attribute__((aligned(16))) uint8_t ss[kPfBN * SR];
 
     const int tid = int(threadIdx.x);
     const int lane = tid & 63;
@@ -293,6 +301,24 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
             *reinterpret_cast<u32x4*>(&xs[8 * ((wave + 8 * i) * kWave + lane)]) = xr[i];
     };
     x_load(0);
+    const int item_rows = half ? kPfBN / 2 : kPfBN;
+    const int row0 = blk * item_rows;  // the item's first weight row
+    u32x4 sr[NSC];
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+        const int j = i * kPfBlock + tid;            // 16-byte piece of the run
+        const int r = j / (K / 256), o = 16 * (j % (K / 256));
+        const bool ok = r < item_rows && row0 + r < A.n;
+        sr[i] = ok ? ld16(w + A.soff + int64_t(row0 + r) * (K / 16) + o) : u32x4{0u, 0u, 0u, 0u};
+    }
+    auto sc_store = [&]() {
+#pragma unroll
+        for (int i = 0; i < NSC; ++i) {
+            const int j = i * kPfBlock + tid;
+            const int r = j / (K / 256), o = 16 * (j % (K / 256));
+            *reinterpret_cast<u32x4*>(&ss[r * SR + o]) = sr[i];
+        }
+    };
     __builtin_amdgcn_sched_barrier(0);
 
     // 2.-5. with NB 16-row blocks a wave: kPfNB, or 1 for half row blocks
@@ -301,21 +327,18 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
         const int n0 = blk * (16 * NB * (kPfBlock / 64)) + wave * 16 * NB;  // this wave's first weight row
         // 2. weight slabs: slab s covers k = 128 s + [0, 128) of this wave's rows
         const uint8_t* wc[NB];
-        const uint8_t* wsc[NB];
     #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int64_t row = min(n0 + 16 * nb + lr, A.n - 1);
             wc[nb] = w + row * (K / 2);
-            wsc[nb] = w + A.soff + row * (K / 16);
         }
-        auto w_load = [&](WStage<NB>& b, int sl) {
+        auto w_load = [&](WStage<NB>& b, int sl) {  // codes only: the scales are in LDS
             const int kb = KW * sl + 32 * lg;
     #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const u32x4 v = ld16(wc[nb] + kb / 2);  // fragment-shaped: ordinary loads (see k_prefill.hip)
     #pragma unroll
                 for (int q = 0; q < 4; ++q) b.c[nb][q] = v[q];
-                b.s[nb] = ld<uint16_t>(wsc[nb] + kb / 16);
             }
         };
         // one slab right behind the activation loads, the rest once the tile is
@@ -328,6 +351,7 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
         // 3. publish the activation tile (the loads complete in order, ahead of
         // the weight loads; the LDS-only barrier leaves those in flight)
         x_store();
+        sc_store();
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
     #pragma unroll
@@ -355,12 +379,17 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
             const WStage<NB> cur = wr[sl % WD];
             if (sl + WD < NS) w_load(wr[sl % WD], sl + WD);
             __builtin_amdgcn_sched_barrier(0);
+            uint32_t scv[NB];  // this slab's two scale bytes of each row block
+    #pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                scv[nb] = *reinterpret_cast<const uint16_t*>(
+                    &ss[(wave * 16 * NB + 16 * nb + lr) * SR + (KW * sl + 32 * lg) / 16]);
     #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 u32x4 bfr[NB];
     #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    const float sc = (q < 2) ? e4m3_to_f32<0>(cur.s[nb]) : e4m3_to_f32<1>(cur.s[nb]);
+                    const float sc = (q < 2) ? e4m3_to_f32<0>(scv[nb]) : e4m3_to_f32<1>(scv[nb]);
                     bfr[nb] = decode8_scaled(cur.c[nb][q], sc);
                 }
                 const int c = 16 * (sl % SPP) + 4 * lg + q;  // chunk within the pass
