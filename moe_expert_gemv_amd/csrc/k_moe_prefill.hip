@@ -283,17 +283,22 @@ __global__ __launch_bounds__(kPfBlock, 4) void k_mpf_gemm(GemmArgs A, MoeWorkspa
     const uint8_t* w = A.w + int64_t(e) * A.stride;
     const float s_t = A.scale[e];
 
-    // 1. activation rows into registers (rows past np repeat the last pair)
+    // 1. activation rows into registers (rows past np repeat the last pair).
+    // Each chunk's source (row and offset) is the same in every pass: found
+    // once, so that a later pass's gather does not wait for the pair table.
     u32x4 xr[NCP];
+    const uint16_t* xsrc[NCP];
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+        const int p = (wave + 8 * i) * kWave + lane;
+        const int row = p / CPR, c = (p % CPR) ^ (row & 15);
+        const int pos = p0 + min(row, np - 1);
+        const int srow = SWIGLU ? ws.pair_tok[pos] : pos;
+        xsrc[i] = A.src + int64_t(srow) * K + 8 * c;
+    }
     auto x_load = [&](int pass) {
 #pragma unroll
-        for (int i = 0; i < NCP; ++i) {
-            const int p = (wave + 8 * i) * kWave + lane;
-            const int row = p / CPR, c = (p % CPR) ^ (row & 15);
-            const int pos = p0 + min(row, np - 1);
-            const int srow = SWIGLU ? ws.pair_tok[pos] : pos;
-            xr[i] = ld16(A.src + int64_t(srow) * K + pass * KP + 8 * c);
-        }
+        for (int i = 0; i < NCP; ++i) xr[i] = ld16(xsrc[i] + pass * KP);
     };
     auto x_store = [&]() {
 #pragma unroll
