@@ -540,8 +540,6 @@ constexpr int kTileMaxPairs = 4 * (kMaxTopK + 1);  // pairs of a tile-path call 
 constexpr int kTileDepth = QG_TILE_DEPTH;
 constexpr int kTileDepthDn = QG_TILE_DEPTH_DN;
 constexpr int kStageBytes = 64 * 1024;  // LDS activation staging per workgroup
-constexpr int kStagePerThread = kStageBytes / 16 / kTileBlock;
-constexpr int kScalesPerThread = (kMaxScaleLds + kTileBlock - 1) / kTileBlock;
 static_assert(kMaxTokens * kMaxTopK <= kTileBlock, "build_csr gives each routed pair its own thread");
 
 // One expert group's weights for one wave: R rows x C chunks per lane.

@@ -49,6 +49,7 @@ constexpr int kXcds = 8;
 constexpr int kGroupThreads = 256;  // placement workgroups
 constexpr int kPfMaxExperts = 1024;  // routed experts of a prefill call, at most
 constexpr int kIdsPerPass = 4 * kGroupThreads;  // ids a workgroup reads per pass (four per thread)
+constexpr int kKeep = 4;  // passes of ids the placement keeps in registers
 
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
@@ -120,15 +121,22 @@ __global__ __launch_bounds__(kGroupThreads) void k_mpf_place(const int32_t* __re
     const int e = int(blockIdx.x), tid = int(threadIdx.x);
     const int pr = t * k;
     for (int j = tid; j < E; j += kGroupThreads) s_hist[j] = 0;
+    // The ids of the first kKeep passes stay in registers for the placement
+    // below (the same four ids per thread and pass), which then reads only
+    // the passes beyond them again.
+    int4 kept[kKeep];
+#pragma unroll
+    for (int j = 0; j < kKeep; ++j) kept[j] = ids4(ids, 4 * tid + j * kIdsPerPass, pr);
     __syncthreads();
-#pragma unroll 4
-    for (int i = 4 * tid; i < pr; i += kIdsPerPass) {
-        const int4 v = ids4(ids, i, pr);
+    auto count = [&](const int4& v) {
         const int id4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             if (id4[q] >= 0 && id4[q] < E) atomicAdd(&s_hist[id4[q]], 1);  // padding and stray ids skipped
-    }
+    };
+#pragma unroll
+    for (int j = 0; j < kKeep; ++j) count(kept[j]);
+    for (int i = 4 * tid + kKeep * kIdsPerPass; i < pr; i += kIdsPerPass) count(ids4(ids, i, pr));
     __syncthreads();
     int off = 0, grp = 0, tiles = 0;  // over the experts before e
     for (int j = tid; j < e; j += kGroupThreads) {
@@ -152,9 +160,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_mpf_place(const int32_t* __re
         for (int j = tid; j * kPfPairs < c; j += kGroupThreads)
             tile_info[1 + tiles + j] = int4{e, off + j * kPfPairs, min(kPfPairs, c - j * kPfPairs), 0};
         int base = off;
-        for (int i0 = 0; i0 < pr; i0 += kIdsPerPass) {  // uniform trip count
-            const int i = i0 + 4 * tid;
-            const int4 v = ids4(ids, i, pr);
+        auto place = [&](const int4& v, int i) {  // one pass: ids i .. i + 3 of this thread
             const int hit[4] = {int(v.x == e), int(v.y == e), int(v.z == e), int(v.w == e)};
             int total;
             int pos = base + block_exclusive_i(hit[0] + hit[1] + hit[2] + hit[3], s_tmp, &total);
@@ -168,7 +174,12 @@ __global__ __launch_bounds__(kGroupThreads) void k_mpf_place(const int32_t* __re
                     ++pos;
                 }
             base += total;
-        }
+        };
+#pragma unroll
+        for (int j = 0; j < kKeep; ++j)
+            if (j * kIdsPerPass < pr) place(kept[j], 4 * tid + j * kIdsPerPass);  // uniform
+        for (int i0 = kKeep * kIdsPerPass; i0 < pr; i0 += kIdsPerPass)  // uniform trip count
+            place(ids4(ids, i0 + 4 * tid, pr), i0 + 4 * tid);
     } else {
         int g = grp;
         if (has_shared) {
